@@ -1,0 +1,264 @@
+"""Plain, slow, fp64 CPU oracle for the MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) imports, calls or links this module; only the tests, the
+smoke check and the bench's CPU-baseline leg do.  It shares no code, tables or
+constants with the HIP path.
+
+Every function follows a passage of the pages ("Writing a fused MoE operator
+in Ascend C" = the fused-operator article; "MoE routing operator: load
+balancing strategy" = the routing article) and is written for a reader to
+check by eye: numpy fp64 throughout, one library call per step, no blocking,
+fusion or reordering beyond what the passage states.
+
+Readings taken where the pages are silent or ambiguous (each is listed with
+its reason in the design notes):
+  * gating is top-k first, then softmax over the k selected logits (fused
+    article, "MoE computation flow" steps 1-2 and the router kernel's step 3);
+  * ties in the top-k go to the lower expert index, and the k slots are in
+    descending logit order (routing article, local top-k scan: strict ">"
+    keeps the first maximum);
+  * GELU is the tanh form 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
+    (Hendrycks & Gimpel 2016), for every workload;
+  * experts have no biases; the router has an optional bias b_r[E];
+  * dispatch is dropless: every (token, slot) pair is computed (the gather
+    routine has no capacity limit).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+SQRT_2_OVER_PI = math.sqrt(2.0 / math.pi)
+
+
+# --- activation ------------------------------------------------------------
+
+def gelu_tanh(z: np.ndarray) -> np.ndarray:
+    """GELU, tanh approximation, in fp64.
+
+    Fused article, expert kernel step 3: Activation(hidden, GELU) between the
+    two matrix multiplies; the tanh form is the reading taken for "GELU".
+    """
+    z = np.asarray(z, dtype=np.float64)
+    return 0.5 * z * (1.0 + np.tanh(SQRT_2_OVER_PI * (z + 0.044715 * z ** 3)))
+
+
+# --- routing + gating (fused article, section 1; routing article) ----------
+
+def router_logits(x: np.ndarray, w_r: np.ndarray, b_r: np.ndarray | None = None) -> np.ndarray:
+    """logits[T,E] = x[T,H] . W_r[H,E] (+ b_r[E]), fp64.
+
+    Fused article, router kernel step 1 (x x W_router on the matrix unit);
+    routing article: the router is a linear layer W_r producing logits.
+    """
+    l = np.asarray(x, np.float64) @ np.asarray(w_r, np.float64)
+    if b_r is not None:
+        l = l + np.asarray(b_r, np.float64)[None, :]
+    return l
+
+
+def topk_ids(logits: np.ndarray, k: int) -> np.ndarray:
+    """ids[T,k]: the k largest logits per token, in descending order, ties to
+    the lower expert index.
+
+    Fused article, router kernel step 2 (TopK per sample); the tie rule is the
+    routing article's scan, which replaces the running maximum only on a
+    strictly greater value.  np.lexsort with keys (e, -l) is a stable sort by
+    (-l, e): the primary key is the last one.
+    """
+    logits = np.asarray(logits, np.float64)
+    T, E = logits.shape
+    if not 1 <= k <= E:
+        raise ValueError("top_k must be in [1, E]")
+    ids = np.empty((T, k), dtype=np.int64)
+    e_idx = np.arange(E)
+    for t in range(T):
+        order = np.lexsort((e_idx, -logits[t]))
+        ids[t] = order[:k]
+    return ids
+
+
+def gate_weights(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """w[T,k] = softmax over the k selected logits, in slot order.
+
+    Fused article, router kernel step 3: Softmax over the top-k scores only.
+    The max is subtracted first (softmax is invariant to the shift).
+    """
+    sel = np.take_along_axis(np.asarray(logits, np.float64), ids, axis=1)
+    m = sel.max(axis=1, keepdims=True)
+    ex = np.exp(sel - m)
+    return ex / ex.sum(axis=1, keepdims=True)
+
+
+def route(x, w_r, b_r, k: int):
+    """(ids[T,k] int64, w[T,k] fp64, logits[T,E] fp64) for one MoE layer."""
+    l = router_logits(x, w_r, b_r)
+    ids = topk_ids(l, k)
+    return ids, gate_weights(l, ids), l
+
+
+# --- dispatch (fused article, GatherTokensByExpert) -----------------------
+
+def dispatch(ids: np.ndarray, E: int):
+    """Group the (token, slot) pairs by expert, as the gather routine does.
+
+    For each expert e in ascending order, scan tokens b in ascending order and
+    slots k in ascending order, appending (b, k) whenever ids[b,k] == e.  The
+    appended rows of expert e form the contiguous block
+    [offsets[e], offsets[e+1]) of the dispatched order.  np.nonzero on the
+    [T,k] mask returns exactly that (row-major, i.e. b then k) order.
+
+    Returns offsets[E+1], sorted_token[R] (token of each dispatched row),
+    sorted_slot[R] (slot k of each row) and inv_pos[T,k] (dispatched row of
+    each (token, slot)).
+    """
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    sorted_token, sorted_slot = [], []
+    for e in range(E):
+        b, s = np.nonzero(ids == e)
+        sorted_token.append(b)
+        sorted_slot.append(s)
+        offsets[e + 1] = offsets[e] + b.size
+    sorted_token = np.concatenate(sorted_token).astype(np.int64)
+    sorted_slot = np.concatenate(sorted_slot).astype(np.int64)
+    inv_pos = np.empty((T, k), dtype=np.int64)
+    inv_pos[sorted_token, sorted_slot] = np.arange(T * k)
+    return offsets, sorted_token, sorted_slot, inv_pos
+
+
+def gather_rows(x: np.ndarray, sorted_token: np.ndarray) -> np.ndarray:
+    """xp[R,H]: the token rows in dispatched order (the gather's Copy)."""
+    return np.asarray(x, np.float64)[sorted_token]
+
+
+# --- experts (fused article, expert kernel step 3) --------------------------
+
+def expert_ffn_block(x_e: np.ndarray, w1_e: np.ndarray, w2_e: np.ndarray) -> np.ndarray:
+    """y_e = GELU(x_e . W1_e) . W2_e for one expert's rows; no biases.
+
+    First matrix multiply M=rows, N=F, K=H; GELU; second M=rows, N=H, K=F.
+    """
+    h = gelu_tanh(np.asarray(x_e, np.float64) @ np.asarray(w1_e, np.float64))
+    return h @ np.asarray(w2_e, np.float64)
+
+
+def expert_ffn(xp: np.ndarray, offsets: np.ndarray, w1, w2) -> np.ndarray:
+    """yp[R,H]: every dispatched row through its expert's FFN.
+
+    w1/w2 are either [E,H,F]/[E,F,H] arrays or callables e -> [H,F]/[F,H]
+    arrays (so a large layer can be processed one expert at a time).  Experts
+    with no rows are skipped, as the expert kernel skips unselected experts.
+    """
+    xp = np.asarray(xp, np.float64)
+    E = len(offsets) - 1
+    H = xp.shape[1]
+    yp = np.zeros((xp.shape[0], _out_width(w2, H)), dtype=np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        yp[a:b] = expert_ffn_block(xp[a:b], _get(w1, e), _get(w2, e))
+    return yp
+
+
+def combine(yp: np.ndarray, inv_pos: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y[T,H] = sum over slots j of w[t,j] * yp[inv_pos[t,j]].
+
+    Fused article, ScatterWithWeights: every dispatched row is scaled by its
+    gate weight and accumulated (not overwritten) into its token's output.
+    """
+    yp = np.asarray(yp, np.float64)
+    T, k = inv_pos.shape
+    y = np.zeros((T, yp.shape[1]), dtype=np.float64)
+    for j in range(k):
+        y += np.asarray(w, np.float64)[:, j:j + 1] * yp[inv_pos[:, j]]
+    return y
+
+
+# --- the whole layer --------------------------------------------------------
+
+def forward(x, w_r, b_r, w1, w2, k: int, ids=None, w=None):
+    """One MoE layer forward, as the fused article's flow states it.
+
+    Routing (TopK of x.W_r), gating (softmax of the k scores), then for each
+    expert: gather its tokens, skip it if it has none, run GELU(x_e W1) W2,
+    and scatter the rows back into y weighted by their gate weights, with "+=".
+
+    ids/w may be given to drive the expert and combine steps with a chosen
+    routing (used when a near-tie lets two routings both be correct); by
+    default they are the oracle's own.
+    Returns dict(y, ids, w, logits).
+    """
+    x = np.asarray(x, np.float64)
+    logits = router_logits(x, w_r, b_r)
+    if ids is None:
+        ids = topk_ids(logits, k)
+    if w is None:
+        w = gate_weights(logits, ids)
+    E = np.asarray(w_r).shape[1]
+    T = x.shape[0]
+    y = np.zeros((T, _out_width(w2, x.shape[1])), dtype=np.float64)
+    for e in range(E):
+        b_idx, s_idx = np.nonzero(ids == e)
+        if b_idx.size == 0:
+            continue
+        y_e = expert_ffn_block(x[b_idx], _get(w1, e), _get(w2, e))
+        np.add.at(y, b_idx, w[b_idx, s_idx][:, None] * y_e)
+    return {"y": y, "ids": ids, "w": w, "logits": logits}
+
+
+def forward_tokens(x_rows, ids_rows, w_rows, w1, w2) -> np.ndarray:
+    """y for a chosen subset of tokens, one token at a time: y[t] = sum_j
+    w[t,j] * FFN_{ids[t,j]}(x[t]).  Used to check sampled outputs of a layer
+    too large for the full oracle."""
+    x_rows = np.asarray(x_rows, np.float64)
+    out = np.zeros((x_rows.shape[0], _out_width(w2, x_rows.shape[1])), dtype=np.float64)
+    for i in range(x_rows.shape[0]):
+        for j in range(ids_rows.shape[1]):
+            e = int(ids_rows[i, j])
+            out[i] += float(w_rows[i, j]) * expert_ffn_block(x_rows[i:i + 1], _get(w1, e), _get(w2, e))[0]
+    return out
+
+
+def dense_bruteforce(x, w1, w2, ids, w, E: int) -> np.ndarray:
+    """Independent formulation for tiny shapes: run every expert on every
+    token, then mix with a dense [T,E] gate matrix that is w[t,j] at
+    (t, ids[t,j]) and zero elsewhere."""
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    M = np.zeros((T, E), dtype=np.float64)
+    for t in range(T):
+        for j in range(ids.shape[1]):
+            M[t, ids[t, j]] += w[t, j]
+    y = 0.0
+    for e in range(E):
+        Z = expert_ffn_block(x, _get(w1, e), _get(w2, e))
+        y = y + M[:, e:e + 1] * Z
+    return np.asarray(y)
+
+
+# --- near ties (reading of the "1e-3 relative" acceptance rule) -------------
+
+def boundary_near_tie(logits: np.ndarray, k: int, rel: float = 1e-3) -> np.ndarray:
+    """bool[T]: the k-th and (k+1)-th largest logits differ by less than rel
+    times the larger magnitude, so either expert is a correct k-th choice."""
+    T, E = logits.shape
+    if k >= E:
+        return np.zeros(T, dtype=bool)
+    s = -np.sort(-np.asarray(logits, np.float64), axis=1)
+    a, b = s[:, k - 1], s[:, k]
+    return np.abs(a - b) < rel * np.maximum(np.abs(a), np.abs(b))
+
+
+def _get(w, e):
+    return w(e) if callable(w) else w[e]
+
+
+def _out_width(w2, default):
+    if callable(w2):
+        return _get(w2, 0).shape[1]
+    return np.asarray(w2).shape[2]
