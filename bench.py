@@ -1,0 +1,217 @@
+"""Throughput of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one moe_forward call (route, dispatch, expert FFN, combine) over one
+batch of synthetic, seeded inputs already resident in HBM.  W untimed steps,
+then exactly K steps between two device synchronisations; value is tokens/s
+over those K steps.  A second, equally long region runs the same kernels
+through the stage entry points with HIP events between the stages (on the
+stream the kernels run on) to get each stage's duration; the expert FFN stage
+is two launches of the grouped-GEMM kernel with equal flops, which gives the
+per-launch roofline of the dominant kernel.  The fp64 oracle is timed on the
+host cores on a bounded sample of the same workload.  One JSON line is
+printed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_inputs as mi  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 (vector and matrix)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "MoE layer fwd tokens/s (T=2048,H=4096,E=8,k=2) + % MFMA/HBM roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_bf16", choices=list(mi.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens in the oracle's timed sample (0: per-workload default)")
+    return ap.parse_args()
+
+
+def alg_counts(cfg, ids: np.ndarray):
+    """Algorithmic flops and HBM bytes of one forward (padding excluded)."""
+    es = 4 if cfg.dtype == "f32" else 2
+    touched = len(np.unique(ids))
+    flops = 2 * cfg.T * cfg.H * cfg.E + 4 * cfg.T * cfg.k * cfg.H * cfg.F
+    bytes_ = es * (cfg.T * cfg.H + cfg.H * cfg.E + 2 * touched * cfg.H * cfg.F + cfg.T * cfg.H) \
+        + 8 * cfg.T * cfg.k
+    return flops, bytes_, touched
+
+
+def gemm_launch_counts(cfg, touched):
+    """Per launch of the grouped expert GEMM (both FFN GEMMs are equal):
+    flops 2*R*H*F; bytes = the touched experts' weight matrix + the A operand
+    rows read + the C rows written."""
+    es = 4 if cfg.dtype == "f32" else 2
+    R = cfg.R
+    flops = 2 * R * cfg.H * cfg.F
+    bytes_ = es * (touched * cfg.H * cfg.F + R * cfg.H + R * cfg.F)
+    return flops, bytes_
+
+
+def time_forward(moe, L, cfg, steps, warmup, ws, y):
+    args = (L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k)
+    for _ in range(warmup):
+        moe.moe_forward(*args, y=y, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        moe.moe_forward(*args, y=y, ws=ws)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_stages(moe, L, cfg, steps, bufs):
+    """Per-stage durations (ms) from HIP events on the launch stream."""
+    names = ["route", "permute", "expert_ffn", "combine"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    ids, w, off, st, inv, xp, yp, y, ws = bufs
+    torch.cuda.synchronize()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record()
+        moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k, topk_ids=ids, topk_w=w, ws=ws)
+        e[1].record()
+        moe.moe_permute(L["x"], ids, cfg.E, expert_offsets=off, sorted_token=st, inv_pos=inv,
+                        xp=xp, ws=ws)
+        e[2].record()
+        moe.moe_expert_ffn(xp, off, L["w1"], L["w2"], yp=yp, ws=ws)
+        e[3].record()
+        moe.moe_combine(yp, inv, w, y=y)
+        e[4].record()
+    torch.cuda.synchronize()
+    out = {}
+    for j, n in enumerate(names):
+        out[n] = float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
+    return out
+
+
+def cpu_baseline(cfg, L, n_tokens):
+    """The fp64 oracle on the first n_tokens tokens of the workload (all the
+    experts they route to), timed on the host cores."""
+    import oracle
+    sel = torch.arange(n_tokens, device="cuda")
+    x = L["x"][sel].cpu()
+    w_r = L["w_r"].cpu()
+    b = None if L["router_bias"] is None else L["router_bias"].cpu()
+    w1 = L["w1"].cpu()
+    w2 = L["w2"].cpu()
+    cores = torch.get_num_threads()
+    t0 = time.perf_counter()
+    up = lambda t: t.to(torch.float64).numpy()  # noqa: E731  (the oracle's own upcast)
+    oracle.forward(up(x), up(w_r), None if b is None else up(b),
+                   lambda e: up(w1[e]), lambda e: up(w2[e]), cfg.k)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tokens} of {cfg.T} tokens of {cfg.name}, fp64 numpy, "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {a.gpus} requested): the MoE forward "
+              "here is a single-GPU hot path with no collectives.", file=sys.stderr)
+        sys.exit(2)
+    import mixture_experts_layer_21_amd as moe
+    cfg = mi.CONFIGS[a.config]
+    torch.cuda.set_device(0)
+    L = mi.make_inputs(cfg, "cuda")
+    dev = "cuda"
+    nbytes = moe.moe_workspace_bytes(cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.torch_dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    y = torch.empty((cfg.T, cfg.H), dtype=cfg.torch_dtype, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: inputs ready, workspace {nbytes / 2**20:.0f} MiB", file=sys.stderr,
+          flush=True)
+
+    sec = time_forward(moe, L, cfg, a.steps, a.warmup, ws, y)
+    print(f"[bench] timed region done: {sec * 1e3:.3f} ms/step", file=sys.stderr, flush=True)
+
+    R = cfg.R
+    bufs = (torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev),
+            torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
+            torch.empty(cfg.E + 1, dtype=torch.int32, device=dev),
+            torch.empty(R, dtype=torch.int32, device=dev),
+            torch.empty(R, dtype=torch.int32, device=dev),
+            torch.empty((R, cfg.H), dtype=cfg.torch_dtype, device=dev),
+            torch.empty((R, cfg.H), dtype=cfg.torch_dtype, device=dev),
+            torch.empty((cfg.T, cfg.H), dtype=cfg.torch_dtype, device=dev), ws)
+    stages = time_stages(moe, L, cfg, a.steps, bufs)
+    ids = bufs[0].cpu().numpy()
+    flops, bytes_, touched = alg_counts(cfg, ids)
+    counts = np.bincount(ids.ravel(), minlength=cfg.E)
+
+    g_flops, g_bytes = gemm_launch_counts(cfg, touched)
+    g_sec = stages["expert_ffn"] / 2 * 1e-3         # two launches per FFN stage
+    peak_mm = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if g_flops / g_bytes >= ridge:
+        roof = {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
+                "achieved": g_flops / g_sec / 1e12, "peak": peak_mm, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": g_bytes / g_sec / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "gemm_bf16_grouped" if cfg.dtype == "bf16" else "gemm_f32_grouped"
+    roof["per_launch"] = {"flops": g_flops, "bytes": g_bytes, "ms": g_sec * 1e3}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        n = a.cpu_sample_tokens or {"tiny_fp32": 64, "mixtral_bf16": 128, "skewed_bf16": 128,
+                                    "many_experts_bf16": 256, "weight_bound_bf16": 4}[cfg.name]
+        cpu = cpu_baseline(cfg, L, min(n, cfg.T))
+
+    layer_tflops = flops / sec / 1e12
+    out = {
+        "metric": METRIC,
+        "value": cfg.T / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded counter-based generator; random-init weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "top_k": cfg.k,
+                   "F": cfg.F, "router_bias0": cfg.bias0, "seed": cfg.seed},
+        "layer_tflops": layer_tflops,
+        "layer_alg_gflop": flops / 1e9,
+        "layer_alg_gbytes": bytes_ / 1e9,
+        "layer_roofline_frac": max(layer_tflops / peak_mm,
+                                   bytes_ / sec / 1e9 / PEAK_HBM_GBS),
+        "experts_touched": int(touched),
+        "expert_rows": {"min": int(counts.min()), "max": int(counts.max())},
+        "stages_ms": stages,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

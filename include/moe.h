@@ -1,0 +1,158 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts layer forward.
+ *
+ * The layer is the one stated in "Writing a fused MoE operator in Ascend C"
+ * (section "MoE computation flow"): for tokens x[T,H],
+ *   1. routing   logits = x . W_r (+ b_r), ids = the top_k experts per token;
+ *   2. gating    w = softmax over the top_k selected logits;
+ *   3. dispatch  the tokens of each expert gathered into a contiguous block;
+ *   4. experts   y_e = GELU(x_e . W1[e]) . W2[e]   (tanh-form GELU, no bias);
+ *   5. combine   y[t] = sum_j w[t,j] * y_{ids[t,j]}[t].
+ * The stage entry points below split the layer at the same cuts as that
+ * article's step list; moe_forward runs all of them.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (memory of the current HIP
+ *     device) unless marked "host".  Layouts are dense row-major with the
+ *     shapes given.  The caller allocates and owns every buffer; the library
+ *     never allocates or frees device memory, never synchronises, and never
+ *     copies device data to the host.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *     the default stream).  Results are ready when the stream reaches them.
+ *   - dtype selects the element type of x, W_r, W1, W2, xp, yp and y:
+ *     MOE_F32 (fp32 throughout) or MOE_BF16 (bf16 storage, fp32
+ *     accumulation; the FFN intermediate is rounded to bf16).  Router bias
+ *     and gate weights are always fp32; expert ids and indices are int32.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     call that returns an error has no device side effects.
+ *   - Results are bitwise deterministic for fixed inputs and shapes (no
+ *     floating-point atomics).
+ *   - The library is stateless and re-entrant.  Calls on different streams
+ *     must not share a workspace.
+ *
+ * Status codes
+ *   MOE_OK                 success (work enqueued)
+ *   MOE_ERR_INVALID_ARG    a required pointer is NULL, a size is <= 0,
+ *                          top_k is outside [1, E], or ws_bytes is smaller
+ *                          than the entry point needs
+ *   MOE_ERR_UNSUPPORTED    dtype is not MOE_F32/MOE_BF16, H or F is not a
+ *                          multiple of 8, E > 1024, top_k > 16, or a size
+ *                          exceeds the int32 index range (T*top_k*max(H,F)
+ *                          elements must stay below 2^31)
+ *   MOE_ERR_LAUNCH         the HIP runtime reported an error for a launch
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_LAUNCH = 3,
+};
+
+typedef int32_t moe_dtype;
+enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+};
+
+/* Host string for a status code (static storage; never NULL). */
+const char* moe_status_string(moe_status status);
+
+/*
+ * Bytes of workspace that moe_forward needs for this layer shape, written to
+ * *bytes (host pointer).  This amount is also enough for every stage entry
+ * point called with the same (or smaller) sizes.  The workspace holds the
+ * router's partial logits, dispatch counters, the dispatched rows xp[T*k,H],
+ * the FFN intermediate h[T*k,F] and the expert outputs yp[T*k,H].
+ */
+moe_status moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k,
+                               int64_t F, moe_dtype dtype, size_t* bytes);
+
+/*
+ * Routing + gating (fused article, section 1 "Routing + Gating";
+ * routing article, "Top-K routing").
+ *   x[T,H], w_r[H,E] in dtype; router_bias[E] fp32 or NULL (no bias).
+ *   logits[t,e] = sum_h x[t,h]*w_r[h,e] + router_bias[e], accumulated in fp32.
+ *   topk_ids[T,top_k] int32: the top_k experts of each token in descending
+ *     logit order; equal logits go to the lower expert index.
+ *   topk_w[T,top_k] fp32: softmax over the top_k selected logits, in the
+ *     same slot order (so each row sums to 1).
+ *   ws/ws_bytes: device workspace (partial logits).
+ */
+moe_status moe_route(const void* x, const void* w_r, const float* router_bias,
+                     int64_t T, int64_t H, int64_t E, int32_t top_k,
+                     moe_dtype dtype, int32_t* topk_ids, float* topk_w,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dispatch (fused article, GatherTokensByExpert): group the R = T*top_k
+ * (token, slot) pairs by expert, dropless, in ascending token order within
+ * each expert (then ascending slot).
+ *   topk_ids[T,top_k] int32 in [0,E) (as produced by moe_route).
+ *   expert_offsets[E+1] int32: expert e owns dispatched rows
+ *     [expert_offsets[e], expert_offsets[e+1]); expert_offsets[E] = R.
+ *   sorted_token[R] int32: source token of each dispatched row.
+ *   inv_pos[T*top_k] int32: dispatched row of pair (t, j), at index t*top_k+j.
+ *   xp[R,H] (dtype): xp[p,:] = x[sorted_token[p],:], a bit copy.
+ * Ids outside [0,E) are not checked on the device and give undefined output.
+ */
+moe_status moe_permute(const void* x, const int32_t* topk_ids,
+                       int64_t T, int64_t H, int64_t E, int32_t top_k,
+                       moe_dtype dtype, int32_t* expert_offsets,
+                       int32_t* sorted_token, int32_t* inv_pos, void* xp,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Experts (fused article, expert kernel step 3: Mmad -> GELU -> Mmad):
+ * for each expert e with rows [expert_offsets[e], expert_offsets[e+1]),
+ *   yp[rows] = GELU(xp[rows] . w1[e]) . w2[e]
+ *   xp[R,H], w1[E,H,F], w2[E,F,H], yp[R,H] in dtype; expert_offsets[E+1]
+ *   int32, non-decreasing, expert_offsets[0] = 0, expert_offsets[E] = R.
+ *   GELU is the tanh form 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+ *   Experts with no rows are skipped (their weights are not read).
+ *   ws holds h[R,F] (dtype).
+ */
+moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets,
+                          const void* w1, const void* w2, int64_t R, int64_t H,
+                          int64_t E, int64_t F, moe_dtype dtype, void* yp,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Combine (fused article, ScatterWithWeights): weighted accumulation of each
+ * token's expert outputs,
+ *   y[t,:] = sum_{j<top_k} topk_w[t,j] * yp[inv_pos[t*top_k+j],:]
+ * summed in fp32 in slot order, then stored in dtype (round to nearest even).
+ *   yp[T*top_k,H], y[T,H] in dtype; inv_pos int32; topk_w fp32.
+ */
+moe_status moe_combine(const void* yp, const int32_t* inv_pos,
+                       const float* topk_w, int64_t T, int64_t H,
+                       int32_t top_k, moe_dtype dtype, void* y, void* stream);
+
+/*
+ * The whole layer forward (fused article, section 3 "full call"): route,
+ * dispatch, experts and combine, enqueued back to back on `stream`.
+ *   y[T,H] (dtype) output.
+ *   topk_ids_out[T,top_k] / topk_w_out[T,top_k]: optional (may be NULL)
+ *     copies of the routing decision and gate weights.
+ *   ws_bytes must be at least moe_workspace_bytes() for the same shape.
+ */
+moe_status moe_forward(const void* x, const void* w_r, const float* router_bias,
+                       const void* w1, const void* w2, int64_t T, int64_t H,
+                       int64_t E, int32_t top_k, int64_t F, moe_dtype dtype,
+                       void* y, int32_t* topk_ids_out, float* topk_w_out,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

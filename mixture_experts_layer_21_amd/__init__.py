@@ -1,0 +1,219 @@
+"""MI355X (gfx950) Mixture-of-Experts layer forward: Python binding.
+
+A thin ctypes layer over libmoe.so (include/moe.h).  Every function here has
+the name of the C entry point it calls and only marshals arguments: it checks
+tensor devices, dtypes and shapes, allocates outputs and the workspace with
+torch (device memory only), passes raw pointers and the current HIP stream,
+and raises on a non-OK status.  All computation happens in the HIP kernels.
+
+Importing this package fails if libmoe.so has not been built
+(python -m mixture_experts_layer_21_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "'python -m mixture_experts_layer_21_amd.build' (needs ROCm hipcc)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_LAUNCH = 0, 1, 2, 3
+MOE_F32, MOE_BF16 = 0, 1
+EXPORTS = ("moe_status_string", "moe_workspace_bytes", "moe_route", "moe_permute",
+           "moe_expert_ffn", "moe_combine", "moe_forward")
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_lib.moe_status_string.restype = ctypes.c_char_p
+_lib.moe_status_string.argtypes = [_i32]
+_lib.moe_workspace_bytes.restype = _i32
+_lib.moe_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+_lib.moe_route.restype = _i32
+_lib.moe_route.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_permute.restype = _i32
+_lib.moe_permute.argtypes = [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                             _sz, _vp]
+_lib.moe_expert_ffn.restype = _i32
+_lib.moe_expert_ffn.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp,
+                                _sz, _vp]
+_lib.moe_combine.restype = _i32
+_lib.moe_combine.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp]
+_lib.moe_forward.restype = _i32
+_lib.moe_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _vp,
+                             _vp, _vp, _vp, _sz, _vp]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {_lib.moe_status_string(status).decode()}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (for callers that pass raw pointers)."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return MOE_F32
+    if t == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t}: use torch.float32 or torch.bfloat16")
+
+
+def _check(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ok(status: int, where: str):
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def moe_workspace_bytes(T: int, H: int, E: int, top_k: int, F: int, dtype: torch.dtype) -> int:
+    n = _sz(0)
+    _ok(_lib.moe_workspace_bytes(T, H, E, top_k, F, _dtype_code(dtype), ctypes.byref(n)),
+        "moe_workspace_bytes")
+    return n.value
+
+
+def _workspace(ws, nbytes: int, dev):
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(ws, "ws", torch.uint8)
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes} bytes")
+    return ws
+
+
+def moe_route(x, w_r, router_bias, top_k: int, topk_ids=None, topk_w=None, ws=None):
+    """Routing + gating.  Returns (topk_ids[T,k] int32, topk_w[T,k] fp32)."""
+    _check(x, "x")
+    T, H = x.shape
+    E = w_r.shape[1]
+    _check(w_r, "w_r", x.dtype, (H, E))
+    if router_bias is not None:
+        _check(router_bias, "router_bias", torch.float32, (E,))
+    dev = x.device
+    topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev) if topk_ids is None else \
+        _check(topk_ids, "topk_ids", torch.int32, (T, top_k))
+    topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if topk_w is None else \
+        _check(topk_w, "topk_w", torch.float32, (T, top_k))
+    ws = _workspace(ws, moe_workspace_bytes(T, H, E, top_k, 8, x.dtype), dev)
+    _ok(_lib.moe_route(_ptr(x), _ptr(w_r), _ptr(router_bias), T, H, E, top_k,
+                       _dtype_code(x.dtype), _ptr(topk_ids), _ptr(topk_w), _ptr(ws),
+                       ws.numel(), _stream(dev)), "moe_route")
+    return topk_ids, topk_w
+
+
+def moe_permute(x, topk_ids, E: int, expert_offsets=None, sorted_token=None, inv_pos=None,
+                xp=None, ws=None):
+    """Dispatch.  Returns (expert_offsets[E+1], sorted_token[R], inv_pos[R], xp[R,H])."""
+    _check(x, "x")
+    T, H = x.shape
+    top_k = topk_ids.shape[1]
+    _check(topk_ids, "topk_ids", torch.int32, (T, top_k))
+    R, dev = T * top_k, x.device
+    expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if expert_offsets is None \
+        else _check(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    sorted_token = torch.empty(R, dtype=torch.int32, device=dev) if sorted_token is None else \
+        _check(sorted_token, "sorted_token", torch.int32, (R,))
+    inv_pos = torch.empty(R, dtype=torch.int32, device=dev) if inv_pos is None else \
+        _check(inv_pos, "inv_pos", torch.int32, (R,))
+    xp = torch.empty((R, H), dtype=x.dtype, device=dev) if xp is None else \
+        _check(xp, "xp", x.dtype, (R, H))
+    ws = _workspace(ws, moe_workspace_bytes(T, H, E, top_k, 8, x.dtype), dev)
+    _ok(_lib.moe_permute(_ptr(x), _ptr(topk_ids), T, H, E, top_k, _dtype_code(x.dtype),
+                         _ptr(expert_offsets), _ptr(sorted_token), _ptr(inv_pos), _ptr(xp),
+                         _ptr(ws), ws.numel(), _stream(dev)), "moe_permute")
+    return expert_offsets, sorted_token, inv_pos, xp
+
+
+def moe_expert_ffn(xp, expert_offsets, w1, w2, yp=None, ws=None):
+    """Experts.  Returns yp[R,H] with yp[rows_e] = GELU(xp[rows_e] W1[e]) W2[e]."""
+    _check(xp, "xp")
+    R, H = xp.shape
+    E, _, F = w1.shape
+    _check(w1, "w1", xp.dtype, (E, H, F))
+    _check(w2, "w2", xp.dtype, (E, F, H))
+    _check(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    dev = xp.device
+    yp = torch.empty((R, H), dtype=xp.dtype, device=dev) if yp is None else \
+        _check(yp, "yp", xp.dtype, (R, H))
+    ws = _workspace(ws, moe_workspace_bytes(R, H, E, 1, F, xp.dtype), dev)
+    _ok(_lib.moe_expert_ffn(_ptr(xp), _ptr(expert_offsets), _ptr(w1), _ptr(w2), R, H, E, F,
+                            _dtype_code(xp.dtype), _ptr(yp), _ptr(ws), ws.numel(),
+                            _stream(dev)), "moe_expert_ffn")
+    return yp
+
+
+def moe_combine(yp, inv_pos, topk_w, y=None):
+    """Combine.  Returns y[T,H] = sum_j topk_w[t,j] * yp[inv_pos[t*k+j]]."""
+    _check(yp, "yp")
+    _check(topk_w, "topk_w", torch.float32)
+    T, top_k = topk_w.shape
+    H = yp.shape[1]
+    _check(inv_pos, "inv_pos", torch.int32)
+    if inv_pos.numel() != T * top_k or yp.shape[0] != T * top_k:
+        raise ValueError("inv_pos / yp do not match topk_w's [T, k]")
+    y = torch.empty((T, H), dtype=yp.dtype, device=yp.device) if y is None else \
+        _check(y, "y", yp.dtype, (T, H))
+    _ok(_lib.moe_combine(_ptr(yp), _ptr(inv_pos), _ptr(topk_w), T, H, top_k,
+                         _dtype_code(yp.dtype), _ptr(y), _stream(yp.device)), "moe_combine")
+    return y
+
+
+def moe_forward(x, w_r, router_bias, w1, w2, top_k: int, y=None, topk_ids_out=None,
+                topk_w_out=None, ws=None):
+    """The whole layer forward.  Returns y[T,H]."""
+    _check(x, "x")
+    T, H = x.shape
+    E = w_r.shape[1]
+    F = w1.shape[2]
+    _check(w_r, "w_r", x.dtype, (H, E))
+    if router_bias is not None:
+        _check(router_bias, "router_bias", torch.float32, (E,))
+    _check(w1, "w1", x.dtype, (E, H, F))
+    _check(w2, "w2", x.dtype, (E, F, H))
+    dev = x.device
+    y = torch.empty((T, H), dtype=x.dtype, device=dev) if y is None else \
+        _check(y, "y", x.dtype, (T, H))
+    if topk_ids_out is not None:
+        _check(topk_ids_out, "topk_ids_out", torch.int32, (T, top_k))
+    if topk_w_out is not None:
+        _check(topk_w_out, "topk_w_out", torch.float32, (T, top_k))
+    ws = _workspace(ws, moe_workspace_bytes(T, H, E, top_k, F, x.dtype), dev)
+    _ok(_lib.moe_forward(_ptr(x), _ptr(w_r), _ptr(router_bias), _ptr(w1), _ptr(w2), T, H, E,
+                         top_k, F, _dtype_code(x.dtype), _ptr(y), _ptr(topk_ids_out),
+                         _ptr(topk_w_out), _ptr(ws), ws.numel(), _stream(dev)), "moe_forward")
+    return y

@@ -1,0 +1,155 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 bit conversions,
+// the GELU epilogue, wave-level scans and the grouped-GEMM tile mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;   // CDNA wavefront width
+constexpr int kXcds = 8;    // MI355X: 8 XCDs, workgroups dealt round-robin
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// GELU, tanh form: 0.5 z (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3).
+// Since 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), this is
+//   z / (1 + 2^(z * (c1 + c2 z^2))),  c1 = -2 sqrt(2/pi) log2(e), c2 = 0.044715 c1,
+// one exp2 and one reciprocal per element.  For z -> -inf the exp2 overflows
+// to +inf and the result is -0; for z -> +inf it tends to z.
+__device__ __forceinline__ float gelu_tanh(float z) {
+  constexpr float c1 = -2.3022082f;        // -2 * 0.7978845608 * 1.4426950409
+  constexpr float c2 = -0.10294324f;       // c1 * 0.044715
+  float z2 = z * z;
+  float t = z * __builtin_fmaf(c2, z2, c1);
+  float e = __builtin_amdgcn_exp2f(t);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_bcast(int v, int src_lane) {
+  return __builtin_amdgcn_readlane(v, src_lane);
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM tile mapping.
+//
+// Expert e owns rows [off[e], off[e+1]) of the dispatched matrix and splits
+// them into m_e = ceil(rows_e / BM) row tiles; each row tile meets all NT
+// column tiles, so the layer has NREAL = NT * sum_e m_e tiles.  Tiles are
+// numbered expert by expert; inside an expert, consecutive tiles share the
+// column tile (the same weight slab) and walk its row tiles, so workgroups
+// running together read one weight slab from HBM once.
+//
+// The grid is launched with an upper bound of tiles (the host does not know
+// the per-expert counts).  Workgroup ids are dealt to the 8 XCDs round-robin,
+// so the id is remapped so that each XCD gets a contiguous run of ceil(NREAL/8)
+// logical tiles, which keeps the tiles that share a weight slab in one XCD's
+// L2.  Every wave of the block computes the same mapping (no LDS, no sync).
+// With off == nullptr the matrix is a single dense group of `dense_rows` rows.
+// ---------------------------------------------------------------------------
+struct Tile {
+  int valid;
+  int e;       // expert (group)
+  int row0;    // first dispatched row of the tile
+  int mrows;   // valid rows in the tile (1..BM)
+  int nt;      // column tile index
+};
+
+__device__ __forceinline__ Tile map_tile(const int* __restrict__ off, int E,
+                                         int dense_rows, int BM, int NT,
+                                         int bid) {
+  Tile tile;
+  tile.valid = 0;
+  const int lane = lane_id();
+  if (off == nullptr) {
+    const int mt = (dense_rows + BM - 1) / BM;
+    const int nreal = mt * NT;
+    const int per = (nreal + kXcds - 1) / kXcds;
+    const int L = (bid % kXcds) * per + bid / kXcds;
+    if (bid / kXcds >= per || L >= nreal) return tile;
+    tile.valid = 1;
+    tile.e = 0;
+    tile.nt = L / mt;
+    const int mi = L % mt;
+    tile.row0 = mi * BM;
+    tile.mrows = min(BM, dense_rows - tile.row0);
+    return tile;
+  }
+  // pass 1: total row tiles
+  int total = 0;
+  for (int c = 0; c < E; c += kWave) {
+    const int e = c + lane;
+    int mt = 0;
+    if (e < E) mt = (off[e + 1] - off[e] + BM - 1) / BM;
+    const int incl = wave_incl_scan(mt);
+    total += wave_bcast(incl, kWave - 1);
+  }
+  const int nreal = total * NT;
+  const int per = (nreal + kXcds - 1) / kXcds;
+  const int L = (bid % kXcds) * per + bid / kXcds;
+  if (bid / kXcds >= per || L >= nreal) return tile;
+  // pass 2: find the expert whose tile range holds L
+  int carry = 0;
+  for (int c = 0; c < E; c += kWave) {
+    const int e = c + lane;
+    int cnt = 0, mt = 0;
+    if (e < E) {
+      cnt = off[e + 1] - off[e];
+      mt = (cnt + BM - 1) / BM;
+    }
+    const int incl = wave_incl_scan(mt);
+    const int lo = (carry + incl - mt) * NT;
+    const int hi = (carry + incl) * NT;
+    const uint64_t hit = __ballot(mt > 0 && L >= lo && L < hi);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      const int e_hit = c + src;
+      const int lo_hit = wave_bcast(lo, src);
+      const int mt_hit = wave_bcast(mt, src);
+      const int cnt_hit = wave_bcast(cnt, src);
+      const int local = L - lo_hit;
+      const int mi = local % mt_hit;
+      tile.valid = 1;
+      tile.e = e_hit;
+      tile.nt = local / mt_hit;
+      tile.row0 = off[e_hit] + mi * BM;
+      tile.mrows = min(BM, cnt_hit - mi * BM);
+      return tile;
+    }
+    carry += wave_bcast(incl, kWave - 1);
+  }
+  return tile;
+}
+
+}  // namespace moe

@@ -1,0 +1,39 @@
+// Internal host-side launchers of the MoE kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace moe {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
+
+// Router work split: TPW expert tiles (of 16) per wave, EG expert groups,
+// S splits of the H axis of KL elements each; logits padded to EP columns.
+struct RoutePlan {
+  int EP, TPW, EG, S, KL;
+};
+RoutePlan plan_route(int T, int H, int E, bool bf16);
+size_t route_ws_bytes(int T, int H, int E, bool bf16);
+hipError_t launch_route(const void* x, const void* w_r, const float* bias, int T, int H,
+                        int E, int k, bool bf16, int32_t* ids, float* w, void* ws,
+                        hipStream_t s);
+
+size_t permute_ws_bytes(int R, int E);
+hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E, int k,
+                          size_t elem_bytes, int32_t* offsets, int32_t* sorted_token,
+                          int32_t* inv_pos, void* xp, void* ws, hipStream_t s);
+
+hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, const int* off, int E,
+                            int R, int K, int N, bool gelu, hipStream_t s);
+hipError_t launch_gemm_f32(const float* A, const float* W, float* C, const int* off, int E,
+                           int R, int K, int N, int ldc, bool gelu, hipStream_t s);
+
+hipError_t launch_combine(const void* yp, const int32_t* inv_pos, const float* w, int T,
+                          int H, int k, bool bf16, void* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,191 @@
+// C ABI of the MoE layer forward: host-side validation, workspace layout and
+// the launch sequence.  Every entry point validates all of its arguments
+// before enqueueing anything, so an error return leaves the device untouched.
+#include "moe.h"
+
+#include "launch.h"
+
+namespace {
+
+using moe::align_up;
+
+constexpr int64_t kMaxE = 1024;
+constexpr int32_t kMaxTopK = 16;
+constexpr int64_t kIndexLimit = (int64_t)1 << 31;
+
+size_t elem_bytes(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
+
+moe_status check_dtype(moe_dtype dt) {
+  return (dt == MOE_F32 || dt == MOE_BF16) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
+// Shape checks shared by the entry points.  T may be 0 (nothing to do).
+moe_status check_shape(int64_t T, int64_t H, int64_t E, int32_t top_k, int64_t F,
+                       moe_dtype dt) {
+  if (T < 0 || H <= 0 || E <= 0 || F <= 0) return MOE_ERR_INVALID_ARG;
+  if (top_k < 1 || top_k > E) return MOE_ERR_INVALID_ARG;
+  if (check_dtype(dt) != MOE_OK) return MOE_ERR_UNSUPPORTED;
+  if (H % 8 != 0 || F % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxE || top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  const int64_t wide = H > F ? H : F;
+  if (T * top_k >= kIndexLimit / wide) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t ffn_ws_bytes(int64_t R, int64_t F, moe_dtype dt) {
+  return align_up((size_t)R * F * elem_bytes(dt));
+}
+
+// moe_forward workspace: routing outputs, dispatch indices, xp, yp, and one
+// stage region shared in time by the router, the dispatch counters and h.
+struct FwdLayout {
+  size_t ids, w, offsets, sorted, inv, xp, yp, stage, total;
+};
+
+FwdLayout fwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_dtype dt) {
+  const int64_t R = T * k;
+  const size_t es = elem_bytes(dt);
+  FwdLayout L;
+  size_t o = 0;
+  L.ids = o;     o += align_up((size_t)R * 4);
+  L.w = o;       o += align_up((size_t)R * 4);
+  L.offsets = o; o += align_up((size_t)(E + 1) * 4);
+  L.sorted = o;  o += align_up((size_t)R * 4);
+  L.inv = o;     o += align_up((size_t)R * 4);
+  L.xp = o;      o += align_up((size_t)R * H * es);
+  L.yp = o;      o += align_up((size_t)R * H * es);
+  L.stage = o;
+  size_t st = moe::route_ws_bytes((int)T, (int)H, (int)E, dt == MOE_BF16);
+  st = std::max(st, moe::permute_ws_bytes((int)R, (int)E));
+  st = std::max(st, ffn_ws_bytes(R, F, dt));
+  L.total = o + st;
+  return L;
+}
+
+moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+moe_status run_ffn(const void* xp, const int32_t* off, const void* w1, const void* w2,
+                   int64_t R, int64_t H, int64_t E, int64_t F, moe_dtype dt, void* yp,
+                   void* h, hipStream_t s) {
+  if (R == 0) return MOE_OK;
+  hipError_t err;
+  if (dt == MOE_BF16) {
+    err = moe::launch_gemm_bf16(xp, w1, h, off, (int)E, (int)R, (int)H, (int)F, true, s);
+    if (err == hipSuccess)
+      err = moe::launch_gemm_bf16(h, w2, yp, off, (int)E, (int)R, (int)F, (int)H, false, s);
+  } else {
+    err = moe::launch_gemm_f32((const float*)xp, (const float*)w1, (float*)h, off, (int)E,
+                               (int)R, (int)H, (int)F, (int)F, true, s);
+    if (err == hipSuccess)
+      err = moe::launch_gemm_f32((const float*)h, (const float*)w2, (float*)yp, off, (int)E,
+                                 (int)R, (int)F, (int)H, (int)H, false, s);
+  }
+  return launch_status(err);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported dtype or size";
+    case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: HIP launch failed";
+    default: return "MOE_ERR_UNKNOWN: unknown status";
+  }
+}
+
+moe_status moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k, int64_t F,
+                               moe_dtype dtype, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  const moe_status st = check_shape(T, H, E, top_k, F, dtype);
+  if (st != MOE_OK) return st;
+  *bytes = fwd_layout(T, H, E, top_k, F, dtype).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const void* x, const void* w_r, const float* router_bias, int64_t T,
+                     int64_t H, int64_t E, int32_t top_k, moe_dtype dtype, int32_t* topk_ids,
+                     float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st = check_shape(T, H, E, top_k, 8, dtype);
+  if (st != MOE_OK) return st;
+  if (!x || !w_r || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe::route_ws_bytes((int)T, (int)H, (int)E, dtype == MOE_BF16))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  return launch_status(moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k,
+                                         dtype == MOE_BF16, topk_ids, topk_w, ws,
+                                         (hipStream_t)stream));
+}
+
+moe_status moe_permute(const void* x, const int32_t* topk_ids, int64_t T, int64_t H, int64_t E,
+                       int32_t top_k, moe_dtype dtype, int32_t* expert_offsets,
+                       int32_t* sorted_token, int32_t* inv_pos, void* xp, void* ws,
+                       size_t ws_bytes, void* stream) {
+  const moe_status st = check_shape(T, H, E, top_k, 8, dtype);
+  if (st != MOE_OK) return st;
+  if (!x || !topk_ids || !expert_offsets || !sorted_token || !inv_pos || !xp || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe::permute_ws_bytes((int)(T * top_k), (int)E)) return MOE_ERR_INVALID_ARG;
+  return launch_status(moe::launch_permute(x, topk_ids, (int)T, (int)H, (int)E, top_k,
+                                           elem_bytes(dtype), expert_offsets, sorted_token,
+                                           inv_pos, xp, ws, (hipStream_t)stream));
+}
+
+moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets, const void* w1,
+                          const void* w2, int64_t R, int64_t H, int64_t E, int64_t F,
+                          moe_dtype dtype, void* yp, void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st = check_shape(R, H, E, 1, F, dtype);
+  if (st != MOE_OK) return st;
+  if (!xp || !expert_offsets || !w1 || !w2 || !yp || !ws) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_ws_bytes(R, F, dtype)) return MOE_ERR_INVALID_ARG;
+  return run_ffn(xp, expert_offsets, w1, w2, R, H, E, F, dtype, yp, ws, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const void* yp, const int32_t* inv_pos, const float* topk_w, int64_t T,
+                       int64_t H, int32_t top_k, moe_dtype dtype, void* y, void* stream) {
+  const moe_status st = check_shape(T, H, top_k, top_k, 8, dtype);
+  if (st != MOE_OK) return st;
+  if (!yp || !inv_pos || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  return launch_status(moe::launch_combine(yp, inv_pos, topk_w, (int)T, (int)H, top_k,
+                                           dtype == MOE_BF16, y, (hipStream_t)stream));
+}
+
+moe_status moe_forward(const void* x, const void* w_r, const float* router_bias, const void* w1,
+                       const void* w2, int64_t T, int64_t H, int64_t E, int32_t top_k,
+                       int64_t F, moe_dtype dtype, void* y, int32_t* topk_ids_out,
+                       float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st = check_shape(T, H, E, top_k, F, dtype);
+  if (st != MOE_OK) return st;
+  if (!x || !w_r || !w1 || !w2 || !y || !ws) return MOE_ERR_INVALID_ARG;
+  const FwdLayout L = fwd_layout(T, H, E, top_k, F, dtype);
+  if (ws_bytes < L.total) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
+  float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
+  int32_t* off = (int32_t*)(base + L.offsets);
+  int32_t* sorted = (int32_t*)(base + L.sorted);
+  int32_t* inv = (int32_t*)(base + L.inv);
+  void* xp = base + L.xp;
+  void* yp = base + L.yp;
+  void* stage = base + L.stage;
+  const bool bf16 = dtype == MOE_BF16;
+  const int64_t R = T * top_k;
+
+  hipError_t err = moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k, bf16,
+                                     ids, w, stage, s);
+  if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  err = moe::launch_permute(x, ids, (int)T, (int)H, (int)E, top_k, elem_bytes(dtype), off,
+                            sorted, inv, xp, stage, s);
+  if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  const moe_status fs = run_ffn(xp, off, w1, w2, R, H, E, F, dtype, yp, stage, s);
+  if (fs != MOE_OK) return fs;
+  return launch_status(moe::launch_combine(yp, inv, w, (int)T, (int)H, top_k, bf16, y, s));
+}
+
+}  // extern "C"

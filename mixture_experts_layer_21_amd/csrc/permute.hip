@@ -1,0 +1,158 @@
+// Dispatch kernels (fused MoE article, GatherTokensByExpert): group the
+// R = T*k (token, slot) pairs by expert, dropless, keeping the article's
+// order inside each expert (ascending token, then slot).  The article scans
+// all pairs once per expert (O(E*R)); here it is a counting sort, O(R):
+//
+//   perm_count   per chunk of CH pairs: expert histogram in LDS -> counts[b][e]
+//   perm_scan    one workgroup: per-expert exclusive scan over chunks
+//                (chunk bases), then exclusive scan over experts -> offsets
+//   perm_place   per chunk: stable rank of each pair among the chunk's pairs
+//                of the same expert (wave ballots + per-wave counts in LDS)
+//                -> sorted_token[pos] = t, inv_pos[t*k+j] = pos
+//   perm_gather  xp[p,:] = x[sorted_token[p],:], 16-byte copies, one wave per row
+//
+// All counts are integers: placement is exact and deterministic.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+constexpr int CH = 1024;   // pairs per chunk (one workgroup of 256 threads)
+
+__global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int R,
+                                                  int E, int32_t* __restrict__ counts) {
+  extern __shared__ int hist[];
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int b = blockIdx.x;
+  const int end = min(R, (b + 1) * CH);
+  for (int i = b * CH + threadIdx.x; i < end; i += 256) atomicAdd(&hist[ids[i]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) counts[(size_t)b * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ counts,
+                                                  int nchunks, int E, int R,
+                                                  int32_t* __restrict__ base,
+                                                  int32_t* __restrict__ offsets) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x;
+  const int lane = e % kWave, wave = e / kWave;
+  int total = 0;
+  if (e < E) {
+    for (int b = 0; b < nchunks; ++b) {
+      const int c = counts[(size_t)b * E + e];
+      base[(size_t)b * E + e] = total;
+      total += c;
+    }
+  }
+  const int incl = wave_incl_scan(total);
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += wsum[w];
+  const int excl = wbase + incl - total;
+  if (e < E) {
+    offsets[e] = excl;
+    for (int b = 0; b < nchunks; ++b) base[(size_t)b * E + e] += excl;
+  }
+  if (e == 0) offsets[E] = R;
+}
+
+__global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ ids, int R,
+                                                  int E, int k,
+                                                  const int32_t* __restrict__ base,
+                                                  int32_t* __restrict__ sorted_token,
+                                                  int32_t* __restrict__ inv_pos) {
+  extern __shared__ int sm[];
+  int* running = sm;          // [E]: next free row of each expert
+  int* wcnt = sm + E;         // [4][E]: pairs of each expert in each wave this round
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int b = blockIdx.x;
+  for (int e = tid; e < E; e += 256) {
+    running[e] = base[(size_t)b * E + e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wcnt[w * E + e] = 0;
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int r = 0; r < CH; r += 256) {
+    const int i = b * CH + r + tid;
+    const bool valid = i < R;
+    const int my_e = valid ? ids[i] : -1;
+    // lanes of this wave holding the same expert
+    uint64_t remaining = __ballot(valid);
+    uint64_t peers = 0;
+    while (remaining) {
+      const int leader = __builtin_ctzll(remaining);
+      const int le = wave_bcast(my_e, leader);
+      const uint64_t m = __ballot(valid && my_e == le);
+      if (valid && my_e == le) peers = m;
+      remaining &= ~m;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    if (valid && rank == 0) wcnt[wave * E + my_e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int pos = running[my_e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w * E + my_e];
+      sorted_token[pos] = i / k;
+      inv_pos[i] = pos;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+      int add = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        add += wcnt[w * E + e];
+        wcnt[w * E + e] = 0;
+      }
+      running[e] += add;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void perm_gather(const u32x4* __restrict__ x,
+                                                   const int32_t* __restrict__ sorted_token,
+                                                   u32x4* __restrict__ xp, int R,
+                                                   int row_chunks) {
+  const int lane = threadIdx.x % kWave;
+  const int nwaves = gridDim.x * 4;
+  for (int p = blockIdx.x * 4 + threadIdx.x / kWave; p < R; p += nwaves) {
+    const u32x4* src = x + (size_t)sorted_token[p] * row_chunks;
+    u32x4* dst = xp + (size_t)p * row_chunks;
+    for (int c = lane; c < row_chunks; c += kWave) dst[c] = src[c];
+  }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int R, int E) {
+  const size_t nchunks = (R + CH - 1) / CH;
+  return 2 * align_up(nchunks * E * sizeof(int32_t));
+}
+
+hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E, int k,
+                          size_t elem_bytes, int32_t* offsets, int32_t* sorted_token,
+                          int32_t* inv_pos, void* xp, void* ws, hipStream_t s) {
+  const int R = T * k;
+  const int nchunks = (R + CH - 1) / CH;
+  int32_t* counts = (int32_t*)ws;
+  int32_t* base = (int32_t*)((char*)ws + align_up((size_t)nchunks * E * sizeof(int32_t)));
+  if (nchunks > 0)
+    hipLaunchKernelGGL(perm_count, dim3(nchunks), dim3(256), E * sizeof(int), s, ids, R, E, counts);
+  // runs even for R == 0 so that the offsets are written (all zero)
+  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, counts, nchunks, E, R, base, offsets);
+  if (nchunks == 0) return hipGetLastError();
+  hipLaunchKernelGGL(perm_place, dim3(nchunks), dim3(256), 5 * E * sizeof(int), s, ids, R, E, k,
+                     base, sorted_token, inv_pos);
+  const int row_chunks = (int)((size_t)H * elem_bytes / 16);
+  const int blocks = std::min(8192, (R + 3) / 4);
+  hipLaunchKernelGGL(perm_gather, dim3(blocks), dim3(256), 0, s, (const u32x4*)x, sorted_token,
+                     (u32x4*)xp, R, row_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -36,7 +36,8 @@ _M1 = 0x7FEB352D
 _M2 = 0x846CA68B
 _STREAM_X, _STREAM_WR, _STREAM_W1, _STREAM_W2 = 1, 2, 3, 4
 _DRAWS = 6            # 6 hashed words -> 12 uniform 16-bit halves per value
-_CHUNK = 1 << 22      # values per generation chunk (bounds temporaries)
+_CHUNK_CPU = 1 << 22  # values per generation chunk (bounds temporaries)
+_CHUNK_GPU = 1 << 25
 
 
 @dataclasses.dataclass(frozen=True)
@@ -121,8 +122,9 @@ def normal_fp32(n: int, keys: tuple[int, int], scale: float, device="cpu") -> to
     """n approximately-N(0, scale**2) fp32 values; bit-identical on CPU and GPU."""
     out = torch.empty(n, dtype=torch.float32, device=device)
     s32 = torch.tensor(scale, dtype=torch.float32, device=device)
-    for start in range(0, n, _CHUNK):
-        m = min(_CHUNK, n - start)
+    chunk = _CHUNK_CPU if torch.device(device).type == "cpu" else _CHUNK_GPU
+    for start in range(0, n, chunk):
+        m = min(chunk, n - start)
         w = uniform_words(m, keys, start, device)
         lo = w & 0xFFFF
         hi = w >> 16

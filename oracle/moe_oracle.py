@@ -156,7 +156,7 @@ def expert_ffn(xp: np.ndarray, offsets: np.ndarray, w1, w2) -> np.ndarray:
     xp = np.asarray(xp, np.float64)
     E = len(offsets) - 1
     H = xp.shape[1]
-    yp = np.zeros((xp.shape[0], _out_width(w2, H)), dtype=np.float64)
+    yp = np.zeros((xp.shape[0], H), dtype=np.float64)
     for e in range(E):
         a, b = int(offsets[e]), int(offsets[e + 1])
         if a == b:
@@ -201,7 +201,7 @@ def forward(x, w_r, b_r, w1, w2, k: int, ids=None, w=None):
         w = gate_weights(logits, ids)
     E = np.asarray(w_r).shape[1]
     T = x.shape[0]
-    y = np.zeros((T, _out_width(w2, x.shape[1])), dtype=np.float64)
+    y = np.zeros((T, x.shape[1]), dtype=np.float64)
     for e in range(E):
         b_idx, s_idx = np.nonzero(ids == e)
         if b_idx.size == 0:
@@ -216,7 +216,7 @@ def forward_tokens(x_rows, ids_rows, w_rows, w1, w2) -> np.ndarray:
     w[t,j] * FFN_{ids[t,j]}(x[t]).  Used to check sampled outputs of a layer
     too large for the full oracle."""
     x_rows = np.asarray(x_rows, np.float64)
-    out = np.zeros((x_rows.shape[0], _out_width(w2, x_rows.shape[1])), dtype=np.float64)
+    out = np.zeros(x_rows.shape, dtype=np.float64)
     for i in range(x_rows.shape[0]):
         for j in range(ids_rows.shape[1]):
             e = int(ids_rows[i, j])
@@ -257,8 +257,3 @@ def boundary_near_tie(logits: np.ndarray, k: int, rel: float = 1e-3) -> np.ndarr
 def _get(w, e):
     return w(e) if callable(w) else w[e]
 
-
-def _out_width(w2, default):
-    if callable(w2):
-        return _get(w2, 0).shape[1]
-    return np.asarray(w2).shape[2]

@@ -1,0 +1,221 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small shapes are checked element by element on every output, at sizes that
+span several 256x256 GEMM tiles with ragged row, column and K tails, plus the
+degenerate cases (T=1, k=1, k=E, E=1, empty experts, skewed routing, exact
+ties).  The five full-size workloads are checked on every routing decision
+and dispatch index, and on sampled output rows that the oracle computes one
+expert at a time, in the same launch configuration the bench times."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from moe_check import (TOL, assert_close_rel, check_routing, expert_getters, f64, gpu_layer,
+                       sample_tokens)
+
+pytestmark = pytest.mark.gpu
+
+import mixture_experts_layer_21_amd as moe  # fails loudly if the library is missing
+
+C = mi.MoEConfig
+SMALL = {
+    "tiny_fp32": mi.CONFIGS["tiny_fp32"],
+    "ragged_bf16": C("ragged_bf16", T=75, H=200, E=5, k=2, F=136, dtype="bf16"),
+    "multitile_bf16": C("multitile_bf16", T=1000, H=256, E=3, k=2, F=392, dtype="bf16"),
+    "ragged_f32": C("ragged_f32", T=70, H=72, E=6, k=3, F=40, dtype="f32"),
+    "multitile_f32": C("multitile_f32", T=300, H=136, E=3, k=2, F=200, dtype="f32"),
+    "topE_bf16": C("topE_bf16", T=33, H=64, E=4, k=4, F=64, dtype="bf16"),
+    "top1_bf16": C("top1_bf16", T=50, H=128, E=16, k=1, F=64, dtype="bf16"),
+    "one_expert_bf16": C("one_expert_bf16", T=40, H=64, E=1, k=1, F=128, dtype="bf16"),
+    "one_token_bf16": C("one_token_bf16", T=1, H=128, E=8, k=2, F=256, dtype="bf16"),
+    "many_small_bf16": C("many_small_bf16", T=128, H=128, E=128, k=8, F=64, dtype="bf16"),
+    "wide_E_bf16": C("wide_E_bf16", T=20, H=64, E=1000, k=16, F=32, dtype="bf16"),
+    "skewed_small_bf16": C("skewed_small_bf16", T=256, H=128, E=8, k=2, F=256, dtype="bf16",
+                           bias0=3.0),
+}
+FULL = [n for n in mi.CONFIG_ORDER]
+
+_cache = {}
+
+
+def layer(cfg):
+    if cfg.name not in _cache:
+        if len(_cache) > 2:          # keep at most a few layers resident
+            _cache.pop(next(iter(_cache)))
+            torch.cuda.empty_cache()
+        print(f"\n[gen] {cfg.name}", flush=True)
+        _cache[cfg.name] = gpu_layer(cfg)
+    return _cache[cfg.name]
+
+
+def ref_logits(cfg, L):
+    return oracle.router_logits(f64(L["x"]), f64(L["w_r"]), f64(L["router_bias"]))
+
+
+def dt(cfg):
+    return cfg.dtype
+
+
+# --- small shapes: every stage, every element ---------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_route_small(name):
+    cfg = SMALL[name]
+    L = layer(cfg)
+    ids, w = moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k)
+    torch.cuda.synchronize()
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), ref_logits(cfg, L), cfg.k)
+    assert np.all(np.abs(w.cpu().numpy().sum(1) - 1) < 1e-5)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_permute_small(name):
+    cfg = SMALL[name]
+    L = layer(cfg)
+    ids, _ = moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k)
+    off, st, inv, xp = moe.moe_permute(L["x"], ids, cfg.E)
+    torch.cuda.synchronize()
+    o_off, o_st, _, o_inv = oracle.dispatch(ids.cpu().numpy().astype(np.int64), cfg.E)
+    np.testing.assert_array_equal(off.cpu().numpy(), o_off)
+    np.testing.assert_array_equal(st.cpu().numpy(), o_st)
+    np.testing.assert_array_equal(inv.cpu().numpy(), o_inv.ravel())
+    assert torch.equal(xp.cpu(), L["x"].cpu()[torch.from_numpy(o_st)])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_expert_ffn_small(name):
+    cfg = SMALL[name]
+    L = layer(cfg)
+    ids, _ = moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k)
+    off, st, inv, xp = moe.moe_permute(L["x"], ids, cfg.E)
+    yp = moe.moe_expert_ffn(xp, off, L["w1"], L["w2"])
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn(f64(xp), off.cpu().numpy(), f64(L["w1"]), f64(L["w2"]))
+    assert_close_rel(f64(yp), ref, TOL[dt(cfg)], f"{name} yp")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_combine_small(name):
+    cfg = SMALL[name]
+    L = layer(cfg)
+    ids, w = moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k)
+    off, st, inv, xp = moe.moe_permute(L["x"], ids, cfg.E)
+    yp = moe.moe_expert_ffn(xp, off, L["w1"], L["w2"])
+    y = moe.moe_combine(yp, inv, w)
+    torch.cuda.synchronize()
+    ref = oracle.combine(f64(yp), inv.cpu().numpy().reshape(cfg.T, cfg.k), f64(w))
+    # only the final rounding of y to the storage dtype separates the two
+    assert_close_rel(f64(y), ref, 4e-3 if cfg.dtype == "bf16" else 1e-6, f"{name} y")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    cfg = SMALL[name]
+    L = layer(cfg)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    y = moe.moe_forward(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k,
+                        topk_ids_out=ids, topk_w_out=w)
+    torch.cuda.synchronize()
+    logits = ref_logits(cfg, L)
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    check_routing(ids_np, w.cpu().numpy(), logits, cfg.k)
+    ref = oracle.forward(f64(L["x"]), f64(L["w_r"]), f64(L["router_bias"]), f64(L["w1"]),
+                         f64(L["w2"]), cfg.k, ids=ids_np,
+                         w=oracle.gate_weights(logits, ids_np))["y"]
+    assert_close_rel(f64(y), ref, TOL[dt(cfg)], f"{name} y")
+
+
+# --- exact ties: integer-valued inputs make every logit exact ---------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("E,k", [(8, 1), (8, 2), (64, 8), (128, 8), (256, 8), (33, 5)])
+def test_route_exact_ties(dtype, E, k):
+    inp = mi.integer_inputs(96, 64, E, 8, -2, 2, seed=E * 31 + k, dtype=dtype, device="cuda")
+    ids, w = moe.moe_route(inp["x"], inp["w_r"], None, k)
+    torch.cuda.synchronize()
+    l = oracle.router_logits(f64(inp["x"]), f64(inp["w_r"]))
+    assert (l == np.round(l)).all()
+    np.testing.assert_array_equal(ids.cpu().numpy(), oracle.topk_ids(l, k))
+    w_np = w.cpu().numpy()
+    if k == 1:
+        assert np.all(w_np == 1.0)
+    np.testing.assert_allclose(w_np, oracle.gate_weights(l, oracle.topk_ids(l, k)), atol=1e-6)
+
+
+def test_generator_is_bit_identical_on_cpu_and_gpu():
+    cfg = mi.CONFIGS["tiny_fp32"]
+    a, b = mi.make_inputs(cfg, "cpu"), mi.make_inputs(cfg, "cuda")
+    for key in ("x", "w_r", "w1", "w2"):
+        assert torch.equal(a[key], b[key].cpu()), key
+    c1 = mi.CONFIGS["many_experts_bf16"]
+    assert torch.equal(mi.make_x(c1, "cpu"), mi.make_x(c1, "cuda").cpu())
+    assert torch.equal(mi.make_w2_expert(c1, 77, "cpu"), mi.make_w2_expert(c1, 77, "cuda").cpu())
+
+
+# --- full-size workloads ------------------------------------------------------
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full(name):
+    cfg = mi.CONFIGS[name]
+    L = layer(cfg)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    y = moe.moe_forward(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k,
+                        topk_ids_out=ids, topk_w_out=w)
+    torch.cuda.synchronize()
+    logits = ref_logits(cfg, L)
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    nb, nw = check_routing(ids_np, w.cpu().numpy(), logits, cfg.k)
+    print(f"[{name}] near ties: boundary {nb}, within-set {nw}", flush=True)
+    excused = np.nonzero((ids_np != oracle.topk_ids(logits, cfg.k)).any(1))[0]
+    sel = sample_tokens(cfg.T, extra=excused)
+    w_ref = oracle.gate_weights(logits[sel], ids_np[sel])
+    g1, g2 = expert_getters(L)
+    x_sel = f64(L["x"][torch.from_numpy(sel).cuda()])
+    y_ref = oracle.forward(x_sel, f64(L["w_r"]), None, g1, g2, cfg.k, ids=ids_np[sel],
+                           w=w_ref)["y"]
+    y_sel = f64(y[torch.from_numpy(sel).cuda()])
+    rel = assert_close_rel(y_sel, y_ref, TOL[dt(cfg)], f"{name} y (sampled)")
+    print(f"[{name}] max|err|/max|y_ref| = {rel:.3e} over {len(sel)} tokens", flush=True)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_dispatch_full(name):
+    cfg = mi.CONFIGS[name]
+    L = layer(cfg)
+    ids, w = moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k)
+    off, st, inv, xp = moe.moe_permute(L["x"], ids, cfg.E)
+    torch.cuda.synchronize()
+    o_off, o_st, _, o_inv = oracle.dispatch(ids.cpu().numpy().astype(np.int64), cfg.E)
+    np.testing.assert_array_equal(off.cpu().numpy(), o_off)
+    np.testing.assert_array_equal(st.cpu().numpy(), o_st)
+    np.testing.assert_array_equal(inv.cpu().numpy(), o_inv.ravel())
+    assert torch.equal(xp, L["x"][st.long()])
+    # sampled rows of the expert FFN on the real shapes
+    yp = moe.moe_expert_ffn(xp, off, L["w1"], L["w2"])
+    torch.cuda.synchronize()
+    g = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([g.choice(cfg.R, 24, replace=False), [0, cfg.R - 1]]))
+    expert_of = np.searchsorted(o_off, rows, side="right") - 1
+    g1, g2 = expert_getters(L)
+    ref = np.zeros((len(rows), cfg.H))
+    for e in np.unique(expert_of):
+        m = expert_of == e
+        ref[m] = oracle.expert_ffn_block(f64(xp[torch.from_numpy(rows[m]).cuda()]), g1(e), g2(e))
+    assert_close_rel(f64(yp[torch.from_numpy(rows).cuda()]), ref, TOL[dt(cfg)], f"{name} yp")
+
+
+@pytest.mark.parametrize("name", ["mixtral_bf16", "many_experts_bf16"])
+def test_forward_is_deterministic(name):
+    cfg = mi.CONFIGS[name]
+    L = layer(cfg)
+    ws = torch.empty(moe.moe_workspace_bytes(cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.torch_dtype),
+                     dtype=torch.uint8, device="cuda")
+    a = moe.moe_forward(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k, ws=ws)
+    ws.fill_(0x5A)
+    b = moe.moe_forward(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
