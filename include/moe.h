@@ -78,6 +78,28 @@ const char* moe_status_string(moe_status status);
 moe_status moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k,
                                int64_t F, moe_dtype dtype, size_t* bytes);
 
+/* Stages, for moe_stage_workspace_bytes. */
+typedef int32_t moe_stage;
+enum {
+  MOE_STAGE_ROUTE = 0,
+  MOE_STAGE_PERMUTE = 1,
+  MOE_STAGE_EXPERT_FFN = 2,
+  MOE_STAGE_COMBINE = 3,
+  MOE_STAGE_FORWARD = 4,
+};
+
+/*
+ * Bytes of workspace one entry point needs for a layer of this shape,
+ * written to *bytes (host pointer): MOE_STAGE_ROUTE -> moe_route,
+ * MOE_STAGE_PERMUTE -> moe_permute, MOE_STAGE_EXPERT_FFN -> moe_expert_ffn
+ * with R = T*top_k rows, MOE_STAGE_COMBINE -> 0 (no workspace),
+ * MOE_STAGE_FORWARD -> moe_forward (same as moe_workspace_bytes).
+ * Returns MOE_ERR_INVALID_ARG for an unknown stage.
+ */
+moe_status moe_stage_workspace_bytes(moe_stage stage, int64_t T, int64_t H,
+                                     int64_t E, int32_t top_k, int64_t F,
+                                     moe_dtype dtype, size_t* bytes);
+
 /*
  * Routing + gating (fused article, section 1 "Routing + Gating";
  * routing article, "Top-K routing").

@@ -7,7 +7,7 @@ torch (device memory only), passes raw pointers and the current HIP stream,
 and raises on a non-OK status.  All computation happens in the HIP kernels.
 
 Importing this package fails if libmoe.so has not been built
-(python -m mixture_experts_layer_21_amd.build).
+(python mixture_experts_layer_21_amd/build.py).
 """
 from __future__ import annotations
 
@@ -21,20 +21,25 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "'python -m mixture_experts_layer_21_amd.build' (needs ROCm hipcc)")
+                      "'python mixture_experts_layer_21_amd/build.py' (needs ROCm hipcc)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_LAUNCH = 0, 1, 2, 3
 MOE_F32, MOE_BF16 = 0, 1
-EXPORTS = ("moe_status_string", "moe_workspace_bytes", "moe_route", "moe_permute",
-           "moe_expert_ffn", "moe_combine", "moe_forward")
+MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_EXPERT_FFN, MOE_STAGE_COMBINE, MOE_STAGE_FORWARD = \
+    0, 1, 2, 3, 4
+EXPORTS = ("moe_status_string", "moe_workspace_bytes", "moe_stage_workspace_bytes", "moe_route",
+           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward")
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _lib.moe_status_string.restype = ctypes.c_char_p
 _lib.moe_status_string.argtypes = [_i32]
 _lib.moe_workspace_bytes.restype = _i32
 _lib.moe_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+_lib.moe_stage_workspace_bytes.restype = _i32
+_lib.moe_stage_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64, _i32, _i64, _i32,
+                                           ctypes.POINTER(_sz)]
 _lib.moe_route.restype = _i32
 _lib.moe_route.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_permute.restype = _i32
@@ -107,6 +112,14 @@ def moe_workspace_bytes(T: int, H: int, E: int, top_k: int, F: int, dtype: torch
     return n.value
 
 
+def moe_stage_workspace_bytes(stage: int, T: int, H: int, E: int, top_k: int, F: int,
+                              dtype: torch.dtype) -> int:
+    n = _sz(0)
+    _ok(_lib.moe_stage_workspace_bytes(stage, T, H, E, top_k, F, _dtype_code(dtype),
+                                       ctypes.byref(n)), "moe_stage_workspace_bytes")
+    return n.value
+
+
 def _workspace(ws, nbytes: int, dev):
     if ws is None:
         return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -129,7 +142,8 @@ def moe_route(x, w_r, router_bias, top_k: int, topk_ids=None, topk_w=None, ws=No
         _check(topk_ids, "topk_ids", torch.int32, (T, top_k))
     topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if topk_w is None else \
         _check(topk_w, "topk_w", torch.float32, (T, top_k))
-    ws = _workspace(ws, moe_workspace_bytes(T, H, E, top_k, 8, x.dtype), dev)
+    ws = _workspace(ws, moe_stage_workspace_bytes(MOE_STAGE_ROUTE, T, H, E, top_k, 8, x.dtype),
+                    dev)
     _ok(_lib.moe_route(_ptr(x), _ptr(w_r), _ptr(router_bias), T, H, E, top_k,
                        _dtype_code(x.dtype), _ptr(topk_ids), _ptr(topk_w), _ptr(ws),
                        ws.numel(), _stream(dev)), "moe_route")
@@ -152,7 +166,8 @@ def moe_permute(x, topk_ids, E: int, expert_offsets=None, sorted_token=None, inv
         _check(inv_pos, "inv_pos", torch.int32, (R,))
     xp = torch.empty((R, H), dtype=x.dtype, device=dev) if xp is None else \
         _check(xp, "xp", x.dtype, (R, H))
-    ws = _workspace(ws, moe_workspace_bytes(T, H, E, top_k, 8, x.dtype), dev)
+    ws = _workspace(ws, moe_stage_workspace_bytes(MOE_STAGE_PERMUTE, T, H, E, top_k, 8, x.dtype),
+                    dev)
     _ok(_lib.moe_permute(_ptr(x), _ptr(topk_ids), T, H, E, top_k, _dtype_code(x.dtype),
                          _ptr(expert_offsets), _ptr(sorted_token), _ptr(inv_pos), _ptr(xp),
                          _ptr(ws), ws.numel(), _stream(dev)), "moe_permute")
@@ -170,7 +185,8 @@ def moe_expert_ffn(xp, expert_offsets, w1, w2, yp=None, ws=None):
     dev = xp.device
     yp = torch.empty((R, H), dtype=xp.dtype, device=dev) if yp is None else \
         _check(yp, "yp", xp.dtype, (R, H))
-    ws = _workspace(ws, moe_workspace_bytes(R, H, E, 1, F, xp.dtype), dev)
+    ws = _workspace(ws, moe_stage_workspace_bytes(MOE_STAGE_EXPERT_FFN, R, H, E, 1, F, xp.dtype),
+                    dev)
     _ok(_lib.moe_expert_ffn(_ptr(xp), _ptr(expert_offsets), _ptr(w1), _ptr(w2), R, H, E, F,
                             _dtype_code(xp.dtype), _ptr(yp), _ptr(ws), ws.numel(),
                             _stream(dev)), "moe_expert_ffn")

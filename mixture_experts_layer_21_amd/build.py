@@ -1,6 +1,8 @@
 """Build the gfx950 MoE library (libmoe.so) in-tree with hipcc.
 
-    python -m mixture_experts_layer_21_amd.build
+    python mixture_experts_layer_21_amd/build.py
+
+(Run it by path: importing the package itself loads the library.)
 
 Each HIP source compiles to an object under _build/, then one shared library
 is linked next to this file.  It always recompiles (the build is the check

@@ -106,6 +106,33 @@ moe_status moe_workspace_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k, i
   return MOE_OK;
 }
 
+moe_status moe_stage_workspace_bytes(moe_stage stage, int64_t T, int64_t H, int64_t E,
+                                     int32_t top_k, int64_t F, moe_dtype dtype,
+                                     size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  const moe_status st = check_shape(T, H, E, top_k, F, dtype);
+  if (st != MOE_OK) return st;
+  switch (stage) {
+    case MOE_STAGE_ROUTE:
+      *bytes = moe::route_ws_bytes((int)T, (int)H, (int)E, dtype == MOE_BF16);
+      return MOE_OK;
+    case MOE_STAGE_PERMUTE:
+      *bytes = moe::permute_ws_bytes((int)(T * top_k), (int)E);
+      return MOE_OK;
+    case MOE_STAGE_EXPERT_FFN:
+      *bytes = ffn_ws_bytes(T * top_k, F, dtype);
+      return MOE_OK;
+    case MOE_STAGE_COMBINE:
+      *bytes = 0;
+      return MOE_OK;
+    case MOE_STAGE_FORWARD:
+      *bytes = fwd_layout(T, H, E, top_k, F, dtype).total;
+      return MOE_OK;
+    default:
+      return MOE_ERR_INVALID_ARG;
+  }
+}
+
 moe_status moe_route(const void* x, const void* w_r, const float* router_bias, int64_t T,
                      int64_t H, int64_t E, int32_t top_k, moe_dtype dtype, int32_t* topk_ids,
                      float* topk_w, void* ws, size_t ws_bytes, void* stream) {

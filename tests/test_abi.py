@@ -155,3 +155,28 @@ def test_empty_batch_is_a_no_op():
     assert _combine(T=0) == OK
     assert _forward(T=0) == OK
     assert _ffn(R=0) == OK
+
+
+def stage_bytes(stage, T, H, E, k, F, dt):
+    n = ctypes.c_size_t(0)
+    st = L.moe_stage_workspace_bytes(stage, T, H, E, k, F, dt, ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("shape", [(2048, 4096, 8, 2, 14336, BF16), (64, 7168, 256, 8, 2048, BF16),
+                                   (4096, 2048, 128, 8, 768, BF16), (64, 128, 8, 2, 256, F32)])
+def test_stage_workspaces_fit_in_the_forward_workspace(shape):
+    st, fwd = stage_bytes(moe.MOE_STAGE_FORWARD, *shape)
+    assert st == OK and fwd == ws_bytes(*shape)[1]
+    for stage in (moe.MOE_STAGE_ROUTE, moe.MOE_STAGE_PERMUTE, moe.MOE_STAGE_EXPERT_FFN,
+                  moe.MOE_STAGE_COMBINE):
+        st, b = stage_bytes(stage, *shape)
+        assert st == OK and 0 <= b <= fwd
+    T, H, E, k, F, dt = shape
+    assert stage_bytes(moe.MOE_STAGE_EXPERT_FFN, *shape)[1] >= T * k * F * (2 if dt == BF16 else 4)
+    assert stage_bytes(moe.MOE_STAGE_COMBINE, *shape)[1] == 0
+
+
+def test_stage_workspace_rejects_unknown_stage():
+    assert stage_bytes(9, 64, 128, 8, 2, 256, F32)[0] == INV
+    assert L.moe_stage_workspace_bytes(0, 64, 128, 8, 2, 256, F32, None) == INV
