@@ -38,7 +38,7 @@
  *   MOE_ERR_UNSUPPORTED    dtype is not MOE_F32/MOE_BF16, H or F is not a
  *                          multiple of 8, E > 1024, top_k > 16, or a size
  *                          exceeds the int32 index range (T*top_k*max(H,F)
- *                          elements must stay below 2^31)
+ *                          and H*F elements must stay below 2^31)
  *   MOE_ERR_LAUNCH         the HIP runtime reported an error for a launch
  */
 #ifndef MOE_MI355X_H

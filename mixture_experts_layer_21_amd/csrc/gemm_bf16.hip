@@ -33,182 +33,313 @@
 namespace moe {
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK + 8;   // bf16 elements per LDS row (144 B)
+constexpr int BK = 32;          // K step (bf16 elements)
+constexpr int STAGES = 4;       // LDS ring: three K steps in flight
+constexpr uint32_t kBufFlags = 0x00020000u;   // raw buffer, 32-bit data format
 
 template <int BM, int BN, int WM, int WN>
 struct GemmShape {
   static constexpr int NT = kWave * WM * WN;          // threads
+  static constexpr int NW = WM * WN;                  // waves
   static constexpr int TM = BM / WM;                  // tokens per wave
   static constexpr int TN = BN / WN;                  // columns per wave
   static constexpr int FM = TM / 32;                  // MFMA blocks (tokens)
   static constexpr int FN = TN / 32;                  // MFMA blocks (columns)
-  static constexpr int A_LOADS = BM * (BK / 8) / NT;  // 16-B chunks per thread
-  static constexpr int KR = 8 * BN / NT;              // W k-rows per thread
-  static constexpr int KCH = BK / KR;                 // k-chunks per column group
-  static_assert(A_LOADS >= 1 && BM * (BK / 8) % NT == 0, "A tile split");
-  static_assert(KR == 4 || KR == 8, "W tile split");
+  static constexpr int A_ROW = BK * 2;                // bytes per token row (64)
+  static constexpr int W_ROW = BN * 2;                // bytes per k row (512)
+  static constexpr int LDS_A = BM * A_ROW;            // bytes per stage
+  static constexpr int LDS_W = BK * W_ROW;
+  static constexpr int LDS_STAGE = LDS_A + LDS_W;
+  // direct-to-LDS loads: one instruction moves 64 lanes x 16 B = 1 KB
+  static constexpr int A_INSTS = LDS_A / 1024 / NW;   // per wave per step
+  static constexpr int W_INSTS = LDS_W / 1024 / NW;
+  static constexpr int LOADS = A_INSTS + W_INSTS;
+  static_assert(A_ROW == 64 && W_ROW == 512, "layout below assumes BK=32, BN=256");
+  static_assert(A_INSTS * NW * 1024 == LDS_A && W_INSTS * NW * 1024 == LDS_W, "load split");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
-  static constexpr int LDS_A = BM * LDS_STRIDE;       // elements per stage
-  static constexpr int LDS_W = BN * LDS_STRIDE;
 };
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kWave * WM * WN) void gemm_bf16_grouped(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-    uint16_t* __restrict__ C, const int* __restrict__ off, int E, int R,
-    int K, int N, int gelu) {
+// LDS layouts (16-byte chunks XOR-swizzled so that MFMA operand reads are
+// free of bank conflicts):
+//   A tile [BM][32] bf16, 64-byte rows: chunk c of row m at c ^ ((m >> 2) & 3);
+//     16 lanes reading 16 rows of one chunk hit 64 distinct banks.
+//   W tile [32][BN] bf16 (the weight slab's natural k-major layout), 512-byte
+//     rows: chunk c of row k at c ^ (4 * (k & 3)); a transposed read covering
+//     4 k-rows x 32 columns hits 64 distinct banks.
+__device__ __forceinline__ int swz_a(int m) { return (m >> 2) & 3; }
+__device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
+
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding and does not wait on LDS/scalar or export counters
+// (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+__device__ constexpr int vmcnt_le(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           (int)kBufFlags);
+}
+
+// 64 lanes x 16 bytes from global memory straight into a 1 KB LDS block:
+// lane t's bytes land at block + 16 t (no VGPRs involved).
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, char* lds_block,
+                                            uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_block, 16, voff, 0, 0, 0);
+}
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16): in each group of 16 lanes,
+// lane i addresses 8 bytes of row i/4 and receives column i of the 4x16 block
+// those addresses cover, i.e. 4 consecutive k of one output column.
+__device__ __forceinline__ u32x2 read_tr(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// One output tile.  NFM (compile time) is the number of 32-row token blocks
+// of this wave that hold valid rows, so the main loop has no branches around
+// its LDS reads and MFMAs (the accumulators stay in AGPRs).
+//
+// Global loads use buffer descriptors whose base advances with k0 and whose
+// size ends at the last valid row of the tile (A) or of the weight slab (W):
+// rows past the tile and k rows past K read as zero, so no clamping or masks
+// appear in the loop.  (Past-K columns of A read the next row, but they meet
+// zero W rows.)  Columns past N read neighbouring data that is never stored.
+template <int BM, int BN, int WM, int WN, int NFM>
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
+                                          const uint16_t* __restrict__ We,
+                                          uint16_t* __restrict__ C, const Tile& tile, int K,
+                                          int N, int gelu, char* lds0, char* lds1, char* lds2,
+                                          char* lds3) {
+  char* const stages[STAGES] = {lds0, lds1, lds2, lds3};
   using S = GemmShape<BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (S::LDS_A + S::LDS_W)];
-
-  const int NTN = (N + BN - 1) / BN;
-  const Tile tile = map_tile(off, E, R, BM, NTN, blockIdx.x);
-  if (!tile.valid) return;
-
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int wm = wave % WM;
   const int wn = wave / WM;
   const int n0 = tile.nt * BN;
-  const uint16_t* __restrict__ We = W + (size_t)tile.e * K * N;
+  const int wrow0 = wm * S::TM;
 
-  // --- global -> register loaders -----------------------------------------
-  // A: chunk c (8 bf16) of rows r = tid/8 + i*(NT/8)
-  const int a_c = tid % 8;
-  const uint16_t* a_src[S::A_LOADS];
+  // --- loader offsets (constant over the K loop) ---------------------------
+  const uint16_t* a_base = A + (size_t)tile.row0 * K;
+  const uint32_t a_bytes = (uint32_t)tile.mrows * K * 2;
+  const uint32_t w_bytes = (uint32_t)K * N * 2;
+  uint32_t a_voff[S::A_INSTS];
+  int a_dst[S::A_INSTS];
 #pragma unroll
-  for (int i = 0; i < S::A_LOADS; ++i) {
-    const int r = tid / 8 + i * (S::NT / 8);
-    const int rr = min(r, tile.mrows - 1);   // padded rows re-read a valid row
-    a_src[i] = A + (size_t)(tile.row0 + rr) * K + a_c * 8;
+  for (int u = 0; u < S::A_INSTS; ++u) {
+    const int q = wave * S::A_INSTS + u;           // 16 rows per instruction
+    const int m = q * 16 + lane / 4;
+    const int c = (lane % 4) ^ swz_a(m);           // logical chunk stored at lane's slot
+    a_voff[u] = (uint32_t)m * K * 2 + c * 16;
+    a_dst[u] = q * 1024;
   }
-  // W: KR consecutive k-rows x 8 columns per thread
-  const int w_kc = tid % S::KCH;
-  const int w_nc = tid / S::KCH;
-  const int w_n = n0 + w_nc * 8;
-  const bool w_n_ok = w_n < N;
-  const uint16_t* w_src = We + (size_t)(w_kc * S::KR) * N + (w_n_ok ? w_n : 0);
-
-  u32x4 a_reg[S::A_LOADS];
-  u32x4 w_reg[S::KR];
-
-  auto load_tiles = [&](int k0) {
-    const bool a_ok = (k0 + a_c * 8) < K;
+  uint32_t w_voff[S::W_INSTS];
+  int w_dst[S::W_INSTS];
 #pragma unroll
-    for (int i = 0; i < S::A_LOADS; ++i) {
-      a_reg[i] = a_ok ? *(const u32x4*)(a_src[i] + k0) : u32x4{0, 0, 0, 0};
-    }
+  for (int u = 0; u < S::W_INSTS; ++u) {
+    const int q = wave * S::W_INSTS + u;           // 2 k rows per instruction
+    const int kr = 2 * q + lane / 32;
+    const int c = (lane % 32) ^ swz_w(kr);
+    w_voff[u] = (uint32_t)kr * N * 2 + (uint32_t)(n0 + c * 8) * 2;
+    w_dst[u] = S::LDS_A + q * 1024;
+  }
+
+  // k0 may pass K on the last steps: the sizes clamp to 0 and every load
+  // returns zero without touching memory.
+  auto issue_loads = [&](int k0, int stage) {
+    const uint32_t a_skip = (uint32_t)k0 * 2, w_skip = (uint32_t)k0 * N * 2;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(a_base + k0, a_bytes > a_skip ? a_bytes - a_skip : 0u);
+    const __amdgpu_buffer_rsrc_t rw =
+        make_rsrc(We + (size_t)k0 * N, w_bytes > w_skip ? w_bytes - w_skip : 0u);
+    char* st = stages[stage];
 #pragma unroll
-    for (int i = 0; i < S::KR; ++i) {
-      const int k = k0 + w_kc * S::KR + i;
-      w_reg[i] = (w_n_ok && k < K) ? *(const u32x4*)(w_src + (size_t)(k0 + i) * N)
-                                   : u32x4{0, 0, 0, 0};
-    }
+    for (int u = 0; u < S::A_INSTS; ++u) load_to_lds(ra, st + a_dst[u], a_voff[u]);
+#pragma unroll
+    for (int u = 0; u < S::W_INSTS; ++u) load_to_lds(rw, st + w_dst[u], w_voff[u]);
   };
 
-  auto store_tiles = [&](int buf) {
-    uint16_t* As = lds + buf * (S::LDS_A + S::LDS_W);
-    uint16_t* Ws = As + S::LDS_A;
+  // --- fragment read offsets ------------------------------------------------
+  // token operand (MFMA B): row wrow0 + 32 j + lane%32, k = kk + 8 (lane/32) + 0..7
+  const int fr = lane % 32;
+  int fa[2];
 #pragma unroll
-    for (int i = 0; i < S::A_LOADS; ++i) {
-      const int r = tid / 8 + i * (S::NT / 8);
-      *(u32x4*)(As + r * LDS_STRIDE + a_c * 8) = a_reg[i];
-    }
-    // transpose the KR x 8 block: column n gets KR consecutive k values
+  for (int h = 0; h < 2; ++h) {
+    const int c = 2 * h + lane / 32;
+    fa[h] = (wrow0 + fr) * S::A_ROW + ((c ^ swz_a(fr)) * 16);
+  }
+  // weight operand (MFMA A, rows = columns n of W): two transposed reads per
+  // 32-column block i, for k = kk + 8 (g/2) + 4 rd + (0..3), g = lane/16, and
+  // column wn*TN + 32 i + 16 (g%2) + lane%16.  The block offset 4i sits in
+  // chunk bits 2..3, which the swizzle also flips, so each (h, rd, i) keeps
+  // its own offset.
+  const int g = lane / 16, li = lane % 16;
+  int fw[2][2][S::FN];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t p[S::KR / 2];
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int q = 0; q < S::KR / 2; ++q) {
-        p[q] = __builtin_amdgcn_perm(w_reg[2 * q + 1][n >> 1], w_reg[2 * q][n >> 1], sel);
+    for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+      for (int i = 0; i < S::FN; ++i) {
+        const int kr = 16 * h + 8 * (g / 2) + 4 * rd + li / 4;
+        const int nn = wn * S::TN + 32 * i + 16 * (g % 2) + 4 * (li % 4);
+        fw[h][rd][i] = S::LDS_A + kr * S::W_ROW + (((nn / 8) ^ swz_w(kr)) * 16) + (nn % 8) * 2;
       }
-      uint16_t* dst = Ws + (w_nc * 8 + n) * LDS_STRIDE + w_kc * S::KR;
-      if constexpr (S::KR == 8) {
-        *(u32x4*)dst = u32x4{p[0], p[1], p[2], p[3]};
-      } else {
-        *(u32x2*)dst = u32x2{p[0], p[1]};
-      }
-    }
-  };
 
-  f32x16 acc[S::FN][S::FM];
+  constexpr int FMA = NFM > 0 ? NFM : 1;
+  f32x16 acc[S::FN][FMA];
 #pragma unroll
   for (int i = 0; i < S::FN; ++i)
 #pragma unroll
-    for (int j = 0; j < S::FM; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < FMA; ++j) acc[i][j] = f32x16{};
 
-  // token blocks of this wave that hold at least one valid row
-  const int wrow0 = wm * S::TM;
-  const int nfm = max(0, min(S::FM, (tile.mrows - wrow0 + 31) / 32));
-
-  const int KT = (K + BK - 1) / BK;
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_tiles((kt + 1) * BK);
-    if (nfm > 0) {
-      const uint16_t* As = lds + buf * (S::LDS_A + S::LDS_W);
-      const uint16_t* Ws = As + S::LDS_A;
-      const int kl = (lane / 32) * 8;
-#pragma unroll
-      for (int kk = 0; kk < BK; kk += 16) {
-        bf16x8 wf[S::FN];
-        bf16x8 af[S::FM];
-#pragma unroll
-        for (int i = 0; i < S::FN; ++i) {
-          const int n = wn * S::TN + i * 32 + (lane % 32);
-          wf[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Ws + n * LDS_STRIDE + kk + kl));
-        }
-#pragma unroll
-        for (int j = 0; j < S::FM; ++j) {
-          if (j < nfm) {
-            const int m = wrow0 + j * 32 + (lane % 32);
-            af[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + m * LDS_STRIDE + kk + kl));
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < S::FM; ++j) {
-          if (j < nfm) {
-#pragma unroll
-            for (int i = 0; i < S::FN; ++i) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
-            }
-          }
-        }
-      }
-    }
-    if (kt + 1 < KT) store_tiles(buf ^ 1);
-    __syncthreads();
-  }
-
-  // --- epilogue: lane holds D[n][m] for m = lane%32 and 4 consecutive n ----
-#pragma unroll
-  for (int j = 0; j < S::FM; ++j) {
-    if (j >= nfm) continue;
-    const int m = wrow0 + j * 32 + (lane % 32);
-    if (m >= tile.mrows) continue;
-    uint16_t* crow = C + (size_t)(tile.row0 + m) * N;
+  auto read_frags = [&](const char* st, int h, bf16x8* wf, bf16x8* af) {
 #pragma unroll
     for (int i = 0; i < S::FN; ++i) {
+      const u32x2 lo = read_tr(st + fw[h][0][i]);
+      const u32x2 hi = read_tr(st + fw[h][1][i]);
+      wf[i] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * S::TN + i * 32 + g * 8 + (lane / 32) * 4;
-        if (n < N) {
-          float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-          float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          if (gelu) {
-            v0 = gelu_tanh(v0); v1 = gelu_tanh(v1);
-            v2 = gelu_tanh(v2); v3 = gelu_tanh(v3);
+    for (int j = 0; j < FMA; ++j)
+      af[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + fa[h] + j * 32 * S::A_ROW));
+  };
+
+  // Software pipeline (BK = 32 per step = two 16-wide k slices, 4 LDS
+  // stages).  Step kt:
+  //   first half   MFMAs of slice 0 (operands already in registers), each
+  //                paired with an LDS read of slice 1's operands;
+  //   middle       wait for this wave's loads of step kt+1, barrier: every
+  //                wave's part of stage kt+1 has landed and every wave is
+  //                done reading stage kt, so step kt+4's loads go into it;
+  //   second half  MFMAs of slice 1, each paired with an LDS read of step
+  //                kt+1's slice-0 operands.
+  // No MFMA waits on an LDS read issued after a barrier, and three steps of
+  // global loads stay in flight.  (A bare s_barrier: a release fence would
+  // wait for every outstanding load.)
+  bf16x8 wf0[S::FN], af0[FMA], wf1[S::FN], af1[FMA];
+  constexpr int NRD = 2 * S::FN + FMA;     // LDS read instructions per slice
+  constexpr int NMF = S::FN * NFM;         // MFMAs per slice
+
+  auto mfma_slice = [&](const bf16x8* wf, const bf16x8* af) {
+    if constexpr (NFM > 0) {
+#pragma unroll
+      for (int j = 0; j < NFM; ++j)
+#pragma unroll
+        for (int i = 0; i < S::FN; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  auto interleave = [&]() {
+    // [MFMA, LDS read] pairs, then the remaining MFMAs or reads
+    constexpr int P = NRD < NMF ? NRD : NMF;
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (NMF > P) __builtin_amdgcn_sched_group_barrier(0x008, NMF - P, 0);
+    if constexpr (NRD > P) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P, 0);
+  };
+
+  auto step = [&](int kt, int stage) {
+    const char* cur = stages[stage];
+    const char* nxt = stages[(stage + 1) % STAGES];
+    read_frags(cur, 1, wf1, af1);
+    mfma_slice(wf0, af0);
+    interleave();
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * S::LOADS));   // step kt+1 landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): reads of stage kt done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    issue_loads((kt + 4) * BK, stage);
+    read_frags(nxt, 0, wf0, af0);
+    mfma_slice(wf1, af1);
+    interleave();
+  };
+
+  // The loop runs a multiple of STAGES steps; steps past K read only zeros
+  // and add nothing.
+  const int KT = (K + BK - 1) / BK;
+  issue_loads(0, 0);
+  issue_loads(BK, 1);
+  issue_loads(2 * BK, 2);
+  issue_loads(3 * BK, 3);
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * S::LOADS));     // step 0 landed
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  read_frags(stages[0], 0, wf0, af0);
+  for (int kt = 0; kt < KT; kt += STAGES) {
+    step(kt, 0);
+    step(kt + 1, 1);
+    step(kt + 2, 2);
+    step(kt + 3, 3);
+  }
+  // drain the loads still in flight before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+
+  // --- epilogue: lane holds D[n][m] for m = lane%32 and 4 consecutive n ----
+  if constexpr (NFM > 0) {
+#pragma unroll
+    for (int j = 0; j < NFM; ++j) {
+      const int m = wrow0 + j * 32 + (lane % 32);
+      if (m >= tile.mrows) continue;
+      uint16_t* crow = C + (size_t)(tile.row0 + m) * N;
+#pragma unroll
+      for (int i = 0; i < S::FN; ++i) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * S::TN + i * 32 + gq * 8 + (lane / 32) * 4;
+          if (n < N) {
+            float v0 = acc[i][j][4 * gq + 0], v1 = acc[i][j][4 * gq + 1];
+            float v2 = acc[i][j][4 * gq + 2], v3 = acc[i][j][4 * gq + 3];
+            if (gelu) {
+              v0 = gelu_tanh(v0); v1 = gelu_tanh(v1);
+              v2 = gelu_tanh(v2); v3 = gelu_tanh(v3);
+            }
+            *(u32x2*)(crow + n) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
           }
-          *(u32x2*)(crow + n) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         }
       }
     }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_grouped(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
+    uint16_t* __restrict__ C, const int* __restrict__ off, int E, int R,
+    int K, int N, int gelu) {
+  using S = GemmShape<BM, BN, WM, WN>;
+  // one LDS array per pipeline stage, so the compiler can tell that a read of
+  // one stage does not wait on the in-flight loads into the others
+  __shared__ __attribute__((aligned(1024))) char lds0[S::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds1[S::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds2[S::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds3[S::LDS_STAGE];
+
+  const int NTN = (N + BN - 1) / BN;
+  const Tile tile = map_tile(off, E, R, BM, NTN, blockIdx.x);
+  if (!tile.valid) return;
+  const uint16_t* We = W + (size_t)tile.e * K * N;
+
+  // 32-row token blocks of this wave that hold valid rows (wave-uniform)
+  const int wm = (threadIdx.x / kWave) % WM;
+  int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
+  nfm = __builtin_amdgcn_readfirstlane(nfm);
+  static_assert(S::FM == 4, "dispatch below covers FM == 4");
+  switch (nfm) {
+    case 4: gemm_tile<BM, BN, WM, WN, 4>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
+    case 3: gemm_tile<BM, BN, WM, WN, 3>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
+    case 2: gemm_tile<BM, BN, WM, WN, 2>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
+    case 1: gemm_tile<BM, BN, WM, WN, 1>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
+    default: gemm_tile<BM, BN, WM, WN, 0>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
   }
 }
 

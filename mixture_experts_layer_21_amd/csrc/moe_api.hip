@@ -29,6 +29,7 @@ moe_status check_shape(int64_t T, int64_t H, int64_t E, int32_t top_k, int64_t F
   if (E > kMaxE || top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
   const int64_t wide = H > F ? H : F;
   if (T * top_k >= kIndexLimit / wide) return MOE_ERR_UNSUPPORTED;
+  if (H * F >= kIndexLimit) return MOE_ERR_UNSUPPORTED;   // one expert's W slab < 4 GiB
   return MOE_OK;
 }
 
