@@ -62,21 +62,7 @@ __device__ __forceinline__ int wave_bcast(int v, int src_lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM tile mapping.
-//
-// Expert e owns rows [off[e], off[e+1]) of the dispatched matrix and splits
-// them into m_e = ceil(rows_e / BM) row tiles; each row tile meets all NT
-// column tiles, so the layer has NREAL = NT * sum_e m_e tiles.  Tiles are
-// numbered expert by expert; inside an expert, consecutive tiles share the
-// column tile (the same weight slab) and walk its row tiles, so workgroups
-// running together read one weight slab from HBM once.
-//
-// The grid is launched with an upper bound of tiles (the host does not know
-// the per-expert counts).  Workgroup ids are dealt to the 8 XCDs round-robin,
-// so the id is remapped so that each XCD gets a contiguous run of ceil(NREAL/8)
-// logical tiles, which keeps the tiles that share a weight slab in one XCD's
-// L2.  Every wave of the block computes the same mapping (no LDS, no sync).
-// With off == nullptr the matrix is a single dense group of `dense_rows` rows.
+// Grouped GEMM tiles (see map_tile below for the numbering and XCD mapping).
 // ---------------------------------------------------------------------------
 struct Tile {
   int valid;
@@ -86,27 +72,11 @@ struct Tile {
   int nt;      // column tile index
 };
 
-__device__ __forceinline__ Tile map_tile(const int* __restrict__ off, int E,
-                                         int dense_rows, int BM, int NT,
-                                         int bid) {
-  Tile tile;
-  tile.valid = 0;
+// Number of row tiles, sum_e ceil(rows_e / BM) (wave-uniform).
+__device__ __forceinline__ int count_row_tiles(const int* __restrict__ off, int E,
+                                               int dense_rows, int BM) {
+  if (off == nullptr) return (dense_rows + BM - 1) / BM;
   const int lane = lane_id();
-  if (off == nullptr) {
-    const int mt = (dense_rows + BM - 1) / BM;
-    const int nreal = mt * NT;
-    const int per = (nreal + kXcds - 1) / kXcds;
-    const int L = (bid % kXcds) * per + bid / kXcds;
-    if (bid / kXcds >= per || L >= nreal) return tile;
-    tile.valid = 1;
-    tile.e = 0;
-    tile.nt = L / mt;
-    const int mi = L % mt;
-    tile.row0 = mi * BM;
-    tile.mrows = min(BM, dense_rows - tile.row0);
-    return tile;
-  }
-  // pass 1: total row tiles
   int total = 0;
   for (int c = 0; c < E; c += kWave) {
     const int e = c + lane;
@@ -115,11 +85,25 @@ __device__ __forceinline__ Tile map_tile(const int* __restrict__ off, int E,
     const int incl = wave_incl_scan(mt);
     total += wave_bcast(incl, kWave - 1);
   }
-  const int nreal = total * NT;
-  const int per = (nreal + kXcds - 1) / kXcds;
-  const int L = (bid % kXcds) * per + bid / kXcds;
-  if (bid / kXcds >= per || L >= nreal) return tile;
-  // pass 2: find the expert whose tile range holds L
+  return total;
+}
+
+// The tile with logical index L (0 <= L < row_tiles * NT).
+__device__ __forceinline__ Tile lookup_tile(const int* __restrict__ off, int E,
+                                            int dense_rows, int BM, int NT, int L) {
+  Tile tile;
+  tile.valid = 0;
+  const int lane = lane_id();
+  if (off == nullptr) {
+    const int mt = (dense_rows + BM - 1) / BM;
+    tile.valid = 1;
+    tile.e = 0;
+    tile.nt = L / mt;
+    const int mi = L % mt;
+    tile.row0 = mi * BM;
+    tile.mrows = min(BM, dense_rows - tile.row0);
+    return tile;
+  }
   int carry = 0;
   for (int c = 0; c < E; c += kWave) {
     const int e = c + lane;
@@ -150,6 +134,40 @@ __device__ __forceinline__ Tile map_tile(const int* __restrict__ off, int E,
     carry += wave_bcast(incl, kWave - 1);
   }
   return tile;
+}
+
+// Grouped GEMM tile mapping.
+//
+// Expert e owns rows [off[e], off[e+1]) of the dispatched matrix and splits
+// them into m_e = ceil(rows_e / BM) row tiles; each row tile meets all NT
+// column tiles, so the layer has NREAL = NT * sum_e m_e tiles.  Tiles are
+// numbered expert by expert; inside an expert, consecutive tiles share the
+// column tile (the same weight slab) and walk its row tiles, so workgroups
+// running together read one weight slab from HBM once.
+//
+// The grid is launched with an upper bound of tiles (the host does not know
+// the per-expert counts).  Workgroup ids are dealt to the 8 XCDs round-robin,
+// so the id is remapped so that each XCD gets a contiguous run of ceil(n/8)
+// logical tiles, which keeps the tiles that share a weight slab in one XCD's
+// L2.  Every wave of the block computes the same mapping (no LDS, no sync).
+// With off == nullptr the matrix is a single dense group of `dense_rows` rows.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int per = (n + kXcds - 1) / kXcds;
+  if (bid / kXcds >= per) return -1;
+  const int L = (bid % kXcds) * per + bid / kXcds;
+  return L < n ? L : -1;
+}
+
+__device__ __forceinline__ Tile map_tile(const int* __restrict__ off, int E,
+                                         int dense_rows, int BM, int NT, int bid) {
+  const int nreal = count_row_tiles(off, E, dense_rows, BM) * NT;
+  const int L = xcd_remap(bid, nreal);
+  if (L < 0) {
+    Tile t;
+    t.valid = 0;
+    return t;
+  }
+  return lookup_tile(off, E, dense_rows, BM, NT, L);
 }
 
 }  // namespace moe

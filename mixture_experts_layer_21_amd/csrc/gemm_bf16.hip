@@ -34,7 +34,8 @@ namespace moe {
 namespace {
 
 constexpr int BK = 32;          // K step (bf16 elements)
-constexpr int STAGES = 4;       // LDS ring: three K steps in flight
+constexpr int STAGES = 4;       // LDS ring: three K steps in flight (128 KB)
+constexpr int MIN_SPLIT_STEPS = 16;   // K steps per piece of a split tile, at least
 constexpr uint32_t kBufFlags = 0x00020000u;   // raw buffer, 32-bit data format
 
 template <int BM, int BN, int WM, int WN>
@@ -100,6 +101,14 @@ __device__ __forceinline__ u32x2 read_tr(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// How a tile's K range is shared: S pieces (S = 1: the whole tile in one
+// workgroup); this piece is s; partials of split tile `slot` live in `part`.
+struct Split {
+  int S, s, slot;
+  float* part;
+  int* counters;
+};
+
 // One output tile.  NFM (compile time) is the number of 32-row token blocks
 // of this wave that hold valid rows, so the main loop has no branches around
 // its LDS reads and MFMAs (the accumulators stay in AGPRs).
@@ -113,8 +122,9 @@ template <int BM, int BN, int WM, int WN, int NFM>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ We,
                                           uint16_t* __restrict__ C, const Tile& tile, int K,
-                                          int N, int gelu, char* lds0, char* lds1, char* lds2,
-                                          char* lds3) {
+                                          int N, int gelu, int kt_begin, int kt_end,
+                                          const Split& sp, char* lds0, char* lds1, char* lds2,
+                                          char* lds3, int* flag) {
   char* const stages[STAGES] = {lds0, lds1, lds2, lds3};
   using S = GemmShape<BM, BN, WM, WN>;
   const int tid = threadIdx.x;
@@ -128,7 +138,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   // --- loader offsets (constant over the K loop) ---------------------------
   const uint16_t* a_base = A + (size_t)tile.row0 * K;
   const uint32_t a_bytes = (uint32_t)tile.mrows * K * 2;
-  const uint32_t w_bytes = (uint32_t)K * N * 2;
+  // W rows at or past k_limit read as zero: a split piece covers only its
+  // own K range
+  const int k_limit = min(K, kt_end * BK);
+  const uint32_t w_bytes = (uint32_t)k_limit * N * 2;
   uint32_t a_voff[S::A_INSTS];
   int a_dst[S::A_INSTS];
 #pragma unroll
@@ -254,35 +267,76 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
     read_frags(cur, 1, wf1, af1);
     mfma_slice(wf0, af0);
     interleave();
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * S::LOADS));   // step kt+1 landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_le((STAGES - 2) * S::LOADS));   // step kt+1 landed
     __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): reads of stage kt done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    issue_loads((kt + 4) * BK, stage);
+    issue_loads((kt + STAGES) * BK, stage);
     read_frags(nxt, 0, wf0, af0);
     mfma_slice(wf1, af1);
     interleave();
   };
 
-  // The loop runs a multiple of STAGES steps; steps past K read only zeros
-  // and add nothing.
-  const int KT = (K + BK - 1) / BK;
-  issue_loads(0, 0);
-  issue_loads(BK, 1);
-  issue_loads(2 * BK, 2);
-  issue_loads(3 * BK, 3);
-  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * S::LOADS));     // step 0 landed
+  // The loop runs a multiple of STAGES steps; steps past the K range read
+  // only zeros and add nothing.
+  const int k0 = kt_begin * BK;
+#pragma unroll
+  for (int st = 0; st < STAGES; ++st) issue_loads(k0 + st * BK, st);
+  __builtin_amdgcn_s_waitcnt(vmcnt_le((STAGES - 1) * S::LOADS));   // first step landed
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   read_frags(stages[0], 0, wf0, af0);
-  for (int kt = 0; kt < KT; kt += STAGES) {
-    step(kt, 0);
-    step(kt + 1, 1);
-    step(kt + 2, 2);
-    step(kt + 3, 3);
+  for (int kt = kt_begin; kt < kt_end; kt += STAGES) {
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st) step(kt + st, st);
   }
   // drain the loads still in flight before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+
+  // --- split tiles: partial sums meet in the workspace ---------------------
+  // Each piece stores its fp32 accumulators, then counts itself in; the last
+  // piece to arrive adds the S partials in split order (so the result does not
+  // depend on arrival order) and runs the epilogue.  sp is uniform over the
+  // workgroup and every wave, whatever its NFM, runs the same two barriers.
+  if (sp.S > 1) {
+    constexpr int PER_PIECE = S::FN * S::FM * 16 * S::NT;
+    if constexpr (NFM > 0) {
+      float* mine = sp.part + ((size_t)sp.slot * sp.S + sp.s) * PER_PIECE;
+#pragma unroll
+      for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < NFM; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; v += 4)
+            *(f32x4*)(mine + (((i * S::FM + j) * 16 + v) * S::NT + tid * 4)) =
+                f32x4{acc[i][j][v], acc[i][j][v + 1], acc[i][j][v + 2], acc[i][j][v + 3]};
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) *flag = atomicAdd(&sp.counters[sp.slot], 1);
+    __syncthreads();
+    if (*flag != sp.S - 1) return;
+    __threadfence();
+    if constexpr (NFM > 0) {
+      const float* all = sp.part + (size_t)sp.slot * sp.S * PER_PIECE;
+#pragma unroll
+      for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < NFM; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; v += 4) {
+            const size_t q = ((i * S::FM + j) * 16 + v) * S::NT + tid * 4;
+            f32x4 sum = *(const f32x4*)(all + q);
+            for (int ps = 1; ps < sp.S; ++ps)
+              sum += *(const f32x4*)(all + (size_t)ps * PER_PIECE + q);
+            acc[i][j][v] = sum[0];
+            acc[i][j][v + 1] = sum[1];
+            acc[i][j][v + 2] = sum[2];
+            acc[i][j][v + 3] = sum[3];
+          }
+    }
+    if (tid == 0) atomicExch(&sp.counters[sp.slot], 0);   // leave the counter clear
+  }
 
   // --- epilogue: lane holds D[n][m] for m = lane%32 and 4 consecutive n ----
   if constexpr (NFM > 0) {
@@ -311,11 +365,16 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   }
 }
 
+// Work split (stream-K style, deterministic): the first floor(n / slots)
+// rounds of `slots` tiles (slots = workgroups the GPU runs at once) run whole;
+// the remaining tiles are split along K into S pieces each, so that the last
+// round keeps every CU busy instead of leaving most of them idle.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_grouped(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     uint16_t* __restrict__ C, const int* __restrict__ off, int E, int R,
-    int K, int N, int gelu) {
+    int K, int N, int gelu, float* __restrict__ part, int* __restrict__ counters,
+    int slots) {
   using S = GemmShape<BM, BN, WM, WN>;
   // one LDS array per pipeline stage, so the compiler can tell that a read of
   // one stage does not wait on the in-flight loads into the others
@@ -323,9 +382,33 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   __shared__ __attribute__((aligned(1024))) char lds1[S::LDS_STAGE];
   __shared__ __attribute__((aligned(1024))) char lds2[S::LDS_STAGE];
   __shared__ __attribute__((aligned(1024))) char lds3[S::LDS_STAGE];
+  __shared__ int flag;
 
   const int NTN = (N + BN - 1) / BN;
-  const Tile tile = map_tile(off, E, R, BM, NTN, blockIdx.x);
+  const int KT = (K + BK - 1) / BK;
+  const int nreal = count_row_tiles(off, E, R, BM) * NTN;
+  const int dp = (nreal / slots) * slots;          // tiles run whole
+  const int sk = nreal - dp;                       // tiles split along K
+  int nsplit = 1;
+  // (short-K GEMMs gain less from filling the last round than the partials
+  // and shorter pipelines cost them)
+  if (sk > 0 && KT >= 8 * MIN_SPLIT_STEPS) nsplit = max(1, min(slots / sk, KT / MIN_SPLIT_STEPS));
+  const int bid = blockIdx.x;
+  int L, kt_begin = 0, kt_end = KT;
+  Split sp{1, 0, 0, part, counters};
+  if (bid < dp) {
+    L = xcd_remap(bid, dp);
+  } else {
+    const int p = bid - dp;
+    if (p >= sk * nsplit) return;
+    L = dp + p / nsplit;
+    sp.S = nsplit;
+    sp.s = p % nsplit;
+    sp.slot = L - dp;
+    kt_begin = sp.s * KT / nsplit;
+    kt_end = (sp.s + 1) * KT / nsplit;
+  }
+  const Tile tile = lookup_tile(off, E, R, BM, NTN, L);
   if (!tile.valid) return;
   const uint16_t* We = W + (size_t)tile.e * K * N;
 
@@ -334,35 +417,71 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
   nfm = __builtin_amdgcn_readfirstlane(nfm);
   static_assert(S::FM == 4, "dispatch below covers FM == 4");
+#define MOE_TILE(NF) gemm_tile<BM, BN, WM, WN, NF>(A, We, C, tile, K, N, gelu, kt_begin, kt_end, \
+                                                 sp, lds0, lds1, lds2, lds3, &flag)
   switch (nfm) {
-    case 4: gemm_tile<BM, BN, WM, WN, 4>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
-    case 3: gemm_tile<BM, BN, WM, WN, 3>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
-    case 2: gemm_tile<BM, BN, WM, WN, 2>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
-    case 1: gemm_tile<BM, BN, WM, WN, 1>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
-    default: gemm_tile<BM, BN, WM, WN, 0>(A, We, C, tile, K, N, gelu, lds0, lds1, lds2, lds3); break;
+    case 4: MOE_TILE(4); break;
+    case 3: MOE_TILE(3); break;
+    case 2: MOE_TILE(2); break;
+    case 1: MOE_TILE(1); break;
+    default: MOE_TILE(0); break;
   }
+#undef MOE_TILE
+}
+
+__global__ void zero_ints(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+int device_slots() {
+  // one 256x256 workgroup per CU (128 KB of LDS), capped at kMaxSlots
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kMaxSlots;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = kMaxSlots;
+    cached[dev] = std::min(cus, kMaxSlots);
+  }
+  return cached[dev];
 }
 
 template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const void* A, const void* W, void* C, const int* off,
-                      int E, int R, int K, int N, bool gelu, hipStream_t s) {
+hipError_t launch_cfg(const void* A, const void* W, void* C, const int* off, int E, int R,
+                      int K, int N, bool gelu, void* split_ws, hipStream_t s) {
   const int NTN = (N + BN - 1) / BN;
   // upper bound of row tiles: sum_e ceil(rows_e / BM) <= ceil(R / BM) + min(E, R)
   const long mt_max = off ? (long)(R + BM - 1) / BM + (long)min(E, R) : (long)(R + BM - 1) / BM;
-  long blocks = mt_max * NTN;
-  blocks = (blocks + kXcds - 1) / kXcds * kXcds;
-  if (blocks <= 0) return hipSuccess;
+  const int slots = device_slots();
+  // whole tiles (< n) plus at most `slots` pieces of split tiles
+  long blocks = mt_max * NTN + slots;
+  if (blocks <= slots) return hipSuccess;
+  float* part = (float*)split_ws;
+  int* counters = (int*)((char*)split_ws + split_part_bytes());
   hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN>), dim3((unsigned)blocks),
                      dim3(kWave * WM * WN), 0, s, (const uint16_t*)A, (const uint16_t*)W,
-                     (uint16_t*)C, off, E, R, K, N, gelu ? 1 : 0);
+                     (uint16_t*)C, off, E, R, K, N, gelu ? 1 : 0, part, counters, slots);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, const int* off,
-                            int E, int R, int K, int N, bool gelu, hipStream_t s) {
-  return launch_cfg<256, 256, 2, 2>(A, W, C, off, E, R, K, N, gelu, s);
+size_t split_part_bytes() { return (size_t)kMaxSlots * 256 * 256 * sizeof(float); }
+size_t split_ws_bytes() { return split_part_bytes() + align_up(kMaxSlots * sizeof(int)); }
+
+hipError_t clear_split_counters(void* split_ws, hipStream_t s) {
+  int* counters = (int*)((char*)split_ws + split_part_bytes());
+  hipLaunchKernelGGL(zero_ints, dim3((kMaxSlots + 255) / 256), dim3(256), 0, s, counters,
+                     kMaxSlots);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, const int* off, int E, int R,
+                            int K, int N, bool gelu, void* split_ws, hipStream_t s) {
+  return launch_cfg<256, 256, 2, 2>(A, W, C, off, E, R, K, N, gelu, split_ws, s);
 }
 
 }  // namespace moe

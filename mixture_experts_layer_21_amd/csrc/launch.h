@@ -28,8 +28,15 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
                           size_t elem_bytes, int32_t* offsets, int32_t* sorted_token,
                           int32_t* inv_pos, void* xp, void* ws, hipStream_t s);
 
+// Split-tile workspace of the bf16 grouped GEMM: fp32 partials of at most
+// kMaxSlots pieces plus one counter per split tile (cleared before the GEMMs
+// of one FFN; every split tile leaves its counter clear again).
+constexpr int kMaxSlots = 256;
+size_t split_part_bytes();
+size_t split_ws_bytes();
+hipError_t clear_split_counters(void* split_ws, hipStream_t s);
 hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, const int* off, int E,
-                            int R, int K, int N, bool gelu, hipStream_t s);
+                            int R, int K, int N, bool gelu, void* split_ws, hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, const float* W, float* C, const int* off, int E,
                            int R, int K, int N, int ldc, bool gelu, hipStream_t s);
 

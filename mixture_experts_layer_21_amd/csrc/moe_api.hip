@@ -33,8 +33,11 @@ moe_status check_shape(int64_t T, int64_t H, int64_t E, int32_t top_k, int64_t F
   return MOE_OK;
 }
 
+// expert FFN workspace: h[R,F], then (bf16) the GEMM's split-tile partials
 size_t ffn_ws_bytes(int64_t R, int64_t F, moe_dtype dt) {
-  return align_up((size_t)R * F * elem_bytes(dt));
+  size_t b = align_up((size_t)R * F * elem_bytes(dt));
+  if (dt == MOE_BF16) b += moe::split_ws_bytes();
+  return b;
 }
 
 // moe_forward workspace: routing outputs, dispatch indices, xp, yp, and one
@@ -71,9 +74,13 @@ moe_status run_ffn(const void* xp, const int32_t* off, const void* w1, const voi
   if (R == 0) return MOE_OK;
   hipError_t err;
   if (dt == MOE_BF16) {
-    err = moe::launch_gemm_bf16(xp, w1, h, off, (int)E, (int)R, (int)H, (int)F, true, s);
+    void* split = (char*)h + align_up((size_t)R * F * elem_bytes(dt));
+    err = moe::clear_split_counters(split, s);
     if (err == hipSuccess)
-      err = moe::launch_gemm_bf16(h, w2, yp, off, (int)E, (int)R, (int)F, (int)H, false, s);
+      err = moe::launch_gemm_bf16(xp, w1, h, off, (int)E, (int)R, (int)H, (int)F, true, split, s);
+    if (err == hipSuccess)
+      err = moe::launch_gemm_bf16(h, w2, yp, off, (int)E, (int)R, (int)F, (int)H, false, split,
+                                  s);
   } else {
     err = moe::launch_gemm_f32((const float*)xp, (const float*)w1, (float*)h, off, (int)E,
                                (int)R, (int)H, (int)F, (int)F, true, s);
