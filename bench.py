@@ -45,7 +45,112 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: per-workload default)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                              "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE counter files into the traffic "
+                         "record under profiles/ and exit")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy")
     return ap.parse_args()
+
+
+GEMM_SOURCES = ["mixture_experts_layer_21_amd/csrc/gemm_bf16.hip",
+                "mixture_experts_layer_21_amd/csrc/common.h"]
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_gemm_bf16_grouped_{workload}.md")
+
+
+def calibrate_copy(mib: int):
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n}))
+
+
+def _counter_per_dispatch(csv_path: str, counter: str, kernel_substr: str):
+    import csv
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {csv_path}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def summarize_traffic(a):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the grouped GEMM, scaled by
+    what the same counters read for a plain copy of known size."""
+    fetch, nd = _counter_per_dispatch(a.summarize_traffic[0], "FETCH_SIZE", "gemm_bf16_grouped")
+    write, _ = _counter_per_dispatch(a.summarize_traffic[1], "WRITE_SIZE", "gemm_bf16_grouped")
+    copy_kernel = "copy"
+    cf, _ = _counter_per_dispatch(a.summarize_traffic[2], "FETCH_SIZE", copy_kernel)
+    cw, _ = _counter_per_dispatch(a.summarize_traffic[3], "WRITE_SIZE", copy_kernel)
+    nbytes = a.copy_mib << 20
+    f_fetch = nbytes / (cf * 1024.0)
+    f_write = nbytes / (cw * 1024.0)
+    rec = {"kernel": "gemm_bf16_grouped", "workload": a.config, "source_hash": gemm_source_hash(),
+           "dispatches": nd, "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "copy_bytes": nbytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_factor": f_fetch, "write_factor": f_write,
+           "traffic_bytes_per_launch": fetch * 1024.0 * f_fetch + write * 1024.0 * f_write}
+    path = traffic_record_path(a.config)
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic of gemm_bf16_grouped on {a.config}\n\n")
+        fh.write("Counters from two rocprofv3 passes over the bench (FETCH_SIZE, then "
+                 "WRITE_SIZE, KiB per dispatch, averaged over the GEMM's dispatches), each "
+                 "scaled by the ratio of true bytes to counted bytes for a plain "
+                 f"{a.copy_mib} MiB device copy (torch copy kernel) under the same counter.\n\n")
+        fh.write("Commands (run from the repository root on the GPU host):\n\n```\n")
+        fh.write(f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o f -- python3 bench.py "
+                 f"--config {a.config} --steps 3 --warmup 1 --no-cpu-baseline\n")
+        fh.write(f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o w -- python3 bench.py "
+                 f"--config {a.config} --steps 3 --warmup 1 --no-cpu-baseline\n")
+        fh.write(f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o cf -- python3 bench.py "
+                 f"--calibrate-copy-mib {a.copy_mib}\n")
+        fh.write(f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o cw -- python3 bench.py "
+                 f"--calibrate-copy-mib {a.copy_mib}\n")
+        fh.write(f"python3 bench.py --config {a.config} --summarize-traffic <f csv> <w csv> "
+                 "<cf csv> <cw csv>\n```\n\n")
+        fh.write(f"| quantity | value |\n|---|---|\n")
+        fh.write(f"| GEMM dispatches averaged | {nd} |\n")
+        fh.write(f"| FETCH_SIZE per dispatch | {fetch:.0f} KiB |\n")
+        fh.write(f"| WRITE_SIZE per dispatch | {write:.0f} KiB |\n")
+        fh.write(f"| copy of {nbytes} B: FETCH / WRITE | {cf:.0f} / {cw:.0f} KiB |\n")
+        fh.write(f"| scale factors fetch / write | {f_fetch:.4f} / {f_write:.4f} |\n")
+        fh.write(f"| HBM bytes per launch | {rec['traffic_bytes_per_launch'] / 1e9:.4f} GB |\n\n")
+        fh.write("The record below is read by bench.py; it is ignored once the GEMM sources "
+                 "change (source_hash).\n\n```json\n" + json.dumps(rec, indent=1) + "\n```\n")
+    print(f"wrote {path}")
+
+
+def read_traffic(workload: str):
+    path = traffic_record_path(workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        rec = json.loads(text.split("```json")[1].split("```")[0])
+    except (IndexError, ValueError):
+        return None
+    if rec.get("source_hash") != gemm_source_hash():
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def alg_counts(cfg, ids: np.ndarray):
@@ -129,6 +234,9 @@ def cpu_baseline(cfg, L, n_tokens):
 
 def main():
     a = parse()
+    if a.summarize_traffic:
+        summarize_traffic(a)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {a.gpus} requested): the MoE forward "
               "here is a single-GPU hot path with no collectives.", file=sys.stderr)
@@ -136,6 +244,9 @@ def main():
     import mixture_experts_layer_21_amd as moe
     cfg = mi.CONFIGS[a.config]
     torch.cuda.set_device(0)
+    if a.calibrate_copy_mib:
+        calibrate_copy(a.calibrate_copy_mib)
+        return
     L = mi.make_inputs(cfg, "cuda")
     dev = "cuda"
     nbytes = moe.moe_workspace_bytes(cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.torch_dtype)
@@ -173,7 +284,7 @@ def main():
         roof = {"bound": "hbm", "achieved": g_bytes / g_sec / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = read_traffic(cfg.name) if cfg.dtype == "bf16" else None
     roof["kernel"] = "gemm_bf16_grouped" if cfg.dtype == "bf16" else "gemm_f32_grouped"
     roof["per_launch"] = {"flops": g_flops, "bytes": g_bytes, "ms": g_sec * 1e3}
 
