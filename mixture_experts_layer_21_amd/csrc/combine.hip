@@ -1,75 +1,98 @@
 // Combine (fused MoE article, ScatterWithWeights): every token's k expert
 // rows, scaled by their gate weights, accumulated into y.  The article adds
-// into y expert by expert; here it is the equivalent gather form, one wave
-// per token summing its k rows in slot order in fp32 (no atomics, so the
-// result is deterministic), then one rounded store per element.
+// into y expert by expert; here it is the equivalent gather form: one thread
+// per (token, 16-byte chunk of the row) sums the token's k rows in slot order
+// in fp32 (no atomics, so the result is deterministic), then makes one
+// rounded store.  All k row loads of a thread are issued before any is used,
+// and the grid has one thread per output chunk, so the pass is bound by HBM
+// bandwidth rather than by load latency even for a handful of tokens.
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
-// bf16: lane handles 8 elements (16 B) per step
+constexpr int kMaxK = 16;
+
+// bf16: a chunk is 8 elements
 __global__ __launch_bounds__(256) void combine_bf16(const u32x4* __restrict__ yp,
                                                     const int32_t* __restrict__ inv_pos,
                                                     const float* __restrict__ w,
-                                                    u32x4* __restrict__ y, int T, int H,
+                                                    u32x4* __restrict__ y, int T, int chunks,
                                                     int k) {
-  const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (t >= T) return;
-  const int chunks = H / 8;
-  for (int c = lane; c < chunks; c += kWave) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
+  const long item = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= (long)T * chunks) return;
+  const int t = (int)(item / chunks), c = (int)(item % chunks);
+  u32x4 v[kMaxK];
+  float wj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
       const int p = inv_pos[(size_t)t * k + j];
-      const float wj = w[(size_t)t * k + j];
-      const u32x4 v = yp[(size_t)p * chunks + c];
+      wj[j] = w[(size_t)t * k + j];
+      v[j] = yp[(size_t)p * chunks + c];
+    }
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = __builtin_fmaf(wj, bf16_to_f32(v[q] & 0xFFFFu), acc[2 * q]);
-        acc[2 * q + 1] = __builtin_fmaf(wj, bf16_to_f32(v[q] >> 16), acc[2 * q + 1]);
+        acc[2 * q] = __builtin_fmaf(wj[j], bf16_to_f32(v[j][q] & 0xFFFFu), acc[2 * q]);
+        acc[2 * q + 1] = __builtin_fmaf(wj[j], bf16_to_f32(v[j][q] >> 16), acc[2 * q + 1]);
       }
     }
-    y[(size_t)t * chunks + c] = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                      pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
   }
+  y[item] = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                  pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
 }
 
-// fp32: lane handles 4 elements (16 B) per step
+// fp32: a chunk is 4 elements
 __global__ __launch_bounds__(256) void combine_f32(const float4* __restrict__ yp,
                                                    const int32_t* __restrict__ inv_pos,
                                                    const float* __restrict__ w,
-                                                   float4* __restrict__ y, int T, int H,
+                                                   float4* __restrict__ y, int T, int chunks,
                                                    int k) {
-  const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (t >= T) return;
-  const int chunks = H / 4;
-  for (int c = lane; c < chunks; c += kWave) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
+  const long item = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= (long)T * chunks) return;
+  const int t = (int)(item / chunks), c = (int)(item % chunks);
+  float4 v[kMaxK];
+  float wj[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
       const int p = inv_pos[(size_t)t * k + j];
-      const float wj = w[(size_t)t * k + j];
-      const float4 v = yp[(size_t)p * chunks + c];
-      acc.x = __builtin_fmaf(wj, v.x, acc.x);
-      acc.y = __builtin_fmaf(wj, v.y, acc.y);
-      acc.z = __builtin_fmaf(wj, v.z, acc.z);
-      acc.w = __builtin_fmaf(wj, v.w, acc.w);
+      wj[j] = w[(size_t)t * k + j];
+      v[j] = yp[(size_t)p * chunks + c];
     }
-    y[(size_t)t * chunks + c] = acc;
   }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      acc.x = __builtin_fmaf(wj[j], v[j].x, acc.x);
+      acc.y = __builtin_fmaf(wj[j], v[j].y, acc.y);
+      acc.z = __builtin_fmaf(wj[j], v[j].z, acc.z);
+      acc.w = __builtin_fmaf(wj[j], v[j].w, acc.w);
+    }
+  }
+  y[item] = acc;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const void* yp, const int32_t* inv_pos, const float* w, int T,
                           int H, int k, bool bf16, void* y, hipStream_t s) {
-  dim3 g((T + 3) / 4), b(256);
+  const int chunks = bf16 ? H / 8 : H / 4;
+  const long items = (long)T * chunks;
+  dim3 g((unsigned)((items + 255) / 256)), b(256);
   if (bf16)
-    hipLaunchKernelGGL(combine_bf16, g, b, 0, s, (const u32x4*)yp, inv_pos, w, (u32x4*)y, T, H, k);
+    hipLaunchKernelGGL(combine_bf16, g, b, 0, s, (const u32x4*)yp, inv_pos, w, (u32x4*)y, T,
+                       chunks, k);
   else
-    hipLaunchKernelGGL(combine_f32, g, b, 0, s, (const float4*)yp, inv_pos, w, (float4*)y, T, H, k);
+    hipLaunchKernelGGL(combine_f32, g, b, 0, s, (const float4*)yp, inv_pos, w, (float4*)y, T,
+                       chunks, k);
   return hipGetLastError();
 }
 

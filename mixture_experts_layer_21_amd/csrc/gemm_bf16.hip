@@ -37,6 +37,7 @@ constexpr int BK = 32;          // K step (bf16 elements)
 constexpr int STAGES = 4;       // LDS ring: three K steps in flight (128 KB)
 constexpr int MIN_SPLIT_STEPS = 16;   // K steps per piece of a split tile, at least
 constexpr uint32_t kBufFlags = 0x00020000u;   // raw buffer, 32-bit data format
+constexpr uint32_t kPastEnd = 0xFFFFFFF0u;    // buffer offset that reads as zero
 
 template <int BM, int BN, int WM, int WN>
 struct GemmShape {
@@ -120,6 +121,7 @@ struct Split {
 // zero W rows.)  Columns past N read neighbouring data that is never stored.
 template <int BM, int BN, int WM, int WN, int NFM>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
+                                          const int* __restrict__ gather, int a_rows,
                                           const uint16_t* __restrict__ We,
                                           uint16_t* __restrict__ C, const Tile& tile, int K,
                                           int N, int gelu, int kt_begin, int kt_end,
@@ -136,8 +138,11 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   const int wrow0 = wm * S::TM;
 
   // --- loader offsets (constant over the K loop) ---------------------------
-  const uint16_t* a_base = A + (size_t)tile.row0 * K;
-  const uint32_t a_bytes = (uint32_t)tile.mrows * K * 2;
+  // Token rows: row0+m of A, or row gather[row0+m] of A when the token rows
+  // are gathered straight from x (dispatch fused into the load).  Rows past
+  // the tile get an offset past the buffer end and read as zero.
+  const uint16_t* a_base = A;
+  const uint32_t a_bytes = (uint32_t)a_rows * K * 2;
   // W rows at or past k_limit read as zero: a split piece covers only its
   // own K range
   const int k_limit = min(K, kt_end * BK);
@@ -149,7 +154,12 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
     const int q = wave * S::A_INSTS + u;           // 16 rows per instruction
     const int m = q * 16 + lane / 4;
     const int c = (lane % 4) ^ swz_a(m);           // logical chunk stored at lane's slot
-    a_voff[u] = (uint32_t)m * K * 2 + c * 16;
+    uint32_t voff = kPastEnd;
+    if (m < tile.mrows) {
+      const int grow = gather ? gather[tile.row0 + m] : tile.row0 + m;
+      voff = (uint32_t)grow * K * 2 + c * 16;
+    }
+    a_voff[u] = voff;
     a_dst[u] = q * 1024;
   }
   uint32_t w_voff[S::W_INSTS];
@@ -371,9 +381,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
 // round keeps every CU busy instead of leaving most of them idle.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_grouped(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-    uint16_t* __restrict__ C, const int* __restrict__ off, int E, int R,
-    int K, int N, int gelu, float* __restrict__ part, int* __restrict__ counters,
+    const uint16_t* __restrict__ A, const int* __restrict__ gather, int a_rows,
+    const uint16_t* __restrict__ W, uint16_t* __restrict__ C, const int* __restrict__ off,
+    int E, int R, int K, int N, int gelu, float* __restrict__ part, int* __restrict__ counters,
     int slots) {
   using S = GemmShape<BM, BN, WM, WN>;
   // one LDS array per pipeline stage, so the compiler can tell that a read of
@@ -417,7 +427,8 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
   nfm = __builtin_amdgcn_readfirstlane(nfm);
   static_assert(S::FM == 4, "dispatch below covers FM == 4");
-#define MOE_TILE(NF) gemm_tile<BM, BN, WM, WN, NF>(A, We, C, tile, K, N, gelu, kt_begin, kt_end, \
+#define MOE_TILE(NF) gemm_tile<BM, BN, WM, WN, NF>(A, gather, a_rows, We, C, tile, K, N, gelu, \
+                                                 kt_begin, kt_end, \
                                                  sp, lds0, lds1, lds2, lds3, &flag)
   switch (nfm) {
     case 4: MOE_TILE(4); break;
@@ -450,8 +461,9 @@ int device_slots() {
 }
 
 template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const void* A, const void* W, void* C, const int* off, int E, int R,
-                      int K, int N, bool gelu, void* split_ws, hipStream_t s) {
+hipError_t launch_cfg(const void* A, const int* gather, int a_rows, const void* W, void* C,
+                      const int* off, int E, int R, int K, int N, bool gelu, void* split_ws,
+                      hipStream_t s) {
   const int NTN = (N + BN - 1) / BN;
   // upper bound of row tiles: sum_e ceil(rows_e / BM) <= ceil(R / BM) + min(E, R)
   const long mt_max = off ? (long)(R + BM - 1) / BM + (long)min(E, R) : (long)(R + BM - 1) / BM;
@@ -462,8 +474,9 @@ hipError_t launch_cfg(const void* A, const void* W, void* C, const int* off, int
   float* part = (float*)split_ws;
   int* counters = (int*)((char*)split_ws + split_part_bytes());
   hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN>), dim3((unsigned)blocks),
-                     dim3(kWave * WM * WN), 0, s, (const uint16_t*)A, (const uint16_t*)W,
-                     (uint16_t*)C, off, E, R, K, N, gelu ? 1 : 0, part, counters, slots);
+                     dim3(kWave * WM * WN), 0, s, (const uint16_t*)A, gather, a_rows,
+                     (const uint16_t*)W, (uint16_t*)C, off, E, R, K, N, gelu ? 1 : 0, part,
+                     counters, slots);
   return hipGetLastError();
 }
 
@@ -479,9 +492,11 @@ hipError_t clear_split_counters(void* split_ws, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, const int* off, int E, int R,
-                            int K, int N, bool gelu, void* split_ws, hipStream_t s) {
-  return launch_cfg<256, 256, 2, 2>(A, W, C, off, E, R, K, N, gelu, split_ws, s);
+hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
+                            void* C, const int* off, int E, int R, int K, int N, bool gelu,
+                            void* split_ws, hipStream_t s) {
+  return launch_cfg<256, 256, 2, 2>(A, gather, a_rows, W, C, off, E, R, K, N, gelu, split_ws,
+                                    s);
 }
 
 }  // namespace moe

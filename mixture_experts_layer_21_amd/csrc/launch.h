@@ -24,6 +24,7 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias, int T
                         hipStream_t s);
 
 size_t permute_ws_bytes(int R, int E);
+// xp == nullptr: indices only (the rows are gathered later by the GEMM)
 hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E, int k,
                           size_t elem_bytes, int32_t* offsets, int32_t* sorted_token,
                           int32_t* inv_pos, void* xp, void* ws, hipStream_t s);
@@ -35,8 +36,11 @@ constexpr int kMaxSlots = 256;
 size_t split_part_bytes();
 size_t split_ws_bytes();
 hipError_t clear_split_counters(void* split_ws, hipStream_t s);
-hipError_t launch_gemm_bf16(const void* A, const void* W, void* C, const int* off, int E,
-                            int R, int K, int N, bool gelu, void* split_ws, hipStream_t s);
+// A holds a_rows rows of K; with gather != nullptr, dispatched row p is row
+// gather[p] of A (the dispatch fused into the GEMM's loads), else row p.
+hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
+                            void* C, const int* off, int E, int R, int K, int N, bool gelu,
+                            void* split_ws, hipStream_t s);
 hipError_t launch_gemm_f32(const float* A, const float* W, float* C, const int* off, int E,
                            int R, int K, int N, int ldc, bool gelu, hipStream_t s);
 

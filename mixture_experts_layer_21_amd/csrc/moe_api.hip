@@ -11,7 +11,7 @@ using moe::align_up;
 
 constexpr int64_t kMaxE = 1024;
 constexpr int32_t kMaxTopK = 16;
-constexpr int64_t kIndexLimit = (int64_t)1 << 31;
+constexpr int64_t kIndexLimit = ((int64_t)1 << 31) - 64;
 
 size_t elem_bytes(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
 
@@ -56,7 +56,8 @@ FwdLayout fwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_
   L.offsets = o; o += align_up((size_t)(E + 1) * 4);
   L.sorted = o;  o += align_up((size_t)R * 4);
   L.inv = o;     o += align_up((size_t)R * 4);
-  L.xp = o;      o += align_up((size_t)R * H * es);
+  L.xp = o;      // fp32 only: the bf16 GEMM gathers token rows from x itself
+  if (dt == MOE_F32) o += align_up((size_t)R * H * es);
   L.yp = o;      o += align_up((size_t)R * H * es);
   L.stage = o;
   size_t st = moe::route_ws_bytes((int)T, (int)H, (int)E, dt == MOE_BF16);
@@ -68,19 +69,23 @@ FwdLayout fwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_
 
 moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
-moe_status run_ffn(const void* xp, const int32_t* off, const void* w1, const void* w2,
-                   int64_t R, int64_t H, int64_t E, int64_t F, moe_dtype dt, void* yp,
-                   void* h, hipStream_t s) {
+// Expert FFN.  The first GEMM reads its token rows from xp (a_rows = R rows,
+// gather == nullptr) or straight from x through gather = sorted_token
+// (a_rows = T rows).
+moe_status run_ffn(const void* xp, const int32_t* gather, int64_t a_rows, const int32_t* off,
+                   const void* w1, const void* w2, int64_t R, int64_t H, int64_t E, int64_t F,
+                   moe_dtype dt, void* yp, void* h, hipStream_t s) {
   if (R == 0) return MOE_OK;
   hipError_t err;
   if (dt == MOE_BF16) {
     void* split = (char*)h + align_up((size_t)R * F * elem_bytes(dt));
     err = moe::clear_split_counters(split, s);
     if (err == hipSuccess)
-      err = moe::launch_gemm_bf16(xp, w1, h, off, (int)E, (int)R, (int)H, (int)F, true, split, s);
+      err = moe::launch_gemm_bf16(xp, gather, (int)a_rows, w1, h, off, (int)E, (int)R, (int)H,
+                                  (int)F, true, split, s);
     if (err == hipSuccess)
-      err = moe::launch_gemm_bf16(h, w2, yp, off, (int)E, (int)R, (int)F, (int)H, false, split,
-                                  s);
+      err = moe::launch_gemm_bf16(h, nullptr, (int)R, w2, yp, off, (int)E, (int)R, (int)F,
+                                  (int)H, false, split, s);
   } else {
     err = moe::launch_gemm_f32((const float*)xp, (const float*)w1, (float*)h, off, (int)E,
                                (int)R, (int)H, (int)F, (int)F, true, s);
@@ -176,7 +181,8 @@ moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets, const v
   if (st != MOE_OK) return st;
   if (!xp || !expert_offsets || !w1 || !w2 || !yp || !ws) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < ffn_ws_bytes(R, F, dtype)) return MOE_ERR_INVALID_ARG;
-  return run_ffn(xp, expert_offsets, w1, w2, R, H, E, F, dtype, yp, ws, (hipStream_t)stream);
+  return run_ffn(xp, nullptr, R, expert_offsets, w1, w2, R, H, E, F, dtype, yp, ws,
+                 (hipStream_t)stream);
 }
 
 moe_status moe_combine(const void* yp, const int32_t* inv_pos, const float* topk_w, int64_t T,
@@ -215,10 +221,13 @@ moe_status moe_forward(const void* x, const void* w_r, const float* router_bias,
   hipError_t err = moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k, bf16,
                                      ids, w, stage, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  // bf16: the first expert GEMM gathers the token rows from x itself, so the
+  // dispatch only builds the indices; fp32 copies the rows into xp.
   err = moe::launch_permute(x, ids, (int)T, (int)H, (int)E, top_k, elem_bytes(dtype), off,
-                            sorted, inv, xp, stage, s);
+                            sorted, inv, bf16 ? nullptr : xp, stage, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
-  const moe_status fs = run_ffn(xp, off, w1, w2, R, H, E, F, dtype, yp, stage, s);
+  const moe_status fs = bf16 ? run_ffn(x, sorted, T, off, w1, w2, R, H, E, F, dtype, yp, stage, s)
+                             : run_ffn(xp, nullptr, R, off, w1, w2, R, H, E, F, dtype, yp, stage, s);
   if (fs != MOE_OK) return fs;
   return launch_status(moe::launch_combine(yp, inv, w, (int)T, (int)H, top_k, bf16, y, s));
 }

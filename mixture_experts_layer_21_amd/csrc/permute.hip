@@ -5,10 +5,13 @@
 //
 //   perm_count   per chunk of CH pairs: expert histogram in LDS -> counts[b][e]
 //   perm_scan    one workgroup: per-expert exclusive scan over chunks
-//                (chunk bases), then exclusive scan over experts -> offsets
-//   perm_place   per chunk: stable rank of each pair among the chunk's pairs
-//                of the same expert (wave ballots + per-wave counts in LDS)
-//                -> sorted_token[pos] = t, inv_pos[t*k+j] = pos
+//                (chunk bases) and over experts (offsets); each expert's
+//                chunks are split among P threads that scan their segments in
+//                parallel, then the segment sums are scanned
+//   perm_place   per chunk (one pair per thread): stable rank of each pair
+//                among the chunk's pairs of the same expert (wave ballots +
+//                per-wave counts in LDS) -> sorted_token[pos] = t,
+//                inv_pos[t*k+j] = pos
 //   perm_gather  xp[p,:] = x[sorted_token[p],:], 16-byte copies, one wave per row
 //
 // All counts are integers: placement is exact and deterministic.
@@ -18,7 +21,7 @@
 namespace moe {
 namespace {
 
-constexpr int CH = 1024;   // pairs per chunk (one workgroup of 256 threads)
+constexpr int CH = 256;    // pairs per chunk (one workgroup of 256 threads)
 
 __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int R,
                                                   int E, int32_t* __restrict__ counts) {
@@ -36,28 +39,53 @@ __global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ co
                                                   int nchunks, int E, int R,
                                                   int32_t* __restrict__ base,
                                                   int32_t* __restrict__ offsets) {
+  __shared__ int seg[1024];     // [P][E]: segment sums, then segment bases
+  __shared__ int tot[1024];     // per-expert totals, then expert offsets
   __shared__ int wsum[16];
-  const int e = threadIdx.x;
-  const int lane = e % kWave, wave = e / kWave;
-  int total = 0;
-  if (e < E) {
-    for (int b = 0; b < nchunks; ++b) {
-      const int c = counts[(size_t)b * E + e];
-      base[(size_t)b * E + e] = total;
-      total += c;
+  const int t = threadIdx.x;
+  const int P = max(1, 1024 / E);          // threads per expert
+  const int e = t % E, p = t / E;
+  const bool active = p < P && t < P * E;
+  const int L = (nchunks + P - 1) / P;     // chunks per thread (contiguous)
+  const int b0 = min(nchunks, p * L), b1 = min(nchunks, b0 + L);
+  int sum = 0;
+  if (active)
+    for (int b = b0; b < b1; ++b) sum += counts[(size_t)b * E + e];
+  if (active) seg[p * E + e] = sum;
+  __syncthreads();
+  if (t < E) {
+    int run = 0;
+    for (int q = 0; q < P; ++q) {
+      const int v = seg[q * E + t];
+      seg[q * E + t] = run;
+      run += v;
     }
+    tot[t] = run;
   }
-  const int incl = wave_incl_scan(total);
+  __syncthreads();
+  // exclusive scan of the expert totals (one thread per expert, E <= 1024)
+  const int lane = t % kWave, wave = t / kWave;
+  const int v = t < E ? tot[t] : 0;
+  const int incl = wave_incl_scan(v);
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
   int wbase = 0;
   for (int w = 0; w < wave; ++w) wbase += wsum[w];
-  const int excl = wbase + incl - total;
-  if (e < E) {
-    offsets[e] = excl;
-    for (int b = 0; b < nchunks; ++b) base[(size_t)b * E + e] += excl;
+  __syncthreads();
+  if (t < E) {
+    tot[t] = wbase + incl - v;
+    offsets[t] = wbase + incl - v;
   }
-  if (e == 0) offsets[E] = R;
+  if (t == 0) offsets[E] = R;
+  __syncthreads();
+  if (active) {
+    int run = tot[e] + seg[p * E + e];
+    for (int b = b0; b < b1; ++b) {
+      const int c = counts[(size_t)b * E + e];
+      base[(size_t)b * E + e] = run;
+      run += c;
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ ids, int R,
@@ -148,6 +176,7 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
   if (nchunks == 0) return hipGetLastError();
   hipLaunchKernelGGL(perm_place, dim3(nchunks), dim3(256), 5 * E * sizeof(int), s, ids, R, E, k,
                      base, sorted_token, inv_pos);
+  if (xp == nullptr) return hipGetLastError();
   const int row_chunks = (int)((size_t)H * elem_bytes / 16);
   const int blocks = std::min(8192, (R + 3) / 4);
   hipLaunchKernelGGL(perm_gather, dim3(blocks), dim3(256), 0, s, (const u32x4*)x, sorted_token,

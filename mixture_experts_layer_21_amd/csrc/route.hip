@@ -103,17 +103,34 @@ __global__ __launch_bounds__(256) void route_select(
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
 
+  // sum the S partial logits in split order; the loads of a batch of 8
+  // splits are all issued before any is added
   float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) v[i] = 0.f;
+  const size_t sstride = (size_t)T * EP;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + i * kWave;
+      if (e < E) {
+        const float* p = part + ((size_t)s0 * T + t) * EP + e;
+        float q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = (s0 + u < S) ? p[u * sstride] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[i] += q[u];
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + i * kWave;
-    float a = -__builtin_inff();
     if (e < E) {
-      a = 0.f;
-      for (int s = 0; s < S; ++s) a += part[((size_t)s * T + t) * EP + e];
-      if (bias) a += bias[e];
+      if (bias) v[i] += bias[e];
+    } else {
+      v[i] = -__builtin_inff();
     }
-    v[i] = a;
   }
   uint32_t taken = 0;            // bit i: v[i] already selected
   float sel_v[16];
