@@ -1,7 +1,8 @@
 // Grouped expert GEMM on bf16 MFMA (gfx950): C[rows_e] = act(A[rows_e] . W[e])
 // for every expert e, rows_e = [off[e], off[e+1]).
 //
-//   A  [R, K] bf16 row-major (dispatched token rows, K contiguous)
+//   A  [R, K] bf16 row-major (dispatched token rows, K contiguous), or the
+//      token matrix x itself with a row-gather list (dispatch fused in)
 //   W  [E, K, N] bf16 row-major (N contiguous, as the layer stores W1/W2)
 //   C  [R, N] bf16 row-major, fp32 accumulation, rounded to nearest even
 //
@@ -11,28 +12,36 @@
 // stream past, section "tiling") mapped onto a tile order that keeps the
 // row tiles of one weight slab adjacent (see map_tile).
 //
-// Design (one 256x256 output tile per workgroup, 4 waves as 2x2, 128x128 per
-// wave, K step 64):
-//  * the weight slab W[e][k0:k0+64, n0:n0+256] is loaded with 16-byte global
-//    loads (8 k-rows x 8 n per thread), transposed in registers with byte
-//    permutes and written to LDS as Ws[n][k] (k contiguous), which is the
-//    operand layout MFMA wants; the token tile goes to LDS as As[m][k];
-//  * rows are padded to 72 bf16 (144 B) so the 16-byte LDS reads of a
-//    32-lane column of rows hit distinct banks;
+// Design (one 256x256 output tile per workgroup and CU; 8 waves as 2 along
+// the tokens x 4 along the columns, two waves per SIMD, 128x64 per wave; K
+// step 32):
+//  * operands move global -> LDS with buffer_load ... lds (no VGPRs), 1 KB
+//    per instruction, into a 4-stage ring (128 KB), three steps in flight;
+//  * W stays in its natural k-major layout in LDS; the MFMA operand (4
+//    consecutive k of one column) comes from ds_read_b64_tr_b16; both
+//    tiles are XOR-swizzled so the operand reads are free of bank conflicts;
 //  * the product is computed transposed, D[n][m] = W^T A^T with
 //    v_mfma_f32_32x32x16_bf16 (W as the MFMA A operand), so each lane ends up
 //    holding 4 consecutive output columns of one token row: epilogue stores
 //    are 8 bytes per lane;
-//  * double-buffered LDS: global loads of step k+1 are in flight while step k
-//    computes; one barrier per step;
 //  * 32-row token blocks beyond the tile's valid rows skip their LDS reads
-//    and MFMAs, so a tile with few rows costs little compute.
+//    and MFMAs (compile-time count per wave), so a tile with few rows costs
+//    little compute;
+//  * tiles of the last partial round are split along K (deterministic
+//    stream-K, see gemm_bf16_grouped).
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 namespace {
 
+#ifndef MOE_WM
+#define MOE_WM 2                // waves along the token rows
+#endif
+#ifndef MOE_WN
+#define MOE_WN 4                // waves along the columns
+#endif
+#define MOE_WPE ((MOE_WM * MOE_WN) / 4)   // waves per SIMD
 constexpr int BK = 32;          // K step (bf16 elements)
 constexpr int STAGES = 4;       // LDS ring: three K steps in flight (128 KB)
 constexpr int MIN_SPLIT_STEPS = 16;   // K steps per piece of a split tile, at least
@@ -380,7 +389,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
 // the remaining tiles are split along K into S pieces each, so that the last
 // round keeps every CU busy instead of leaving most of them idle.
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_bf16_grouped(
+__global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(MOE_WPE, MOE_WPE))) void gemm_bf16_grouped(
     const uint16_t* __restrict__ A, const int* __restrict__ gather, int a_rows,
     const uint16_t* __restrict__ W, uint16_t* __restrict__ C, const int* __restrict__ off,
     int E, int R, int K, int N, int gelu, float* __restrict__ part, int* __restrict__ counters,
@@ -426,11 +435,14 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   const int wm = (threadIdx.x / kWave) % WM;
   int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
   nfm = __builtin_amdgcn_readfirstlane(nfm);
-  static_assert(S::FM == 4, "dispatch below covers FM == 4");
-#define MOE_TILE(NF) gemm_tile<BM, BN, WM, WN, NF>(A, gather, a_rows, We, C, tile, K, N, gelu, \
-                                                 kt_begin, kt_end, \
-                                                 sp, lds0, lds1, lds2, lds3, &flag)
+  static_assert(S::FM == 4 || S::FM == 8, "dispatch below covers FM of 4 or 8");
+#define MOE_TILE(NF) gemm_tile<BM, BN, WM, WN, (NF <= S::FM ? NF : S::FM)>( \
+    A, gather, a_rows, We, C, tile, K, N, gelu, kt_begin, kt_end, sp, lds0, lds1, lds2, lds3, &flag)
   switch (nfm) {
+    case 8: MOE_TILE(8); break;
+    case 7: MOE_TILE(7); break;
+    case 6: MOE_TILE(6); break;
+    case 5: MOE_TILE(5); break;
     case 4: MOE_TILE(4); break;
     case 3: MOE_TILE(3); break;
     case 2: MOE_TILE(2); break;
@@ -495,8 +507,8 @@ hipError_t clear_split_counters(void* split_ws, hipStream_t s) {
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
                             void* C, const int* off, int E, int R, int K, int N, bool gelu,
                             void* split_ws, hipStream_t s) {
-  return launch_cfg<256, 256, 2, 2>(A, gather, a_rows, W, C, off, E, R, K, N, gelu, split_ws,
-                                    s);
+  return launch_cfg<256, 256, MOE_WM, MOE_WN>(A, gather, a_rows, W, C, off, E, R, K, N, gelu,
+                                              split_ws, s);
 }
 
 }  // namespace moe
