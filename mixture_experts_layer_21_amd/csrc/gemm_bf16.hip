@@ -32,6 +32,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -42,8 +44,9 @@ namespace {
 #define MOE_WN 4                // waves along the columns
 #endif
 #define MOE_WPE ((MOE_WM * MOE_WN) / 4)   // waves per SIMD
-constexpr int BK = 32;          // K step (bf16 elements)
-constexpr int STAGES = 4;       // LDS ring: three K steps in flight (128 KB)
+constexpr int BK = 32;          // K step (bf16 elements): two 16-wide MFMA slices
+constexpr int W_STAGES = 4;     // weight ring: one K step per stage, 3 in flight
+constexpr int A_STAGES = 2;     // token ring: two K steps (128-byte rows) per stage
 constexpr int MIN_SPLIT_STEPS = 16;   // K steps per piece of a split tile, at least
 constexpr uint32_t kBufFlags = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr uint32_t kPastEnd = 0xFFFFFFF0u;    // buffer offset that reads as zero
@@ -56,28 +59,31 @@ struct GemmShape {
   static constexpr int TN = BN / WN;                  // columns per wave
   static constexpr int FM = TM / 32;                  // MFMA blocks (tokens)
   static constexpr int FN = TN / 32;                  // MFMA blocks (columns)
-  static constexpr int A_ROW = BK * 2;                // bytes per token row (64)
+  static constexpr int A_ROW = 2 * BK * 2;            // bytes per token row per stage (128)
   static constexpr int W_ROW = BN * 2;                // bytes per k row (512)
-  static constexpr int LDS_A = BM * A_ROW;            // bytes per stage
-  static constexpr int LDS_W = BK * W_ROW;
-  static constexpr int LDS_STAGE = LDS_A + LDS_W;
+  static constexpr int LDS_A = BM * A_ROW;            // bytes per token stage (32 KB)
+  static constexpr int LDS_W = BK * W_ROW;            // bytes per weight stage (16 KB)
   // direct-to-LDS loads: one instruction moves 64 lanes x 16 B = 1 KB
-  static constexpr int A_INSTS = LDS_A / 1024 / NW;   // per wave per step
-  static constexpr int W_INSTS = LDS_W / 1024 / NW;
-  static constexpr int LOADS = A_INSTS + W_INSTS;
-  static_assert(A_ROW == 64 && W_ROW == 512, "layout below assumes BK=32, BN=256");
+  static constexpr int A_INSTS = LDS_A / 1024 / NW;   // per wave per token stage
+  static constexpr int W_INSTS = LDS_W / 1024 / NW;   // per wave per K step
+  static_assert(A_ROW == 128 && W_ROW == 512, "layout below assumes BK=32, BN=256");
   static_assert(A_INSTS * NW * 1024 == LDS_A && W_INSTS * NW * 1024 == LDS_W, "load split");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
 };
 
+// Why the token rows are 128 bytes: the vector memory path keeps a bounded
+// number of cache-line requests in flight per CU, so the load rate is set by
+// the request count, and a 64-byte row piece costs a whole request for half a
+// line.  Loading two K steps of a row at once makes every request a full line.
+//
 // LDS layouts (16-byte chunks XOR-swizzled so that MFMA operand reads are
 // free of bank conflicts):
-//   A tile [BM][32] bf16, 64-byte rows: chunk c of row m at c ^ ((m >> 2) & 3);
+//   token stage [BM][64] bf16, 128-byte rows: chunk c of row m at c ^ ((m >> 1) & 7);
 //     16 lanes reading 16 rows of one chunk hit 64 distinct banks.
-//   W tile [32][BN] bf16 (the weight slab's natural k-major layout), 512-byte
-//     rows: chunk c of row k at c ^ (4 * (k & 3)); a transposed read covering
-//     4 k-rows x 32 columns hits 64 distinct banks.
-__device__ __forceinline__ int swz_a(int m) { return (m >> 2) & 3; }
+//   weight stage [32][BN] bf16 (the weight slab's natural k-major layout),
+//     512-byte rows: chunk c of row k at c ^ (4 * (k & 3)); a transposed read
+//     covering 4 k-rows x 32 columns hits 64 distinct banks.
+__device__ __forceinline__ int swz_a(int m) { return (m >> 1) & 7; }
 __device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
 
 
@@ -91,8 +97,15 @@ __device__ constexpr int vmcnt_le(int n) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
+// (base and size are wave-uniform; readfirstlane states it, so that the
+// descriptor is built in scalar registers and no per-lane loop appears)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes),
                                            (int)kBufFlags);
 }
 
@@ -119,24 +132,31 @@ struct Split {
   int* counters;
 };
 
+// LDS of one workgroup: the two rings, one array per stage, so the compiler
+// can tell that a read of one stage does not wait on the loads into another.
+struct Lds {
+  char* a[A_STAGES];
+  char* w[W_STAGES];
+  int* flag;
+};
+
 // One output tile.  NFM (compile time) is the number of 32-row token blocks
 // of this wave that hold valid rows, so the main loop has no branches around
-// its LDS reads and MFMAs (the accumulators stay in AGPRs).
+// its LDS reads and MFMAs (the accumulators stay in registers).
 //
 // Global loads use buffer descriptors whose base advances with k0 and whose
 // size ends at the last valid row of the tile (A) or of the weight slab (W):
-// rows past the tile and k rows past K read as zero, so no clamping or masks
-// appear in the loop.  (Past-K columns of A read the next row, but they meet
-// zero W rows.)  Columns past N read neighbouring data that is never stored.
+// rows past the tile and k rows past the piece's K range read as zero, so no
+// clamping or masks appear in the loop.  (Past-K columns of A read the next
+// row, but they meet zero W rows.)  Columns past N read neighbouring data that
+// is never stored.
 template <int BM, int BN, int WM, int WN, int NFM>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
                                           const int* __restrict__ gather, int a_rows,
                                           const uint16_t* __restrict__ We,
                                           uint16_t* __restrict__ C, const Tile& tile, int K,
                                           int N, int gelu, int kt_begin, int kt_end,
-                                          const Split& sp, char* lds0, char* lds1, char* lds2,
-                                          char* lds3, int* flag) {
-  char* const stages[STAGES] = {lds0, lds1, lds2, lds3};
+                                          const Split& sp, const Lds& lds) {
   using S = GemmShape<BM, BN, WM, WN>;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -150,7 +170,6 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   // Token rows: row0+m of A, or row gather[row0+m] of A when the token rows
   // are gathered straight from x (dispatch fused into the load).  Rows past
   // the tile get an offset past the buffer end and read as zero.
-  const uint16_t* a_base = A;
   const uint32_t a_bytes = (uint32_t)a_rows * K * 2;
   // W rows at or past k_limit read as zero: a split piece covers only its
   // own K range
@@ -160,9 +179,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   int a_dst[S::A_INSTS];
 #pragma unroll
   for (int u = 0; u < S::A_INSTS; ++u) {
-    const int q = wave * S::A_INSTS + u;           // 16 rows per instruction
-    const int m = q * 16 + lane / 4;
-    const int c = (lane % 4) ^ swz_a(m);           // logical chunk stored at lane's slot
+    const int q = wave * S::A_INSTS + u;           // 8 rows per instruction
+    const int m = q * 8 + lane / 8;
+    const int c = (lane % 8) ^ swz_a(m);           // logical chunk stored at lane's slot
     uint32_t voff = kPastEnd;
     if (m < tile.mrows) {
       const int grow = gather ? gather[tile.row0 + m] : tile.row0 + m;
@@ -179,35 +198,40 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
     const int kr = 2 * q + lane / 32;
     const int c = (lane % 32) ^ swz_w(kr);
     w_voff[u] = (uint32_t)kr * N * 2 + (uint32_t)(n0 + c * 8) * 2;
-    w_dst[u] = S::LDS_A + q * 1024;
+    w_dst[u] = q * 1024;
   }
 
   // k0 may pass K on the last steps: the sizes clamp to 0 and every load
   // returns zero without touching memory.
-  auto issue_loads = [&](int k0, int stage) {
-    const uint32_t a_skip = (uint32_t)k0 * 2, w_skip = (uint32_t)k0 * N * 2;
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(a_base + k0, a_bytes > a_skip ? a_bytes - a_skip : 0u);
+  auto load_w = [&](int k0, char* st) {
+    const uint32_t skip = (uint32_t)k0 * N * 2;
     const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(We + (size_t)k0 * N, w_bytes > w_skip ? w_bytes - w_skip : 0u);
-    char* st = stages[stage];
-#pragma unroll
-    for (int u = 0; u < S::A_INSTS; ++u) load_to_lds(ra, st + a_dst[u], a_voff[u]);
+        make_rsrc(We + (size_t)k0 * N, w_bytes > skip ? w_bytes - skip : 0u);
 #pragma unroll
     for (int u = 0; u < S::W_INSTS; ++u) load_to_lds(rw, st + w_dst[u], w_voff[u]);
   };
+  auto load_a = [&](int k0, char* st) {            // K steps k0 / BK and k0 / BK + 1
+    const uint32_t skip = (uint32_t)k0 * 2;
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(A + k0, a_bytes > skip ? a_bytes - skip : 0u);
+#pragma unroll
+    for (int u = 0; u < S::A_INSTS; ++u) load_to_lds(ra, st + a_dst[u], a_voff[u]);
+  };
 
   // --- fragment read offsets ------------------------------------------------
-  // token operand (MFMA B): row wrow0 + 32 j + lane%32, k = kk + 8 (lane/32) + 0..7
+  // token operand (MFMA B): row wrow0 + 32 j + lane%32, k = 32 par + 16 h +
+  // 8 (lane/32) + 0..7 of the token stage (par: which of its two K steps)
   const int fr = lane % 32;
-  int fa[2];
+  int fa[2][2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = 2 * h + lane / 32;
-    fa[h] = (wrow0 + fr) * S::A_ROW + ((c ^ swz_a(fr)) * 16);
-  }
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 4 * par + 2 * h + lane / 32;
+      fa[par][h] = (wrow0 + fr) * S::A_ROW + ((c ^ swz_a(fr)) * 16);
+    }
   // weight operand (MFMA A, rows = columns n of W): two transposed reads per
-  // 32-column block i, for k = kk + 8 (g/2) + 4 rd + (0..3), g = lane/16, and
+  // 32-column block i, for k = 16 h + 8 (g/2) + 4 rd + (0..3), g = lane/16, and
   // column wn*TN + 32 i + 16 (g%2) + lane%16.  The block offset 4i sits in
   // chunk bits 2..3, which the swizzle also flips, so each (h, rd, i) keeps
   // its own offset.
@@ -221,7 +245,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
       for (int i = 0; i < S::FN; ++i) {
         const int kr = 16 * h + 8 * (g / 2) + 4 * rd + li / 4;
         const int nn = wn * S::TN + 32 * i + 16 * (g % 2) + 4 * (li % 4);
-        fw[h][rd][i] = S::LDS_A + kr * S::W_ROW + (((nn / 8) ^ swz_w(kr)) * 16) + (nn % 8) * 2;
+        fw[h][rd][i] = kr * S::W_ROW + (((nn / 8) ^ swz_w(kr)) * 16) + (nn % 8) * 2;
       }
 
   constexpr int FMA = NFM > 0 ? NFM : 1;
@@ -231,30 +255,37 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
 #pragma unroll
     for (int j = 0; j < FMA; ++j) acc[i][j] = f32x16{};
 
-  auto read_frags = [&](const char* st, int h, bf16x8* wf, bf16x8* af) {
+  auto read_frags = [&](const char* wst, const char* ast, int par, int h, bf16x8* wf,
+                        bf16x8* af) {
 #pragma unroll
     for (int i = 0; i < S::FN; ++i) {
-      const u32x2 lo = read_tr(st + fw[h][0][i]);
-      const u32x2 hi = read_tr(st + fw[h][1][i]);
+      const u32x2 lo = read_tr(wst + fw[h][0][i]);
+      const u32x2 hi = read_tr(wst + fw[h][1][i]);
       wf[i] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
 #pragma unroll
     for (int j = 0; j < FMA; ++j)
-      af[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + fa[h] + j * 32 * S::A_ROW));
+      af[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(ast + fa[par][h] + j * 32 * S::A_ROW));
   };
 
-  // Software pipeline (BK = 32 per step = two 16-wide k slices, 4 LDS
-  // stages).  Step kt:
+  // Software pipeline.  Step kt (local index, one K step of BK) uses weight
+  // stage kt % 4 and token stage (kt / 2) % 2, half `kt % 2` of it:
   //   first half   MFMAs of slice 0 (operands already in registers), each
   //                paired with an LDS read of slice 1's operands;
   //   middle       wait for this wave's loads of step kt+1, barrier: every
-  //                wave's part of stage kt+1 has landed and every wave is
-  //                done reading stage kt, so step kt+4's loads go into it;
+  //                wave's part of step kt+1 has landed and every wave is done
+  //                reading step kt, so weight stage kt % 4 takes step kt+4
+  //                and, after an odd step, token stage (kt / 2) % 2 takes
+  //                steps kt+3 and kt+4;
   //   second half  MFMAs of slice 1, each paired with an LDS read of step
   //                kt+1's slice-0 operands.
-  // No MFMA waits on an LDS read issued after a barrier, and three steps of
-  // global loads stay in flight.  (A bare s_barrier: a release fence would
-  // wait for every outstanding load.)
+  // Loads are issued in the order W(j+4) [, A(j+3, j+4) for odd j] at step j,
+  // and the prologue issues W0 W1 A01 W2 W3 A23, so (with vector-memory
+  // counts retiring in issue order) step kt+1's data is in once at most
+  //   even kt:  2 W + 2 A  (A(kt, kt+1), W(kt+2), W(kt+3), A(kt+2, kt+3))
+  //   odd kt:   1 W        (W(kt+3))
+  // loads of this wave are outstanding.  (A bare s_barrier: a release fence
+  // would wait for every outstanding load.)
   bf16x8 wf0[S::FN], af0[FMA], wf1[S::FN], af1[FMA];
   constexpr int NRD = 2 * S::FN + FMA;     // LDS read instructions per slice
   constexpr int NMF = S::FN * NFM;         // MFMAs per slice
@@ -280,34 +311,51 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
     if constexpr (NRD > P) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P, 0);
   };
 
-  auto step = [&](int kt, int stage) {
-    const char* cur = stages[stage];
-    const char* nxt = stages[(stage + 1) % STAGES];
-    read_frags(cur, 1, wf1, af1);
+  const int k0 = kt_begin * BK;
+  // step kt of the unrolled group of 4: weight stage ST, token stage ST / 2
+  auto step = [&](int kt, auto st_c) {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr int PAR = ST % 2;
+    const char* wcur = lds.w[ST];
+    const char* acur = lds.a[ST / 2];
+    const char* wnxt = lds.w[(ST + 1) % W_STAGES];
+    const char* anxt = lds.a[((ST + 1) / 2) % A_STAGES];
+    read_frags(wcur, acur, PAR, 1, wf1, af1);
     mfma_slice(wf0, af0);
     interleave();
-    __builtin_amdgcn_s_waitcnt(vmcnt_le((STAGES - 2) * S::LOADS));   // step kt+1 landed
-    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): reads of stage kt done
+    if constexpr (PAR == 0)
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * S::W_INSTS + 2 * S::A_INSTS));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(S::W_INSTS));
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): reads of step kt done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    issue_loads((kt + STAGES) * BK, stage);
-    read_frags(nxt, 0, wf0, af0);
+    load_w(k0 + (kt + W_STAGES) * BK, lds.w[ST]);
+    if constexpr (PAR == 1) load_a(k0 + (kt + 3) * BK, lds.a[ST / 2]);
+    read_frags(wnxt, anxt, 1 - PAR, 0, wf0, af0);
     mfma_slice(wf1, af1);
     interleave();
   };
 
-  // The loop runs a multiple of STAGES steps; steps past the K range read
-  // only zeros and add nothing.
-  const int k0 = kt_begin * BK;
-#pragma unroll
-  for (int st = 0; st < STAGES; ++st) issue_loads(k0 + st * BK, st);
-  __builtin_amdgcn_s_waitcnt(vmcnt_le((STAGES - 1) * S::LOADS));   // first step landed
+  // The loop runs a multiple of 4 steps; steps past the K range meet zero
+  // weight rows and add nothing.
+  load_w(k0, lds.w[0]);
+  load_w(k0 + BK, lds.w[1]);
+  load_a(k0, lds.a[0]);
+  load_w(k0 + 2 * BK, lds.w[2]);
+  load_w(k0 + 3 * BK, lds.w[3]);
+  load_a(k0 + 2 * BK, lds.a[1]);
+  // step 0's data (W0, A01) is in once W2, W3, A23 alone are outstanding
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * S::W_INSTS + S::A_INSTS));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  read_frags(stages[0], 0, wf0, af0);
-  for (int kt = kt_begin; kt < kt_end; kt += STAGES) {
-#pragma unroll
-    for (int st = 0; st < STAGES; ++st) step(kt + st, st);
+  read_frags(lds.w[0], lds.a[0], 0, 0, wf0, af0);
+  const int nsteps = kt_end - kt_begin;
+  for (int kt = 0; kt < nsteps; kt += W_STAGES) {
+    step(kt + 0, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
+    step(kt + 2, std::integral_constant<int, 2>{});
+    step(kt + 3, std::integral_constant<int, 3>{});
   }
   // drain the loads still in flight before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
@@ -332,9 +380,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
     }
     __threadfence();
     __syncthreads();
-    if (tid == 0) *flag = atomicAdd(&sp.counters[sp.slot], 1);
+    if (tid == 0) *lds.flag = atomicAdd(&sp.counters[sp.slot], 1);
     __syncthreads();
-    if (*flag != sp.S - 1) return;
+    if (*lds.flag != sp.S - 1) return;
     __threadfence();
     if constexpr (NFM > 0) {
       const float* all = sp.part + (size_t)sp.slot * sp.S * PER_PIECE;
@@ -384,6 +432,28 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   }
 }
 
+// gemm_tile with NFM = nfm (0 <= nfm <= NF), chosen at run time from a
+// wave-uniform count.
+template <int BM, int BN, int WM, int WN, int NF>
+__device__ __forceinline__ void run_tile(int nfm, const uint16_t* __restrict__ A,
+                                         const int* __restrict__ gather, int a_rows,
+                                         const uint16_t* __restrict__ We,
+                                         uint16_t* __restrict__ C, const Tile& tile, int K,
+                                         int N, int gelu, int kt_begin, int kt_end,
+                                         const Split& sp, const Lds& lds) {
+  if constexpr (NF == 0) {
+    gemm_tile<BM, BN, WM, WN, 0>(A, gather, a_rows, We, C, tile, K, N, gelu, kt_begin, kt_end,
+                                 sp, lds);
+  } else {
+    if (nfm == NF)
+      gemm_tile<BM, BN, WM, WN, NF>(A, gather, a_rows, We, C, tile, K, N, gelu, kt_begin,
+                                    kt_end, sp, lds);
+    else
+      run_tile<BM, BN, WM, WN, NF - 1>(nfm, A, gather, a_rows, We, C, tile, K, N, gelu,
+                                       kt_begin, kt_end, sp, lds);
+  }
+}
+
 // Work split (stream-K style, deterministic): the first floor(n / slots)
 // rounds of `slots` tiles (slots = workgroups the GPU runs at once) run whole;
 // the remaining tiles are split along K into S pieces each, so that the last
@@ -395,13 +465,14 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     int E, int R, int K, int N, int gelu, float* __restrict__ part, int* __restrict__ counters,
     int slots) {
   using S = GemmShape<BM, BN, WM, WN>;
-  // one LDS array per pipeline stage, so the compiler can tell that a read of
-  // one stage does not wait on the in-flight loads into the others
-  __shared__ __attribute__((aligned(1024))) char lds0[S::LDS_STAGE];
-  __shared__ __attribute__((aligned(1024))) char lds1[S::LDS_STAGE];
-  __shared__ __attribute__((aligned(1024))) char lds2[S::LDS_STAGE];
-  __shared__ __attribute__((aligned(1024))) char lds3[S::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) char a0[S::LDS_A];
+  __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
+  __shared__ __attribute__((aligned(1024))) char w0[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char w1[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char w2[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char w3[S::LDS_W];
   __shared__ int flag;
+  const Lds lds{{a0, a1}, {w0, w1, w2, w3}, &flag};
 
   const int NTN = (N + BN - 1) / BN;
   const int KT = (K + BK - 1) / BK;
@@ -435,21 +506,8 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   const int wm = (threadIdx.x / kWave) % WM;
   int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
   nfm = __builtin_amdgcn_readfirstlane(nfm);
-  static_assert(S::FM == 4 || S::FM == 8, "dispatch below covers FM of 4 or 8");
-#define MOE_TILE(NF) gemm_tile<BM, BN, WM, WN, (NF <= S::FM ? NF : S::FM)>( \
-    A, gather, a_rows, We, C, tile, K, N, gelu, kt_begin, kt_end, sp, lds0, lds1, lds2, lds3, &flag)
-  switch (nfm) {
-    case 8: MOE_TILE(8); break;
-    case 7: MOE_TILE(7); break;
-    case 6: MOE_TILE(6); break;
-    case 5: MOE_TILE(5); break;
-    case 4: MOE_TILE(4); break;
-    case 3: MOE_TILE(3); break;
-    case 2: MOE_TILE(2); break;
-    case 1: MOE_TILE(1); break;
-    default: MOE_TILE(0); break;
-  }
-#undef MOE_TILE
+  run_tile<BM, BN, WM, WN, S::FM>(nfm, A, gather, a_rows, We, C, tile, K, N, gelu, kt_begin,
+                                  kt_end, sp, lds);
 }
 
 __global__ void zero_ints(int* p, int n) {
