@@ -66,6 +66,7 @@ struct GemmShape {
   // direct-to-LDS loads: one instruction moves 64 lanes x 16 B = 1 KB
   static constexpr int A_INSTS = LDS_A / 1024 / NW;   // per wave per token stage
   static constexpr int W_INSTS = LDS_W / 1024 / NW;   // per wave per K step
+  static constexpr int PER_PIECE = FN * FM * 16 * NT; // fp32 partials of a split tile piece
   static_assert(A_ROW == 128 && W_ROW == 512, "layout below assumes BK=32, BN=256");
   static_assert(A_INSTS * NW * 1024 == LDS_A && W_INSTS * NW * 1024 == LDS_W, "load split");
   static_assert(FM >= 1 && FN >= 1, "wave tile");
@@ -129,7 +130,6 @@ __device__ __forceinline__ u32x2 read_tr(const char* p) {
 struct Split {
   int S, s, slot;
   float* part;
-  int* counters;
 };
 
 // LDS of one workgroup: the two rings, one array per stage, so the compiler
@@ -137,8 +137,70 @@ struct Split {
 struct Lds {
   char* a[A_STAGES];
   char* w[W_STAGES];
-  int* flag;
 };
+
+// Epilogue of one output tile from the accumulators (callers have made the
+// token ring free: no wave reads it any more).
+template <int BM, int BN, int WM, int WN, int NFM, int FMA>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN, WM, WN>::FN][FMA],
+                                           uint16_t* __restrict__ C, const Tile& tile, int N,
+                                           int gelu, const Lds& lds) {
+  using S = GemmShape<BM, BN, WM, WN>;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+  const int n0 = tile.nt * BN;
+  const int wrow0 = wm * S::TM;
+  // Lane holds D[n][m] for m = lane%32 and 4 consecutive n.  Stored straight
+  // to C, one instruction would touch 32 rows with 16 bytes each, 32 partial
+  // lines; instead each wave stages 64 rows of its TM x TN block at a time
+  // (GELU applied, bf16) in its own 8 KB of the now idle token ring, 128-byte
+  // rows with 16-byte chunk c of row r at c ^ (r & 7), and writes them back
+  // row by row: each instruction then stores 8 whole 128-byte row pieces.
+  static_assert(S::TN * 2 == 128 && S::NW * 8192 <= A_STAGES * S::LDS_A, "staging layout");
+  char* const stg = (wave < S::NW / 2 ? lds.a[0] : lds.a[1]) + (wave % (S::NW / 2)) * 8192;
+  if constexpr (NFM > 0) {
+#pragma unroll
+    for (int p = 0; p < NFM; p += 2) {               // 2 blocks of 32 rows per pass
+#pragma unroll
+      for (int j = p; j < p + 2 && j < NFM; ++j) {
+        const int r = (j - p) * 32 + (lane % 32);
+#pragma unroll
+        for (int i = 0; i < S::FN; ++i) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            float v0 = acc[i][j][4 * gq + 0], v1 = acc[i][j][4 * gq + 1];
+            float v2 = acc[i][j][4 * gq + 2], v3 = acc[i][j][4 * gq + 3];
+            if (gelu) {
+              v0 = gelu_tanh(v0); v1 = gelu_tanh(v1);
+              v2 = gelu_tanh(v2); v3 = gelu_tanh(v3);
+            }
+            const int c = i * 4 + gq;                // 16-byte chunk of the 128-byte row
+            *(u32x2*)(stg + r * 128 + ((c ^ (r & 7)) * 16) + (lane / 32) * 8) =
+                u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): this wave's writes are in
+      __builtin_amdgcn_wave_barrier();
+      constexpr int ROWS = 32 * 2;
+#pragma unroll
+      for (int q = 0; q < ROWS / 8; ++q) {           // 8 rows per instruction
+        const int r = q * 8 + lane / 8;
+        if (p * 32 + r >= NFM * 32) break;           // (odd NFM: half a pass)
+        const int slot = lane % 8;
+        const int m = wrow0 + p * 32 + r;
+        const int n = n0 + wn * S::TN + (slot ^ (r & 7)) * 8;
+        const u32x4 v = *(const u32x4*)(stg + r * 128 + slot * 16);
+        if (m < tile.mrows && n < N) *(u32x4*)(C + (size_t)(tile.row0 + m) * N + n) = v;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);            // reads done before the next pass writes
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
 
 // One output tile.  NFM (compile time) is the number of 32-row token blocks
 // of this wave that hold valid rows, so the main loop has no branches around
@@ -360,15 +422,12 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   // drain the loads still in flight before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 
-  // --- split tiles: partial sums meet in the workspace ---------------------
-  // Each piece stores its fp32 accumulators, then counts itself in; the last
-  // piece to arrive adds the S partials in split order (so the result does not
-  // depend on arrival order) and runs the epilogue.  sp is uniform over the
-  // workgroup and every wave, whatever its NFM, runs the same two barriers.
+  // --- split tiles: the piece leaves its fp32 partial sums in the workspace
+  // (in register order: thread-contiguous 16-byte groups, so every store
+  // instruction writes 8 KB in one run); a second launch adds them up.
   if (sp.S > 1) {
-    constexpr int PER_PIECE = S::FN * S::FM * 16 * S::NT;
     if constexpr (NFM > 0) {
-      float* mine = sp.part + ((size_t)sp.slot * sp.S + sp.s) * PER_PIECE;
+      float* mine = sp.part + ((size_t)sp.slot * sp.S + sp.s) * S::PER_PIECE;
 #pragma unroll
       for (int i = 0; i < S::FN; ++i)
 #pragma unroll
@@ -378,58 +437,13 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
             *(f32x4*)(mine + (((i * S::FM + j) * 16 + v) * S::NT + tid * 4)) =
                 f32x4{acc[i][j][v], acc[i][j][v + 1], acc[i][j][v + 2], acc[i][j][v + 3]};
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) *lds.flag = atomicAdd(&sp.counters[sp.slot], 1);
-    __syncthreads();
-    if (*lds.flag != sp.S - 1) return;
-    __threadfence();
-    if constexpr (NFM > 0) {
-      const float* all = sp.part + (size_t)sp.slot * sp.S * PER_PIECE;
-#pragma unroll
-      for (int i = 0; i < S::FN; ++i)
-#pragma unroll
-        for (int j = 0; j < NFM; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; v += 4) {
-            const size_t q = ((i * S::FM + j) * 16 + v) * S::NT + tid * 4;
-            f32x4 sum = *(const f32x4*)(all + q);
-            for (int ps = 1; ps < sp.S; ++ps)
-              sum += *(const f32x4*)(all + (size_t)ps * PER_PIECE + q);
-            acc[i][j][v] = sum[0];
-            acc[i][j][v + 1] = sum[1];
-            acc[i][j][v + 2] = sum[2];
-            acc[i][j][v + 3] = sum[3];
-          }
-    }
-    if (tid == 0) atomicExch(&sp.counters[sp.slot], 0);   // leave the counter clear
+    return;
   }
+  // one barrier first, because other waves may still read the K loop's last
+  // stages
+  __syncthreads();
+  store_tile<BM, BN, WM, WN, NFM>(acc, C, tile, N, gelu, lds);
 
-  // --- epilogue: lane holds D[n][m] for m = lane%32 and 4 consecutive n ----
-  if constexpr (NFM > 0) {
-#pragma unroll
-    for (int j = 0; j < NFM; ++j) {
-      const int m = wrow0 + j * 32 + (lane % 32);
-      if (m >= tile.mrows) continue;
-      uint16_t* crow = C + (size_t)(tile.row0 + m) * N;
-#pragma unroll
-      for (int i = 0; i < S::FN; ++i) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * S::TN + i * 32 + gq * 8 + (lane / 32) * 4;
-          if (n < N) {
-            float v0 = acc[i][j][4 * gq + 0], v1 = acc[i][j][4 * gq + 1];
-            float v2 = acc[i][j][4 * gq + 2], v3 = acc[i][j][4 * gq + 3];
-            if (gelu) {
-              v0 = gelu_tanh(v0); v1 = gelu_tanh(v1);
-              v2 = gelu_tanh(v2); v3 = gelu_tanh(v3);
-            }
-            *(u32x2*)(crow + n) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          }
-        }
-      }
-    }
-  }
 }
 
 // gemm_tile with NFM = nfm (0 <= nfm <= NF), chosen at run time from a
@@ -456,14 +470,36 @@ __device__ __forceinline__ void run_tile(int nfm, const uint16_t* __restrict__ A
 
 // Work split (stream-K style, deterministic): the first floor(n / slots)
 // rounds of `slots` tiles (slots = workgroups the GPU runs at once) run whole;
-// the remaining tiles are split along K into S pieces each, so that the last
-// round keeps every CU busy instead of leaving most of them idle.
+// the remaining sk tiles are split along K into S pieces each, so that the
+// last round keeps every CU busy instead of leaving most of them idle.  The
+// pieces leave fp32 partials and gemm_split_reduce adds them in split order
+// in the next launch: the end of a launch is what makes one XCD's writes
+// visible to another without flushing L2 caches mid-kernel.
+struct SplitPlan {
+  int dp, sk, nsplit, KT;
+};
+template <int BM, int BN>
+__device__ __forceinline__ SplitPlan split_plan(const int* __restrict__ off, int E, int R,
+                                                int K, int N, int slots) {
+  SplitPlan pl;
+  const int NTN = (N + BN - 1) / BN;
+  pl.KT = (K + BK - 1) / BK;
+  const int nreal = count_row_tiles(off, E, R, BM) * NTN;
+  pl.dp = (nreal / slots) * slots;                 // tiles run whole
+  pl.sk = nreal - pl.dp;                           // tiles split along K
+  pl.nsplit = 1;
+  // (short-K GEMMs gain less from filling the last round than the partials
+  // and shorter pipelines cost them)
+  if (pl.sk > 0 && pl.KT >= 8 * MIN_SPLIT_STEPS)
+    pl.nsplit = max(1, min(slots / pl.sk, pl.KT / MIN_SPLIT_STEPS));
+  return pl;
+}
+
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(MOE_WPE, MOE_WPE))) void gemm_bf16_grouped(
     const uint16_t* __restrict__ A, const int* __restrict__ gather, int a_rows,
     const uint16_t* __restrict__ W, uint16_t* __restrict__ C, const int* __restrict__ off,
-    int E, int R, int K, int N, int gelu, float* __restrict__ part, int* __restrict__ counters,
-    int slots) {
+    int E, int R, int K, int N, int gelu, float* __restrict__ part, int slots) {
   using S = GemmShape<BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(1024))) char a0[S::LDS_A];
   __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
@@ -471,33 +507,25 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   __shared__ __attribute__((aligned(1024))) char w1[S::LDS_W];
   __shared__ __attribute__((aligned(1024))) char w2[S::LDS_W];
   __shared__ __attribute__((aligned(1024))) char w3[S::LDS_W];
-  __shared__ int flag;
-  const Lds lds{{a0, a1}, {w0, w1, w2, w3}, &flag};
+  const Lds lds{{a0, a1}, {w0, w1, w2, w3}};
 
-  const int NTN = (N + BN - 1) / BN;
-  const int KT = (K + BK - 1) / BK;
-  const int nreal = count_row_tiles(off, E, R, BM) * NTN;
-  const int dp = (nreal / slots) * slots;          // tiles run whole
-  const int sk = nreal - dp;                       // tiles split along K
-  int nsplit = 1;
-  // (short-K GEMMs gain less from filling the last round than the partials
-  // and shorter pipelines cost them)
-  if (sk > 0 && KT >= 8 * MIN_SPLIT_STEPS) nsplit = max(1, min(slots / sk, KT / MIN_SPLIT_STEPS));
+  const SplitPlan pl = split_plan<BM, BN>(off, E, R, K, N, slots);
   const int bid = blockIdx.x;
-  int L, kt_begin = 0, kt_end = KT;
-  Split sp{1, 0, 0, part, counters};
-  if (bid < dp) {
-    L = xcd_remap(bid, dp);
+  int L, kt_begin = 0, kt_end = pl.KT;
+  Split sp{1, 0, 0, part};
+  if (bid < pl.dp) {
+    L = xcd_remap(bid, pl.dp);
   } else {
-    const int p = bid - dp;
-    if (p >= sk * nsplit) return;
-    L = dp + p / nsplit;
-    sp.S = nsplit;
-    sp.s = p % nsplit;
-    sp.slot = L - dp;
-    kt_begin = sp.s * KT / nsplit;
-    kt_end = (sp.s + 1) * KT / nsplit;
+    const int p = bid - pl.dp;
+    if (p >= pl.sk * pl.nsplit) return;
+    L = pl.dp + p / pl.nsplit;
+    sp.S = pl.nsplit;
+    sp.s = p % pl.nsplit;
+    sp.slot = L - pl.dp;
+    kt_begin = sp.s * pl.KT / pl.nsplit;
+    kt_end = (sp.s + 1) * pl.KT / pl.nsplit;
   }
+  const int NTN = (N + BN - 1) / BN;
   const Tile tile = lookup_tile(off, E, R, BM, NTN, L);
   if (!tile.valid) return;
   const uint16_t* We = W + (size_t)tile.e * K * N;
@@ -510,9 +538,69 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
                                   kt_end, sp, lds);
 }
 
-__global__ void zero_ints(int* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+// Sum of the S partials of split tile `slot` in split order, then the tile's
+// epilogue.
+template <int BM, int BN, int WM, int WN, int NF>
+__device__ __forceinline__ void reduce_tile(int nfm, const float* __restrict__ all, int nsplit,
+                                            uint16_t* __restrict__ C, const Tile& tile, int N,
+                                            int gelu, const Lds& lds) {
+  using S = GemmShape<BM, BN, WM, WN>;
+  if constexpr (NF > 0) {
+    if (nfm != NF) {
+      reduce_tile<BM, BN, WM, WN, NF - 1>(nfm, all, nsplit, C, tile, N, gelu, lds);
+      return;
+    }
+    const int tid = threadIdx.x;
+    f32x16 acc[S::FN][NF];
+    // one 32-row block at a time, all its loads of one piece in flight together
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      f32x4 run[S::FN][4];
+      for (int ps = 0; ps < nsplit; ++ps) {
+        const float* src = all + (size_t)ps * S::PER_PIECE;
+        f32x4 t[S::FN][4];
+#pragma unroll
+        for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+          for (int vq = 0; vq < 4; ++vq)
+            t[i][vq] = *(const f32x4*)(src + (((i * S::FM + j) * 16 + 4 * vq) * S::NT + tid * 4));
+#pragma unroll
+        for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+          for (int vq = 0; vq < 4; ++vq) run[i][vq] = ps == 0 ? t[i][vq] : run[i][vq] + t[i][vq];
+      }
+#pragma unroll
+      for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * vq + e] = run[i][vq][e];
+    }
+    store_tile<BM, BN, WM, WN, NF>(acc, C, tile, N, gelu, lds);
+  }
+}
+
+// One workgroup per split tile (at most kMaxSlots / 2 of them: a split needs
+// nsplit >= 2, so sk <= slots / 2).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
+    uint16_t* __restrict__ C, const int* __restrict__ off, int E, int R, int K, int N,
+    int gelu, const float* __restrict__ part, int slots) {
+  using S = GemmShape<BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(1024))) char a0[S::LDS_A];
+  __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
+  const Lds lds{{a0, a1}, {nullptr, nullptr, nullptr, nullptr}};
+  const SplitPlan pl = split_plan<BM, BN>(off, E, R, K, N, slots);
+  const int slot = blockIdx.x;
+  if (pl.nsplit < 2 || slot >= pl.sk) return;
+  const int NTN = (N + BN - 1) / BN;
+  const Tile tile = lookup_tile(off, E, R, BM, NTN, pl.dp + slot);
+  if (!tile.valid) return;
+  const int wm = (threadIdx.x / kWave) % WM;
+  int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
+  nfm = __builtin_amdgcn_readfirstlane(nfm);
+  reduce_tile<BM, BN, WM, WN, S::FM>(nfm, part + (size_t)slot * pl.nsplit * S::PER_PIECE,
+                                     pl.nsplit, C, tile, N, gelu, lds);
 }
 
 int device_slots() {
@@ -542,25 +630,25 @@ hipError_t launch_cfg(const void* A, const int* gather, int a_rows, const void* 
   long blocks = mt_max * NTN + slots;
   if (blocks <= slots) return hipSuccess;
   float* part = (float*)split_ws;
-  int* counters = (int*)((char*)split_ws + split_part_bytes());
   hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN>), dim3((unsigned)blocks),
                      dim3(kWave * WM * WN), 0, s, (const uint16_t*)A, gather, a_rows,
                      (const uint16_t*)W, (uint16_t*)C, off, E, R, K, N, gelu ? 1 : 0, part,
-                     counters, slots);
-  return hipGetLastError();
+                     slots);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // tiles are split only when K has at least 8 * MIN_SPLIT_STEPS steps
+  if ((K + BK - 1) / BK >= 8 * MIN_SPLIT_STEPS) {
+    hipLaunchKernelGGL((gemm_split_reduce<BM, BN, WM, WN>), dim3(kMaxSlots / 2),
+                       dim3(kWave * WM * WN), 0, s, (uint16_t*)C, off, E, R, K, N,
+                       gelu ? 1 : 0, (const float*)part, slots);
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 }  // namespace
 
-size_t split_part_bytes() { return (size_t)kMaxSlots * 256 * 256 * sizeof(float); }
-size_t split_ws_bytes() { return split_part_bytes() + align_up(kMaxSlots * sizeof(int)); }
-
-hipError_t clear_split_counters(void* split_ws, hipStream_t s) {
-  int* counters = (int*)((char*)split_ws + split_part_bytes());
-  hipLaunchKernelGGL(zero_ints, dim3((kMaxSlots + 255) / 256), dim3(256), 0, s, counters,
-                     kMaxSlots);
-  return hipGetLastError();
-}
+size_t split_ws_bytes() { return (size_t)kMaxSlots * 256 * 256 * sizeof(float); }
 
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
                             void* C, const int* off, int E, int R, int K, int N, bool gelu,

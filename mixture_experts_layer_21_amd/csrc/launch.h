@@ -30,12 +30,10 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
                           int32_t* inv_pos, void* xp, void* ws, hipStream_t s);
 
 // Split-tile workspace of the bf16 grouped GEMM: fp32 partials of at most
-// kMaxSlots pieces plus one counter per split tile (cleared before the GEMMs
-// of one FFN; every split tile leaves its counter clear again).
+// kMaxSlots pieces (written by one GEMM launch, summed by the next kernel on
+// the stream; nothing in it needs clearing).
 constexpr int kMaxSlots = 256;
-size_t split_part_bytes();
 size_t split_ws_bytes();
-hipError_t clear_split_counters(void* split_ws, hipStream_t s);
 // A holds a_rows rows of K; with gather != nullptr, dispatched row p is row
 // gather[p] of A (the dispatch fused into the GEMM's loads), else row p.
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,

@@ -79,9 +79,7 @@ moe_status run_ffn(const void* xp, const int32_t* gather, int64_t a_rows, const 
   hipError_t err;
   if (dt == MOE_BF16) {
     void* split = (char*)h + align_up((size_t)R * F * elem_bytes(dt));
-    err = moe::clear_split_counters(split, s);
-    if (err == hipSuccess)
-      err = moe::launch_gemm_bf16(xp, gather, (int)a_rows, w1, h, off, (int)E, (int)R, (int)H,
+    err = moe::launch_gemm_bf16(xp, gather, (int)a_rows, w1, h, off, (int)E, (int)R, (int)H,
                                   (int)F, true, split, s);
     if (err == hipSuccess)
       err = moe::launch_gemm_bf16(h, nullptr, (int)R, w2, yp, off, (int)E, (int)R, (int)F,
