@@ -139,12 +139,13 @@ struct Lds {
   char* w[W_STAGES];
 };
 
-// Epilogue of one output tile from the accumulators (callers have made the
-// token ring free: no wave reads it any more).
+// Epilogue of one output tile from the accumulators: acc[.][j] holds 32-row
+// block jbase + j of the wave (callers have made the token ring free: no wave
+// reads it any more).
 template <int BM, int BN, int WM, int WN, int NFM, int FMA>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN, WM, WN>::FN][FMA],
                                            uint16_t* __restrict__ C, const Tile& tile, int N,
-                                           int gelu, const Lds& lds) {
+                                           int gelu, const Lds& lds, int jbase = 0) {
   using S = GemmShape<BM, BN, WM, WN>;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -191,7 +192,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
         const int r = q * 8 + lane / 8;
         if (p * 32 + r >= NFM * 32) break;           // (odd NFM: half a pass)
         const int slot = lane % 8;
-        const int m = wrow0 + p * 32 + r;
+        const int m = wrow0 + (jbase + p) * 32 + r;
         const int n = n0 + wn * S::TN + (slot ^ (r & 7)) * 8;
         const u32x4 v = *(const u32x4*)(stg + r * 128 + slot * 16);
         if (m < tile.mrows && n < N) *(u32x4*)(C + (size_t)(tile.row0 + m) * N + n) = v;
@@ -538,50 +539,9 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
                                   kt_end, sp, lds);
 }
 
-// Sum of the S partials of split tile `slot` in split order, then the tile's
-// epilogue.
-template <int BM, int BN, int WM, int WN, int NF>
-__device__ __forceinline__ void reduce_tile(int nfm, const float* __restrict__ all, int nsplit,
-                                            uint16_t* __restrict__ C, const Tile& tile, int N,
-                                            int gelu, const Lds& lds) {
-  using S = GemmShape<BM, BN, WM, WN>;
-  if constexpr (NF > 0) {
-    if (nfm != NF) {
-      reduce_tile<BM, BN, WM, WN, NF - 1>(nfm, all, nsplit, C, tile, N, gelu, lds);
-      return;
-    }
-    const int tid = threadIdx.x;
-    f32x16 acc[S::FN][NF];
-    // one 32-row block at a time, all its loads of one piece in flight together
-#pragma unroll
-    for (int j = 0; j < NF; ++j) {
-      f32x4 run[S::FN][4];
-      for (int ps = 0; ps < nsplit; ++ps) {
-        const float* src = all + (size_t)ps * S::PER_PIECE;
-        f32x4 t[S::FN][4];
-#pragma unroll
-        for (int i = 0; i < S::FN; ++i)
-#pragma unroll
-          for (int vq = 0; vq < 4; ++vq)
-            t[i][vq] = *(const f32x4*)(src + (((i * S::FM + j) * 16 + 4 * vq) * S::NT + tid * 4));
-#pragma unroll
-        for (int i = 0; i < S::FN; ++i)
-#pragma unroll
-          for (int vq = 0; vq < 4; ++vq) run[i][vq] = ps == 0 ? t[i][vq] : run[i][vq] + t[i][vq];
-      }
-#pragma unroll
-      for (int i = 0; i < S::FN; ++i)
-#pragma unroll
-        for (int vq = 0; vq < 4; ++vq)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * vq + e] = run[i][vq][e];
-    }
-    store_tile<BM, BN, WM, WN, NF>(acc, C, tile, N, gelu, lds);
-  }
-}
-
-// One workgroup per split tile (at most kMaxSlots / 2 of them: a split needs
-// nsplit >= 2, so sk <= slots / 2).
+// Split tiles: one workgroup per (split tile, 32-row block jb of every
+// wave).  Each wave adds the S partials of its block in split order, two
+// pieces' loads in flight per round trip, and stores the block.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
     uint16_t* __restrict__ C, const int* __restrict__ off, int E, int R, int K, int N,
@@ -591,16 +551,47 @@ __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
   __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
   const Lds lds{{a0, a1}, {nullptr, nullptr, nullptr, nullptr}};
   const SplitPlan pl = split_plan<BM, BN>(off, E, R, K, N, slots);
-  const int slot = blockIdx.x;
+  const int slot = blockIdx.x / S::FM, jb = blockIdx.x % S::FM;
   if (pl.nsplit < 2 || slot >= pl.sk) return;
   const int NTN = (N + BN - 1) / BN;
   const Tile tile = lookup_tile(off, E, R, BM, NTN, pl.dp + slot);
   if (!tile.valid) return;
-  const int wm = (threadIdx.x / kWave) % WM;
-  int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
-  nfm = __builtin_amdgcn_readfirstlane(nfm);
-  reduce_tile<BM, BN, WM, WN, S::FM>(nfm, part + (size_t)slot * pl.nsplit * S::PER_PIECE,
-                                     pl.nsplit, C, tile, N, gelu, lds);
+  const int tid = threadIdx.x;
+  const int wm = (tid / kWave) % WM;
+  const int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
+  if (__builtin_amdgcn_readfirstlane(nfm) <= jb) return;   // no valid rows in this block
+  const float* all = part + (size_t)slot * pl.nsplit * S::PER_PIECE;
+  auto load = [&](int ps, f32x4 (&t)[S::FN][4]) {
+    const float* src = all + (size_t)ps * S::PER_PIECE;
+#pragma unroll
+    for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq)
+        t[i][vq] = *(const f32x4*)(src + (((i * S::FM + jb) * 16 + 4 * vq) * S::NT + tid * 4));
+  };
+  f32x4 run[S::FN][4];
+  load(0, run);
+  for (int ps = 1; ps < pl.nsplit; ps += 2) {
+    f32x4 t0[S::FN][4], t1[S::FN][4];
+    load(ps, t0);
+    const bool two = ps + 1 < pl.nsplit;
+    if (two) load(ps + 1, t1);
+#pragma unroll
+    for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) {
+        run[i][vq] += t0[i][vq];
+        if (two) run[i][vq] += t1[i][vq];
+      }
+  }
+  f32x16 acc[S::FN][1];
+#pragma unroll
+  for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+    for (int vq = 0; vq < 4; ++vq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][0][4 * vq + e] = run[i][vq][e];
+  store_tile<BM, BN, WM, WN, 1>(acc, C, tile, N, gelu, lds, jb);
 }
 
 int device_slots() {
@@ -638,7 +629,8 @@ hipError_t launch_cfg(const void* A, const int* gather, int a_rows, const void* 
   if (err != hipSuccess) return err;
   // tiles are split only when K has at least 8 * MIN_SPLIT_STEPS steps
   if ((K + BK - 1) / BK >= 8 * MIN_SPLIT_STEPS) {
-    hipLaunchKernelGGL((gemm_split_reduce<BM, BN, WM, WN>), dim3(kMaxSlots / 2),
+    hipLaunchKernelGGL((gemm_split_reduce<BM, BN, WM, WN>),
+                       dim3(kMaxSlots / 2 * GemmShape<BM, BN, WM, WN>::FM),
                        dim3(kWave * WM * WN), 0, s, (uint16_t*)C, off, E, R, K, N,
                        gelu ? 1 : 0, (const float*)part, slots);
     err = hipGetLastError();
