@@ -3,13 +3,15 @@
 // routing article's scan fixes ties to the lower expert index).
 //
 // bf16 path
-//   wr_transpose      W_r[H,E] -> WrT[EP,H] (EP = E rounded up to 16, zero
-//                     rows), so both MFMA operands are k-contiguous.
-//   route_logits_bf16 MFMA 16x16x32 bf16 with fp32 accumulation.  Each wave is
-//                     an independent work item (16 tokens, TPW expert tiles of
-//                     16, one K split) and loads its operands straight from
-//                     global memory (x from HBM once per expert group, WrT from
-//                     L2).  Partial logits go to part[S][T][EP] (fp32).
+//   route_logits_bf16 MFMA 16x16x32 bf16 with fp32 accumulation.  A workgroup
+//                     owns one expert group (TPW tiles of 16 experts) and one
+//                     split of the H axis (KL rows) for 4 token tiles of 16,
+//                     one per wave.  The W_r block [KL][16 TPW] is staged in
+//                     LDS once in its natural k-major layout and read by the
+//                     waves with transposed LDS reads (4 consecutive k of one
+//                     expert per lane and read); the token operand comes
+//                     straight from global memory.  Partial logits go to
+//                     part[S][T][EP] (fp32, EP = E rounded up to 16).
 // fp32 path: the logits come from the fp32 grouped GEMM in dense mode.
 //
 //   route_select      one wave per token: sums the S partial logits in fixed
@@ -22,49 +24,65 @@
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(256) void wr_transpose(const uint16_t* __restrict__ wr,
-                                                    uint16_t* __restrict__ wrT,
-                                                    int H, int E, int EP) {
-  __shared__ uint16_t tile[64][65];
-  const int h0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-  for (int i = ty; i < 64; i += 4) {
-    const int h = h0 + i, e = e0 + tx;
-    tile[i][tx] = (h < H && e < E) ? wr[(size_t)h * E + e] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int e = e0 + i, h = h0 + tx;
-    if (e < EP && h < H) wrT[(size_t)e * H + h] = tile[tx][i];
-  }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16): in each group of 16 lanes,
+// lane i addresses 8 bytes of row i/4 and receives column i of the 4x16 block
+// those addresses cover.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
 }
 
 template <int TPW>
 __global__ __launch_bounds__(256) void route_logits_bf16(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wrT,
-    float* __restrict__ part, int T, int H, int EP, int EG, int S, int KL,
-    int n_items) {
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_r,
+    float* __restrict__ part, int T, int H, int E, int EP, int EG, int S, int KL) {
+  extern __shared__ __attribute__((aligned(16))) char wb[];   // [KL][16 TPW] bf16
+  constexpr int ROW = TPW * 16 * 2;                            // bytes per k row
   const int lane = threadIdx.x % kWave;
-  const int item = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (item >= n_items) return;
-  const int eg = item % EG;
-  const int s = (item / EG) % S;
-  const int tt = item / (EG * S);
-  const int NET = EP / 16;
-
+  const int wave = threadIdx.x / kWave;
+  const int eg = blockIdx.x % EG;
+  const int s = (blockIdx.x / EG) % S;
+  const int tg = blockIdx.x / (EG * S);
   const int k_begin = s * KL;
   const int k_end = min(H, k_begin + KL);
+  const int e0 = eg * TPW * 16;
+
+  // stage W_r[k_begin:k_begin+KL, e0:e0+16 TPW]; rows past H and experts
+  // past E are zero
+  {
+    constexpr int CH = TPW * 2;                    // 8-expert chunks per row
+    const bool vec = (E % 8) == 0;
+    for (int q = threadIdx.x; q < KL * CH; q += blockDim.x) {
+      const int r = q / CH, c = q % CH;
+      const int k = k_begin + r, e = e0 + c * 8;
+      u32x4 v = {0, 0, 0, 0};
+      if (k < k_end) {
+        if (vec) {
+          if (e < E) v = *(const u32x4*)(w_r + (size_t)k * E + e);
+        } else {
+          uint16_t h[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) h[u] = (e + u < E) ? w_r[(size_t)k * E + e + u] : (uint16_t)0;
+          v = u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                    h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+        }
+      }
+      *(u32x4*)(wb + r * ROW + c * 16) = v;
+    }
+  }
+  __syncthreads();
+
+  const int tt = tg * 4 + wave;
+  if (tt * 16 >= T) return;
   const int tok = min(tt * 16 + (lane % 16), T - 1);
   const int kl = (lane / 16) * 8;
   const uint16_t* xr = x + (size_t)tok * H + kl;
-  const uint16_t* wr[TPW];
-  bool tile_ok[TPW];
-#pragma unroll
-  for (int j = 0; j < TPW; ++j) {
-    const int et = eg * TPW + j;
-    tile_ok[j] = et < NET;
-    wr[j] = wrT + (size_t)((tile_ok[j] ? et : 0) * 16 + (lane % 16)) * H + kl;
-  }
+  // B operand: lane holds expert e0 + 16 j + lane%16 and k = 8 (lane/16) + 0..7
+  // of the step, as two transposed reads of 4 rows each
+  const int li = lane % 16;
+  const int rd_off = (8 * (lane / 16) + li / 4) * ROW + (li % 4) * 8;
 
   f32x4 acc[TPW];
 #pragma unroll
@@ -73,19 +91,23 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
   for (int k0 = k_begin; k0 < k_end; k0 += 32) {
     const bool ok = k0 + kl < k_end;
     const u32x4 a = ok ? *(const u32x4*)(xr + k0) : u32x4{0, 0, 0, 0};
+    const char* base = wb + (k0 - k_begin) * ROW + rd_off;
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-      const u32x4 b = ok ? *(const u32x4*)(wr[j] + k0) : u32x4{0, 0, 0, 0};
+      const u32x2 lo = lds_read_tr(base + j * 32);
+      const u32x2 hi = lds_read_tr(base + 4 * ROW + j * 32);
+      const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
       acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b),
                                                        acc[j], 0, 0, 0);
     }
   }
-  // D[i][j]: lane holds expert column j = lane%16, token rows 4*(lane/16)+v
+  // D: lane holds expert column lane%16 of tile j, token rows 4*(lane/16)+v
+  const int NET = EP / 16;
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
-    if (!tile_ok[j]) continue;
-    const int e = (eg * TPW + j) * 16 + (lane % 16);
+    if (eg * TPW + j >= NET) continue;
+    const int e = e0 + j * 16 + (lane % 16);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int t = tt * 16 + (lane / 16) * 4 + v;
@@ -103,25 +125,26 @@ __global__ __launch_bounds__(256) void route_select(
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
 
-  // sum the S partial logits in split order; the loads of a batch of 8
-  // splits are all issued before any is added
+  // sum the S partial logits in split order; all loads of a batch of SB
+  // splits (for every expert of the lane) are issued before any is added
+  constexpr int SB = NPL <= 4 ? 8 : (NPL <= 8 ? 4 : 2);
   float v[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) v[i] = 0.f;
   const size_t sstride = (size_t)T * EP;
-  for (int s0 = 0; s0 < S; s0 += 8) {
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    float q[NPL][SB];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
       const int e = lane + i * kWave;
-      if (e < E) {
-        const float* p = part + ((size_t)s0 * T + t) * EP + e;
-        float q[8];
+      const float* p = part + ((size_t)s0 * T + t) * EP + e;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) q[u] = (s0 + u < S) ? p[u * sstride] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[i] += q[u];
-      }
+      for (int u = 0; u < SB; ++u) q[i][u] = (e < E && s0 + u < S) ? p[u * sstride] : 0.f;
     }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+#pragma unroll
+      for (int u = 0; u < SB; ++u) v[i] += q[i][u];
   }
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
@@ -201,11 +224,14 @@ RoutePlan plan_route(int T, int H, int E, bool bf16) {
   while (tpw < 16 && tpw * 4 < NET) tpw *= 2;
   p.TPW = tpw;
   p.EG = (NET + tpw - 1) / tpw;
+  // about 2048 waves in all, and a staged W_r block of at most 64 KB
+  // (KL * 32 TPW bytes)
   const int TT = (T + 15) / 16;
   const long base_items = std::max<long>(1, (long)TT * p.EG);
   int S = (int)std::min<long>(64, std::max<long>(1, (2048 + base_items - 1) / base_items));
   int KL = (H + S - 1) / S;
   KL = (KL + 31) / 32 * 32;
+  KL = std::min(KL, 2048 / tpw);
   p.KL = KL;
   p.S = (H + KL - 1) / KL;
   return p;
@@ -213,9 +239,7 @@ RoutePlan plan_route(int T, int H, int E, bool bf16) {
 
 size_t route_ws_bytes(int T, int H, int E, bool bf16) {
   const RoutePlan p = plan_route(T, H, E, bf16);
-  size_t b = align_up((size_t)p.S * T * p.EP * sizeof(float));
-  if (bf16) b += align_up((size_t)p.EP * H * 2);
-  return b;
+  return align_up((size_t)p.S * T * p.EP * sizeof(float));
 }
 
 hipError_t launch_route(const void* x, const void* w_r, const float* bias,
@@ -224,18 +248,17 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
   const RoutePlan p = plan_route(T, H, E, bf16);
   float* part = (float*)ws;
   if (bf16) {
-    uint16_t* wrT = (uint16_t*)((char*)ws + align_up((size_t)p.S * T * p.EP * sizeof(float)));
-    hipLaunchKernelGGL(wr_transpose, dim3((H + 63) / 64, (p.EP + 63) / 64), dim3(256), 0, s,
-                       (const uint16_t*)w_r, wrT, H, E, p.EP);
-    const int TT = (T + 15) / 16;
-    const int n_items = TT * p.EG * p.S;
-    dim3 g((n_items + 3) / 4), b(256);
+    const int TG = ((T + 15) / 16 + 3) / 4;
+    dim3 g((unsigned)(TG * p.EG * p.S)), b(256);
+    const size_t lds = (size_t)p.KL * p.TPW * 32;
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* wb = (const uint16_t*)w_r;
     switch (p.TPW) {
-      case 1: hipLaunchKernelGGL(route_logits_bf16<1>, g, b, 0, s, (const uint16_t*)x, wrT, part, T, H, p.EP, p.EG, p.S, p.KL, n_items); break;
-      case 2: hipLaunchKernelGGL(route_logits_bf16<2>, g, b, 0, s, (const uint16_t*)x, wrT, part, T, H, p.EP, p.EG, p.S, p.KL, n_items); break;
-      case 4: hipLaunchKernelGGL(route_logits_bf16<4>, g, b, 0, s, (const uint16_t*)x, wrT, part, T, H, p.EP, p.EG, p.S, p.KL, n_items); break;
-      case 8: hipLaunchKernelGGL(route_logits_bf16<8>, g, b, 0, s, (const uint16_t*)x, wrT, part, T, H, p.EP, p.EG, p.S, p.KL, n_items); break;
-      default: hipLaunchKernelGGL(route_logits_bf16<16>, g, b, 0, s, (const uint16_t*)x, wrT, part, T, H, p.EP, p.EG, p.S, p.KL, n_items); break;
+      case 1: hipLaunchKernelGGL(route_logits_bf16<1>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
+      case 2: hipLaunchKernelGGL(route_logits_bf16<2>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
+      case 4: hipLaunchKernelGGL(route_logits_bf16<4>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
+      case 8: hipLaunchKernelGGL(route_logits_bf16<8>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
+      default: hipLaunchKernelGGL(route_logits_bf16<16>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
     }
   } else {
     hipError_t err = launch_gemm_f32((const float*)x, (const float*)w_r, part, nullptr, 1, T, H, E,
