@@ -37,13 +37,8 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_WM
-#define MOE_WM 2                // waves along the token rows
-#endif
-#ifndef MOE_WN
-#define MOE_WN 4                // waves along the columns
-#endif
-#define MOE_WPE ((MOE_WM * MOE_WN) / 4)   // waves per SIMD
+constexpr int kWM = 2;          // waves along the token rows
+constexpr int kWN = 4;          // waves along the columns (8 waves: two per SIMD)
 constexpr int BK = 32;          // K step (bf16 elements): two 16-wide MFMA slices
 constexpr int W_STAGES = 4;     // weight ring: one K step per stage, 3 in flight
 constexpr int A_STAGES = 2;     // token ring: two K steps (128-byte rows) per stage
@@ -497,7 +492,7 @@ __device__ __forceinline__ SplitPlan split_plan(const int* __restrict__ off, int
 }
 
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(MOE_WPE, MOE_WPE))) void gemm_bf16_grouped(
+__global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_grouped(
     const uint16_t* __restrict__ A, const int* __restrict__ gather, int a_rows,
     const uint16_t* __restrict__ W, uint16_t* __restrict__ C, const int* __restrict__ off,
     int E, int R, int K, int N, int gelu, float* __restrict__ part, int slots) {
@@ -645,7 +640,7 @@ size_t split_ws_bytes() { return (size_t)kMaxSlots * 256 * 256 * sizeof(float); 
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
                             void* C, const int* off, int E, int R, int K, int N, bool gelu,
                             void* split_ws, hipStream_t s) {
-  return launch_cfg<256, 256, MOE_WM, MOE_WN>(A, gather, a_rows, W, C, off, E, R, K, N, gelu,
+  return launch_cfg<256, 256, kWM, kWN>(A, gather, a_rows, W, C, off, E, R, K, N, gelu,
                                               split_ws, s);
 }
 
