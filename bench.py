@@ -82,22 +82,36 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibration_copy_bytes": n}))
 
 
-def _counter_per_dispatch(csv_path: str, counter: str, kernel_substr: str):
+def _counter_totals(csv_path: str, counter: str, kernel_substr: str, required: bool = True):
+    """(sum over dispatches, number of dispatches) of a counter for the kernels
+    whose name contains kernel_substr."""
     import csv
     vals = {}
     for r in csv.DictReader(open(csv_path)):
         if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
             vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
-    if not vals:
+    if not vals and required:
         raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {csv_path}")
-    return sum(vals.values()) / len(vals), len(vals)
+    return sum(vals.values()), len(vals)
+
+
+def _counter_per_dispatch(csv_path: str, counter: str, kernel_substr: str):
+    total, n = _counter_totals(csv_path, counter, kernel_substr)
+    return total / n, n
 
 
 def summarize_traffic(a):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the grouped GEMM, scaled by
-    what the same counters read for a plain copy of known size."""
-    fetch, nd = _counter_per_dispatch(a.summarize_traffic[0], "FETCH_SIZE", "gemm_bf16_grouped")
-    write, _ = _counter_per_dispatch(a.summarize_traffic[1], "WRITE_SIZE", "gemm_bf16_grouped")
+    """FETCH_SIZE / WRITE_SIZE (KiB per launch) of the grouped GEMM, scaled by
+    what the same counters read for a plain copy of known size.  A launch of
+    the GEMM is its main kernel plus the split-tile reduce kernel that follows
+    it, so both kernels' counts are added and divided by the number of main
+    kernel dispatches."""
+    fg, nd = _counter_totals(a.summarize_traffic[0], "FETCH_SIZE", "gemm_bf16_grouped")
+    wg, _ = _counter_totals(a.summarize_traffic[1], "WRITE_SIZE", "gemm_bf16_grouped")
+    fr, nr = _counter_totals(a.summarize_traffic[0], "FETCH_SIZE", "gemm_split_reduce", False)
+    wr, _ = _counter_totals(a.summarize_traffic[1], "WRITE_SIZE", "gemm_split_reduce", False)
+    fetch = (fg + fr) / nd
+    write = (wg + wr) / nd
     copy_kernel = "copy"
     cf, _ = _counter_per_dispatch(a.summarize_traffic[2], "FETCH_SIZE", copy_kernel)
     cw, _ = _counter_per_dispatch(a.summarize_traffic[3], "WRITE_SIZE", copy_kernel)
@@ -105,7 +119,9 @@ def summarize_traffic(a):
     f_fetch = nbytes / (cf * 1024.0)
     f_write = nbytes / (cw * 1024.0)
     rec = {"kernel": "gemm_bf16_grouped", "workload": a.config, "source_hash": gemm_source_hash(),
-           "dispatches": nd, "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "dispatches": nd, "reduce_dispatches": nr,
+           "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
+           "reduce_fetch_kib_per_launch": fr / nd, "reduce_write_kib_per_launch": wr / nd,
            "copy_bytes": nbytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_factor": f_fetch, "write_factor": f_write,
            "traffic_bytes_per_launch": fetch * 1024.0 * f_fetch + write * 1024.0 * f_write}
@@ -113,7 +129,8 @@ def summarize_traffic(a):
     with open(path, "w") as fh:
         fh.write(f"# HBM traffic of gemm_bf16_grouped on {a.config}\n\n")
         fh.write("Counters from two rocprofv3 passes over the bench (FETCH_SIZE, then "
-                 "WRITE_SIZE, KiB per dispatch, averaged over the GEMM's dispatches), each "
+                 "WRITE_SIZE, KiB per launch: gemm_bf16_grouped plus the gemm_split_reduce "
+                 "kernel that follows each launch, averaged over the launches), each "
                  "scaled by the ratio of true bytes to counted bytes for a plain "
                  f"{a.copy_mib} MiB device copy (torch copy kernel) under the same counter.\n\n")
         fh.write("Commands (run from the repository root on the GPU host):\n\n```\n")
@@ -128,9 +145,9 @@ def summarize_traffic(a):
         fh.write(f"python3 bench.py --config {a.config} --summarize-traffic <f csv> <w csv> "
                  "<cf csv> <cw csv>\n```\n\n")
         fh.write(f"| quantity | value |\n|---|---|\n")
-        fh.write(f"| GEMM dispatches averaged | {nd} |\n")
-        fh.write(f"| FETCH_SIZE per dispatch | {fetch:.0f} KiB |\n")
-        fh.write(f"| WRITE_SIZE per dispatch | {write:.0f} KiB |\n")
+        fh.write(f"| GEMM launches averaged (reduce dispatches) | {nd} ({nr}) |\n")
+        fh.write(f"| FETCH_SIZE per launch (of it, reduce) | {fetch:.0f} KiB ({fr / nd:.0f} KiB) |\n")
+        fh.write(f"| WRITE_SIZE per launch (of it, reduce) | {write:.0f} KiB ({wr / nd:.0f} KiB) |\n")
         fh.write(f"| copy of {nbytes} B: FETCH / WRITE | {cf:.0f} / {cw:.0f} KiB |\n")
         fh.write(f"| scale factors fetch / write | {f_fetch:.4f} / {f_write:.4f} |\n")
         fh.write(f"| HBM bytes per launch | {rec['traffic_bytes_per_launch'] / 1e9:.4f} GB |\n\n")
@@ -164,9 +181,10 @@ def alg_counts(cfg, ids: np.ndarray):
 
 
 def gemm_launch_counts(cfg, touched):
-    """Per launch of the grouped expert GEMM (both FFN GEMMs are equal):
-    flops 2*R*H*F; bytes = the touched experts' weight matrix + the A operand
-    rows read + the C rows written."""
+    """Per launch of the grouped expert GEMM (both FFN GEMMs are equal; a
+    launch is the main kernel plus its split-tile reduce): flops 2*R*H*F;
+    bytes = the touched experts' weight matrix + the A operand rows read + the
+    C rows written."""
     es = 4 if cfg.dtype == "f32" else 2
     R = cfg.R
     flops = 2 * R * cfg.H * cfg.F
@@ -285,7 +303,8 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = read_traffic(cfg.name) if cfg.dtype == "bf16" else None
-    roof["kernel"] = "gemm_bf16_grouped" if cfg.dtype == "bf16" else "gemm_f32_grouped"
+    roof["kernel"] = ("gemm_bf16_grouped + gemm_split_reduce" if cfg.dtype == "bf16"
+                      else "gemm_f32_grouped")
     roof["per_launch"] = {"flops": g_flops, "bytes": g_bytes, "ms": g_sec * 1e3}
 
     cpu = None
