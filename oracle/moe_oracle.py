@@ -21,8 +21,22 @@ its reason in the design notes):
   * GELU is the tanh form 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
     (Hendrycks & Gimpel 2016), for every workload;
   * experts have no biases; the router has an optional bias b_r[E];
-  * dispatch is dropless: every (token, slot) pair is computed (the gather
-    routine has no capacity limit).
+  * dispatch is dropless by default: every (token, slot) pair is computed
+    (the gather routine has no capacity limit).
+
+Variants (the CANN MoE operator-optimization article, "the CANN article"):
+  * gating "softmax_topk": softmax over all E logits first, then the k
+    largest probabilities kept as they are, not renormalised (section 2.1,
+    Softmax -> Top-k -> mask);
+  * a router weight in fp32 while the experts are half precision (section
+    4.2) needs nothing here: every input is upcast to fp64 exactly;
+  * capacity-limited dispatch: each expert keeps at most `capacity` rows,
+    capacity = ceil(capacity_factor * T * k / E) (section 4.3 gives the
+    factor 1.2; the fused-operator article's dispatch makes blocks of
+    [num_experts, expert_capacity]).  The kept rows of an expert are its
+    first `capacity` (token, slot) pairs in the gather's scan order; a dropped
+    pair contributes nothing to y and the other weights are not renormalised
+    (the routing article names token dropping for overloaded experts).
 """
 from __future__ import annotations
 
@@ -80,28 +94,55 @@ def topk_ids(logits: np.ndarray, k: int) -> np.ndarray:
     return ids
 
 
-def gate_weights(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
-    """w[T,k] = softmax over the k selected logits, in slot order.
+GATINGS = ("topk_softmax", "softmax_topk")
 
-    Fused article, router kernel step 3: Softmax over the top-k scores only.
+
+def gate_weights(logits: np.ndarray, ids: np.ndarray, gating: str = "topk_softmax") -> np.ndarray:
+    """w[T,k] in slot order.
+
+    "topk_softmax" (default): softmax over the k selected logits only (fused
+    article, router kernel step 3).
+    "softmax_topk": softmax over all E logits, then the probabilities of the
+    k selected experts, not renormalised (CANN article, section 2.1).  Softmax
+    is monotone, so the selected experts are the same either way.
     The max is subtracted first (softmax is invariant to the shift).
     """
-    sel = np.take_along_axis(np.asarray(logits, np.float64), ids, axis=1)
-    m = sel.max(axis=1, keepdims=True)
-    ex = np.exp(sel - m)
-    return ex / ex.sum(axis=1, keepdims=True)
+    logits = np.asarray(logits, np.float64)
+    sel = np.take_along_axis(logits, ids, axis=1)
+    if gating == "topk_softmax":
+        m = sel.max(axis=1, keepdims=True)
+        ex = np.exp(sel - m)
+        return ex / ex.sum(axis=1, keepdims=True)
+    if gating == "softmax_topk":
+        m = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - m)
+        p = p / p.sum(axis=1, keepdims=True)
+        return np.take_along_axis(p, ids, axis=1)
+    raise ValueError(f"unknown gating {gating!r}")
 
 
-def route(x, w_r, b_r, k: int):
+def route(x, w_r, b_r, k: int, gating: str = "topk_softmax"):
     """(ids[T,k] int64, w[T,k] fp64, logits[T,E] fp64) for one MoE layer."""
     l = router_logits(x, w_r, b_r)
     ids = topk_ids(l, k)
-    return ids, gate_weights(l, ids), l
+    return ids, gate_weights(l, ids, gating), l
 
 
 # --- dispatch (fused article, GatherTokensByExpert) -----------------------
 
-def dispatch(ids: np.ndarray, E: int):
+def expert_capacity(T: int, k: int, E: int, capacity_factor: float) -> int:
+    """Rows each expert may keep: ceil(capacity_factor * T * k / E); 0 means
+    no limit (capacity_factor <= 0).  CANN article, section 4.3 (factor);
+    fused article, MoE computation flow ([num_experts, expert_capacity]).
+    Computed in exact rational arithmetic from the factor's decimal value."""
+    from fractions import Fraction
+    if capacity_factor <= 0:
+        return 0
+    q = Fraction(str(capacity_factor)) * T * k / E
+    return int(-((-q.numerator) // q.denominator))
+
+
+def dispatch(ids: np.ndarray, E: int, capacity: int = 0):
     """Group the (token, slot) pairs by expert, as the gather routine does.
 
     For each expert e in ascending order, scan tokens b in ascending order and
@@ -109,10 +150,12 @@ def dispatch(ids: np.ndarray, E: int):
     appended rows of expert e form the contiguous block
     [offsets[e], offsets[e+1]) of the dispatched order.  np.nonzero on the
     [T,k] mask returns exactly that (row-major, i.e. b then k) order.
+    With capacity > 0 only the first `capacity` pairs of each expert in that
+    order are appended; the others are dropped (inv_pos = -1).
 
-    Returns offsets[E+1], sorted_token[R] (token of each dispatched row),
-    sorted_slot[R] (slot k of each row) and inv_pos[T,k] (dispatched row of
-    each (token, slot)).
+    Returns offsets[E+1], sorted_token[R'] (token of each dispatched row),
+    sorted_slot[R'] (slot k of each row) and inv_pos[T,k] (dispatched row of
+    each (token, slot), -1 if dropped); R' = offsets[E].
     """
     ids = np.asarray(ids)
     T, k = ids.shape
@@ -120,13 +163,15 @@ def dispatch(ids: np.ndarray, E: int):
     sorted_token, sorted_slot = [], []
     for e in range(E):
         b, s = np.nonzero(ids == e)
+        if capacity > 0:
+            b, s = b[:capacity], s[:capacity]
         sorted_token.append(b)
         sorted_slot.append(s)
         offsets[e + 1] = offsets[e] + b.size
     sorted_token = np.concatenate(sorted_token).astype(np.int64)
     sorted_slot = np.concatenate(sorted_slot).astype(np.int64)
-    inv_pos = np.empty((T, k), dtype=np.int64)
-    inv_pos[sorted_token, sorted_slot] = np.arange(T * k)
+    inv_pos = np.full((T, k), -1, dtype=np.int64)
+    inv_pos[sorted_token, sorted_slot] = np.arange(offsets[E])
     return offsets, sorted_token, sorted_slot, inv_pos
 
 
@@ -166,7 +211,8 @@ def expert_ffn(xp: np.ndarray, offsets: np.ndarray, w1, w2) -> np.ndarray:
 
 
 def combine(yp: np.ndarray, inv_pos: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """y[T,H] = sum over slots j of w[t,j] * yp[inv_pos[t,j]].
+    """y[T,H] = sum over slots j of w[t,j] * yp[inv_pos[t,j]], over the slots
+    that were not dropped (inv_pos >= 0).
 
     Fused article, ScatterWithWeights: every dispatched row is scaled by its
     gate weight and accumulated (not overwritten) into its token's output.
@@ -175,18 +221,21 @@ def combine(yp: np.ndarray, inv_pos: np.ndarray, w: np.ndarray) -> np.ndarray:
     T, k = inv_pos.shape
     y = np.zeros((T, yp.shape[1]), dtype=np.float64)
     for j in range(k):
-        y += np.asarray(w, np.float64)[:, j:j + 1] * yp[inv_pos[:, j]]
+        kept = inv_pos[:, j] >= 0
+        y[kept] += np.asarray(w, np.float64)[kept, j:j + 1] * yp[inv_pos[kept, j]]
     return y
 
 
 # --- the whole layer --------------------------------------------------------
 
-def forward(x, w_r, b_r, w1, w2, k: int, ids=None, w=None):
+def forward(x, w_r, b_r, w1, w2, k: int, ids=None, w=None, gating: str = "topk_softmax",
+            capacity: int = 0):
     """One MoE layer forward, as the fused article's flow states it.
 
-    Routing (TopK of x.W_r), gating (softmax of the k scores), then for each
-    expert: gather its tokens, skip it if it has none, run GELU(x_e W1) W2,
-    and scatter the rows back into y weighted by their gate weights, with "+=".
+    Routing (TopK of x.W_r), gating (softmax of the k scores, or the gating
+    variant), then for each expert: gather its tokens (its first `capacity`
+    ones when capacity > 0), skip it if it has none, run GELU(x_e W1) W2, and
+    scatter the rows back into y weighted by their gate weights, with "+=".
 
     ids/w may be given to drive the expert and combine steps with a chosen
     routing (used when a near-tie lets two routings both be correct); by
@@ -198,12 +247,14 @@ def forward(x, w_r, b_r, w1, w2, k: int, ids=None, w=None):
     if ids is None:
         ids = topk_ids(logits, k)
     if w is None:
-        w = gate_weights(logits, ids)
+        w = gate_weights(logits, ids, gating)
     E = np.asarray(w_r).shape[1]
     T = x.shape[0]
     y = np.zeros((T, x.shape[1]), dtype=np.float64)
     for e in range(E):
         b_idx, s_idx = np.nonzero(ids == e)
+        if capacity > 0:
+            b_idx, s_idx = b_idx[:capacity], s_idx[:capacity]
         if b_idx.size == 0:
             continue
         y_e = expert_ffn_block(x[b_idx], _get(w1, e), _get(w2, e))

@@ -287,3 +287,161 @@ def test_integer_inputs_give_exact_logits_in_bf16():
     # fp32 accumulation of the same products is exact: |l| <= 4*64 = 256
     l32 = (inp["x"].float() @ inp["w_r"].float()).numpy()
     np.testing.assert_array_equal(l, l32.astype(np.float64))
+
+
+# --- gating variant: softmax over all experts, then top-k (not renormalised) --
+
+def _read_gating_golden():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "gating_softmax_topk.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        t, l, ids, w = [p.strip() for p in line.split("|")]
+        rows.append((np.array([float(v) for v in l.split()]), [int(v) for v in ids.split()],
+                     np.array([float(v) for v in w.split()])))
+    return rows
+
+
+def test_softmax_topk_golden():
+    rows = _read_gating_golden()
+    W_r = np.stack([r[0] for r in rows])
+    x = np.eye(4)
+    ids, w, _ = oracle.route(x, W_r, None, 2, gating="softmax_topk")
+    for t, (_, ids_ref, w_ref) in enumerate(rows):
+        assert list(ids[t]) == ids_ref
+        np.testing.assert_allclose(w[t], w_ref, rtol=1e-14)
+
+
+def test_gating_variants_agree_on_selection_and_ratios():
+    l = RNG.standard_normal((50, 16)) * 3
+    ids = oracle.topk_ids(l, 4)
+    a = oracle.gate_weights(l, ids, "topk_softmax")
+    b = oracle.gate_weights(l, ids, "softmax_topk")
+    # both are proportional to exp(l) of the selected experts: equal ratios
+    np.testing.assert_allclose(a[:, 1:] / a[:, :1], b[:, 1:] / b[:, :1], rtol=1e-12)
+    # the top-k softmax sums to one; the full softmax's top-k share is less
+    np.testing.assert_allclose(a.sum(axis=1), 1.0, rtol=1e-14)
+    assert np.all(b.sum(axis=1) < 1.0)
+    # b is a times the selected experts' share of the full softmax
+    share = np.exp(np.take_along_axis(l, ids, 1)).sum(1) / np.exp(l).sum(1)
+    np.testing.assert_allclose(b, a * share[:, None], rtol=1e-12)
+
+
+def test_softmax_topk_full_k_is_full_softmax():
+    l = RNG.standard_normal((20, 6))
+    ids = oracle.topk_ids(l, 6)
+    b = oracle.gate_weights(l, ids, "softmax_topk")
+    full = scipy.special.softmax(l, axis=1)
+    np.testing.assert_allclose(b, np.take_along_axis(full, ids, 1), rtol=1e-13)
+    np.testing.assert_allclose(b.sum(axis=1), 1.0, rtol=1e-13)
+
+
+def test_softmax_topk_shift_invariant():
+    l = RNG.standard_normal((10, 8))
+    ids = oracle.topk_ids(l, 2)
+    np.testing.assert_allclose(oracle.gate_weights(l + 100.0, ids, "softmax_topk"),
+                               oracle.gate_weights(l, ids, "softmax_topk"), rtol=1e-12)
+
+
+def test_unknown_gating_rejected():
+    with pytest.raises(ValueError):
+        oracle.gate_weights(np.zeros((1, 2)), np.zeros((1, 1), dtype=np.int64), "softmax")
+
+
+# --- capacity-limited dispatch ---------------------------------------------------
+
+def _read_capacity_golden():
+    d = {}
+    for line in open(os.path.join(GOLDEN, "dispatch_capacity_tiny.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        key, rest = line.split(None, 1)
+        if "/" in rest:
+            d[key] = np.array([[int(v) for v in r.split()] for r in rest.split("/")])
+        elif key == "factor":
+            d[key] = float(rest)
+        else:
+            vals = [int(v) for v in rest.split()]
+            d[key] = vals[0] if len(vals) == 1 and key in ("T", "k", "E", "capacity") else np.array(vals)
+    return d
+
+
+def test_capacity_golden():
+    g = _read_capacity_golden()
+    assert oracle.expert_capacity(g["T"], g["k"], g["E"], g["factor"]) == g["capacity"]
+    off, st, ss, inv = oracle.dispatch(g["ids"], g["E"], g["capacity"])
+    np.testing.assert_array_equal(off, g["offsets"])
+    np.testing.assert_array_equal(st, g["sorted_token"])
+    np.testing.assert_array_equal(ss, g["sorted_slot"])
+    np.testing.assert_array_equal(inv, g["inv_pos"])
+
+
+def test_expert_capacity_values():
+    # ceil(factor * T * k / E), exact: the pages' factor 1.2 at the layer shapes
+    assert oracle.expert_capacity(2048, 2, 8, 1.2) == 615      # 614.4
+    assert oracle.expert_capacity(4096, 8, 128, 1.2) == 308    # 307.2
+    assert oracle.expert_capacity(64, 2, 8, 1.0) == 16         # exactly 16
+    assert oracle.expert_capacity(64, 8, 256, 1.2) == 3        # 2.4
+    assert oracle.expert_capacity(64, 2, 8, 0.0) == 0          # no limit
+    assert oracle.expert_capacity(7, 1, 7, 0.5) == 1           # 0.5
+
+
+def _brute_dispatch(ids, E, cap):
+    """Pure-Python brute force: walk all pairs in (t, j) order, count per
+    expert, keep while under the cap."""
+    T, k = ids.shape
+    kept = {e: [] for e in range(E)}
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if cap <= 0 or len(kept[e]) < cap:
+                kept[e].append((t, j))
+    return kept
+
+
+@pytest.mark.parametrize("cap", [0, 1, 2, 3, 5, 1000])
+def test_capacity_dispatch_bruteforce(cap):
+    g = np.random.default_rng(cap)
+    T, k, E = 23, 3, 5
+    ids = np.stack([g.permutation(E)[:k] for _ in range(T)])
+    off, st, ss, inv = oracle.dispatch(ids, E, cap)
+    kept = _brute_dispatch(ids, E, cap)
+    pos = 0
+    for e in range(E):
+        assert off[e] == pos
+        for (t, j) in kept[e]:
+            assert st[pos] == t and ss[pos] == j and inv[t, j] == pos
+            pos += 1
+    assert off[E] == pos == len(st)
+    assert (inv >= 0).sum() == pos
+    if cap == 0 or cap >= T:
+        full = oracle.dispatch(ids, E)
+        for a, b in zip(full, (off, st, ss, inv)):
+            np.testing.assert_array_equal(a, b)
+
+
+def test_capacity_forward_matches_dense_with_dropped_weights_zeroed():
+    T, H, E, F, k = 12, 16, 4, 24, 2
+    x, W_r, W1, W2 = _rand_layer(T, H, E, F, seed=7)
+    cap = 3
+    out = oracle.forward(x, W_r, None, W1, W2, k, capacity=cap)
+    ids, w = out["ids"], out["w"]
+    _, _, _, inv = oracle.dispatch(ids, E, cap)
+    assert (inv < 0).any()                       # the cap really drops pairs
+    w_kept = np.where(inv >= 0, w, 0.0)
+    ref = oracle.dense_bruteforce(x, W1, W2, ids, w_kept, E)
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+    # the staged pipeline (dispatch, expert FFN, combine) agrees
+    off, st, _, inv = oracle.dispatch(ids, E, cap)
+    yp = oracle.expert_ffn(oracle.gather_rows(x, st), off, W1, W2)
+    np.testing.assert_allclose(oracle.combine(yp, inv, w), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_capacity_all_dropped_token_is_zero():
+    # every token on expert 0 with cap 1: only token 0 keeps its slot
+    ids = np.zeros((4, 1), dtype=np.int64)
+    off, st, _, inv = oracle.dispatch(ids, 2, 1)
+    np.testing.assert_array_equal(off, [0, 1, 1])
+    np.testing.assert_array_equal(inv[:, 0], [0, -1, -1, -1])
+    y = oracle.combine(np.ones((1, 3)), inv, np.ones((4, 1)))
+    np.testing.assert_array_equal(y, [[1, 1, 1], [0, 0, 0], [0, 0, 0], [0, 0, 0]])
