@@ -65,6 +65,18 @@ enum {
   MOE_BF16 = 1,
 };
 
+/* Gate weights (moe_route_ex, moe_forward_ex). */
+typedef int32_t moe_gating;
+enum {
+  /* softmax over the top_k selected logits: each row of topk_w sums to 1
+     (fused article, section 1 "Routing + Gating"; the default everywhere) */
+  MOE_GATE_TOPK_SOFTMAX = 0,
+  /* softmax over all E logits, then the probabilities of the top_k selected
+     experts, not renormalised (CANN MoE operator article, section 2.1:
+     Softmax -> Top-k -> mask); the selected experts are the same */
+  MOE_GATE_SOFTMAX_TOPK = 1,
+};
+
 /* Host string for a status code (static storage; never NULL). */
 const char* moe_status_string(moe_status status);
 
@@ -117,6 +129,39 @@ moe_status moe_route(const void* x, const void* w_r, const float* router_bias,
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Routing + gating with the variants of the CANN MoE operator article:
+ *   router_dtype: element type of w_r.  Either dtype itself, or MOE_F32 with
+ *     dtype MOE_BF16: an fp32 router for bf16 tokens (section 4.2 keeps the
+ *     routing network in FP32); the products x*w_r are then formed from the
+ *     fp32 weights (accumulated in fp32).  Any other pair returns
+ *     MOE_ERR_UNSUPPORTED.
+ *   gating: MOE_GATE_TOPK_SOFTMAX or MOE_GATE_SOFTMAX_TOPK (else
+ *     MOE_ERR_INVALID_ARG).
+ * Everything else as moe_route, which is moe_route_ex(..., dtype, dtype,
+ * MOE_GATE_TOPK_SOFTMAX, ...).  The workspace size is the same for both
+ * router types (moe_stage_workspace_bytes with MOE_STAGE_ROUTE).
+ */
+moe_status moe_route_ex(const void* x, const void* w_r, const float* router_bias,
+                        int64_t T, int64_t H, int64_t E, int32_t top_k,
+                        moe_dtype dtype, moe_dtype router_dtype, moe_gating gating,
+                        int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * Expert capacity (CANN MoE operator article, section 4.3, capacity_factor;
+ * fused article, "MoE computation flow": dispatch into [num_experts,
+ * expert_capacity] blocks): *capacity (host) = ceil(F * T * top_k / E) for
+ * the factor F = factor_num / factor_den, computed exactly in integers (the
+ * article's 1.2 is 6/5).  factor_num <= 0 gives 0 (no limit).  Returns
+ * MOE_ERR_INVALID_ARG for a NULL capacity, T < 0, top_k < 1, E < 1 or
+ * factor_den <= 0, and MOE_ERR_UNSUPPORTED when factor_num or factor_den
+ * exceeds 2^20, T exceeds 2^31, E exceeds 2^20 or the result exceeds
+ * INT32_MAX.  Host only; enqueues nothing.
+ */
+moe_status moe_expert_capacity(int64_t T, int32_t top_k, int64_t E, int64_t factor_num,
+                               int64_t factor_den, int32_t* capacity);
+
+/*
  * Dispatch (fused article, GatherTokensByExpert): group the R = T*top_k
  * (token, slot) pairs by expert, dropless, in ascending token order within
  * each expert (then ascending slot).
@@ -135,11 +180,29 @@ moe_status moe_permute(const void* x, const int32_t* topk_ids,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Capacity-limited dispatch (same articles as moe_expert_capacity): as
+ * moe_permute, but each expert keeps only its first `capacity` pairs in the
+ * dispatch order (ascending token, then slot); the other pairs are dropped:
+ *   inv_pos[t*top_k+j] = -1 for a dropped pair;
+ *   expert_offsets[e+1] - expert_offsets[e] = min(pairs of e, capacity), so
+ *     expert_offsets[E] (the kept rows) may be less than T*top_k;
+ *   sorted_token and xp are written for the kept rows only.
+ * capacity <= 0 means no limit (exactly moe_permute).  Same workspace as
+ * moe_permute.
+ */
+moe_status moe_permute_ex(const void* x, const int32_t* topk_ids,
+                          int64_t T, int64_t H, int64_t E, int32_t top_k,
+                          moe_dtype dtype, int32_t capacity, int32_t* expert_offsets,
+                          int32_t* sorted_token, int32_t* inv_pos, void* xp,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Experts (fused article, expert kernel step 3: Mmad -> GELU -> Mmad):
  * for each expert e with rows [expert_offsets[e], expert_offsets[e+1]),
  *   yp[rows] = GELU(xp[rows] . w1[e]) . w2[e]
  *   xp[R,H], w1[E,H,F], w2[E,F,H], yp[R,H] in dtype; expert_offsets[E+1]
- *   int32, non-decreasing, expert_offsets[0] = 0, expert_offsets[E] = R.
+ *   int32, non-decreasing, expert_offsets[0] = 0, expert_offsets[E] <= R
+ *   (rows from expert_offsets[E] on are neither read nor written).
  *   GELU is the tanh form 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
  *   Experts with no rows are skipped (their weights are not read).
  *   ws holds h[R,F] (dtype).
@@ -154,6 +217,7 @@ moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets,
  * token's expert outputs,
  *   y[t,:] = sum_{j<top_k} topk_w[t,j] * yp[inv_pos[t*top_k+j],:]
  * summed in fp32 in slot order, then stored in dtype (round to nearest even).
+ * A slot with inv_pos < 0 (dropped by moe_permute_ex) adds nothing.
  *   yp[T*top_k,H], y[T,H] in dtype; inv_pos int32; topk_w fp32.
  */
 moe_status moe_combine(const void* yp, const int32_t* inv_pos,
@@ -173,6 +237,20 @@ moe_status moe_forward(const void* x, const void* w_r, const float* router_bias,
                        int64_t E, int32_t top_k, int64_t F, moe_dtype dtype,
                        void* y, int32_t* topk_ids_out, float* topk_w_out,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole layer forward with the variants: router_dtype and gating as in
+ * moe_route_ex, capacity as in moe_permute_ex (<= 0: dropless).  A token
+ * whose slots are all dropped gets y[t,:] = 0.  moe_forward is
+ * moe_forward_ex(..., dtype, dtype, MOE_GATE_TOPK_SOFTMAX, 0, ...); the
+ * workspace is moe_workspace_bytes() for the same shape.
+ */
+moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bias,
+                          const void* w1, const void* w2, int64_t T, int64_t H,
+                          int64_t E, int32_t top_k, int64_t F, moe_dtype dtype,
+                          moe_dtype router_dtype, moe_gating gating, int32_t capacity,
+                          void* y, int32_t* topk_ids_out, float* topk_w_out,
+                          void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

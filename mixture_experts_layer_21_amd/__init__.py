@@ -29,8 +29,10 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_LAUNCH = 0, 1, 2, 3
 MOE_F32, MOE_BF16 = 0, 1
 MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_EXPERT_FFN, MOE_STAGE_COMBINE, MOE_STAGE_FORWARD = \
     0, 1, 2, 3, 4
+MOE_GATE_TOPK_SOFTMAX, MOE_GATE_SOFTMAX_TOPK = 0, 1
 EXPORTS = ("moe_status_string", "moe_workspace_bytes", "moe_stage_workspace_bytes", "moe_route",
-           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward")
+           "moe_route_ex", "moe_expert_capacity", "moe_permute", "moe_permute_ex",
+           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex")
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _lib.moe_status_string.restype = ctypes.c_char_p
@@ -42,9 +44,17 @@ _lib.moe_stage_workspace_bytes.argtypes = [_i32, _i64, _i64, _i64, _i32, _i64, _
                                            ctypes.POINTER(_sz)]
 _lib.moe_route.restype = _i32
 _lib.moe_route.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_route_ex.restype = _i32
+_lib.moe_route_ex.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
+                              _vp, _sz, _vp]
+_lib.moe_expert_capacity.restype = _i32
+_lib.moe_expert_capacity.argtypes = [_i64, _i32, _i64, _i64, _i64, ctypes.POINTER(_i32)]
 _lib.moe_permute.restype = _i32
 _lib.moe_permute.argtypes = [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                              _sz, _vp]
+_lib.moe_permute_ex.restype = _i32
+_lib.moe_permute_ex.argtypes = [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                _vp, _sz, _vp]
 _lib.moe_expert_ffn.restype = _i32
 _lib.moe_expert_ffn.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp,
                                 _sz, _vp]
@@ -53,6 +63,9 @@ _lib.moe_combine.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp]
 _lib.moe_forward.restype = _i32
 _lib.moe_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _vp,
                              _vp, _vp, _vp, _sz, _vp]
+_lib.moe_forward_ex.restype = _i32
+_lib.moe_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _i32,
+                                _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 
 
 class MoEError(RuntimeError):
@@ -150,6 +163,39 @@ def moe_route(x, w_r, router_bias, top_k: int, topk_ids=None, topk_w=None, ws=No
     return topk_ids, topk_w
 
 
+def moe_route_ex(x, w_r, router_bias, top_k: int, gating: int = MOE_GATE_TOPK_SOFTMAX,
+                 topk_ids=None, topk_w=None, ws=None):
+    """Routing + gating with the variants: w_r may be fp32 for bf16 x (an fp32
+    router), gating is MOE_GATE_TOPK_SOFTMAX or MOE_GATE_SOFTMAX_TOPK.
+    Returns (topk_ids[T,k] int32, topk_w[T,k] fp32)."""
+    _check(x, "x")
+    T, H = x.shape
+    E = w_r.shape[1]
+    _check(w_r, "w_r", None, (H, E))
+    if router_bias is not None:
+        _check(router_bias, "router_bias", torch.float32, (E,))
+    dev = x.device
+    topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev) if topk_ids is None else \
+        _check(topk_ids, "topk_ids", torch.int32, (T, top_k))
+    topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if topk_w is None else \
+        _check(topk_w, "topk_w", torch.float32, (T, top_k))
+    ws = _workspace(ws, moe_stage_workspace_bytes(MOE_STAGE_ROUTE, T, H, E, top_k, 8, x.dtype),
+                    dev)
+    _ok(_lib.moe_route_ex(_ptr(x), _ptr(w_r), _ptr(router_bias), T, H, E, top_k,
+                          _dtype_code(x.dtype), _dtype_code(w_r.dtype), gating, _ptr(topk_ids),
+                          _ptr(topk_w), _ptr(ws), ws.numel(), _stream(dev)), "moe_route_ex")
+    return topk_ids, topk_w
+
+
+def moe_expert_capacity(T: int, top_k: int, E: int, factor_num: int, factor_den: int) -> int:
+    """Rows each expert keeps: ceil(factor_num * T * top_k / (factor_den * E));
+    0 (no limit) for factor_num <= 0."""
+    c = _i32(0)
+    _ok(_lib.moe_expert_capacity(T, top_k, E, factor_num, factor_den, ctypes.byref(c)),
+        "moe_expert_capacity")
+    return c.value
+
+
 def moe_permute(x, topk_ids, E: int, expert_offsets=None, sorted_token=None, inv_pos=None,
                 xp=None, ws=None):
     """Dispatch.  Returns (expert_offsets[E+1], sorted_token[R], inv_pos[R], xp[R,H])."""
@@ -171,6 +217,32 @@ def moe_permute(x, topk_ids, E: int, expert_offsets=None, sorted_token=None, inv
     _ok(_lib.moe_permute(_ptr(x), _ptr(topk_ids), T, H, E, top_k, _dtype_code(x.dtype),
                          _ptr(expert_offsets), _ptr(sorted_token), _ptr(inv_pos), _ptr(xp),
                          _ptr(ws), ws.numel(), _stream(dev)), "moe_permute")
+    return expert_offsets, sorted_token, inv_pos, xp
+
+
+def moe_permute_ex(x, topk_ids, E: int, capacity: int, expert_offsets=None, sorted_token=None,
+                   inv_pos=None, xp=None, ws=None):
+    """Capacity-limited dispatch (capacity <= 0: dropless).  Returns
+    (expert_offsets[E+1], sorted_token[R], inv_pos[R], xp[R,H]); dropped pairs
+    have inv_pos -1 and only the first expert_offsets[E] rows are written."""
+    _check(x, "x")
+    T, H = x.shape
+    top_k = topk_ids.shape[1]
+    _check(topk_ids, "topk_ids", torch.int32, (T, top_k))
+    R, dev = T * top_k, x.device
+    expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev) if expert_offsets is None \
+        else _check(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    sorted_token = torch.empty(R, dtype=torch.int32, device=dev) if sorted_token is None else \
+        _check(sorted_token, "sorted_token", torch.int32, (R,))
+    inv_pos = torch.empty(R, dtype=torch.int32, device=dev) if inv_pos is None else \
+        _check(inv_pos, "inv_pos", torch.int32, (R,))
+    xp = torch.empty((R, H), dtype=x.dtype, device=dev) if xp is None else \
+        _check(xp, "xp", x.dtype, (R, H))
+    ws = _workspace(ws, moe_stage_workspace_bytes(MOE_STAGE_PERMUTE, T, H, E, top_k, 8, x.dtype),
+                    dev)
+    _ok(_lib.moe_permute_ex(_ptr(x), _ptr(topk_ids), T, H, E, top_k, _dtype_code(x.dtype),
+                            capacity, _ptr(expert_offsets), _ptr(sorted_token), _ptr(inv_pos),
+                            _ptr(xp), _ptr(ws), ws.numel(), _stream(dev)), "moe_permute_ex")
     return expert_offsets, sorted_token, inv_pos, xp
 
 
@@ -232,4 +304,32 @@ def moe_forward(x, w_r, router_bias, w1, w2, top_k: int, y=None, topk_ids_out=No
     _ok(_lib.moe_forward(_ptr(x), _ptr(w_r), _ptr(router_bias), _ptr(w1), _ptr(w2), T, H, E,
                          top_k, F, _dtype_code(x.dtype), _ptr(y), _ptr(topk_ids_out),
                          _ptr(topk_w_out), _ptr(ws), ws.numel(), _stream(dev)), "moe_forward")
+    return y
+
+
+def moe_forward_ex(x, w_r, router_bias, w1, w2, top_k: int, gating: int = MOE_GATE_TOPK_SOFTMAX,
+                   capacity: int = 0, y=None, topk_ids_out=None, topk_w_out=None, ws=None):
+    """The layer forward with the variants: w_r may be fp32 for bf16 x, gating
+    as in moe_route_ex, capacity as in moe_permute_ex.  Returns y[T,H]."""
+    _check(x, "x")
+    T, H = x.shape
+    E = w_r.shape[1]
+    F = w1.shape[2]
+    _check(w_r, "w_r", None, (H, E))
+    if router_bias is not None:
+        _check(router_bias, "router_bias", torch.float32, (E,))
+    _check(w1, "w1", x.dtype, (E, H, F))
+    _check(w2, "w2", x.dtype, (E, F, H))
+    dev = x.device
+    y = torch.empty((T, H), dtype=x.dtype, device=dev) if y is None else \
+        _check(y, "y", x.dtype, (T, H))
+    if topk_ids_out is not None:
+        _check(topk_ids_out, "topk_ids_out", torch.int32, (T, top_k))
+    if topk_w_out is not None:
+        _check(topk_w_out, "topk_w_out", torch.float32, (T, top_k))
+    ws = _workspace(ws, moe_workspace_bytes(T, H, E, top_k, F, x.dtype), dev)
+    _ok(_lib.moe_forward_ex(_ptr(x), _ptr(w_r), _ptr(router_bias), _ptr(w1), _ptr(w2), T, H, E,
+                            top_k, F, _dtype_code(x.dtype), _dtype_code(w_r.dtype), gating,
+                            capacity, _ptr(y), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
+                            ws.numel(), _stream(dev)), "moe_forward_ex")
     return y

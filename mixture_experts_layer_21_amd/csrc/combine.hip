@@ -5,7 +5,8 @@
 // in fp32 (no atomics, so the result is deterministic), then makes one
 // rounded store.  All k row loads of a thread are issued before any is used,
 // and the grid has one thread per output chunk, so the pass is bound by HBM
-// bandwidth rather than by load latency even for a handful of tokens.
+// bandwidth rather than by load latency even for a handful of tokens.  A slot
+// dropped by a capacity-limited dispatch (inv_pos < 0) adds nothing.
 #include "common.h"
 #include "launch.h"
 
@@ -29,8 +30,8 @@ __global__ __launch_bounds__(256) void combine_bf16(const u32x4* __restrict__ yp
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
       const int p = inv_pos[(size_t)t * k + j];
-      wj[j] = w[(size_t)t * k + j];
-      v[j] = yp[(size_t)p * chunks + c];
+      wj[j] = p >= 0 ? w[(size_t)t * k + j] : 0.f;
+      v[j] = p >= 0 ? yp[(size_t)p * chunks + c] : u32x4{0, 0, 0, 0};
     }
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(256) void combine_f32(const float4* __restrict__ yp
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
       const int p = inv_pos[(size_t)t * k + j];
-      wj[j] = w[(size_t)t * k + j];
-      v[j] = yp[(size_t)p * chunks + c];
+      wj[j] = p >= 0 ? w[(size_t)t * k + j] : 0.f;
+      v[j] = p >= 0 ? yp[(size_t)p * chunks + c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

@@ -206,8 +206,8 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
 // size ends at the last valid row of the tile (A) or of the weight slab (W):
 // rows past the tile and k rows past the piece's K range read as zero, so no
 // clamping or masks appear in the loop.  (Past-K columns of A read the next
-// row, but they meet zero W rows.)  Columns past N read neighbouring data that
-// is never stored.
+// row of the tile, or x's next row when the rows are gathered, but they meet
+// zero W rows.)  Columns past N read neighbouring data that is never stored.
 template <int BM, int BN, int WM, int WN, int NFM>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
                                           const int* __restrict__ gather, int a_rows,
@@ -228,7 +228,12 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   // Token rows: row0+m of A, or row gather[row0+m] of A when the token rows
   // are gathered straight from x (dispatch fused into the load).  Rows past
   // the tile get an offset past the buffer end and read as zero.
-  const uint32_t a_bytes = (uint32_t)a_rows * K * 2;
+  // (a K tail reads past the end of a row into the next one, where it meets
+  // zero W rows; contiguous A ends at the tile's last row so that the read
+  // past it returns zeros: rows beyond the tile, such as the unwritten rows of
+  // a capacity-limited dispatch, may hold any bits, NaN included)
+  const uint32_t a_bytes =
+      (uint32_t)(gather ? a_rows : min(a_rows, tile.row0 + tile.mrows)) * K * 2;
   // W rows at or past k_limit read as zero: a split piece covers only its
   // own K range
   const int k_limit = min(K, kt_end * BK);

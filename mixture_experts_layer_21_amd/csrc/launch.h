@@ -17,17 +17,24 @@ inline size_t align_up(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
 struct RoutePlan {
   int EP, TPW, EG, S, KL;
 };
-RoutePlan plan_route(int T, int H, int E, bool bf16);
+// wf32: W_r is fp32 while x is bf16 (an fp32 router for bf16 tokens)
+RoutePlan plan_route(int T, int H, int E, bool bf16, bool wf32);
+// enough for either router weight type
 size_t route_ws_bytes(int T, int H, int E, bool bf16);
+// softmax_all: gate weights are the top-k probabilities of the softmax over
+// all E logits (not renormalised); otherwise the softmax of the k winners
 hipError_t launch_route(const void* x, const void* w_r, const float* bias, int T, int H,
-                        int E, int k, bool bf16, int32_t* ids, float* w, void* ws,
-                        hipStream_t s);
+                        int E, int k, bool bf16, bool wf32, bool softmax_all, int32_t* ids,
+                        float* w, void* ws, hipStream_t s);
 
 size_t permute_ws_bytes(int R, int E);
-// xp == nullptr: indices only (the rows are gathered later by the GEMM)
+// xp == nullptr: indices only (the rows are gathered later by the GEMM).
+// capacity > 0: each expert keeps its first `capacity` pairs, the others get
+// inv_pos = -1; capacity <= 0: dropless.
 hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E, int k,
-                          size_t elem_bytes, int32_t* offsets, int32_t* sorted_token,
-                          int32_t* inv_pos, void* xp, void* ws, hipStream_t s);
+                          int capacity, size_t elem_bytes, int32_t* offsets,
+                          int32_t* sorted_token, int32_t* inv_pos, void* xp, void* ws,
+                          hipStream_t s);
 
 // Split-tile workspace of the bf16 grouped GEMM: fp32 partials of at most
 // kMaxSlots pieces (written by one GEMM launch, summed by the next kernel on

@@ -19,6 +19,15 @@ moe_status check_dtype(moe_dtype dt) {
   return (dt == MOE_F32 || dt == MOE_BF16) ? MOE_OK : MOE_ERR_UNSUPPORTED;
 }
 
+// Router weight type: the token type, or fp32 for bf16 tokens.
+moe_status check_router(moe_dtype dt, moe_dtype router_dtype, moe_gating gating) {
+  if (gating != MOE_GATE_TOPK_SOFTMAX && gating != MOE_GATE_SOFTMAX_TOPK)
+    return MOE_ERR_INVALID_ARG;
+  if (router_dtype == dt) return MOE_OK;
+  if (dt == MOE_BF16 && router_dtype == MOE_F32) return MOE_OK;
+  return MOE_ERR_UNSUPPORTED;
+}
+
 // Shape checks shared by the entry points.  T may be 0 (nothing to do).
 moe_status check_shape(int64_t T, int64_t H, int64_t E, int32_t top_k, int64_t F,
                        moe_dtype dt) {
@@ -144,32 +153,70 @@ moe_status moe_stage_workspace_bytes(moe_stage stage, int64_t T, int64_t H, int6
   }
 }
 
-moe_status moe_route(const void* x, const void* w_r, const float* router_bias, int64_t T,
-                     int64_t H, int64_t E, int32_t top_k, moe_dtype dtype, int32_t* topk_ids,
-                     float* topk_w, void* ws, size_t ws_bytes, void* stream) {
-  const moe_status st = check_shape(T, H, E, top_k, 8, dtype);
+moe_status moe_expert_capacity(int64_t T, int32_t top_k, int64_t E, int64_t factor_num,
+                               int64_t factor_den, int32_t* capacity) {
+  if (!capacity || T < 0 || top_k < 1 || E < 1 || factor_den <= 0) return MOE_ERR_INVALID_ARG;
+  if (factor_num <= 0) {
+    *capacity = 0;
+    return MOE_OK;
+  }
+  // ceil(num * T * k / (den * E)) in integers; the operands stay far below
+  // 2^63 for the sizes the other entry points accept
+  if (factor_num > ((int64_t)1 << 20) || factor_den > ((int64_t)1 << 20) ||
+      T > ((int64_t)1 << 31) || E > ((int64_t)1 << 20))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t num = factor_num * T * top_k, den = factor_den * E;
+  const int64_t c = (num + den - 1) / den;
+  if (c > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  *capacity = (int32_t)c;
+  return MOE_OK;
+}
+
+moe_status moe_route_ex(const void* x, const void* w_r, const float* router_bias, int64_t T,
+                        int64_t H, int64_t E, int32_t top_k, moe_dtype dtype,
+                        moe_dtype router_dtype, moe_gating gating, int32_t* topk_ids,
+                        float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(T, H, E, top_k, 8, dtype);
+  if (st != MOE_OK) return st;
+  st = check_router(dtype, router_dtype, gating);
   if (st != MOE_OK) return st;
   if (!x || !w_r || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe::route_ws_bytes((int)T, (int)H, (int)E, dtype == MOE_BF16))
     return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   return launch_status(moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k,
-                                         dtype == MOE_BF16, topk_ids, topk_w, ws,
+                                         dtype == MOE_BF16, router_dtype != dtype,
+                                         gating == MOE_GATE_SOFTMAX_TOPK, topk_ids, topk_w, ws,
                                          (hipStream_t)stream));
+}
+
+moe_status moe_route(const void* x, const void* w_r, const float* router_bias, int64_t T,
+                     int64_t H, int64_t E, int32_t top_k, moe_dtype dtype, int32_t* topk_ids,
+                     float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  return moe_route_ex(x, w_r, router_bias, T, H, E, top_k, dtype, dtype, MOE_GATE_TOPK_SOFTMAX,
+                      topk_ids, topk_w, ws, ws_bytes, stream);
+}
+
+moe_status moe_permute_ex(const void* x, const int32_t* topk_ids, int64_t T, int64_t H,
+                          int64_t E, int32_t top_k, moe_dtype dtype, int32_t capacity,
+                          int32_t* expert_offsets, int32_t* sorted_token, int32_t* inv_pos,
+                          void* xp, void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st = check_shape(T, H, E, top_k, 8, dtype);
+  if (st != MOE_OK) return st;
+  if (!x || !topk_ids || !expert_offsets || !sorted_token || !inv_pos || !xp || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe::permute_ws_bytes((int)(T * top_k), (int)E)) return MOE_ERR_INVALID_ARG;
+  return launch_status(moe::launch_permute(x, topk_ids, (int)T, (int)H, (int)E, top_k, capacity,
+                                           elem_bytes(dtype), expert_offsets, sorted_token,
+                                           inv_pos, xp, ws, (hipStream_t)stream));
 }
 
 moe_status moe_permute(const void* x, const int32_t* topk_ids, int64_t T, int64_t H, int64_t E,
                        int32_t top_k, moe_dtype dtype, int32_t* expert_offsets,
                        int32_t* sorted_token, int32_t* inv_pos, void* xp, void* ws,
                        size_t ws_bytes, void* stream) {
-  const moe_status st = check_shape(T, H, E, top_k, 8, dtype);
-  if (st != MOE_OK) return st;
-  if (!x || !topk_ids || !expert_offsets || !sorted_token || !inv_pos || !xp || !ws)
-    return MOE_ERR_INVALID_ARG;
-  if (ws_bytes < moe::permute_ws_bytes((int)(T * top_k), (int)E)) return MOE_ERR_INVALID_ARG;
-  return launch_status(moe::launch_permute(x, topk_ids, (int)T, (int)H, (int)E, top_k,
-                                           elem_bytes(dtype), expert_offsets, sorted_token,
-                                           inv_pos, xp, ws, (hipStream_t)stream));
+  return moe_permute_ex(x, topk_ids, T, H, E, top_k, dtype, 0, expert_offsets, sorted_token,
+                        inv_pos, xp, ws, ws_bytes, stream);
 }
 
 moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets, const void* w1,
@@ -193,11 +240,14 @@ moe_status moe_combine(const void* yp, const int32_t* inv_pos, const float* topk
                                            dtype == MOE_BF16, y, (hipStream_t)stream));
 }
 
-moe_status moe_forward(const void* x, const void* w_r, const float* router_bias, const void* w1,
-                       const void* w2, int64_t T, int64_t H, int64_t E, int32_t top_k,
-                       int64_t F, moe_dtype dtype, void* y, int32_t* topk_ids_out,
-                       float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
-  const moe_status st = check_shape(T, H, E, top_k, F, dtype);
+moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bias,
+                          const void* w1, const void* w2, int64_t T, int64_t H, int64_t E,
+                          int32_t top_k, int64_t F, moe_dtype dtype, moe_dtype router_dtype,
+                          moe_gating gating, int32_t capacity, void* y, int32_t* topk_ids_out,
+                          float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(T, H, E, top_k, F, dtype);
+  if (st != MOE_OK) return st;
+  st = check_router(dtype, router_dtype, gating);
   if (st != MOE_OK) return st;
   if (!x || !w_r || !w1 || !w2 || !y || !ws) return MOE_ERR_INVALID_ARG;
   const FwdLayout L = fwd_layout(T, H, E, top_k, F, dtype);
@@ -217,17 +267,29 @@ moe_status moe_forward(const void* x, const void* w_r, const float* router_bias,
   const int64_t R = T * top_k;
 
   hipError_t err = moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k, bf16,
+                                     router_dtype != dtype, gating == MOE_GATE_SOFTMAX_TOPK,
                                      ids, w, stage, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
   // bf16: the first expert GEMM gathers the token rows from x itself, so the
-  // dispatch only builds the indices; fp32 copies the rows into xp.
-  err = moe::launch_permute(x, ids, (int)T, (int)H, (int)E, top_k, elem_bytes(dtype), off,
-                            sorted, inv, bf16 ? nullptr : xp, stage, s);
+  // dispatch only builds the indices; fp32 copies the rows into xp.  With a
+  // capacity fewer than R rows are kept; the GEMMs take their row counts from
+  // the offsets, so R only bounds the grid.
+  err = moe::launch_permute(x, ids, (int)T, (int)H, (int)E, top_k, capacity, elem_bytes(dtype),
+                            off, sorted, inv, bf16 ? nullptr : xp, stage, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
   const moe_status fs = bf16 ? run_ffn(x, sorted, T, off, w1, w2, R, H, E, F, dtype, yp, stage, s)
                              : run_ffn(xp, nullptr, R, off, w1, w2, R, H, E, F, dtype, yp, stage, s);
   if (fs != MOE_OK) return fs;
   return launch_status(moe::launch_combine(yp, inv, w, (int)T, (int)H, top_k, bf16, y, s));
+}
+
+moe_status moe_forward(const void* x, const void* w_r, const float* router_bias, const void* w1,
+                       const void* w2, int64_t T, int64_t H, int64_t E, int32_t top_k,
+                       int64_t F, moe_dtype dtype, void* y, int32_t* topk_ids_out,
+                       float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  return moe_forward_ex(x, w_r, router_bias, w1, w2, T, H, E, top_k, F, dtype, dtype,
+                        MOE_GATE_TOPK_SOFTMAX, 0, y, topk_ids_out, topk_w_out, ws, ws_bytes,
+                        stream);
 }
 
 }  // extern "C"

@@ -1,18 +1,23 @@
 // Dispatch kernels (fused MoE article, GatherTokensByExpert): group the
-// R = T*k (token, slot) pairs by expert, dropless, keeping the article's
-// order inside each expert (ascending token, then slot).  The article scans
-// all pairs once per expert (O(E*R)); here it is a counting sort, O(R):
+// R = T*k (token, slot) pairs by expert, keeping the article's order inside
+// each expert (ascending token, then slot).  The article scans all pairs once
+// per expert (O(E*R)); here it is a counting sort, O(R).  With a capacity
+// (the article's [num_experts, expert_capacity] blocks; CANN MoE article,
+// section 4.3) each expert keeps only its first `cap` pairs in that order.
 //
 //   perm_count   per chunk of CH pairs: expert histogram in LDS -> counts[b][e]
-//   perm_scan    one workgroup: per-expert exclusive scan over chunks
-//                (chunk bases) and over experts (offsets); each expert's
-//                chunks are split among P threads that scan their segments in
-//                parallel, then the segment sums are scanned
+//   perm_scan    one workgroup: per-expert exclusive scan over chunks (each
+//                chunk's rank base inside its expert) and over experts of
+//                min(count, cap) (offsets); each expert's chunks are split
+//                among P threads that scan their segments in parallel, then
+//                the segment sums are scanned
 //   perm_place   per chunk (one pair per thread): stable rank of each pair
-//                among the chunk's pairs of the same expert (wave ballots +
-//                per-wave counts in LDS) -> sorted_token[pos] = t,
-//                inv_pos[t*k+j] = pos
-//   perm_gather  xp[p,:] = x[sorted_token[p],:], 16-byte copies, one wave per row
+//                among its expert's pairs (chunk base + wave ballots +
+//                per-wave counts in LDS); rank < cap -> sorted_token[pos] = t,
+//                inv_pos[t*k+j] = pos with pos = offsets[e] + rank; otherwise
+//                the pair is dropped, inv_pos = -1
+//   perm_gather  xp[p,:] = x[sorted_token[p],:] for p < offsets[E], 16-byte
+//                copies, one wave per row
 //
 // All counts are integers: placement is exact and deterministic.
 #include "common.h"
@@ -36,7 +41,7 @@ __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ id
 }
 
 __global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ counts,
-                                                  int nchunks, int E, int R,
+                                                  int nchunks, int E, int cap,
                                                   int32_t* __restrict__ base,
                                                   int32_t* __restrict__ offsets) {
   __shared__ int seg[1024];     // [P][E]: segment sums, then segment bases
@@ -63,23 +68,24 @@ __global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ co
     tot[t] = run;
   }
   __syncthreads();
-  // exclusive scan of the expert totals (one thread per expert, E <= 1024)
+  // exclusive scan of the kept expert totals min(total, cap) (one thread per
+  // expert, E <= 1024)
   const int lane = t % kWave, wave = t / kWave;
-  const int v = t < E ? tot[t] : 0;
+  const int v = t < E ? min(tot[t], cap) : 0;
   const int incl = wave_incl_scan(v);
   if (lane == kWave - 1) wsum[wave] = incl;
   __syncthreads();
   int wbase = 0;
   for (int w = 0; w < wave; ++w) wbase += wsum[w];
-  __syncthreads();
-  if (t < E) {
-    tot[t] = wbase + incl - v;
-    offsets[t] = wbase + incl - v;
+  if (t < E) offsets[t] = wbase + incl - v;
+  if (t == 0) {
+    int all = 0;
+    for (int w = 0; w < 16; ++w) all += wsum[w];
+    offsets[E] = all;
   }
-  if (t == 0) offsets[E] = R;
-  __syncthreads();
+  // chunk bases: the rank, inside its expert, of each chunk's first pair
   if (active) {
-    int run = tot[e] + seg[p * E + e];
+    int run = seg[p * E + e];
     for (int b = b0; b < b1; ++b) {
       const int c = counts[(size_t)b * E + e];
       base[(size_t)b * E + e] = run;
@@ -89,12 +95,13 @@ __global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ co
 }
 
 __global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ ids, int R,
-                                                  int E, int k,
+                                                  int E, int k, int cap,
                                                   const int32_t* __restrict__ base,
+                                                  const int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ sorted_token,
                                                   int32_t* __restrict__ inv_pos) {
   extern __shared__ int sm[];
-  int* running = sm;          // [E]: next free row of each expert
+  int* running = sm;          // [E]: rank of the next pair of each expert
   int* wcnt = sm + E;         // [4][E]: pairs of each expert in each wave this round
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int b = blockIdx.x;
@@ -123,10 +130,15 @@ __global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ id
     if (valid && rank == 0) wcnt[wave * E + my_e] = __popcll(peers);
     __syncthreads();
     if (valid) {
-      int pos = running[my_e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w * E + my_e];
-      sorted_token[pos] = i / k;
-      inv_pos[i] = pos;
+      int r_e = running[my_e] + rank;
+      for (int w = 0; w < wave; ++w) r_e += wcnt[w * E + my_e];
+      if (r_e < cap) {
+        const int pos = offsets[my_e] + r_e;
+        sorted_token[pos] = i / k;
+        inv_pos[i] = pos;
+      } else {
+        inv_pos[i] = -1;
+      }
     }
     __syncthreads();
     for (int e = tid; e < E; e += 256) {
@@ -144,10 +156,11 @@ __global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ id
 
 __global__ __launch_bounds__(256) void perm_gather(const u32x4* __restrict__ x,
                                                    const int32_t* __restrict__ sorted_token,
-                                                   u32x4* __restrict__ xp, int R,
-                                                   int row_chunks) {
+                                                   const int32_t* __restrict__ offsets, int E,
+                                                   u32x4* __restrict__ xp, int row_chunks) {
   const int lane = threadIdx.x % kWave;
   const int nwaves = gridDim.x * 4;
+  const int R = offsets[E];                      // kept rows
   for (int p = blockIdx.x * 4 + threadIdx.x / kWave; p < R; p += nwaves) {
     const u32x4* src = x + (size_t)sorted_token[p] * row_chunks;
     u32x4* dst = xp + (size_t)p * row_chunks;
@@ -163,24 +176,26 @@ size_t permute_ws_bytes(int R, int E) {
 }
 
 hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E, int k,
-                          size_t elem_bytes, int32_t* offsets, int32_t* sorted_token,
-                          int32_t* inv_pos, void* xp, void* ws, hipStream_t s) {
+                          int capacity, size_t elem_bytes, int32_t* offsets,
+                          int32_t* sorted_token, int32_t* inv_pos, void* xp, void* ws,
+                          hipStream_t s) {
   const int R = T * k;
+  const int cap = capacity > 0 ? capacity : R;   // R: nothing is dropped
   const int nchunks = (R + CH - 1) / CH;
   int32_t* counts = (int32_t*)ws;
   int32_t* base = (int32_t*)((char*)ws + align_up((size_t)nchunks * E * sizeof(int32_t)));
   if (nchunks > 0)
     hipLaunchKernelGGL(perm_count, dim3(nchunks), dim3(256), E * sizeof(int), s, ids, R, E, counts);
   // runs even for R == 0 so that the offsets are written (all zero)
-  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, counts, nchunks, E, R, base, offsets);
+  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, counts, nchunks, E, cap, base, offsets);
   if (nchunks == 0) return hipGetLastError();
   hipLaunchKernelGGL(perm_place, dim3(nchunks), dim3(256), 5 * E * sizeof(int), s, ids, R, E, k,
-                     base, sorted_token, inv_pos);
+                     cap, base, offsets, sorted_token, inv_pos);
   if (xp == nullptr) return hipGetLastError();
   const int row_chunks = (int)((size_t)H * elem_bytes / 16);
   const int blocks = std::min(8192, (R + 3) / 4);
   hipLaunchKernelGGL(perm_gather, dim3(blocks), dim3(256), 0, s, (const u32x4*)x, sorted_token,
-                     (u32x4*)xp, R, row_chunks);
+                     offsets, E, (u32x4*)xp, row_chunks);
   return hipGetLastError();
 }
 

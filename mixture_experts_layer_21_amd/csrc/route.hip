@@ -12,12 +12,20 @@
 //                     expert per lane and read); the token operand comes
 //                     straight from global memory.  Partial logits go to
 //                     part[S][T][EP] (fp32, EP = E rounded up to 16).
+//                     With an fp32 W_r (an fp32 router for bf16 tokens, the
+//                     CANN article's section 4.2) each weight is staged as
+//                     three bf16 planes, w = hi + mid + lo (hi and mid
+//                     truncations, lo the rounded rest), and every k-step
+//                     runs three MFMAs: each product x*part is exact in fp32,
+//                     so the sum is an fp32-accumulated x . W_r.
 // fp32 path: the logits come from the fp32 grouped GEMM in dense mode.
 //
 //   route_select      one wave per token: sums the S partial logits in fixed
 //                     order, adds the bias, takes k rounds of a 64-lane
-//                     (value desc, index asc) arg-max, then the softmax of the
-//                     k winners; writes ids[T,k] and w[T,k].
+//                     (value desc, index asc) arg-max, then the gate weights:
+//                     the softmax of the k winners, or (softmax-then-top-k
+//                     gating, CANN article section 2.1) their probabilities
+//                     under the softmax over all E; writes ids[T,k], w[T,k].
 #include "common.h"
 #include "launch.h"
 
@@ -34,12 +42,28 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <int TPW>
+// fp32 -> (hi, mid, lo) bf16 bits with hi + mid + lo == w up to the rounding
+// of lo (hi, mid: truncations; each remainder is exact in fp32).
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t u = __float_as_uint(w);
+  hi = u >> 16;
+  const float r1 = w - __uint_as_float(u & 0xFFFF0000u);
+  const uint32_t u1 = __float_as_uint(r1);
+  mid = u1 >> 16;
+  const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
+  const uint32_t u2 = __float_as_uint(r2);
+  lo = (u2 + 0x7FFFu + ((u2 >> 16) & 1u)) >> 16;
+}
+
+template <int TPW, bool WF32>
 __global__ __launch_bounds__(256) void route_logits_bf16(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_r,
+    const uint16_t* __restrict__ x, const void* __restrict__ w_r_any,
     float* __restrict__ part, int T, int H, int E, int EP, int EG, int S, int KL) {
-  extern __shared__ __attribute__((aligned(16))) char wb[];   // [KL][16 TPW] bf16
+  // [NP][KL][16 TPW] bf16: one plane, or the hi/mid/lo planes of an fp32 W_r
+  extern __shared__ __attribute__((aligned(16))) char wb[];
+  constexpr int NP = WF32 ? 3 : 1;
   constexpr int ROW = TPW * 16 * 2;                            // bytes per k row
+  const size_t plane = (size_t)KL * ROW;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int eg = blockIdx.x % EG;
@@ -57,19 +81,44 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
     for (int q = threadIdx.x; q < KL * CH; q += blockDim.x) {
       const int r = q / CH, c = q % CH;
       const int k = k_begin + r, e = e0 + c * 8;
-      u32x4 v = {0, 0, 0, 0};
-      if (k < k_end) {
-        if (vec) {
-          if (e < E) v = *(const u32x4*)(w_r + (size_t)k * E + e);
-        } else {
-          uint16_t h[8];
+      if constexpr (!WF32) {
+        const uint16_t* w_r = (const uint16_t*)w_r_any;
+        u32x4 v = {0, 0, 0, 0};
+        if (k < k_end) {
+          if (vec) {
+            if (e < E) v = *(const u32x4*)(w_r + (size_t)k * E + e);
+          } else {
+            uint16_t h[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) h[u] = (e + u < E) ? w_r[(size_t)k * E + e + u] : (uint16_t)0;
-          v = u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
-                    h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+            for (int u = 0; u < 8; ++u) h[u] = (e + u < E) ? w_r[(size_t)k * E + e + u] : (uint16_t)0;
+            v = u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                      h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+          }
         }
+        *(u32x4*)(wb + r * ROW + c * 16) = v;
+      } else {
+        const float* w_r = (const float*)w_r_any;
+        float f[8];
+        if (k < k_end && vec && e < E) {
+          const float4 a = *(const float4*)(w_r + (size_t)k * E + e);
+          const float4 b = *(const float4*)(w_r + (size_t)k * E + e + 4);
+          f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+          f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            f[u] = (k < k_end && e + u < E) ? w_r[(size_t)k * E + e + u] : 0.f;
+        }
+        uint32_t hi[8], mid[8], lo[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) split3(f[u], hi[u], mid[u], lo[u]);
+        *(u32x4*)(wb + r * ROW + c * 16) =
+            u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+        *(u32x4*)(wb + plane + r * ROW + c * 16) =
+            u32x4{mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16), mid[4] | (mid[5] << 16), mid[6] | (mid[7] << 16)};
+        *(u32x4*)(wb + 2 * plane + r * ROW + c * 16) =
+            u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
       }
-      *(u32x4*)(wb + r * ROW + c * 16) = v;
     }
   }
   __syncthreads();
@@ -93,13 +142,16 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
     const u32x4 a = ok ? *(const u32x4*)(xr + k0) : u32x4{0, 0, 0, 0};
     const char* base = wb + (k0 - k_begin) * ROW + rd_off;
 #pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const u32x2 lo = lds_read_tr(base + j * 32);
-      const u32x2 hi = lds_read_tr(base + 4 * ROW + j * 32);
-      const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b),
-                                                       acc[j], 0, 0, 0);
+    for (int pl = 0; pl < NP; ++pl) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        const u32x2 lo = lds_read_tr(base + pl * plane + j * 32);
+        const u32x2 hi = lds_read_tr(base + pl * plane + 4 * ROW + j * 32);
+        const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                         __builtin_bit_cast(bf16x8, b),
+                                                         acc[j], 0, 0, 0);
+      }
     }
   }
   // D: lane holds expert column lane%16 of tile j, token rows 4*(lane/16)+v
@@ -120,7 +172,7 @@ template <int NPL>
 __global__ __launch_bounds__(256) void route_select(
     const float* __restrict__ part, const float* __restrict__ bias,
     int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int EP,
-    int S, int k) {
+    int S, int k, int softmax_all) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
@@ -188,12 +240,23 @@ __global__ __launch_bounds__(256) void route_select(
       sel_e[j] = be;
     }
   }
-  // softmax over the k winners (slot 0 holds the maximum)
+  // softmax over the k winners, or over all E experts (slot 0 holds the
+  // maximum either way)
   const float m = sel_v[0];
   float sum = 0.f;
+  if (softmax_all) {
+    float part_sum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if (j < k) sum += expf(sel_v[j] - m);
+    for (int i = 0; i < NPL; ++i)
+      if (lane + i * kWave < E) part_sum += expf(v[i] - m);
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) part_sum += __shfl_xor(part_sum, d, kWave);
+    sum = part_sum;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k) sum += expf(sel_v[j] - m);
+  }
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (j < k && lane == j) {
@@ -205,14 +268,14 @@ __global__ __launch_bounds__(256) void route_select(
 
 template <int NPL>
 void launch_select(const float* part, const float* bias, int32_t* ids, float* w,
-                   int T, int E, int EP, int S, int k, hipStream_t s) {
+                   int T, int E, int EP, int S, int k, int softmax_all, hipStream_t s) {
   hipLaunchKernelGGL((route_select<NPL>), dim3((T + 3) / 4), dim3(256), 0, s,
-                     part, bias, ids, w, T, E, EP, S, k);
+                     part, bias, ids, w, T, E, EP, S, k, softmax_all);
 }
 
 }  // namespace
 
-RoutePlan plan_route(int T, int H, int E, bool bf16) {
+RoutePlan plan_route(int T, int H, int E, bool bf16, bool wf32) {
   RoutePlan p;
   p.EP = (E + 15) / 16 * 16;
   const int NET = p.EP / 16;
@@ -225,41 +288,50 @@ RoutePlan plan_route(int T, int H, int E, bool bf16) {
   p.TPW = tpw;
   p.EG = (NET + tpw - 1) / tpw;
   // about 2048 waves in all, and a staged W_r block of at most 64 KB
-  // (KL * 32 TPW bytes)
+  // (KL * 32 TPW bytes per bf16 plane; three planes for an fp32 W_r)
   const int TT = (T + 15) / 16;
   const long base_items = std::max<long>(1, (long)TT * p.EG);
   int S = (int)std::min<long>(64, std::max<long>(1, (2048 + base_items - 1) / base_items));
   int KL = (H + S - 1) / S;
   KL = (KL + 31) / 32 * 32;
-  KL = std::min(KL, 2048 / tpw);
+  KL = std::min(KL, (wf32 ? 512 : 2048) / tpw);
   p.KL = KL;
   p.S = (H + KL - 1) / KL;
   return p;
 }
 
 size_t route_ws_bytes(int T, int H, int E, bool bf16) {
-  const RoutePlan p = plan_route(T, H, E, bf16);
-  return align_up((size_t)p.S * T * p.EP * sizeof(float));
+  // enough for either router weight type
+  const RoutePlan a = plan_route(T, H, E, bf16, false);
+  const RoutePlan b = plan_route(T, H, E, bf16, bf16);
+  return align_up((size_t)std::max(a.S, b.S) * T * a.EP * sizeof(float));
 }
 
 hipError_t launch_route(const void* x, const void* w_r, const float* bias,
-                        int T, int H, int E, int k, bool bf16, int32_t* ids,
-                        float* w, void* ws, hipStream_t s) {
-  const RoutePlan p = plan_route(T, H, E, bf16);
+                        int T, int H, int E, int k, bool bf16, bool wf32, bool softmax_all,
+                        int32_t* ids, float* w, void* ws, hipStream_t s) {
+  const RoutePlan p = plan_route(T, H, E, bf16, wf32);
   float* part = (float*)ws;
   if (bf16) {
     const int TG = ((T + 15) / 16 + 3) / 4;
     dim3 g((unsigned)(TG * p.EG * p.S)), b(256);
-    const size_t lds = (size_t)p.KL * p.TPW * 32;
+    const size_t lds = (size_t)p.KL * p.TPW * 32 * (wf32 ? 3 : 1);
     const uint16_t* xb = (const uint16_t*)x;
-    const uint16_t* wb = (const uint16_t*)w_r;
+#define MOE_ROUTE_LOGITS(TPW_)                                                              \
+    if (wf32)                                                                                \
+      hipLaunchKernelGGL((route_logits_bf16<TPW_, true>), g, b, lds, s, xb, w_r, part, T, H,  \
+                         E, p.EP, p.EG, p.S, p.KL);                                          \
+    else                                                                                     \
+      hipLaunchKernelGGL((route_logits_bf16<TPW_, false>), g, b, lds, s, xb, w_r, part, T, H, \
+                         E, p.EP, p.EG, p.S, p.KL)
     switch (p.TPW) {
-      case 1: hipLaunchKernelGGL(route_logits_bf16<1>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
-      case 2: hipLaunchKernelGGL(route_logits_bf16<2>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
-      case 4: hipLaunchKernelGGL(route_logits_bf16<4>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
-      case 8: hipLaunchKernelGGL(route_logits_bf16<8>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
-      default: hipLaunchKernelGGL(route_logits_bf16<16>, g, b, lds, s, xb, wb, part, T, H, E, p.EP, p.EG, p.S, p.KL); break;
+      case 1: MOE_ROUTE_LOGITS(1); break;
+      case 2: MOE_ROUTE_LOGITS(2); break;
+      case 4: MOE_ROUTE_LOGITS(4); break;
+      case 8: MOE_ROUTE_LOGITS(8); break;
+      default: MOE_ROUTE_LOGITS(16); break;
     }
+#undef MOE_ROUTE_LOGITS
   } else {
     hipError_t err = launch_gemm_f32((const float*)x, (const float*)w_r, part, nullptr, 1, T, H, E,
                                      p.EP, false, s);
@@ -268,11 +340,12 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int npl = (E + kWave - 1) / kWave;
-  if (npl <= 1) launch_select<1>(part, bias, ids, w, T, E, p.EP, p.S, k, s);
-  else if (npl <= 2) launch_select<2>(part, bias, ids, w, T, E, p.EP, p.S, k, s);
-  else if (npl <= 4) launch_select<4>(part, bias, ids, w, T, E, p.EP, p.S, k, s);
-  else if (npl <= 8) launch_select<8>(part, bias, ids, w, T, E, p.EP, p.S, k, s);
-  else launch_select<16>(part, bias, ids, w, T, E, p.EP, p.S, k, s);
+  const int sa = softmax_all ? 1 : 0;
+  if (npl <= 1) launch_select<1>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
+  else if (npl <= 2) launch_select<2>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
+  else if (npl <= 4) launch_select<4>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
+  else if (npl <= 8) launch_select<8>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
+  else launch_select<16>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
   return hipGetLastError();
 }
 

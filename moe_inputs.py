@@ -149,6 +149,14 @@ def make_w_r(cfg: MoEConfig, device="cpu") -> torch.Tensor:
     return _fill((cfg.H, cfg.E), _STREAM_WR, 0, 1.0 / math.sqrt(cfg.H), cfg, device)
 
 
+def make_w_r_f32(cfg: MoEConfig, device="cpu") -> torch.Tensor:
+    """W_r from the same stream as make_w_r, kept in fp32 (an fp32 router for
+    a layer whose other tensors are bf16)."""
+    n = cfg.H * cfg.E
+    return normal_fp32(n, stream_keys(cfg.seed, _STREAM_WR, 0), 1.0 / math.sqrt(cfg.H),
+                       device).view(cfg.H, cfg.E)
+
+
 def make_router_bias(cfg: MoEConfig, device="cpu"):
     """fp32 [E] router bias, or None when the workload has no bias."""
     if cfg.bias0 == 0.0:

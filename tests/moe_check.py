@@ -50,7 +50,8 @@ def valid_topk(l_row: np.ndarray, ids_row: np.ndarray) -> bool:
     return True
 
 
-def check_routing(ids_gpu: np.ndarray, w_gpu: np.ndarray, logits_ref: np.ndarray, k: int):
+def check_routing(ids_gpu: np.ndarray, w_gpu: np.ndarray, logits_ref: np.ndarray, k: int,
+                  gating: str = "topk_softmax"):
     """Assert the routing acceptance rule; return (n_boundary, n_within)."""
     ids_ref = oracle.topk_ids(logits_ref, k)
     ids_gpu = np.asarray(ids_gpu, np.int64)
@@ -64,7 +65,7 @@ def check_routing(ids_gpu: np.ndarray, w_gpu: np.ndarray, logits_ref: np.ndarray
             n_within += 1
         else:
             n_boundary += 1
-    w_ref = oracle.gate_weights(logits_ref, ids_gpu)
+    w_ref = oracle.gate_weights(logits_ref, ids_gpu, gating)
     err = np.abs(np.asarray(w_gpu, np.float64) - w_ref).max()
     assert err <= W_ATOL, f"gate weights differ by {err}"
     return n_boundary, n_within

@@ -180,3 +180,84 @@ def test_stage_workspaces_fit_in_the_forward_workspace(shape):
 def test_stage_workspace_rejects_unknown_stage():
     assert stage_bytes(9, 64, 128, 8, 2, 256, F32)[0] == INV
     assert L.moe_stage_workspace_bytes(0, 64, 128, 8, 2, 256, F32, None) == INV
+
+
+# --- variants: gating, fp32 router, capacity -------------------------------------
+
+GT, GS = moe.MOE_GATE_TOPK_SOFTMAX, moe.MOE_GATE_SOFTMAX_TOPK
+
+
+def _route_ex(x=P, wr=P, b=N, T=64, H=128, E=8, k=2, dt=BF16, rdt=BF16, g=GT, ids=P, w=P, ws=P,
+              nb=1 << 30):
+    return L.moe_route_ex(x, wr, b, T, H, E, k, dt, rdt, g, ids, w, ws, nb, N)
+
+
+def _permute_ex(x=P, ids=P, T=64, H=128, E=8, k=2, dt=BF16, cap=10, off=P, st=P, inv=P, xp=P,
+                ws=P, nb=1 << 30):
+    return L.moe_permute_ex(x, ids, T, H, E, k, dt, cap, off, st, inv, xp, ws, nb, N)
+
+
+def _forward_ex(x=P, wr=P, b=N, w1=P, w2=P, T=64, H=128, E=8, k=2, F=256, dt=BF16, rdt=BF16,
+                g=GT, cap=0, y=P, ids=N, w=N, ws=P, nb=1 << 30):
+    return L.moe_forward_ex(x, wr, b, w1, w2, T, H, E, k, F, dt, rdt, g, cap, y, ids, w, ws, nb, N)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(g=2), INV), (dict(g=-1), INV), (dict(dt=F32, rdt=BF16), UNS), (dict(rdt=7), UNS),
+    (dict(x=N), INV), (dict(wr=N), INV), (dict(ids=N), INV), (dict(w=N), INV), (dict(ws=N), INV),
+    (dict(nb=16), INV), (dict(k=9), INV), (dict(dt=3, rdt=3), UNS), (dict(H=100), UNS),
+])
+def test_route_ex_rejects(kw, expect):
+    assert _route_ex(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=N), INV), (dict(ids=N), INV), (dict(off=N), INV), (dict(st=N), INV),
+    (dict(inv=N), INV), (dict(xp=N), INV), (dict(ws=N), INV), (dict(nb=0), INV),
+    (dict(k=0), INV), (dict(dt=2), UNS), (dict(H=12), UNS),
+])
+def test_permute_ex_rejects(kw, expect):
+    assert _permute_ex(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(g=5), INV), (dict(dt=F32, rdt=BF16), UNS), (dict(x=N), INV), (dict(wr=N), INV),
+    (dict(w1=N), INV), (dict(w2=N), INV), (dict(y=N), INV), (dict(ws=N), INV),
+    (dict(nb=1024), INV), (dict(k=9), INV), (dict(F=12), UNS),
+])
+def test_forward_ex_rejects(kw, expect):
+    assert _forward_ex(**kw) == expect
+
+
+def test_variants_accept_valid_router_pairs_on_empty_batch():
+    # T = 0 validates everything and enqueues nothing
+    for dt, rdt in ((BF16, BF16), (BF16, F32), (F32, F32)):
+        for g in (GT, GS):
+            assert _route_ex(T=0, dt=dt, rdt=rdt, g=g) == OK
+            assert _forward_ex(T=0, dt=dt, rdt=rdt, g=g, cap=3) == OK
+
+
+def _cap(T, k, E, num, den):
+    c = ctypes.c_int32(-7)
+    st = L.moe_expert_capacity(T, k, E, num, den, ctypes.byref(c))
+    return st, c.value
+
+
+@pytest.mark.parametrize("T,k,E,num,den", [
+    (2048, 2, 8, 6, 5), (4096, 8, 128, 6, 5), (64, 2, 8, 1, 1), (64, 8, 256, 6, 5),
+    (5, 2, 3, 3, 5), (7, 1, 7, 1, 2), (1, 1, 1024, 1, 1), (0, 2, 8, 6, 5), (100, 3, 7, 0, 1),
+])
+def test_expert_capacity_matches_oracle(T, k, E, num, den):
+    import oracle
+    st, c = _cap(T, k, E, num, den)
+    assert st == OK
+    assert c == oracle.expert_capacity(T, k, E, num / den if num > 0 else 0.0)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((64, 2, 8, 6, 0), INV), ((-1, 2, 8, 6, 5), INV), ((64, 0, 8, 6, 5), INV), ((64, 2, 0, 6, 5), INV),
+    ((64, 2, 8, 1 << 21, 5), UNS), ((64, 2, 8, 6, 1 << 21), UNS),
+])
+def test_expert_capacity_rejects(args, expect):
+    assert _cap(*args)[0] == expect
+    assert L.moe_expert_capacity(64, 2, 8, 6, 5, None) == INV

@@ -1,0 +1,221 @@
+"""Parity of the variant entry points (moe_route_ex, moe_permute_ex,
+moe_forward_ex) with the fp64 oracle: softmax-then-top-k gating, an fp32
+router for bf16 tokens, and capacity-limited dispatch.  Dispatch indices are
+compared bit for bit (dropped pairs included); routing and y follow the same
+acceptance rules as the dropless path."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from moe_check import TOL, assert_close_rel, check_routing, expert_getters, f64, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+import mixture_experts_layer_21_amd as moe  # fails loudly if the library is missing
+
+C = mi.MoEConfig
+GS, GT = moe.MOE_GATE_SOFTMAX_TOPK, moe.MOE_GATE_TOPK_SOFTMAX
+SMALL = {
+    "tiny_fp32": mi.CONFIGS["tiny_fp32"],
+    "ragged_bf16": C("ragged_bf16", T=75, H=200, E=5, k=2, F=136, dtype="bf16"),
+    "multitile_bf16": C("multitile_bf16", T=1000, H=256, E=3, k=2, F=392, dtype="bf16"),
+    "ragged_f32": C("ragged_f32", T=70, H=72, E=6, k=3, F=40, dtype="f32"),
+    "top1_bf16": C("top1_bf16", T=50, H=128, E=16, k=1, F=64, dtype="bf16"),
+    "one_token_bf16": C("one_token_bf16", T=1, H=128, E=8, k=2, F=256, dtype="bf16"),
+    "many_small_bf16": C("many_small_bf16", T=128, H=128, E=128, k=8, F=64, dtype="bf16"),
+    "wide_E_bf16": C("wide_E_bf16", T=20, H=64, E=1000, k=16, F=32, dtype="bf16"),
+    "skewed_small_bf16": C("skewed_small_bf16", T=256, H=128, E=8, k=2, F=256, dtype="bf16",
+                           bias0=3.0),
+    "longH_bf16": C("longH_bf16", T=40, H=4096, E=24, k=3, F=64, dtype="bf16"),
+}
+BF16_SMALL = [n for n, c in SMALL.items() if c.dtype == "bf16"]
+_cache = {}
+
+
+def layer(cfg):
+    if cfg.name not in _cache:
+        if len(_cache) > 3:
+            _cache.pop(next(iter(_cache)))
+            torch.cuda.empty_cache()
+        print(f"\n[gen] {cfg.name}", flush=True)
+        L = mi.make_inputs(cfg, "cuda")
+        if cfg.dtype == "bf16":
+            L["w_r32"] = mi.make_w_r_f32(cfg, "cuda")
+        _cache[cfg.name] = L
+    return _cache[cfg.name]
+
+
+def logits_of(L, w_r):
+    return oracle.router_logits(f64(L["x"]), f64(w_r), f64(L["router_bias"]))
+
+
+def caps(cfg):
+    R = cfg.T * cfg.k
+    out = {0, 1, 2, oracle.expert_capacity(cfg.T, cfg.k, cfg.E, 0.6),
+           oracle.expert_capacity(cfg.T, cfg.k, cfg.E, 1.2), R}
+    return sorted(out)
+
+
+# --- routing variants ---------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_route_softmax_topk(name):
+    cfg = SMALL[name]
+    L = layer(cfg)
+    ids, w = moe.moe_route_ex(L["x"], L["w_r"], L["router_bias"], cfg.k, gating=GS)
+    ids0, _ = moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k)
+    torch.cuda.synchronize()
+    # same logits, same selection: ids bit-identical to the default gating
+    assert torch.equal(ids, ids0)
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), logits_of(L, L["w_r"]), cfg.k,
+                  gating="softmax_topk")
+    s = w.cpu().numpy().sum(1)
+    assert np.all(s <= 1 + 1e-5)
+    if cfg.k == cfg.E:
+        assert np.all(np.abs(s - 1) < 1e-5)
+
+
+@pytest.mark.parametrize("name", BF16_SMALL)
+@pytest.mark.parametrize("gating", [GT, GS])
+def test_route_fp32_router(name, gating):
+    cfg = SMALL[name]
+    L = layer(cfg)
+    ids, w = moe.moe_route_ex(L["x"], L["w_r32"], L["router_bias"], cfg.k, gating=gating)
+    torch.cuda.synchronize()
+    nb, nw = check_routing(ids.cpu().numpy(), w.cpu().numpy(), logits_of(L, L["w_r32"]), cfg.k,
+                           gating="softmax_topk" if gating == GS else "topk_softmax")
+    print(f"[{name}] fp32 router near ties: boundary {nb}, within-set {nw}", flush=True)
+
+
+def test_fp32_router_is_not_the_bf16_router():
+    # the fp32 weights differ from their bf16 rounding; the fp32 path must
+    # follow the fp32 values (logits checked to 1e-5 relative via w)
+    cfg = SMALL["many_small_bf16"]
+    L = layer(cfg)
+    assert not torch.equal(L["w_r32"].to(torch.bfloat16).float(), L["w_r32"])
+    ids, w = moe.moe_route_ex(L["x"], L["w_r32"], None, cfg.k, gating=GS)
+    torch.cuda.synchronize()
+    l32 = logits_of(L, L["w_r32"])
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), l32, cfg.k, gating="softmax_topk")
+
+
+# --- capacity-limited dispatch ------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_permute_capacity(name):
+    cfg = SMALL[name]
+    L = layer(cfg)
+    ids, _ = moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k)
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    for cap in caps(cfg):
+        off, st, inv, xp = moe.moe_permute_ex(L["x"], ids, cfg.E, cap)
+        torch.cuda.synchronize()
+        o_off, o_st, _, o_inv = oracle.dispatch(ids_np, cfg.E, cap)
+        np.testing.assert_array_equal(off.cpu().numpy(), o_off, err_msg=f"cap {cap}")
+        Rk = int(o_off[-1])
+        np.testing.assert_array_equal(st.cpu().numpy()[:Rk], o_st, err_msg=f"cap {cap}")
+        np.testing.assert_array_equal(inv.cpu().numpy(), o_inv.ravel(), err_msg=f"cap {cap}")
+        assert torch.equal(xp[:Rk], L["x"][st[:Rk].long()])
+
+
+# --- the whole layer with the variants ----------------------------------------
+
+VARIANTS = {
+    "softmax_topk": dict(gating=GS, cap=None, f32r=False),
+    "capacity_1.2": dict(gating=GT, cap=1.2, f32r=False),
+    "capacity_0.6": dict(gating=GT, cap=0.6, f32r=False),
+    "fp32_router": dict(gating=GT, cap=None, f32r=True),
+    "all": dict(gating=GS, cap=1.2, f32r=True),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_forward_ex_small(name, variant):
+    cfg = SMALL[name]
+    v = VARIANTS[variant]
+    if v["f32r"] and cfg.dtype != "bf16":
+        pytest.skip("the fp32 router variant is for bf16 layers")
+    L = layer(cfg)
+    w_r = L["w_r32"] if v["f32r"] else L["w_r"]
+    cap = oracle.expert_capacity(cfg.T, cfg.k, cfg.E, v["cap"]) if v["cap"] else 0
+    gname = "softmax_topk" if v["gating"] == GS else "topk_softmax"
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    y = moe.moe_forward_ex(L["x"], w_r, L["router_bias"], L["w1"], L["w2"], cfg.k,
+                           gating=v["gating"], capacity=cap, topk_ids_out=ids, topk_w_out=w)
+    torch.cuda.synchronize()
+    logits = logits_of(L, w_r)
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    check_routing(ids_np, w.cpu().numpy(), logits, cfg.k, gating=gname)
+    w_ref = oracle.gate_weights(logits, ids_np, gname)
+    y_ref = oracle.forward(f64(L["x"]), f64(w_r), f64(L["router_bias"]), f64(L["w1"]),
+                           f64(L["w2"]), cfg.k, ids=ids_np, w=w_ref, capacity=cap)["y"]
+    rel = assert_close_rel(f64(y), y_ref, TOL[cfg.dtype], f"{name}/{variant} y")
+    if cap:
+        _, _, _, inv = oracle.dispatch(ids_np, cfg.E, cap)
+        dropped_all = np.nonzero((inv < 0).all(axis=1))[0]
+        assert torch.count_nonzero(y[torch.from_numpy(dropped_all).cuda()]) == 0
+    print(f"[{name}/{variant}] cap {cap}: max|err|/max|y_ref| = {rel:.3e}", flush=True)
+
+
+# --- full-size workloads ------------------------------------------------------
+
+@pytest.mark.parametrize("name,variant", [("skewed_bf16", "capacity_1.2"),
+                                          ("mixtral_bf16", "all"),
+                                          ("many_experts_bf16", "all")])
+def test_forward_ex_full(name, variant):
+    cfg = mi.CONFIGS[name]
+    v = VARIANTS[variant]
+    L = mi.make_inputs(cfg, "cuda")
+    w_r = mi.make_w_r_f32(cfg, "cuda") if v["f32r"] else L["w_r"]
+    cap = oracle.expert_capacity(cfg.T, cfg.k, cfg.E, v["cap"]) if v["cap"] else 0
+    gname = "softmax_topk" if v["gating"] == GS else "topk_softmax"
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    y = moe.moe_forward_ex(L["x"], w_r, L["router_bias"], L["w1"], L["w2"], cfg.k,
+                           gating=v["gating"], capacity=cap, topk_ids_out=ids, topk_w_out=w)
+    torch.cuda.synchronize()
+    logits = oracle.router_logits(f64(L["x"]), f64(w_r), f64(L["router_bias"]))
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    nb, nw = check_routing(ids_np, w.cpu().numpy(), logits, cfg.k, gating=gname)
+    _, _, _, inv = oracle.dispatch(ids_np, cfg.E, cap)
+    n_drop = int((inv < 0).sum())
+    print(f"[{name}/{variant}] cap {cap}, dropped pairs {n_drop}, near ties {nb}/{nw}",
+          flush=True)
+    if v["cap"] and name == "skewed_bf16":
+        assert n_drop > 1000          # expert 0 is far over capacity
+    dropped_tok = np.nonzero((inv < 0).any(axis=1))[0][:8]
+    sel = sample_tokens(cfg.T, extra=dropped_tok)
+    w_ref = oracle.gate_weights(logits[sel], ids_np[sel], gname)
+    w_ref = np.where(inv[sel] >= 0, w_ref, 0.0)       # dropped slots add nothing
+    g1, g2 = expert_getters(L)
+    x_sel = f64(L["x"][torch.from_numpy(sel).cuda()])
+    y_ref = oracle.forward(x_sel, f64(w_r), None, g1, g2, cfg.k, ids=ids_np[sel], w=w_ref)["y"]
+    y_sel = f64(y[torch.from_numpy(sel).cuda()])
+    rel = assert_close_rel(y_sel, y_ref, TOL["bf16"], f"{name}/{variant} y (sampled)")
+    print(f"[{name}/{variant}] max|err|/max|y_ref| = {rel:.3e} over {len(sel)} tokens",
+          flush=True)
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "multitile_bf16", "ragged_f32", "longH_bf16"])
+def test_expert_ffn_ignores_rows_past_offsets(name):
+    # rows from expert_offsets[E] on are neither read nor written: fill them
+    # with NaN and check the kept rows (every element) against the oracle
+    cfg = SMALL[name]
+    L = layer(cfg)
+    ids, _ = moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k)
+    cap = max(1, oracle.expert_capacity(cfg.T, cfg.k, cfg.E, 0.6))
+    off, st, inv, xp = moe.moe_permute_ex(L["x"], ids, cfg.E, cap)
+    torch.cuda.synchronize()
+    Rk = int(off[-1].item())
+    assert Rk < cfg.R
+    xp[Rk:] = float("nan")
+    yp = torch.full_like(xp, float("nan"))
+    moe.moe_expert_ffn(xp, off, L["w1"], L["w2"], yp=yp)
+    torch.cuda.synchronize()
+    assert torch.isnan(yp[Rk:]).all()             # untouched
+    ref = oracle.expert_ffn(f64(xp[:Rk]), off.cpu().numpy(), f64(L["w1"]), f64(L["w2"]))
+    assert_close_rel(f64(yp[:Rk]), ref, TOL[cfg.dtype], f"{name} yp kept rows")
