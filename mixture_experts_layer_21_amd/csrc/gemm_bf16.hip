@@ -491,7 +491,7 @@ __device__ __forceinline__ SplitPlan split_plan(const int* __restrict__ off, int
   pl.nsplit = 1;
   // (short-K GEMMs gain less from filling the last round than the partials
   // and shorter pipelines cost them)
-  if (pl.sk > 0 && pl.KT >= 8 * MIN_SPLIT_STEPS)
+  if (pl.sk > 0 && pl.KT >= 4 * MIN_SPLIT_STEPS)
     pl.nsplit = max(1, min(slots / pl.sk, pl.KT / MIN_SPLIT_STEPS));
   return pl;
 }
@@ -627,8 +627,8 @@ hipError_t launch_cfg(const void* A, const int* gather, int a_rows, const void* 
                      slots);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // tiles are split only when K has at least 8 * MIN_SPLIT_STEPS steps
-  if ((K + BK - 1) / BK >= 8 * MIN_SPLIT_STEPS) {
+  // tiles are split only when K has at least 4 * MIN_SPLIT_STEPS steps
+  if ((K + BK - 1) / BK >= 4 * MIN_SPLIT_STEPS) {
     hipLaunchKernelGGL((gemm_split_reduce<BM, BN, WM, WN>),
                        dim3(kMaxSlots / 2 * GemmShape<BM, BN, WM, WN>::FM),
                        dim3(kWave * WM * WN), 0, s, (uint16_t*)C, off, E, R, K, N,
