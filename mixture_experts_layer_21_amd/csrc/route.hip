@@ -74,50 +74,75 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
   const int e0 = eg * TPW * 16;
 
   // stage W_r[k_begin:k_begin+KL, e0:e0+16 TPW]; rows past H and experts
-  // past E are zero
+  // past E are zero.  Each thread moves 8-expert chunks, SB of them per
+  // batch with all the batch's loads issued before its LDS stores.
   {
     constexpr int CH = TPW * 2;                    // 8-expert chunks per row
+    constexpr int SB = WF32 ? 4 : 8;               // chunks per thread per batch
     const bool vec = (E % 8) == 0;
-    for (int q = threadIdx.x; q < KL * CH; q += blockDim.x) {
-      const int r = q / CH, c = q % CH;
-      const int k = k_begin + r, e = e0 + c * 8;
+    const int total = KL * CH;
+    for (int q0 = threadIdx.x; q0 < total; q0 += SB * 256) {
       if constexpr (!WF32) {
         const uint16_t* w_r = (const uint16_t*)w_r_any;
-        u32x4 v = {0, 0, 0, 0};
-        if (k < k_end) {
-          if (vec) {
-            if (e < E) v = *(const u32x4*)(w_r + (size_t)k * E + e);
-          } else {
-            uint16_t h[8];
+        u32x4 v[SB];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) h[u] = (e + u < E) ? w_r[(size_t)k * E + e + u] : (uint16_t)0;
-            v = u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
-                      h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+        for (int u = 0; u < SB; ++u) {
+          const int q = q0 + u * 256;
+          const int r = q / CH, c = q % CH;
+          const int k = k_begin + r, e = e0 + c * 8;
+          v[u] = u32x4{0, 0, 0, 0};
+          if (q < total && k < k_end) {
+            if (vec) {
+              if (e < E) v[u] = *(const u32x4*)(w_r + (size_t)k * E + e);
+            } else {
+              uint16_t h[8];
+#pragma unroll
+              for (int t = 0; t < 8; ++t)
+                h[t] = (e + t < E) ? w_r[(size_t)k * E + e + t] : (uint16_t)0;
+              v[u] = u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                           h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+            }
           }
         }
-        *(u32x4*)(wb + r * ROW + c * 16) = v;
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int q = q0 + u * 256;
+          if (q < total) *(u32x4*)(wb + (q / CH) * ROW + (q % CH) * 16) = v[u];
+        }
       } else {
         const float* w_r = (const float*)w_r_any;
-        float f[8];
-        if (k < k_end && vec && e < E) {
-          const float4 a = *(const float4*)(w_r + (size_t)k * E + e);
-          const float4 b = *(const float4*)(w_r + (size_t)k * E + e + 4);
-          f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-          f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-        } else {
+        float f[SB][8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            f[u] = (k < k_end && e + u < E) ? w_r[(size_t)k * E + e + u] : 0.f;
+        for (int u = 0; u < SB; ++u) {
+          const int q = q0 + u * 256;
+          const int r = q / CH, c = q % CH;
+          const int k = k_begin + r, e = e0 + c * 8;
+          if (q < total && k < k_end && vec && e < E) {
+            const float4 a = *(const float4*)(w_r + (size_t)k * E + e);
+            const float4 b = *(const float4*)(w_r + (size_t)k * E + e + 4);
+            f[u][0] = a.x; f[u][1] = a.y; f[u][2] = a.z; f[u][3] = a.w;
+            f[u][4] = b.x; f[u][5] = b.y; f[u][6] = b.z; f[u][7] = b.w;
+          } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+              f[u][t] = (q < total && k < k_end && e + t < E) ? w_r[(size_t)k * E + e + t] : 0.f;
+          }
         }
-        uint32_t hi[8], mid[8], lo[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) split3(f[u], hi[u], mid[u], lo[u]);
-        *(u32x4*)(wb + r * ROW + c * 16) =
-            u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-        *(u32x4*)(wb + plane + r * ROW + c * 16) =
-            u32x4{mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16), mid[4] | (mid[5] << 16), mid[6] | (mid[7] << 16)};
-        *(u32x4*)(wb + 2 * plane + r * ROW + c * 16) =
-            u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+        for (int u = 0; u < SB; ++u) {
+          const int q = q0 + u * 256;
+          if (q >= total) continue;
+          const int r = q / CH, c = q % CH;
+          uint32_t hi[8], mid[8], lo[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) split3(f[u][t], hi[t], mid[t], lo[t]);
+          *(u32x4*)(wb + r * ROW + c * 16) =
+              u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+          *(u32x4*)(wb + plane + r * ROW + c * 16) =
+              u32x4{mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16), mid[4] | (mid[5] << 16), mid[6] | (mid[7] << 16)};
+          *(u32x4*)(wb + 2 * plane + r * ROW + c * 16) =
+              u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+        }
       }
     }
   }
@@ -137,20 +162,37 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
 #pragma unroll
   for (int j = 0; j < TPW; ++j) acc[j] = f32x4{};
 
-  for (int k0 = k_begin; k0 < k_end; k0 += 32) {
-    const bool ok = k0 + kl < k_end;
-    const u32x4 a = ok ? *(const u32x4*)(xr + k0) : u32x4{0, 0, 0, 0};
-    const char* base = wb + (k0 - k_begin) * ROW + rd_off;
+  // token rows: PF K steps of loads in flight ahead of the MFMAs (each step's
+  // 16 bytes per lane would otherwise wait a full memory latency)
+  constexpr int PF = 8;
+  const int nst = (k_end - k_begin + 31) / 32;
+  auto load_x = [&](int st) -> u32x4 {
+    const int k0 = k_begin + st * 32;
+    return (st < nst && k0 + kl < k_end) ? *(const u32x4*)(xr + k0) : u32x4{0, 0, 0, 0};
+  };
+  u32x4 abuf[PF];
 #pragma unroll
-    for (int pl = 0; pl < NP; ++pl) {
+  for (int p = 0; p < PF; ++p) abuf[p] = load_x(p);
+  for (int s0 = 0; s0 < nst; s0 += PF) {
 #pragma unroll
-      for (int j = 0; j < TPW; ++j) {
-        const u32x2 lo = lds_read_tr(base + pl * plane + j * 32);
-        const u32x2 hi = lds_read_tr(base + pl * plane + 4 * ROW + j * 32);
-        const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                         __builtin_bit_cast(bf16x8, b),
-                                                         acc[j], 0, 0, 0);
+    for (int p = 0; p < PF; ++p) {
+      const int st = s0 + p;
+      if (st < nst) {
+        const u32x4 a = abuf[p];
+        abuf[p] = load_x(st + PF);
+        const char* base = wb + st * 32 * ROW + rd_off;
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl) {
+#pragma unroll
+          for (int j = 0; j < TPW; ++j) {
+            const u32x2 lo = lds_read_tr(base + pl * plane + j * 32);
+            const u32x2 hi = lds_read_tr(base + pl * plane + 4 * ROW + j * 32);
+            const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                             __builtin_bit_cast(bf16x8, b),
+                                                             acc[j], 0, 0, 0);
+          }
+        }
       }
     }
   }
