@@ -18,6 +18,10 @@
 //                the pair is dropped, inv_pos = -1
 //   perm_gather  xp[p,:] = x[sorted_token[p],:] for p < offsets[E], 16-byte
 //                copies, one wave per row
+//   perm_small   for small layers (E <= 256, R <= 16384) the first three in one
+//                workgroup of 16 waves, one launch: each wave ranks a
+//                contiguous run of pairs, the per-wave counts are scanned,
+//                then every pair is placed (the same stable order)
 //
 // All counts are integers: placement is exact and deterministic.
 #include "common.h"
@@ -168,6 +172,103 @@ __global__ __launch_bounds__(256) void perm_gather(const u32x4* __restrict__ x,
   }
 }
 
+constexpr int kSmallE = 256, kSmallR = 16384;
+constexpr int kSmallWaves = 16, kSmallChunks = kSmallR / (kSmallWaves * kWave);   // 16
+
+// One workgroup of 16 waves.  Wave w owns a contiguous run of 64-pair chunks
+// (pairs in index order), ranks each pair inside its expert among the wave's
+// pairs so far (ballot peers + a wave-private running count), and after one
+// barrier the per-wave counts give both the expert totals and each wave's
+// starting rank.  Every pair's id is loaded up front, so the only serial
+// latency is the ranking arithmetic itself.
+__global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int R, int E,
+                                                   int k, int cap, int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ sorted_token,
+                                                   int32_t* __restrict__ inv_pos) {
+  __shared__ int wcnt[kSmallWaves][kSmallE];   // pairs per (wave, expert), then start ranks
+  __shared__ int off_s[kSmallE];               // kept-row offset of each expert
+  __shared__ int wsum[kSmallWaves];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int nch = (R + kWave - 1) / kWave;
+  const int cpw = (nch + kSmallWaves - 1) / kSmallWaves;   // chunks per wave, <= 16
+  const int c0 = wave * cpw;
+  int my_e[kSmallChunks], rk[kSmallChunks];
+#pragma unroll
+  for (int j = 0; j < kSmallChunks; ++j) {
+    const int i = (c0 + j) * kWave + lane;
+    my_e[j] = (j < cpw && i < R) ? ids[i] : -1;
+  }
+  for (int t = tid; t < kSmallWaves * E; t += 1024) wcnt[t / E][t % E] = 0;
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+  for (int j = 0; j < kSmallChunks; ++j) {
+    if (j < cpw) {
+      const int e = my_e[j];
+      const bool valid = e >= 0;
+      uint64_t remaining = __ballot(valid);
+      uint64_t peers = 0;
+      while (remaining) {
+        const int leader = __builtin_ctzll(remaining);
+        const int le = wave_bcast(e, leader);
+        const uint64_t m = __ballot(valid && e == le);
+        if (valid && e == le) peers = m;
+        remaining &= ~m;
+      }
+      const int before = __popcll(peers & lt_mask);
+      const int cnt = valid ? wcnt[wave][e] : 0;
+      rk[j] = cnt + before;
+      // one lane per peer group advances the count, after every lane has read it
+      if (valid && before == 0) wcnt[wave][e] = cnt + __popcll(peers);
+    } else {
+      rk[j] = 0;
+    }
+  }
+  __syncthreads();
+  // per expert: start rank of each wave (exclusive scan over waves), total
+  int total = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int v = wcnt[w][tid];
+      wcnt[w][tid] = total;
+      total += v;
+    }
+  }
+  // exclusive scan of the kept totals min(total, cap) over experts (4 waves)
+  const int v = tid < E ? min(total, cap) : 0;
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  if (tid < E) {
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += wsum[w];
+    off_s[tid] = wbase + incl - v;
+    offsets[tid] = wbase + incl - v;
+  }
+  if (tid == 0) {
+    int all = 0;
+    for (int w = 0; w < kSmallWaves; ++w) all += wsum[w];
+    offsets[E] = all;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSmallChunks; ++j) {
+    const int e = my_e[j];
+    if (e >= 0) {
+      const int i = (c0 + j) * kWave + lane;
+      const int r_e = wcnt[wave][e] + rk[j];
+      if (r_e < cap) {
+        const int pos = off_s[e] + r_e;
+        sorted_token[pos] = i / k;
+        inv_pos[i] = pos;
+      } else {
+        inv_pos[i] = -1;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int R, int E) {
@@ -184,13 +285,20 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
   const int nchunks = (R + CH - 1) / CH;
   int32_t* counts = (int32_t*)ws;
   int32_t* base = (int32_t*)((char*)ws + align_up((size_t)nchunks * E * sizeof(int32_t)));
-  if (nchunks > 0)
-    hipLaunchKernelGGL(perm_count, dim3(nchunks), dim3(256), E * sizeof(int), s, ids, R, E, counts);
-  // runs even for R == 0 so that the offsets are written (all zero)
-  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, counts, nchunks, E, cap, base, offsets);
-  if (nchunks == 0) return hipGetLastError();
-  hipLaunchKernelGGL(perm_place, dim3(nchunks), dim3(256), 5 * E * sizeof(int), s, ids, R, E, k,
-                     cap, base, offsets, sorted_token, inv_pos);
+  if (R > 0 && E <= kSmallE && R <= kSmallR) {
+    hipLaunchKernelGGL(perm_small, dim3(1), dim3(1024), 0, s, ids, R, E, k, cap, offsets,
+                       sorted_token, inv_pos);
+  } else {
+    if (nchunks > 0)
+      hipLaunchKernelGGL(perm_count, dim3(nchunks), dim3(256), E * sizeof(int), s, ids, R, E,
+                         counts);
+    // runs even for R == 0 so that the offsets are written (all zero)
+    hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, counts, nchunks, E, cap, base,
+                       offsets);
+    if (nchunks == 0) return hipGetLastError();
+    hipLaunchKernelGGL(perm_place, dim3(nchunks), dim3(256), 5 * E * sizeof(int), s, ids, R, E,
+                       k, cap, base, offsets, sorted_token, inv_pos);
+  }
   if (xp == nullptr) return hipGetLastError();
   const int row_chunks = (int)((size_t)H * elem_bytes / 16);
   const int blocks = std::min(8192, (R + 3) / 4);
