@@ -1,4 +1,4 @@
-"""Plain, slow, fp64 CPU oracle for the MoE layer forward.
+"""Plain, slow, fp64 CPU oracle for the MoE layer forward and its backward.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
 its Python binding) imports, calls or links this module; only the tests, the
@@ -37,6 +37,15 @@ Variants (the CANN MoE operator-optimization article, "the CANN article"):
     first `capacity` (token, slot) pairs in the gather's scan order; a dropped
     pair contributes nothing to y and the other weights are not renormalised
     (the routing article names token dropping for overloaded experts).
+
+Backward (the CANN article's training setting: section 3 names the backward
+pass's gradient aggregation, section 4.2 keeps the router in fp32, section 5
+times whole training steps).  The pages print no gradient formulas; the
+reading taken is the exact derivative of the forward above for a loss whose
+gradient with respect to y is dy.  The top-k choice and the capacity drop are
+piecewise constant in the logits, so no gradient flows through them: the
+gradient reaches the logits only through the gate weights of the selected
+experts, and a dropped pair's weight gets none (it does not reach y).
 """
 from __future__ import annotations
 
@@ -60,6 +69,18 @@ def gelu_tanh(z: np.ndarray) -> np.ndarray:
 
 
 # --- routing + gating (fused article, section 1; routing article) ----------
+
+def gelu_tanh_grad(z: np.ndarray) -> np.ndarray:
+    """d GELU / dz for the tanh form, in fp64.
+
+    With u = sqrt(2/pi) (z + 0.044715 z^3) and GELU = 0.5 z (1 + tanh u):
+    0.5 (1 + tanh u) + 0.5 z (1 - tanh(u)^2) sqrt(2/pi) (1 + 3 * 0.044715 z^2).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    th = np.tanh(SQRT_2_OVER_PI * (z + 0.044715 * z ** 3))
+    du = SQRT_2_OVER_PI * (1.0 + 3.0 * 0.044715 * z ** 2)
+    return 0.5 * (1.0 + th) + 0.5 * z * (1.0 - th ** 2) * du
+
 
 def router_logits(x: np.ndarray, w_r: np.ndarray, b_r: np.ndarray | None = None) -> np.ndarray:
     """logits[T,E] = x[T,H] . W_r[H,E] (+ b_r[E]), fp64.
@@ -118,6 +139,39 @@ def gate_weights(logits: np.ndarray, ids: np.ndarray, gating: str = "topk_softma
         p = np.exp(logits - m)
         p = p / p.sum(axis=1, keepdims=True)
         return np.take_along_axis(p, ids, axis=1)
+    raise ValueError(f"unknown gating {gating!r}")
+
+
+def gate_weights_grad(logits: np.ndarray, ids: np.ndarray, dw: np.ndarray,
+                      gating: str = "topk_softmax") -> np.ndarray:
+    """dlogits[T,E] from dw[T,k], the gradient with respect to the gate
+    weights, by the softmax's Jacobian (no gradient through the choice of ids).
+
+    "topk_softmax": w = softmax of the k selected logits, so the selected
+    logit of slot j gets w_j (dw_j - sum_j' w_j' dw_j') and the other logits 0.
+    "softmax_topk": p = softmax of all E logits and w_j = p[ids_j]; with
+    g_e = dw_j where e = ids_j (0 for unselected e), logit e gets
+    p_e (g_e - sum_e' p_e' g_e').
+    """
+    logits = np.asarray(logits, np.float64)
+    dw = np.asarray(dw, np.float64)
+    T, E = logits.shape
+    dl = np.zeros((T, E), dtype=np.float64)
+    if gating == "topk_softmax":
+        w = gate_weights(logits, ids, gating)
+        s = (w * dw).sum(axis=1, keepdims=True)
+        dsel = w * (dw - s)
+        for j in range(ids.shape[1]):
+            dl[np.arange(T), ids[:, j]] += dsel[:, j]
+        return dl
+    if gating == "softmax_topk":
+        m = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - m)
+        p = p / p.sum(axis=1, keepdims=True)
+        g = np.zeros((T, E), dtype=np.float64)
+        for j in range(ids.shape[1]):
+            g[np.arange(T), ids[:, j]] += dw[:, j]
+        return p * (g - (p * g).sum(axis=1, keepdims=True))
     raise ValueError(f"unknown gating {gating!r}")
 
 
@@ -260,6 +314,66 @@ def forward(x, w_r, b_r, w1, w2, k: int, ids=None, w=None, gating: str = "topk_s
         y_e = expert_ffn_block(x[b_idx], _get(w1, e), _get(w2, e))
         np.add.at(y, b_idx, w[b_idx, s_idx][:, None] * y_e)
     return {"y": y, "ids": ids, "w": w, "logits": logits}
+
+
+def backward(x, w_r, b_r, w1, w2, k: int, dy, ids=None, gating: str = "topk_softmax",
+             capacity: int = 0):
+    """Gradients of the layer forward for an output gradient dy[T,H].
+
+    Each step is the chain rule through one step of forward(), taken in the
+    reverse order:
+      combine      y[t] += w[t,j] yp[p]   ->  dw[t,j] = dy[t] . yp[p],
+                                              dyp[p] = w[t,j] dy[t]
+      expert GEMM2 yp = h W2_e            ->  dW2_e = h^T dyp,  dh = dyp W2_e^T
+      GELU         h = GELU(z)            ->  dz = dh * GELU'(z)
+      expert GEMM1 z = x_e W1_e           ->  dW1_e = x_e^T dz, dx_e = dz W1_e^T
+      dispatch     x_e = x[tokens of e]   ->  dx[t] += dx_e rows of token t
+      gating       w = gate(logits)       ->  dlogits (gate_weights_grad)
+      router       logits = x W_r + b_r   ->  dx += dlogits W_r^T,
+                                              dW_r = x^T dlogits, db_r = sum_t dlogits
+    ids may be given (a routing chosen on a near tie); the gate weights are
+    then recomputed from the oracle's logits for those ids.
+    Returns dict(dx, dw_r, db_r, dw1, dw2, dw, dlogits, ids, w).
+    """
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    w_r64 = np.asarray(w_r, np.float64)
+    T, H = x.shape
+    E = w_r64.shape[1]
+    logits = router_logits(x, w_r, b_r)
+    if ids is None:
+        ids = topk_ids(logits, k)
+    ids = np.asarray(ids, np.int64)
+    w = gate_weights(logits, ids, gating)
+    offsets, sorted_token, sorted_slot, _ = dispatch(ids, E, capacity)
+    w1_0 = np.asarray(_get(w1, 0))
+    F = w1_0.shape[1]
+    dx = np.zeros((T, H), dtype=np.float64)
+    dw1 = np.zeros((E, H, F), dtype=np.float64)
+    dw2 = np.zeros((E, F, H), dtype=np.float64)
+    dw = np.zeros(ids.shape, dtype=np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        tok, slot = sorted_token[a:b], sorted_slot[a:b]
+        w1_e = np.asarray(_get(w1, e), np.float64)
+        w2_e = np.asarray(_get(w2, e), np.float64)
+        x_e = x[tok]
+        z = x_e @ w1_e
+        h = gelu_tanh(z)
+        y_e = h @ w2_e
+        g = dy[tok]
+        dw[tok, slot] = (g * y_e).sum(axis=1)
+        dy_e = w[tok, slot][:, None] * g
+        dw2[e] = h.T @ dy_e
+        dz = (dy_e @ w2_e.T) * gelu_tanh_grad(z)
+        dw1[e] = x_e.T @ dz
+        np.add.at(dx, tok, dz @ w1_e.T)
+    dl = gate_weights_grad(logits, ids, dw, gating)
+    dx += dl @ w_r64.T
+    return {"dx": dx, "dw_r": x.T @ dl, "db_r": dl.sum(axis=0), "dw1": dw1, "dw2": dw2,
+            "dw": dw, "dlogits": dl, "ids": ids, "w": w}
 
 
 def forward_tokens(x_rows, ids_rows, w_rows, w1, w2) -> np.ndarray:
