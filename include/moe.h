@@ -252,6 +252,69 @@ moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bi
                           void* y, int32_t* topk_ids_out, float* topk_w_out,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Training: a forward that keeps what the backward needs, and the backward.
+ *
+ * The pages describe training with this layer (CANN MoE article: section 3,
+ * the backward pass's gradient aggregation; section 4.2, the router kept in
+ * fp32; section 5, whole training steps) but print no gradient formulas.
+ * The backward computes the exact derivative of the forward above for an
+ * output gradient dy: no gradient flows through the top-k choice or the
+ * capacity drop (both are piecewise constant in the logits), so the logits
+ * receive gradient only through the gate weights of the selected experts;
+ * a dropped (token, slot) pair's weight gets none.  GELU' is that of the tanh
+ * form.  Accumulation is fp32; bf16 results are rounded to nearest even.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * *bytes = size of the state moe_forward_train keeps for moe_backward
+ * (dispatch indices, fp32 logits [T,E], the first expert GEMM's
+ * pre-activation z [T*top_k,F] and GELU(z), the expert outputs
+ * [T*top_k,H]).  Its layout is private to the library.
+ */
+moe_status moe_saved_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k, int64_t F,
+                           moe_dtype dtype, size_t* bytes);
+
+/* *bytes = workspace moe_backward needs for this shape. */
+moe_status moe_backward_workspace_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k,
+                                        int64_t F, moe_dtype dtype, size_t* bytes);
+
+/*
+ * moe_forward_ex that also fills `saved` (device, caller-owned, at least
+ * moe_saved_bytes()) for moe_backward.  topk_ids / topk_w are required here
+ * (the backward takes them back).  y, ids and w equal moe_forward_ex's for
+ * the same inputs.  ws as for moe_forward_ex.  With T == 0 nothing is
+ * enqueued and x, y, topk_ids, topk_w (empty) may be NULL.
+ */
+moe_status moe_forward_train(const void* x, const void* w_r, const float* router_bias,
+                             const void* w1, const void* w2, int64_t T, int64_t H, int64_t E,
+                             int32_t top_k, int64_t F, moe_dtype dtype, moe_dtype router_dtype,
+                             moe_gating gating, int32_t capacity, void* y, int32_t* topk_ids,
+                             float* topk_w, void* saved, size_t saved_bytes, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the layer for dy[T,H] (dtype), after moe_forward_train with the
+ * same inputs, shape, types and gating (its topk_ids, topk_w and `saved`,
+ * unchanged; the capacity is already in `saved`).  Outputs (device, caller
+ * owned, fully overwritten):
+ *   dx[T,H] (dtype), dw_r[H,E] (router_dtype), dw1[E,H,F], dw2[E,F,H] (dtype);
+ *   db_r[E] fp32, optional (NULL: not computed; the router bias's gradient);
+ *   dtopk_w[T,top_k] fp32, optional (NULL: kept in the workspace): the
+ *   gradient with respect to the gate weights (0 for dropped pairs).
+ * An expert that received no rows gets zero weight gradients.
+ * ws_bytes must be at least moe_backward_workspace_bytes().  Errors as for
+ * the forward; enqueued on `stream`, nothing allocated or synchronised.
+ * With T == 0 the weight gradients are zero-filled and dy, x, topk_ids,
+ * topk_w, dx (empty) may be NULL.
+ */
+moe_status moe_backward(const void* dy, const void* x, const void* w_r, const void* w1,
+                        const void* w2, int64_t T, int64_t H, int64_t E, int32_t top_k,
+                        int64_t F, moe_dtype dtype, moe_dtype router_dtype, moe_gating gating,
+                        const int32_t* topk_ids, const float* topk_w, const void* saved,
+                        size_t saved_bytes, void* dx, void* dw_r, float* db_r, void* dw1,
+                        void* dw2, float* dtopk_w, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

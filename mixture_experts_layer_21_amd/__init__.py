@@ -1,4 +1,4 @@
-"""MI355X (gfx950) Mixture-of-Experts layer forward: Python binding.
+"""MI355X (gfx950) Mixture-of-Experts layer forward and backward: Python binding.
 
 A thin ctypes layer over libmoe.so (include/moe.h).  Every function here has
 the name of the C entry point it calls and only marshals arguments: it checks
@@ -32,7 +32,8 @@ MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_EXPERT_FFN, MOE_STAGE_COMBINE, MOE
 MOE_GATE_TOPK_SOFTMAX, MOE_GATE_SOFTMAX_TOPK = 0, 1
 EXPORTS = ("moe_status_string", "moe_workspace_bytes", "moe_stage_workspace_bytes", "moe_route",
            "moe_route_ex", "moe_expert_capacity", "moe_permute", "moe_permute_ex",
-           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex")
+           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex", "moe_saved_bytes",
+           "moe_backward_workspace_bytes", "moe_forward_train", "moe_backward")
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _lib.moe_status_string.restype = ctypes.c_char_p
@@ -66,6 +67,18 @@ _lib.moe_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i
 _lib.moe_forward_ex.restype = _i32
 _lib.moe_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _i32,
                                 _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_saved_bytes.restype = _i32
+_lib.moe_saved_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
+_lib.moe_backward_workspace_bytes.restype = _i32
+_lib.moe_backward_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i32,
+                                              ctypes.POINTER(_sz)]
+_lib.moe_forward_train.restype = _i32
+_lib.moe_forward_train.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32,
+                                   _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]
+_lib.moe_backward.restype = _i32
+_lib.moe_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _i32,
+                              _i32, _vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                              _vp]
 
 
 class MoEError(RuntimeError):
@@ -333,3 +346,89 @@ def moe_forward_ex(x, w_r, router_bias, w1, w2, top_k: int, gating: int = MOE_GA
                             capacity, _ptr(y), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
                             ws.numel(), _stream(dev)), "moe_forward_ex")
     return y
+
+
+def moe_saved_bytes(T: int, H: int, E: int, top_k: int, F: int, dtype: torch.dtype) -> int:
+    n = _sz(0)
+    _ok(_lib.moe_saved_bytes(T, H, E, top_k, F, _dtype_code(dtype), ctypes.byref(n)),
+        "moe_saved_bytes")
+    return n.value
+
+
+def moe_backward_workspace_bytes(T: int, H: int, E: int, top_k: int, F: int,
+                                 dtype: torch.dtype) -> int:
+    n = _sz(0)
+    _ok(_lib.moe_backward_workspace_bytes(T, H, E, top_k, F, _dtype_code(dtype),
+                                          ctypes.byref(n)), "moe_backward_workspace_bytes")
+    return n.value
+
+
+def moe_forward_train(x, w_r, router_bias, w1, w2, top_k: int,
+                      gating: int = MOE_GATE_TOPK_SOFTMAX, capacity: int = 0, y=None,
+                      topk_ids=None, topk_w=None, saved=None, ws=None):
+    """moe_forward_ex that also keeps the state moe_backward needs.
+    Returns (y, topk_ids, topk_w, saved)."""
+    _check(x, "x")
+    T, H = x.shape
+    E = w_r.shape[1]
+    F = w1.shape[2]
+    _check(w_r, "w_r", None, (H, E))
+    if router_bias is not None:
+        _check(router_bias, "router_bias", torch.float32, (E,))
+    _check(w1, "w1", x.dtype, (E, H, F))
+    _check(w2, "w2", x.dtype, (E, F, H))
+    dev = x.device
+    y = torch.empty((T, H), dtype=x.dtype, device=dev) if y is None else \
+        _check(y, "y", x.dtype, (T, H))
+    topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev) if topk_ids is None else \
+        _check(topk_ids, "topk_ids", torch.int32, (T, top_k))
+    topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if topk_w is None else \
+        _check(topk_w, "topk_w", torch.float32, (T, top_k))
+    saved = _workspace(saved, moe_saved_bytes(T, H, E, top_k, F, x.dtype), dev)
+    ws = _workspace(ws, moe_workspace_bytes(T, H, E, top_k, F, x.dtype), dev)
+    _ok(_lib.moe_forward_train(_ptr(x), _ptr(w_r), _ptr(router_bias), _ptr(w1), _ptr(w2), T, H,
+                               E, top_k, F, _dtype_code(x.dtype), _dtype_code(w_r.dtype), gating,
+                               capacity, _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(saved),
+                               saved.numel(), _ptr(ws), ws.numel(), _stream(dev)),
+        "moe_forward_train")
+    return y, topk_ids, topk_w, saved
+
+
+def moe_backward(dy, x, w_r, w1, w2, top_k: int, topk_ids, topk_w, saved,
+                 gating: int = MOE_GATE_TOPK_SOFTMAX, with_bias_grad: bool = False, out=None,
+                 ws=None):
+    """Backward of the layer after moe_forward_train (same inputs and gating).
+    Returns dict(dx, dw_r, db_r (None unless with_bias_grad), dw1, dw2, dw): dw is
+    the gradient with respect to the gate weights.  `out` may hold preallocated
+    tensors under those names."""
+    _check(x, "x")
+    T, H = x.shape
+    E = w_r.shape[1]
+    F = w1.shape[2]
+    _check(dy, "dy", x.dtype, (T, H))
+    _check(w_r, "w_r", None, (H, E))
+    _check(w1, "w1", x.dtype, (E, H, F))
+    _check(w2, "w2", x.dtype, (E, F, H))
+    _check(topk_ids, "topk_ids", torch.int32, (T, top_k))
+    _check(topk_w, "topk_w", torch.float32, (T, top_k))
+    _check(saved, "saved", torch.uint8)
+    dev = x.device
+    out = dict(out or {})
+    shapes = {"dx": ((T, H), x.dtype), "dw_r": ((H, E), w_r.dtype), "dw1": ((E, H, F), x.dtype),
+              "dw2": ((E, F, H), x.dtype), "dw": ((T, top_k), torch.float32)}
+    if with_bias_grad:
+        shapes["db_r"] = ((E,), torch.float32)
+    for name, (shape, dt) in shapes.items():
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=dt, device=dev)
+        else:
+            _check(out[name], name, dt, shape)
+    out.setdefault("db_r", None)
+    ws = _workspace(ws, moe_backward_workspace_bytes(T, H, E, top_k, F, x.dtype), dev)
+    _ok(_lib.moe_backward(_ptr(dy), _ptr(x), _ptr(w_r), _ptr(w1), _ptr(w2), T, H, E, top_k, F,
+                          _dtype_code(x.dtype), _dtype_code(w_r.dtype), gating, _ptr(topk_ids),
+                          _ptr(topk_w), _ptr(saved), saved.numel(), _ptr(out["dx"]),
+                          _ptr(out["dw_r"]), _ptr(out["db_r"]), _ptr(out["dw1"]),
+                          _ptr(out["dw2"]), _ptr(out["dw"]), _ptr(ws), ws.numel(),
+                          _stream(dev)), "moe_backward")
+    return out

@@ -1,0 +1,458 @@
+// Backward of the MoE layer: the kernels around the expert GEMMs.
+//
+// The layer's gradient for an output gradient dy (the chain rule through the
+// forward of the fused MoE article, taken step by step in reverse; the CANN
+// MoE article's training setting, sections 3 and 4.2):
+//   combine_bwd   per (token, slot) pair with dispatched row p:
+//                 dw = dy[t] . yp[p] (fp32) and dyp[p] = w * dy[t]
+//   router_bwd    per token: the logit gradient dl[t, 0..E) (fp32) through the
+//                 softmax's Jacobian (no gradient through the top-k choice)
+//   router_wgrad  dW_r = x^T dl and db_r = sum_t dl, split over tokens into
+//                 fp32 partials that router_wgrad_reduce adds in split order
+//   dx_finish     dx[t] = sum_j dxp[inv_pos[t, j]] + dl[t] . W_r^T
+// The expert GEMMs in between (dz = dyp W2^T * GELU'(z), dW2 = h^T dyp,
+// dxp = dz W1^T, dW1 = xp^T dz) run on the grouped GEMM kernels.
+// Every sum runs in a fixed order: the results are deterministic.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+  return v;
+}
+
+// 8 consecutive elements of a row as fp32 (bf16 rows: one 16-byte load)
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* row, int c, float (&v)[8]) {
+  if constexpr (BF16) {
+    const u32x4 q = ((const u32x4*)row)[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(q[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_to_f32(q[i] >> 16);
+    }
+  } else {
+    const f32x4 a = ((const f32x4*)row)[2 * c], b = ((const f32x4*)row)[2 * c + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store8(void* row, int c, const float (&v)[8]) {
+  if constexpr (BF16) {
+    ((u32x4*)row)[c] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  } else {
+    ((f32x4*)row)[2 * c] = f32x4{v[0], v[1], v[2], v[3]};
+    ((f32x4*)row)[2 * c + 1] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+// One wave per (token, slot) pair i = t * k + j.  Dropped pairs (p < 0) get
+// dw = 0 and no dyp row.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_bwd(const void* __restrict__ dy,
+                                                   const void* __restrict__ yp,
+                                                   const int32_t* __restrict__ inv_pos,
+                                                   const float* __restrict__ w, int T, int H,
+                                                   int k, float* __restrict__ dw,
+                                                   void* __restrict__ dyp) {
+  const int lane = threadIdx.x % kWave;
+  const int i = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (i >= T * k) return;
+  const int p = inv_pos[i];
+  if (p < 0) {
+    if (lane == 0) dw[i] = 0.f;
+    return;
+  }
+  const size_t es = BF16 ? 2 : 4;
+  const char* g = (const char*)dy + (size_t)(i / k) * H * es;
+  const char* y = (const char*)yp + (size_t)p * H * es;
+  char* d = (char*)dyp + (size_t)p * H * es;
+  const float wi = w[i];
+  float dot = 0.f;
+  for (int c = lane; c < H / 8; c += kWave) {
+    float a[8], b[8], o[8];
+    load8<BF16>(g, c, a);
+    load8<BF16>(y, c, b);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      dot = __builtin_fmaf(a[q], b[q], dot);
+      o[q] = wi * a[q];
+    }
+    store8<BF16>(d, c, o);
+  }
+  dot = wave_sum(dot);
+  if (lane == 0) dw[i] = dot;
+}
+
+// One wave per token: dl[t, e] for every expert (dense, fp32).
+//   top-k then softmax:  dl[ids_j] = w_j (dw_j - sum_j' w_j dw_j'), else 0
+//   softmax then top-k:  p = softmax(logits[t]);  g_e = dw_j where e = ids_j
+//                        (else 0);  dl_e = p_e (g_e - sum_e' p_e' g_e')
+template <int NPL>
+__global__ __launch_bounds__(256) void router_bwd(const float* __restrict__ logits,
+                                                  const int32_t* __restrict__ ids,
+                                                  const float* __restrict__ w,
+                                                  const float* __restrict__ dw, int T, int E,
+                                                  int k, int softmax_all,
+                                                  float* __restrict__ dl) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  // slot j's (id, dw, w) in lane j
+  int my_id = -1;
+  float my_dw = 0.f, my_w = 0.f;
+  if (lane < k) {
+    my_id = ids[(size_t)t * k + lane];
+    my_dw = dw[(size_t)t * k + lane];
+    my_w = w[(size_t)t * k + lane];
+  }
+  // g[i]: dw of the slot holding expert lane + 64 i (0 if none)
+  float g[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) g[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int id = __builtin_amdgcn_readlane(my_id, j);
+    const float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_dw), j));
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (lane + i * kWave == id) g[i] = v;
+  }
+  float out[NPL];
+  if (!softmax_all) {
+    const float s = wave_sum(my_w * my_dw);
+    float wsel[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) wsel[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int id = __builtin_amdgcn_readlane(my_id, j);
+      const float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j));
+#pragma unroll
+      for (int i = 0; i < NPL; ++i)
+        if (lane + i * kWave == id) wsel[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) out[i] = wsel[i] * (g[i] - s);
+  } else {
+    float l[NPL];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + i * kWave;
+      l[i] = e < E ? logits[(size_t)t * E + e] : -__builtin_inff();
+      m = fmaxf(m, l[i]);
+    }
+    m = wave_max(m);
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      l[i] = lane + i * kWave < E ? __expf(l[i] - m) : 0.f;
+      z += l[i];
+    }
+    const float inv = 1.f / wave_sum(z);
+    float pg = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      l[i] *= inv;
+      pg += l[i] * g[i];
+    }
+    const float s = wave_sum(pg);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) out[i] = l[i] * (g[i] - s);
+  }
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + i * kWave;
+    if (e < E) dl[(size_t)t * E + e] = out[i];
+  }
+}
+
+// Router weight gradient, one workgroup per (512 h block, 16 expert block,
+// token split): thread tid owns h = h0 + 2 tid, h0 + 2 tid + 1 and 16
+// experts; dl of 64 tokens at a time is staged in LDS and read as broadcasts.
+// The split's sums go to part[s][H][E] (and db's to partb[s][E]).
+constexpr int kWgH = 512, kWgE = 16, kWgT = 64;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_wgrad(const void* __restrict__ x,
+                                                    const float* __restrict__ dl, int T, int H,
+                                                    int E, int S, float* __restrict__ part,
+                                                    float* __restrict__ partb) {
+  __shared__ float dls[kWgT][kWgE];
+  const int tid = threadIdx.x;
+  const int HB = (H + kWgH - 1) / kWgH, EB = (E + kWgE - 1) / kWgE;
+  const int hb = blockIdx.x % HB, eb = (blockIdx.x / HB) % EB, s = blockIdx.x / (HB * EB);
+  const int t_begin = (int)((long)s * T / S), t_end = (int)((long)(s + 1) * T / S);
+  const int h = hb * kWgH + 2 * tid;
+  const int e0 = eb * kWgE;
+  float acc[2][kWgE], accb[kWgE];
+#pragma unroll
+  for (int e = 0; e < kWgE; ++e) {
+    acc[0][e] = acc[1][e] = 0.f;
+    accb[e] = 0.f;
+  }
+  const bool bias_thread = hb == 0 && tid == 0;
+  for (int tb = t_begin; tb < t_end; tb += kWgT) {
+    const int nt = min(kWgT, t_end - tb);
+    __syncthreads();
+    for (int q = tid; q < kWgT * kWgE; q += 256) {
+      const int tt = q / kWgE, e = q % kWgE;
+      dls[tt][e] = (tt < nt && e0 + e < E) ? dl[(size_t)(tb + tt) * E + e0 + e] : 0.f;
+    }
+    __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+      float x0 = 0.f, x1 = 0.f;
+      if (h < H) {
+        if constexpr (BF16) {
+          const uint32_t v = *(const uint32_t*)((const uint16_t*)x + (size_t)(tb + tt) * H + h);
+          x0 = bf16_to_f32(v & 0xFFFFu);
+          x1 = bf16_to_f32(v >> 16);
+        } else {
+          const float* r = (const float*)x + (size_t)(tb + tt) * H + h;
+          x0 = r[0];
+          x1 = r[1];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kWgE; ++e) {
+        const float d = dls[tt][e];
+        acc[0][e] = __builtin_fmaf(x0, d, acc[0][e]);
+        acc[1][e] = __builtin_fmaf(x1, d, acc[1][e]);
+        if (bias_thread) accb[e] += d;
+      }
+    }
+  }
+  if (h < H) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int e = 0; e < kWgE; ++e)
+        if (e0 + e < E) part[((size_t)s * H + h + r) * E + e0 + e] = acc[r][e];
+  }
+  if (bias_thread) {
+#pragma unroll
+    for (int e = 0; e < kWgE; ++e)
+      if (e0 + e < E) partb[(size_t)s * E + e0 + e] = accb[e];
+  }
+}
+
+// dW_r[h][e] = sum over splits in order; stored in W_r's type.  The first
+// E threads also finish db_r.
+template <bool WBF16>
+__global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restrict__ part,
+                                                           const float* __restrict__ partb,
+                                                           int H, int E, int S,
+                                                           void* __restrict__ dw_r,
+                                                           float* __restrict__ db_r) {
+  const size_t n = (size_t)H * E;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    float v = 0.f;
+    for (int s = 0; s < S; ++s) v += part[(size_t)s * n + i];
+    if constexpr (WBF16)
+      ((uint16_t*)dw_r)[i] = (uint16_t)f32_to_bf16(v);
+    else
+      ((float*)dw_r)[i] = v;
+  }
+  if (db_r && blockIdx.x == 0 && threadIdx.x < E) {
+    for (int e = threadIdx.x; e < E; e += 256) {
+      float v = 0.f;
+      for (int s = 0; s < S; ++s) v += partb[(size_t)s * E + e];
+      db_r[e] = v;
+    }
+  }
+}
+
+// dx for 16 tokens x 1024 columns per workgroup: thread tid owns columns
+// h0 + 4 tid .. + 3.  The router term sum_e dl[t][e] W_r[h][e] reads W_r's
+// rows (E contiguous) 8 experts at a time with dl from LDS (broadcasts); the
+// expert term adds the token's dispatched rows of dxp (slots in order).
+constexpr int kDxT = 16, kDxH = 1024;
+
+template <bool BF16, bool WBF16>
+__global__ __launch_bounds__(256) void dx_finish(const void* __restrict__ dxp,
+                                                 const int32_t* __restrict__ inv_pos,
+                                                 const float* __restrict__ dl,
+                                                 const void* __restrict__ w_r, int T, int H,
+                                                 int E, int k, void* __restrict__ dx) {
+  extern __shared__ float dls[];      // [kDxT][E]
+  const int tid = threadIdx.x;
+  const int HB = (H + kDxH - 1) / kDxH;
+  const int t0 = (blockIdx.x / HB) * kDxT;
+  const int h = (blockIdx.x % HB) * kDxH + 4 * tid;
+  const int nt = min(kDxT, T - t0);
+  for (int q = tid; q < kDxT * E; q += 256) {
+    const int tt = q / E;
+    dls[q] = tt < nt ? dl[(size_t)(t0 + tt) * E + q % E] : 0.f;
+  }
+  __syncthreads();
+  if (h >= H) return;
+  float acc[kDxT][4];
+#pragma unroll
+  for (int tt = 0; tt < kDxT; ++tt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[tt][q] = 0.f;
+  const bool vec = (E % 8) == 0;
+  for (int e = 0; e < E; e += 8) {
+    float wv[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const size_t row = (size_t)(h + q) * E;
+      if (vec) {
+        if constexpr (WBF16) {
+          load8<true>((const uint16_t*)w_r + row, e / 8, wv[q]);
+        } else {
+          load8<false>((const float*)w_r + row, e / 8, wv[q]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float v = 0.f;
+          if (e + u < E) {
+            if constexpr (WBF16) v = bf16_to_f32(((const uint16_t*)w_r)[row + e + u]);
+            else v = ((const float*)w_r)[row + e + u];
+          }
+          wv[q][u] = v;
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < kDxT; ++tt) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float d = e + u < E ? dls[tt * E + e + u] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[tt][q] = __builtin_fmaf(d, wv[q][u], acc[tt][q]);
+      }
+    }
+  }
+  const size_t es = BF16 ? 2 : 4;
+  for (int tt = 0; tt < nt; ++tt) {
+    const int t = t0 + tt;
+    for (int j = 0; j < k; ++j) {
+      const int p = inv_pos[(size_t)t * k + j];
+      if (p < 0) continue;
+      const char* src = (const char*)dxp + ((size_t)p * H + h) * es;
+      if constexpr (BF16) {
+        const u32x2 v = *(const u32x2*)src;
+        acc[tt][0] += bf16_to_f32(v[0] & 0xFFFFu);
+        acc[tt][1] += bf16_to_f32(v[0] >> 16);
+        acc[tt][2] += bf16_to_f32(v[1] & 0xFFFFu);
+        acc[tt][3] += bf16_to_f32(v[1] >> 16);
+      } else {
+        const f32x4 v = *(const f32x4*)src;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[tt][q] += v[q];
+      }
+    }
+    char* dst = (char*)dx + ((size_t)t * H + h) * es;
+    if constexpr (BF16)
+      *(u32x2*)dst = u32x2{pack_bf16x2(acc[tt][0], acc[tt][1]), pack_bf16x2(acc[tt][2], acc[tt][3])};
+    else
+      *(f32x4*)dst = f32x4{acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]};
+  }
+}
+
+// zero fill with 16-byte stores (bytes a multiple of 16, base 16-byte aligned)
+__global__ __launch_bounds__(256) void fill_zero16(u32x4* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+int wgrad_splits(int T, int H, int E) {
+  const int blocks = ((H + kWgH - 1) / kWgH) * ((E + kWgE - 1) / kWgE);
+  const int s = std::max(1, std::min(T / 32, 256 / std::max(1, blocks)));
+  return std::max(1, std::min(s, std::max(1, T)));
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>(4096, (n + 255) / 256);
+  hipLaunchKernelGGL(fill_zero16, dim3(blocks), dim3(256), 0, s, (u32x4*)p, n);
+  return hipGetLastError();
+}
+
+size_t router_wgrad_ws_bytes(int T, int H, int E) {
+  const int S = wgrad_splits(T, H, E);
+  return align_up((size_t)S * H * E * sizeof(float)) + align_up((size_t)S * E * sizeof(float));
+}
+
+hipError_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* inv_pos,
+                              const float* w, int T, int H, int k, bool bf16, float* dw,
+                              void* dyp, hipStream_t s) {
+  const int pairs = T * k;
+  if (pairs == 0) return hipSuccess;
+  dim3 g((pairs + 3) / 4), b(256);
+  if (bf16) hipLaunchKernelGGL((combine_bwd<true>), g, b, 0, s, dy, yp, inv_pos, w, T, H, k, dw, dyp);
+  else hipLaunchKernelGGL((combine_bwd<false>), g, b, 0, s, dy, yp, inv_pos, w, T, H, k, dw, dyp);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* logits, const int32_t* ids, const float* w,
+                             const float* dw, int T, int E, int k, bool softmax_all, float* dl,
+                             hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 g((T + 3) / 4), b(256);
+  const int npl = (E + kWave - 1) / kWave;
+  const int sa = softmax_all ? 1 : 0;
+  if (npl <= 1) hipLaunchKernelGGL((router_bwd<1>), g, b, 0, s, logits, ids, w, dw, T, E, k, sa, dl);
+  else if (npl <= 2) hipLaunchKernelGGL((router_bwd<2>), g, b, 0, s, logits, ids, w, dw, T, E, k, sa, dl);
+  else if (npl <= 4) hipLaunchKernelGGL((router_bwd<4>), g, b, 0, s, logits, ids, w, dw, T, E, k, sa, dl);
+  else if (npl <= 8) hipLaunchKernelGGL((router_bwd<8>), g, b, 0, s, logits, ids, w, dw, T, E, k, sa, dl);
+  else hipLaunchKernelGGL((router_bwd<16>), g, b, 0, s, logits, ids, w, dw, T, E, k, sa, dl);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wgrad(const void* x, const float* dl, int T, int H, int E, bool x_bf16,
+                               bool w_bf16, void* dw_r, float* db_r, void* ws, hipStream_t s) {
+  const int S = wgrad_splits(T, H, E);
+  float* part = (float*)ws;
+  float* partb = (float*)((char*)ws + align_up((size_t)S * H * E * sizeof(float)));
+  const int HB = (H + kWgH - 1) / kWgH, EB = (E + kWgE - 1) / kWgE;
+  dim3 g((unsigned)(HB * EB * S)), b(256);
+  if (x_bf16) hipLaunchKernelGGL((router_wgrad<true>), g, b, 0, s, x, dl, T, H, E, S, part, partb);
+  else hipLaunchKernelGGL((router_wgrad<false>), g, b, 0, s, x, dl, T, H, E, S, part, partb);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t n = (size_t)H * E;
+  dim3 g2((unsigned)((n + 255) / 256));
+  if (w_bf16) hipLaunchKernelGGL((router_wgrad_reduce<true>), g2, b, 0, s, part, partb, H, E, S, dw_r, db_r);
+  else hipLaunchKernelGGL((router_wgrad_reduce<false>), g2, b, 0, s, part, partb, H, E, S, dw_r, db_r);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_finish(const void* dxp, const int32_t* inv_pos, const float* dl,
+                            const void* w_r, int T, int H, int E, int k, bool bf16, bool w_bf16,
+                            void* dx, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int HB = (H + kDxH - 1) / kDxH;
+  dim3 g((unsigned)(((T + kDxT - 1) / kDxT) * HB)), b(256);
+  const size_t lds = (size_t)kDxT * E * sizeof(float);
+  if (bf16) {
+    if (w_bf16) hipLaunchKernelGGL((dx_finish<true, true>), g, b, lds, s, dxp, inv_pos, dl, w_r, T, H, E, k, dx);
+    else hipLaunchKernelGGL((dx_finish<true, false>), g, b, lds, s, dxp, inv_pos, dl, w_r, T, H, E, k, dx);
+  } else {
+    hipLaunchKernelGGL((dx_finish<false, false>), g, b, lds, s, dxp, inv_pos, dl, w_r, T, H, E, k, dx);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

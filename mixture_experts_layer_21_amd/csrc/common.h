@@ -44,6 +44,20 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// d GELU / dz of the tanh form.  With s = 1 / (1 + exp(-2u)) = 0.5 (1 + tanh u),
+// GELU = z s, so GELU' = s + 2 z s (1 - s) u' with u' = sqrt(2/pi) (1 + 3 * 0.044715 z^2).
+// s (1 - s) is formed as s - s^2, which stays 0 (not inf * 0) when exp2 overflows.
+__device__ __forceinline__ float gelu_tanh_grad(float z) {
+  constexpr float c1 = -2.3022082f;        // -2 * sqrt(2/pi) * log2(e)
+  constexpr float c2 = -0.10294324f;       // c1 * 0.044715
+  constexpr float k1 = 1.5957692f;         // 2 * sqrt(2/pi)
+  constexpr float k2 = 0.21406445f;        // k1 * 3 * 0.044715
+  const float z2 = z * z;
+  const float e = __builtin_amdgcn_exp2f(z * __builtin_fmaf(c2, z2, c1));
+  const float s = __builtin_amdgcn_rcpf(1.0f + e);
+  return __builtin_fmaf(z * (s - s * s), __builtin_fmaf(k2, z2, k1), s);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

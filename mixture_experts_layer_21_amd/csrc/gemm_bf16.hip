@@ -41,7 +41,6 @@ constexpr int kWM = 2;          // waves along the token rows
 constexpr int kWN = 4;          // waves along the columns (8 waves: two per SIMD)
 constexpr int BK = 32;          // K step (bf16 elements): two 16-wide MFMA slices
 constexpr int W_STAGES = 4;     // weight ring: one K step per stage, 3 in flight
-constexpr int A_STAGES = 2;     // token ring: two K steps (128-byte rows) per stage
 constexpr int MIN_SPLIT_STEPS = 16;   // K steps per piece of a split tile, at least
 constexpr uint32_t kBufFlags = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr uint32_t kPastEnd = 0xFFFFFFF0u;    // buffer offset that reads as zero
@@ -127,20 +126,60 @@ struct Split {
   float* part;
 };
 
-// LDS of one workgroup: the two rings, one array per stage, so the compiler
-// can tell that a read of one stage does not wait on the loads into another.
+// Operand arrangements (C = A . B for each expert):
+//   NN  A [rows][K] (K contiguous) and B = W_e [K][N] (N contiguous): the
+//       forward's expert products;
+//   NT  A [rows][K] and B = W_e^T with W_e stored [N][K] (K contiguous): the
+//       backward's products with a transposed expert weight;
+//   TN  A = P_e^T and B = Q_e with P_e [K][M], Q_e [K][N] row-major, K running
+//       over the expert's dispatched rows: the expert weight gradients.
+// A K-contiguous operand is staged as rows of 128 bytes (two K steps) and
+// read with plain 16-byte LDS reads; a k-major operand is staged as 32 rows of
+// 256 columns (one K step) and read with the transposed LDS read.
+enum Kind { kNN = 0, kNT = 1, kTN = 2 };
+// epilogues each arrangement is used with (bit 1 << EP_x)
+constexpr int kind_epilogues(int kind) {
+  return kind == kNN ? (1 << EP_PLAIN) | (1 << EP_GELU)
+                     : kind == kNT ? (1 << EP_PLAIN) | (1 << EP_DGELU) : (1 << EP_PLAIN);
+}
+
+// Arguments of one grouped GEMM launch.
+struct GemmArgs {
+  const uint16_t* A;      // NN/NT: token rows [a_rows][K]; TN: P (this expert's rows first)
+  const int* gather;      // NN/NT: dispatched row p is row gather[p] of A (nullptr: row p)
+  int a_rows;             // NN/NT: rows of A
+  const uint16_t* B;      // NN: W [E][K][N]; NT: W [E][N][K]; TN: Q (this expert's rows first)
+  uint16_t* C;            // NN/NT: [R][N] dispatched rows; TN: this expert's [M][N]
+  int K, N, M;            // M: TN only (row length of P)
+  int ep;                 // epilogue (EP_PLAIN, EP_GELU, EP_DGELU)
+  const uint16_t* aux;    // EP_DGELU: z [R][N], read where C is written
+  uint16_t* zout;         // NN: also store the accumulators before GELU here ([R][N])
+};
+
+// LDS of one workgroup: one array per stage, so the compiler can tell that a
+// read of one stage does not wait on the loads into another.
+//   NN: a[0..1] token stages (32 KB), w[0..3] weight stages (16 KB)
+//   NT: a[0..1] token stages, w[0..1] transposed-weight stages (32 KB)
+//   TN: a[0..3] P stages, w[0..3] Q stages (16 KB)
+// stg: this wave's 8 KB epilogue staging area (inside the rings).
 struct Lds {
-  char* a[A_STAGES];
-  char* w[W_STAGES];
+  char* a[4];
+  char* w[4];
+  char* stg;
 };
 
 // Epilogue of one output tile from the accumulators: acc[.][j] holds 32-row
-// block jbase + j of the wave (callers have made the token ring free: no wave
-// reads it any more).
-template <int BM, int BN, int WM, int WN, int NFM, int FMA>
+// block jbase + j of the wave (callers have made the rings free: no wave
+// reads them any more).
+//   EP_PLAIN  C = acc;  EP_GELU  C = GELU(acc);
+//   EP_DGELU  C = acc * GELU'(z), z read from aux at the same row and column.
+// EPS: the epilogues this instantiation supports (bit 1 << EP_x), so that a
+// kernel carries only the code of its own.
+template <int BM, int BN, int WM, int WN, int EPS, int NFM, int FMA>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN, WM, WN>::FN][FMA],
                                            uint16_t* __restrict__ C, const Tile& tile, int N,
-                                           int gelu, const Lds& lds, int jbase = 0) {
+                                           int ep, const uint16_t* __restrict__ aux, char* stg,
+                                           int jbase = 0) {
   using S = GemmShape<BM, BN, WM, WN>;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -152,26 +191,44 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
   // Lane holds D[n][m] for m = lane%32 and 4 consecutive n.  Stored straight
   // to C, one instruction would touch 32 rows with 16 bytes each, 32 partial
   // lines; instead each wave stages 64 rows of its TM x TN block at a time
-  // (GELU applied, bf16) in its own 8 KB of the now idle token ring, 128-byte
+  // (epilogue applied, bf16) in its own 8 KB of the idle rings, 128-byte
   // rows with 16-byte chunk c of row r at c ^ (r & 7), and writes them back
   // row by row: each instruction then stores 8 whole 128-byte row pieces.
-  static_assert(S::TN * 2 == 128 && S::NW * 8192 <= A_STAGES * S::LDS_A, "staging layout");
-  char* const stg = (wave < S::NW / 2 ? lds.a[0] : lds.a[1]) + (wave % (S::NW / 2)) * 8192;
+  static_assert(S::TN * 2 == 128, "staging layout");
   if constexpr (NFM > 0) {
 #pragma unroll
     for (int p = 0; p < NFM; p += 2) {               // 2 blocks of 32 rows per pass
 #pragma unroll
       for (int j = p; j < p + 2 && j < NFM; ++j) {
         const int r = (j - p) * 32 + (lane % 32);
+        u32x2 zq[S::FN][4];
+        if ((EPS & (1 << EP_DGELU)) && ep == EP_DGELU) {
+          const int m = wrow0 + (jbase + j) * 32 + (lane % 32);
+          const int nc = n0 + wn * S::TN + 4 * (lane / 32);
+          const uint16_t* zr = aux + (size_t)(tile.row0 + min(m, tile.mrows - 1)) * N + nc;
+#pragma unroll
+          for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+              zq[i][gq] = (m < tile.mrows && nc + 32 * i + 8 * gq < N)
+                              ? *(const u32x2*)(zr + 32 * i + 8 * gq)
+                              : u32x2{0u, 0u};
+        }
 #pragma unroll
         for (int i = 0; i < S::FN; ++i) {
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
             float v0 = acc[i][j][4 * gq + 0], v1 = acc[i][j][4 * gq + 1];
             float v2 = acc[i][j][4 * gq + 2], v3 = acc[i][j][4 * gq + 3];
-            if (gelu) {
+            if ((EPS & (1 << EP_GELU)) && ep == EP_GELU) {
               v0 = gelu_tanh(v0); v1 = gelu_tanh(v1);
               v2 = gelu_tanh(v2); v3 = gelu_tanh(v3);
+            } else if ((EPS & (1 << EP_DGELU)) && ep == EP_DGELU) {
+              const u32x2 z = zq[i][gq];
+              v0 *= gelu_tanh_grad(bf16_to_f32(z[0] & 0xFFFFu));
+              v1 *= gelu_tanh_grad(bf16_to_f32(z[0] >> 16));
+              v2 *= gelu_tanh_grad(bf16_to_f32(z[1] & 0xFFFFu));
+              v3 *= gelu_tanh_grad(bf16_to_f32(z[1] >> 16));
             }
             const int c = i * 4 + gq;                // 16-byte chunk of the 128-byte row
             *(u32x2*)(stg + r * 128 + ((c ^ (r & 7)) * 16) + (lane / 32) * 8) =
@@ -198,23 +255,99 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
   }
 }
 
-// One output tile.  NFM (compile time) is the number of 32-row token blocks
-// of this wave that hold valid rows, so the main loop has no branches around
+// K-contiguous operand loader: ROWS rows of 128 bytes (two K steps) per
+// stage, row r of the stage is memory row row_of(r) (-1: none, reads zero).
+// With MASK, 8-element chunks at or past k_limit read zero (for operands
+// whose K tail would otherwise read the next row's data).
+template <int ROWS, int NW, bool MASK>
+struct RowLoader {
+  static constexpr int INSTS = ROWS * 128 / 1024 / NW;   // 1 KB per instruction
+  uint32_t voff[INSTS];
+  int dst[INSTS];
+  int ck[INSTS];          // first k of the lane's chunk inside the stage
+  const uint16_t* base;
+  uint32_t bytes;
+  int k_limit;
+  template <class RowOf>
+  __device__ __forceinline__ void init(const uint16_t* b, uint32_t nbytes, int K, int kl,
+                                       int wave, int lane, RowOf row_of) {
+    base = b;
+    bytes = nbytes;
+    k_limit = kl;
+#pragma unroll
+    for (int u = 0; u < INSTS; ++u) {
+      const int q = wave * INSTS + u;                // 8 rows per instruction
+      const int r = q * 8 + lane / 8;
+      const int c = (lane % 8) ^ swz_a(r);           // logical chunk stored at lane's slot
+      const int mr = row_of(r);
+      voff[u] = mr >= 0 ? (uint32_t)mr * K * 2 + c * 16 : kPastEnd;
+      dst[u] = q * 1024;
+      ck[u] = c * 8;
+    }
+  }
+  // K steps k0 / BK and k0 / BK + 1
+  __device__ __forceinline__ void load(int k0, char* st) const {
+    const uint32_t skip = (uint32_t)k0 * 2;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0, bytes > skip ? bytes - skip : 0u);
+#pragma unroll
+    for (int u = 0; u < INSTS; ++u) {
+      uint32_t vo = voff[u];
+      if constexpr (MASK) vo = (k0 + ck[u] < k_limit) ? vo : kPastEnd;
+      load_to_lds(r, st + dst[u], vo);
+    }
+  }
+};
+
+// k-major operand loader: 32 k rows of 256 columns (512 bytes) per stage.
+// Rows at or past k_limit read zero (the descriptor ends there); columns
+// past the operand's width read neighbouring data that feeds only outputs
+// that are never stored.
+template <int NW>
+struct ColLoader {
+  static constexpr int INSTS = 32 * 512 / 1024 / NW;     // 2 k rows per instruction
+  uint32_t voff[INSTS];
+  int dst[INSTS];
+  const uint16_t* base;
+  int ld;
+  uint32_t bytes;
+  __device__ __forceinline__ void init(const uint16_t* b, int ldim, int k_limit, int col0,
+                                       int wave, int lane) {
+    base = b;
+    ld = ldim;
+    bytes = (uint32_t)k_limit * ldim * 2;
+#pragma unroll
+    for (int u = 0; u < INSTS; ++u) {
+      const int q = wave * INSTS + u;
+      const int kr = 2 * q + lane / 32;
+      const int c = (lane % 32) ^ swz_w(kr);
+      voff[u] = (uint32_t)kr * ldim * 2 + (uint32_t)(col0 + c * 8) * 2;
+      dst[u] = q * 1024;
+    }
+  }
+  // k0 may pass the limit on the last steps: the size clamps to 0 and every
+  // load returns zero without touching memory.
+  __device__ __forceinline__ void load(int k0, char* st) const {
+    const uint32_t skip = (uint32_t)k0 * ld * 2;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(base + (size_t)k0 * ld, bytes > skip ? bytes - skip : 0u);
+#pragma unroll
+    for (int u = 0; u < INSTS; ++u) load_to_lds(r, st + dst[u], voff[u]);
+  }
+};
+
+// One output tile.  NFM (compile time) is the number of 32-row blocks of
+// this wave that hold valid rows, so the main loop has no branches around
 // its LDS reads and MFMAs (the accumulators stay in registers).
 //
 // Global loads use buffer descriptors whose base advances with k0 and whose
-// size ends at the last valid row of the tile (A) or of the weight slab (W):
-// rows past the tile and k rows past the piece's K range read as zero, so no
-// clamping or masks appear in the loop.  (Past-K columns of A read the next
-// row of the tile, or x's next row when the rows are gathered, but they meet
-// zero W rows.)  Columns past N read neighbouring data that is never stored.
-template <int BM, int BN, int WM, int WN, int NFM>
-__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
-                                          const int* __restrict__ gather, int a_rows,
-                                          const uint16_t* __restrict__ We,
-                                          uint16_t* __restrict__ C, const Tile& tile, int K,
-                                          int N, int gelu, int kt_begin, int kt_end,
-                                          const Split& sp, const Lds& lds) {
+// size ends at the last valid row of the tile (token rows) or at the piece's
+// K limit (k-major operands): rows past the tile and k rows past the piece's
+// K range read as zero, so no clamping appears in the loop.  In NN, past-K
+// columns of A read the next row of the tile (or x's next row when the rows
+// are gathered) but meet zero W rows; NT masks both operands' K tails.
+template <int KIND, int BM, int BN, int WM, int WN, int NFM>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, int kt_begin,
+                                          int kt_end, const Split& sp, const Lds& lds) {
   using S = GemmShape<BM, BN, WM, WN>;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -223,134 +356,128 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   const int wn = wave / WM;
   const int n0 = tile.nt * BN;
   const int wrow0 = wm * S::TM;
-
-  // --- loader offsets (constant over the K loop) ---------------------------
-  // Token rows: row0+m of A, or row gather[row0+m] of A when the token rows
-  // are gathered straight from x (dispatch fused into the load).  Rows past
-  // the tile get an offset past the buffer end and read as zero.
-  // (a K tail reads past the end of a row into the next one, where it meets
-  // zero W rows; contiguous A ends at the tile's last row so that the read
-  // past it returns zeros: rows beyond the tile, such as the unwritten rows of
-  // a capacity-limited dispatch, may hold any bits, NaN included)
-  const uint32_t a_bytes =
-      (uint32_t)(gather ? a_rows : min(a_rows, tile.row0 + tile.mrows)) * K * 2;
-  // W rows at or past k_limit read as zero: a split piece covers only its
-  // own K range
+  const int K = g.K, N = g.N;
   const int k_limit = min(K, kt_end * BK);
-  const uint32_t w_bytes = (uint32_t)k_limit * N * 2;
-  uint32_t a_voff[S::A_INSTS];
-  int a_dst[S::A_INSTS];
-#pragma unroll
-  for (int u = 0; u < S::A_INSTS; ++u) {
-    const int q = wave * S::A_INSTS + u;           // 8 rows per instruction
-    const int m = q * 8 + lane / 8;
-    const int c = (lane % 8) ^ swz_a(m);           // logical chunk stored at lane's slot
-    uint32_t voff = kPastEnd;
-    if (m < tile.mrows) {
-      const int grow = gather ? gather[tile.row0 + m] : tile.row0 + m;
-      voff = (uint32_t)grow * K * 2 + c * 16;
-    }
-    a_voff[u] = voff;
-    a_dst[u] = q * 1024;
-  }
-  uint32_t w_voff[S::W_INSTS];
-  int w_dst[S::W_INSTS];
-#pragma unroll
-  for (int u = 0; u < S::W_INSTS; ++u) {
-    const int q = wave * S::W_INSTS + u;           // 2 k rows per instruction
-    const int kr = 2 * q + lane / 32;
-    const int c = (lane % 32) ^ swz_w(kr);
-    w_voff[u] = (uint32_t)kr * N * 2 + (uint32_t)(n0 + c * 8) * 2;
-    w_dst[u] = q * 1024;
-  }
 
-  // k0 may pass K on the last steps: the sizes clamp to 0 and every load
-  // returns zero without touching memory.
-  auto load_w = [&](int k0, char* st) {
-    const uint32_t skip = (uint32_t)k0 * N * 2;
-    const __amdgpu_buffer_rsrc_t rw =
-        make_rsrc(We + (size_t)k0 * N, w_bytes > skip ? w_bytes - skip : 0u);
-#pragma unroll
-    for (int u = 0; u < S::W_INSTS; ++u) load_to_lds(rw, st + w_dst[u], w_voff[u]);
-  };
-  auto load_a = [&](int k0, char* st) {            // K steps k0 / BK and k0 / BK + 1
-    const uint32_t skip = (uint32_t)k0 * 2;
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(A + k0, a_bytes > skip ? a_bytes - skip : 0u);
-#pragma unroll
-    for (int u = 0; u < S::A_INSTS; ++u) load_to_lds(ra, st + a_dst[u], a_voff[u]);
-  };
+  // --- loaders (offsets constant over the K loop) ----------------------------
+  // m side: token rows (NN, NT), or P's k rows (TN)
+  // n side: W's k rows (NN), W's rows n (NT), or Q's k rows (TN)
+  RowLoader<BM, S::NW, KIND == kNT> la;
+  ColLoader<S::NW> lp;
+  ColLoader<S::NW> lw;
+  RowLoader<BN, S::NW, true> lb;
+  if constexpr (KIND != kTN) {
+    // Token rows: row0+m of A, or row gather[row0+m] of A when the token rows
+    // are gathered straight from x (dispatch fused into the load).  Contiguous
+    // A ends at the tile's last row, so that a read past it returns zeros:
+    // rows beyond the tile, such as the unwritten rows of a capacity-limited
+    // dispatch, may hold any bits, NaN included.
+    const uint32_t a_bytes =
+        (uint32_t)(g.gather ? g.a_rows : min(g.a_rows, tile.row0 + tile.mrows)) * K * 2;
+    la.init(g.A, a_bytes, K, k_limit, wave, lane, [&](int m) {
+      return m < tile.mrows ? (g.gather ? g.gather[tile.row0 + m] : tile.row0 + m) : -1;
+    });
+  } else {
+    lp.init(g.A, g.M, K, tile.row0, wave, lane);
+  }
+  const uint16_t* We = g.B + (KIND == kTN ? 0 : (size_t)tile.e * K * N);
+  if constexpr (KIND == kNT) {
+    lb.init(We, (uint32_t)N * K * 2, K, k_limit, wave, lane,
+            [&](int r) { return n0 + r < N ? n0 + r : -1; });
+  } else {
+    lw.init(We, N, k_limit, n0, wave, lane);
+  }
+  constexpr int AI = KIND == kTN ? ColLoader<S::NW>::INSTS : RowLoader<BM, S::NW, false>::INSTS;
+  constexpr int BI = KIND == kNT ? RowLoader<BN, S::NW, true>::INSTS : ColLoader<S::NW>::INSTS;
 
   // --- fragment read offsets ------------------------------------------------
-  // token operand (MFMA B): row wrow0 + 32 j + lane%32, k = 32 par + 16 h +
-  // 8 (lane/32) + 0..7 of the token stage (par: which of its two K steps)
+  // K-contiguous operand (16-byte reads): row rbase + lane%32 (+ 32 per
+  // block), k = 32 par + 16 h + 8 (lane/32) + 0..7 of the stage (par: which of
+  // its two K steps).
   const int fr = lane % 32;
-  int fa[2][2];
+  auto row_off = [&](int rbase, int (&o)[2][2]) {
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
+    for (int par = 0; par < 2; ++par)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = 4 * par + 2 * h + lane / 32;
-      fa[par][h] = (wrow0 + fr) * S::A_ROW + ((c ^ swz_a(fr)) * 16);
-    }
-  // weight operand (MFMA A, rows = columns n of W): two transposed reads per
-  // 32-column block i, for k = 16 h + 8 (g/2) + 4 rd + (0..3), g = lane/16, and
-  // column wn*TN + 32 i + 16 (g%2) + lane%16.  The block offset 4i sits in
-  // chunk bits 2..3, which the swizzle also flips, so each (h, rd, i) keeps
-  // its own offset.
-  const int g = lane / 16, li = lane % 16;
-  int fw[2][2][S::FN];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd)
-#pragma unroll
-      for (int i = 0; i < S::FN; ++i) {
-        const int kr = 16 * h + 8 * (g / 2) + 4 * rd + li / 4;
-        const int nn = wn * S::TN + 32 * i + 16 * (g % 2) + 4 * (li % 4);
-        fw[h][rd][i] = kr * S::W_ROW + (((nn / 8) ^ swz_w(kr)) * 16) + (nn % 8) * 2;
+      for (int h = 0; h < 2; ++h) {
+        const int c = 4 * par + 2 * h + lane / 32;
+        o[par][h] = (rbase + fr) * 128 + ((c ^ swz_a(fr)) * 16);
       }
-
+  };
+  // k-major operand (transposed reads): two reads per 32-column block i, for
+  // k = 16 h + 8 (g/2) + 4 rd + (0..3), g = lane/16, and column cbase + 32 i +
+  // 16 (g%2) + lane%16.  The block offset 4i sits in chunk bits 2..3, which
+  // the swizzle also flips, so each (h, rd, i) keeps its own offset.
+  const int gg = lane / 16, li = lane % 16;
+  auto col_off = [&](int cbase, auto& o, int nblk) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+        for (int i = 0; i < nblk; ++i) {
+          const int kr = 16 * h + 8 * (gg / 2) + 4 * rd + li / 4;
+          const int nn = cbase + 32 * i + 16 * (gg % 2) + 4 * (li % 4);
+          o[h][rd][i] = kr * 512 + (((nn / 8) ^ swz_w(kr)) * 16) + (nn % 8) * 2;
+        }
+  };
   constexpr int FMA = NFM > 0 ? NFM : 1;
+  int fn_row[2][2], fm_row[2][2];
+  int fn_col[2][2][S::FN], fm_col[2][2][FMA];
+  if constexpr (KIND == kNT) row_off(wn * S::TN, fn_row); else col_off(wn * S::TN, fn_col, S::FN);
+  if constexpr (KIND == kTN) col_off(wrow0, fm_col, FMA); else row_off(wrow0, fm_row);
+
   f32x16 acc[S::FN][FMA];
 #pragma unroll
   for (int i = 0; i < S::FN; ++i)
 #pragma unroll
     for (int j = 0; j < FMA; ++j) acc[i][j] = f32x16{};
 
+  // n side -> MFMA A operand (rows = output columns n), m side -> MFMA B
   auto read_frags = [&](const char* wst, const char* ast, int par, int h, bf16x8* wf,
                         bf16x8* af) {
 #pragma unroll
     for (int i = 0; i < S::FN; ++i) {
-      const u32x2 lo = read_tr(wst + fw[h][0][i]);
-      const u32x2 hi = read_tr(wst + fw[h][1][i]);
-      wf[i] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      if constexpr (KIND == kNT) {
+        wf[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(wst + fn_row[par][h] + i * 32 * 128));
+      } else {
+        const u32x2 lo = read_tr(wst + fn_col[h][0][i]);
+        const u32x2 hi = read_tr(wst + fn_col[h][1][i]);
+        wf[i] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      }
     }
 #pragma unroll
-    for (int j = 0; j < FMA; ++j)
-      af[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(ast + fa[par][h] + j * 32 * S::A_ROW));
+    for (int j = 0; j < FMA; ++j) {
+      if constexpr (KIND == kTN) {
+        const u32x2 lo = read_tr(ast + fm_col[h][0][j]);
+        const u32x2 hi = read_tr(ast + fm_col[h][1][j]);
+        af[j] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      } else {
+        af[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(ast + fm_row[par][h] + j * 32 * 128));
+      }
+    }
   };
 
-  // Software pipeline.  Step kt (local index, one K step of BK) uses weight
-  // stage kt % 4 and token stage (kt / 2) % 2, half `kt % 2` of it:
+  // Software pipeline.  Step kt (local index, one K step of BK):
   //   first half   MFMAs of slice 0 (operands already in registers), each
   //                paired with an LDS read of slice 1's operands;
   //   middle       wait for this wave's loads of step kt+1, barrier: every
   //                wave's part of step kt+1 has landed and every wave is done
-  //                reading step kt, so weight stage kt % 4 takes step kt+4
-  //                and, after an odd step, token stage (kt / 2) % 2 takes
-  //                steps kt+3 and kt+4;
+  //                reading step kt, whose stages then take new loads;
   //   second half  MFMAs of slice 1, each paired with an LDS read of step
   //                kt+1's slice-0 operands.
-  // Loads are issued in the order W(j+4) [, A(j+3, j+4) for odd j] at step j,
-  // and the prologue issues W0 W1 A01 W2 W3 A23, so (with vector-memory
-  // counts retiring in issue order) step kt+1's data is in once at most
-  //   even kt:  2 W + 2 A  (A(kt, kt+1), W(kt+2), W(kt+3), A(kt+2, kt+3))
-  //   odd kt:   1 W        (W(kt+3))
-  // loads of this wave are outstanding.  (A bare s_barrier: a release fence
-  // would wait for every outstanding load.)
+  // Stages and loads (vector-memory counts retire in issue order):
+  //   NN  W stage kt % 4, token stage (kt / 2) % 2.  Step j issues W(j+4) and,
+  //       odd j, A(j+3, j+4); the prologue W0 W1 A01 W2 W3 A23.  Step kt+1's
+  //       data is in once at most 2 W + 2 A (even kt) or 1 W (odd kt) loads
+  //       are outstanding.
+  //   NT  both stages (kt / 2) % 2.  Odd j issues A(j+3, j+4) B(j+3, j+4);
+  //       the prologue A01 B01 A23 B23.  Wait: A + B (even kt), 0 (odd kt).
+  //   TN  both stages kt % 4.  Step j issues P(j+4) Q(j+4); the prologue
+  //       P0 Q0 .. P3 Q3.  Wait: 2 (P + Q).
+  // (A bare s_barrier: a release fence would wait for every outstanding load.)
   bf16x8 wf0[S::FN], af0[FMA], wf1[S::FN], af1[FMA];
-  constexpr int NRD = 2 * S::FN + FMA;     // LDS read instructions per slice
+  constexpr int NRD = (KIND == kNT ? S::FN : 2 * S::FN) + (KIND == kTN ? 2 * FMA : FMA);
   constexpr int NMF = S::FN * NFM;         // MFMAs per slice
 
   auto mfma_slice = [&](const bf16x8* wf, const bf16x8* af) {
@@ -375,41 +502,72 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   };
 
   const int k0 = kt_begin * BK;
-  // step kt of the unrolled group of 4: weight stage ST, token stage ST / 2
+  // step kt of the unrolled group of 4
   auto step = [&](int kt, auto st_c) {
     constexpr int ST = decltype(st_c)::value;
     constexpr int PAR = ST % 2;
-    const char* wcur = lds.w[ST];
-    const char* acur = lds.a[ST / 2];
-    const char* wnxt = lds.w[(ST + 1) % W_STAGES];
-    const char* anxt = lds.a[((ST + 1) / 2) % A_STAGES];
-    read_frags(wcur, acur, PAR, 1, wf1, af1);
+    constexpr int WS = KIND == kNT ? ST / 2 : ST;              // n-side stage
+    constexpr int WN1 = KIND == kNT ? ((ST + 1) / 2) % 2 : (ST + 1) % 4;
+    constexpr int AS = KIND == kTN ? ST : ST / 2;              // m-side stage
+    constexpr int AN1 = KIND == kTN ? (ST + 1) % 4 : ((ST + 1) / 2) % 2;
+    read_frags(lds.w[WS], lds.a[AS], PAR, 1, wf1, af1);
     mfma_slice(wf0, af0);
     interleave();
-    if constexpr (PAR == 0)
-      __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * S::W_INSTS + 2 * S::A_INSTS));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_le(S::W_INSTS));
+    if constexpr (KIND == kNN) {
+      if constexpr (PAR == 0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * BI + 2 * AI));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_le(BI));
+    } else if constexpr (KIND == kNT) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(PAR == 0 ? AI + BI : 0));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * (AI + BI)));
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): reads of step kt done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    load_w(k0 + (kt + W_STAGES) * BK, lds.w[ST]);
-    if constexpr (PAR == 1) load_a(k0 + (kt + 3) * BK, lds.a[ST / 2]);
-    read_frags(wnxt, anxt, 1 - PAR, 0, wf0, af0);
+    if constexpr (KIND == kNN) {
+      lw.load(k0 + (kt + W_STAGES) * BK, lds.w[ST]);
+      if constexpr (PAR == 1) la.load(k0 + (kt + 3) * BK, lds.a[ST / 2]);
+    } else if constexpr (KIND == kNT) {
+      if constexpr (PAR == 1) {
+        la.load(k0 + (kt + 3) * BK, lds.a[ST / 2]);
+        lb.load(k0 + (kt + 3) * BK, lds.w[ST / 2]);
+      }
+    } else {
+      lp.load(k0 + (kt + 4) * BK, lds.a[ST]);
+      lw.load(k0 + (kt + 4) * BK, lds.w[ST]);
+    }
+    read_frags(lds.w[WN1], lds.a[AN1], 1 - PAR, 0, wf0, af0);
     mfma_slice(wf1, af1);
     interleave();
   };
 
   // The loop runs a multiple of 4 steps; steps past the K range meet zero
-  // weight rows and add nothing.
-  load_w(k0, lds.w[0]);
-  load_w(k0 + BK, lds.w[1]);
-  load_a(k0, lds.a[0]);
-  load_w(k0 + 2 * BK, lds.w[2]);
-  load_w(k0 + 3 * BK, lds.w[3]);
-  load_a(k0 + 2 * BK, lds.a[1]);
-  // step 0's data (W0, A01) is in once W2, W3, A23 alone are outstanding
-  __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * S::W_INSTS + S::A_INSTS));
+  // rows (or zero chunks) and add nothing.
+  if constexpr (KIND == kNN) {
+    lw.load(k0, lds.w[0]);
+    lw.load(k0 + BK, lds.w[1]);
+    la.load(k0, lds.a[0]);
+    lw.load(k0 + 2 * BK, lds.w[2]);
+    lw.load(k0 + 3 * BK, lds.w[3]);
+    la.load(k0 + 2 * BK, lds.a[1]);
+    // step 0's data (W0, A01) is in once W2, W3, A23 alone are outstanding
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * BI + AI));
+  } else if constexpr (KIND == kNT) {
+    la.load(k0, lds.a[0]);
+    lb.load(k0, lds.w[0]);
+    la.load(k0 + 2 * BK, lds.a[1]);
+    lb.load(k0 + 2 * BK, lds.w[1]);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(AI + BI));
+  } else {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      lp.load(k0 + s4 * BK, lds.a[s4]);
+      lw.load(k0 + s4 * BK, lds.w[s4]);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * (AI + BI)));
+  }
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   read_frags(lds.w[0], lds.a[0], 0, 0, wf0, af0);
@@ -443,29 +601,25 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ A,
   // one barrier first, because other waves may still read the K loop's last
   // stages
   __syncthreads();
-  store_tile<BM, BN, WM, WN, NFM>(acc, C, tile, N, gelu, lds);
-
+  constexpr int EPS = kind_epilogues(KIND);
+  if constexpr (KIND == kNN)
+    if (g.zout) store_tile<BM, BN, WM, WN, 1, NFM>(acc, g.zout, tile, N, EP_PLAIN, nullptr, lds.stg);
+  store_tile<BM, BN, WM, WN, EPS, NFM>(acc, g.C, tile, N, g.ep, g.aux, lds.stg);
 }
 
 // gemm_tile with NFM = nfm (0 <= nfm <= NF), chosen at run time from a
 // wave-uniform count.
-template <int BM, int BN, int WM, int WN, int NF>
-__device__ __forceinline__ void run_tile(int nfm, const uint16_t* __restrict__ A,
-                                         const int* __restrict__ gather, int a_rows,
-                                         const uint16_t* __restrict__ We,
-                                         uint16_t* __restrict__ C, const Tile& tile, int K,
-                                         int N, int gelu, int kt_begin, int kt_end,
-                                         const Split& sp, const Lds& lds) {
+template <int KIND, int BM, int BN, int WM, int WN, int NF>
+__device__ __forceinline__ void run_tile(int nfm, const GemmArgs& g, const Tile& tile,
+                                         int kt_begin, int kt_end, const Split& sp,
+                                         const Lds& lds) {
   if constexpr (NF == 0) {
-    gemm_tile<BM, BN, WM, WN, 0>(A, gather, a_rows, We, C, tile, K, N, gelu, kt_begin, kt_end,
-                                 sp, lds);
+    gemm_tile<KIND, BM, BN, WM, WN, 0>(g, tile, kt_begin, kt_end, sp, lds);
   } else {
     if (nfm == NF)
-      gemm_tile<BM, BN, WM, WN, NF>(A, gather, a_rows, We, C, tile, K, N, gelu, kt_begin,
-                                    kt_end, sp, lds);
+      gemm_tile<KIND, BM, BN, WM, WN, NF>(g, tile, kt_begin, kt_end, sp, lds);
     else
-      run_tile<BM, BN, WM, WN, NF - 1>(nfm, A, gather, a_rows, We, C, tile, K, N, gelu,
-                                       kt_begin, kt_end, sp, lds);
+      run_tile<KIND, BM, BN, WM, WN, NF - 1>(nfm, g, tile, kt_begin, kt_end, sp, lds);
   }
 }
 
@@ -496,21 +650,32 @@ __device__ __forceinline__ SplitPlan split_plan(const int* __restrict__ off, int
   return pl;
 }
 
-template <int BM, int BN, int WM, int WN>
+// this wave's 8 KB of epilogue staging inside two 32 KB regions
+__device__ __forceinline__ char* staging(char* lo, char* hi, int nw) {
+  const int wave = threadIdx.x / kWave;
+  return (wave < nw / 2 ? lo : hi) + (wave % (nw / 2)) * 8192;
+}
+
+// Grouped GEMM over dispatched rows (NN: the forward's expert products; NT:
+// the backward's products with transposed expert weights).
+template <int KIND, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_grouped(
-    const uint16_t* __restrict__ A, const int* __restrict__ gather, int a_rows,
-    const uint16_t* __restrict__ W, uint16_t* __restrict__ C, const int* __restrict__ off,
-    int E, int R, int K, int N, int gelu, float* __restrict__ part, int slots) {
+    GemmArgs g, const int* __restrict__ off, int E, int R, float* __restrict__ part,
+    int slots) {
   using S = GemmShape<BM, BN, WM, WN>;
+  static_assert(KIND != kTN, "TN has its own kernel");
   __shared__ __attribute__((aligned(1024))) char a0[S::LDS_A];
   __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
-  __shared__ __attribute__((aligned(1024))) char w0[S::LDS_W];
-  __shared__ __attribute__((aligned(1024))) char w1[S::LDS_W];
-  __shared__ __attribute__((aligned(1024))) char w2[S::LDS_W];
-  __shared__ __attribute__((aligned(1024))) char w3[S::LDS_W];
-  const Lds lds{{a0, a1}, {w0, w1, w2, w3}};
+  constexpr int WB = KIND == kNT ? S::LDS_A : S::LDS_W;       // n-side stage bytes
+  constexpr int WST = KIND == kNT ? 2 : 4;
+  __shared__ __attribute__((aligned(1024))) char w0[WB];
+  __shared__ __attribute__((aligned(1024))) char w1[WB];
+  __shared__ __attribute__((aligned(1024))) char w2[WST == 4 ? WB : 1];
+  __shared__ __attribute__((aligned(1024))) char w3[WST == 4 ? WB : 1];
+  static_assert(S::NW * 8192 <= 2 * S::LDS_A, "staging layout");
+  const Lds lds{{a0, a1, nullptr, nullptr}, {w0, w1, w2, w3}, staging(a0, a1, S::NW)};
 
-  const SplitPlan pl = split_plan<BM, BN>(off, E, R, K, N, slots);
+  const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots);
   const int bid = blockIdx.x;
   int L, kt_begin = 0, kt_end = pl.KT;
   Split sp{1, 0, 0, part};
@@ -526,34 +691,90 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     kt_begin = sp.s * pl.KT / pl.nsplit;
     kt_end = (sp.s + 1) * pl.KT / pl.nsplit;
   }
-  const int NTN = (N + BN - 1) / BN;
+  const int NTN = (g.N + BN - 1) / BN;
   const Tile tile = lookup_tile(off, E, R, BM, NTN, L);
   if (!tile.valid) return;
-  const uint16_t* We = W + (size_t)tile.e * K * N;
 
   // 32-row token blocks of this wave that hold valid rows (wave-uniform)
   const int wm = (threadIdx.x / kWave) % WM;
   int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
   nfm = __builtin_amdgcn_readfirstlane(nfm);
-  run_tile<BM, BN, WM, WN, S::FM>(nfm, A, gather, a_rows, We, C, tile, K, N, gelu, kt_begin,
-                                  kt_end, sp, lds);
+  run_tile<KIND, BM, BN, WM, WN, S::FM>(nfm, g, tile, kt_begin, kt_end, sp, lds);
+}
+
+// Expert weight gradients: C_e[M][N] = P_e^T Q_e for every expert e, where
+// P_e and Q_e are rows [off[e], off[e+1]) of P [R][M] and Q [R][N].  One
+// 256x256 tile of one expert per workgroup; K = the expert's row count (an
+// expert with no rows gets a zero gradient).  Tiles are numbered expert by
+// expert, column tile outer and row tile inner, then dealt to the XCDs in
+// contiguous runs (xcd_remap).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_wgrad(
+    const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, uint16_t* __restrict__ C,
+    const int* __restrict__ off, int E, int M, int N) {
+  using S = GemmShape<BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(1024))) char p0[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char p1[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char p2[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char p3[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char q0[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char q1[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char q2[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char q3[S::LDS_W];
+  // staging: waves 0..1 in p0, 2..3 in p1, 4..5 in p2, 6..7 in p3
+  static_assert(S::NW == 8 && S::LDS_W == 16384, "staging layout");
+  const int wave = threadIdx.x / kWave;
+  char* const sbase = wave < 2 ? p0 : wave < 4 ? p1 : wave < 6 ? p2 : p3;
+  const Lds lds{{p0, p1, p2, p3}, {q0, q1, q2, q3}, sbase + (wave % 2) * 8192};
+
+  const int MT = (M + BM - 1) / BM, NTN = (N + BN - 1) / BN;
+  const int per_e = MT * NTN;
+  const int L = xcd_remap(blockIdx.x, E * per_e);
+  if (L < 0) return;
+  const int e = L / per_e, r = L % per_e;
+  Tile tile;
+  tile.valid = 1;
+  tile.e = e;
+  tile.row0 = (r % MT) * BM;
+  tile.mrows = min(BM, M - tile.row0);
+  tile.nt = r / MT;
+  const int kb = off[e];
+  const int rows = off[e + 1] - kb;
+  GemmArgs g;
+  g.A = P + (size_t)kb * M;
+  g.gather = nullptr;
+  g.a_rows = 0;
+  g.B = Q + (size_t)kb * N;
+  g.C = C + (size_t)e * M * N;
+  g.K = rows;
+  g.N = N;
+  g.M = M;
+  g.ep = EP_PLAIN;
+  g.aux = nullptr;
+  g.zout = nullptr;
+  const int wm = wave % WM;
+  int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
+  nfm = __builtin_amdgcn_readfirstlane(nfm);
+  const Split sp{1, 0, 0, nullptr};
+  run_tile<kTN, BM, BN, WM, WN, S::FM>(nfm, g, tile, 0, (rows + BK - 1) / BK, sp, lds);
 }
 
 // Split tiles: one workgroup per (split tile, 32-row block jb of every
 // wave).  Each wave adds the S partials of its block in split order, two
-// pieces' loads in flight per round trip, and stores the block.
-template <int BM, int BN, int WM, int WN>
+// pieces' loads in flight per round trip, and stores the block (with the
+// launch's epilogue; zout as in the GEMM).
+template <int KIND, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
-    uint16_t* __restrict__ C, const int* __restrict__ off, int E, int R, int K, int N,
-    int gelu, const float* __restrict__ part, int slots) {
+    GemmArgs g, const int* __restrict__ off, int E, int R, const float* __restrict__ part,
+    int slots) {
   using S = GemmShape<BM, BN, WM, WN>;
   __shared__ __attribute__((aligned(1024))) char a0[S::LDS_A];
   __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
-  const Lds lds{{a0, a1}, {nullptr, nullptr, nullptr, nullptr}};
-  const SplitPlan pl = split_plan<BM, BN>(off, E, R, K, N, slots);
+  char* const stg = staging(a0, a1, S::NW);
+  const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots);
   const int slot = blockIdx.x / S::FM, jb = blockIdx.x % S::FM;
   if (pl.nsplit < 2 || slot >= pl.sk) return;
-  const int NTN = (N + BN - 1) / BN;
+  const int NTN = (g.N + BN - 1) / BN;
   const Tile tile = lookup_tile(off, E, R, BM, NTN, pl.dp + slot);
   if (!tile.valid) return;
   const int tid = threadIdx.x;
@@ -591,7 +812,9 @@ __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
     for (int vq = 0; vq < 4; ++vq)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][0][4 * vq + e] = run[i][vq][e];
-  store_tile<BM, BN, WM, WN, 1>(acc, C, tile, N, gelu, lds, jb);
+  if constexpr (KIND == kNN)
+    if (g.zout) store_tile<BM, BN, WM, WN, 1, 1>(acc, g.zout, tile, g.N, EP_PLAIN, nullptr, stg, jb);
+  store_tile<BM, BN, WM, WN, kind_epilogues(KIND), 1>(acc, g.C, tile, g.N, g.ep, g.aux, stg, jb);
 }
 
 int device_slots() {
@@ -609,11 +832,10 @@ int device_slots() {
   return cached[dev];
 }
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_cfg(const void* A, const int* gather, int a_rows, const void* W, void* C,
-                      const int* off, int E, int R, int K, int N, bool gelu, void* split_ws,
+template <int KIND, int BM, int BN, int WM, int WN>
+hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* split_ws,
                       hipStream_t s) {
-  const int NTN = (N + BN - 1) / BN;
+  const int NTN = (g.N + BN - 1) / BN;
   // upper bound of row tiles: sum_e ceil(rows_e / BM) <= ceil(R / BM) + min(E, R)
   const long mt_max = off ? (long)(R + BM - 1) / BM + (long)min(E, R) : (long)(R + BM - 1) / BM;
   const int slots = device_slots();
@@ -621,18 +843,15 @@ hipError_t launch_cfg(const void* A, const int* gather, int a_rows, const void* 
   long blocks = mt_max * NTN + slots;
   if (blocks <= slots) return hipSuccess;
   float* part = (float*)split_ws;
-  hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN>), dim3((unsigned)blocks),
-                     dim3(kWave * WM * WN), 0, s, (const uint16_t*)A, gather, a_rows,
-                     (const uint16_t*)W, (uint16_t*)C, off, E, R, K, N, gelu ? 1 : 0, part,
-                     slots);
+  hipLaunchKernelGGL((gemm_bf16_grouped<KIND, BM, BN, WM, WN>), dim3((unsigned)blocks),
+                     dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // tiles are split only when K has at least 4 * MIN_SPLIT_STEPS steps
-  if ((K + BK - 1) / BK >= 4 * MIN_SPLIT_STEPS) {
-    hipLaunchKernelGGL((gemm_split_reduce<BM, BN, WM, WN>),
+  if ((g.K + BK - 1) / BK >= 4 * MIN_SPLIT_STEPS) {
+    hipLaunchKernelGGL((gemm_split_reduce<KIND, BM, BN, WM, WN>),
                        dim3(kMaxSlots / 2 * GemmShape<BM, BN, WM, WN>::FM),
-                       dim3(kWave * WM * WN), 0, s, (uint16_t*)C, off, E, R, K, N,
-                       gelu ? 1 : 0, (const float*)part, slots);
+                       dim3(kWave * WM * WN), 0, s, g, off, E, R, (const float*)part, slots);
     err = hipGetLastError();
   }
   return err;
@@ -643,10 +862,34 @@ hipError_t launch_cfg(const void* A, const int* gather, int a_rows, const void* 
 size_t split_ws_bytes() { return (size_t)kMaxSlots * 256 * 256 * sizeof(float); }
 
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
-                            void* C, const int* off, int E, int R, int K, int N, bool gelu,
-                            void* split_ws, hipStream_t s) {
-  return launch_cfg<256, 256, kWM, kWN>(A, gather, a_rows, W, C, off, E, R, K, N, gelu,
-                                              split_ws, s);
+                            bool w_nk, void* C, const int* off, int E, int R, int K, int N,
+                            int ep, const void* aux, void* zout, void* split_ws,
+                            hipStream_t s) {
+  GemmArgs g;
+  g.A = (const uint16_t*)A;
+  g.gather = gather;
+  g.a_rows = a_rows;
+  g.B = (const uint16_t*)W;
+  g.C = (uint16_t*)C;
+  g.K = K;
+  g.N = N;
+  g.M = 0;
+  g.ep = ep;
+  g.aux = (const uint16_t*)aux;
+  g.zout = (uint16_t*)zout;
+  if (w_nk) return launch_cfg<kNT, 256, 256, kWM, kWN>(g, off, E, R, split_ws, s);
+  return launch_cfg<kNN, 256, 256, kWM, kWN>(g, off, E, R, split_ws, s);
+}
+
+hipError_t launch_gemm_bf16_wgrad(const void* P, const void* Q, void* C, const int* off, int E,
+                                  int M, int N, hipStream_t s) {
+  const long tiles = (long)E * ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles == 0) return hipSuccess;
+  const long blocks = (tiles + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((gemm_bf16_wgrad<256, 256, kWM, kWN>), dim3((unsigned)blocks),
+                     dim3(kWave * kWM * kWN), 0, s, (const uint16_t*)P, (const uint16_t*)Q,
+                     (uint16_t*)C, off, E, M, N);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -22,10 +22,11 @@ RoutePlan plan_route(int T, int H, int E, bool bf16, bool wf32);
 // enough for either router weight type
 size_t route_ws_bytes(int T, int H, int E, bool bf16);
 // softmax_all: gate weights are the top-k probabilities of the softmax over
-// all E logits (not renormalised); otherwise the softmax of the k winners
+// all E logits (not renormalised); otherwise the softmax of the k winners.
+// logits != nullptr: the fp32 logits [T,E] (bias included) are kept there.
 hipError_t launch_route(const void* x, const void* w_r, const float* bias, int T, int H,
                         int E, int k, bool bf16, bool wf32, bool softmax_all, int32_t* ids,
-                        float* w, void* ws, hipStream_t s);
+                        float* w, float* logits, void* ws, hipStream_t s);
 
 size_t permute_ws_bytes(int R, int E);
 // xp == nullptr: indices only (the rows are gathered later by the GEMM).
@@ -41,15 +42,59 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
 // the stream; nothing in it needs clearing).
 constexpr int kMaxSlots = 256;
 size_t split_ws_bytes();
-// A holds a_rows rows of K; with gather != nullptr, dispatched row p is row
-// gather[p] of A (the dispatch fused into the GEMM's loads), else row p.
+// GEMM epilogues: C = acc, GELU(acc), or acc * GELU'(z) with z read from an
+// [R][N] matrix at the place C is written.
+enum Epilogue { EP_PLAIN = 0, EP_GELU = 1, EP_DGELU = 2 };
+// C[rows_e] = epilogue(A[rows_e] . B_e) for every expert e.  A holds a_rows
+// rows of K; with gather != nullptr, dispatched row p is row gather[p] of A
+// (the dispatch fused into the GEMM's loads), else row p.  B_e is W[e] as
+// [K][N] (w_nk false) or its transpose, W[e] stored [N][K] (w_nk true).
+// zout != nullptr: the accumulators are also stored there before the
+// epilogue (the pre-activation a training forward keeps).
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
-                            void* C, const int* off, int E, int R, int K, int N, bool gelu,
-                            void* split_ws, hipStream_t s);
+                            bool w_nk, void* C, const int* off, int E, int R, int K, int N,
+                            int ep, const void* aux, void* zout, void* split_ws,
+                            hipStream_t s);
+// C[e] = P_e^T . Q_e ([M][N] per expert) with P_e, Q_e the rows
+// [off[e], off[e+1]) of P [R][M] and Q [R][N] (expert weight gradients).
+hipError_t launch_gemm_bf16_wgrad(const void* P, const void* Q, void* C, const int* off, int E,
+                                  int M, int N, hipStream_t s);
+// zout != nullptr: the accumulators are also stored there before GELU
 hipError_t launch_gemm_f32(const float* A, const float* W, float* C, const int* off, int E,
-                           int R, int K, int N, int ldc, bool gelu, hipStream_t s);
+                           int R, int K, int N, int ldc, bool gelu, float* zout, hipStream_t s);
+// C[rows_e] = A[rows_e] . W_e^T with W stored [E][N][K]; with dgelu_z != nullptr
+// the result is multiplied by GELU'(dgelu_z) ([R][N], like C)
+hipError_t launch_gemm_f32_nt(const float* A, const float* W, float* C, const int* off, int E,
+                              int R, int K, int N, const float* dgelu_z, hipStream_t s);
+// C[e] = P_e^T . Q_e ([M][N] per expert), rows [off[e], off[e+1]) of P [R][M], Q [R][N]
+hipError_t launch_gemm_f32_wgrad(const float* P, const float* Q, float* C, const int* off, int E,
+                                 int M, int N, hipStream_t s);
 
 hipError_t launch_combine(const void* yp, const int32_t* inv_pos, const float* w, int T,
                           int H, int k, bool bf16, void* y, hipStream_t s);
+
+// xp[p] = x[sorted_token[p]] for the rows p < offsets[E] (grid sized by R)
+hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, const int32_t* offsets,
+                              int E, int R, int H, size_t elem_bytes, void* xp, hipStream_t s);
+
+// Backward kernels (backward.hip)
+// zero `bytes` (a multiple of 16) at p (16-byte aligned) with a kernel
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+size_t router_wgrad_ws_bytes(int T, int H, int E);
+// dw[T*k] = dy[t] . yp[p] and dyp[p] = w * dy[t] for every kept pair
+hipError_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* inv_pos,
+                              const float* w, int T, int H, int k, bool bf16, float* dw,
+                              void* dyp, hipStream_t s);
+// dl[T,E] (fp32, dense) from the gate weights' gradient dw
+hipError_t launch_router_bwd(const float* logits, const int32_t* ids, const float* w,
+                             const float* dw, int T, int E, int k, bool softmax_all, float* dl,
+                             hipStream_t s);
+// dW_r = x^T dl (W_r's type), db_r = sum_t dl (skipped when db_r is null)
+hipError_t launch_router_wgrad(const void* x, const float* dl, int T, int H, int E, bool x_bf16,
+                               bool w_bf16, void* dw_r, float* db_r, void* ws, hipStream_t s);
+// dx[t] = sum_j dxp[inv_pos[t,j]] + dl[t] . W_r^T
+hipError_t launch_dx_finish(const void* dxp, const int32_t* inv_pos, const float* dl,
+                            const void* w_r, int T, int H, int E, int k, bool bf16, bool w_bf16,
+                            void* dx, hipStream_t s);
 
 }  // namespace moe

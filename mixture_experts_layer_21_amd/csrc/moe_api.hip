@@ -1,5 +1,5 @@
-// C ABI of the MoE layer forward: host-side validation, workspace layout and
-// the launch sequence.  Every entry point validates all of its arguments
+// C ABI of the MoE layer forward and backward: host-side validation,
+// workspace layouts and the launch sequences.  Every entry point validates all of its arguments
 // before enqueueing anything, so an error return leaves the device untouched.
 #include "moe.h"
 
@@ -80,27 +80,79 @@ moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E
 
 // Expert FFN.  The first GEMM reads its token rows from xp (a_rows = R rows,
 // gather == nullptr) or straight from x through gather = sorted_token
-// (a_rows = T rows).
+// (a_rows = T rows); h[R,F] takes GELU(z) and, when z != nullptr, z[R,F] the
+// pre-activation; split is the bf16 GEMM's split-tile workspace.
 moe_status run_ffn(const void* xp, const int32_t* gather, int64_t a_rows, const int32_t* off,
                    const void* w1, const void* w2, int64_t R, int64_t H, int64_t E, int64_t F,
-                   moe_dtype dt, void* yp, void* h, hipStream_t s) {
+                   moe_dtype dt, void* yp, void* h, void* z, void* split, hipStream_t s) {
   if (R == 0) return MOE_OK;
   hipError_t err;
   if (dt == MOE_BF16) {
-    void* split = (char*)h + align_up((size_t)R * F * elem_bytes(dt));
-    err = moe::launch_gemm_bf16(xp, gather, (int)a_rows, w1, h, off, (int)E, (int)R, (int)H,
-                                  (int)F, true, split, s);
+    err = moe::launch_gemm_bf16(xp, gather, (int)a_rows, w1, false, h, off, (int)E, (int)R,
+                                (int)H, (int)F, moe::EP_GELU, nullptr, z, split, s);
     if (err == hipSuccess)
-      err = moe::launch_gemm_bf16(h, nullptr, (int)R, w2, yp, off, (int)E, (int)R, (int)F,
-                                  (int)H, false, split, s);
+      err = moe::launch_gemm_bf16(h, nullptr, (int)R, w2, false, yp, off, (int)E, (int)R,
+                                  (int)F, (int)H, moe::EP_PLAIN, nullptr, nullptr, split, s);
   } else {
     err = moe::launch_gemm_f32((const float*)xp, (const float*)w1, (float*)h, off, (int)E,
-                               (int)R, (int)H, (int)F, (int)F, true, s);
+                               (int)R, (int)H, (int)F, (int)F, true, (float*)z, s);
     if (err == hipSuccess)
       err = moe::launch_gemm_f32((const float*)h, (const float*)w2, (float*)yp, off, (int)E,
-                                 (int)R, (int)F, (int)H, (int)H, false, s);
+                                 (int)R, (int)F, (int)H, (int)H, false, nullptr, s);
   }
   return launch_status(err);
+}
+
+// h[R,F] then the split workspace, inside an expert-FFN workspace
+void* ffn_split(void* ws, int64_t R, int64_t F, moe_dtype dt) {
+  return (char*)ws + align_up((size_t)R * F * elem_bytes(dt));
+}
+
+// State a training forward keeps for the backward (caller-owned, opaque):
+// dispatch indices, the fp32 logits, z and h of the first expert GEMM and
+// the expert outputs yp.
+struct SavedLayout {
+  size_t offsets, sorted, inv, logits, z, h, yp, total;
+};
+
+SavedLayout saved_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_dtype dt) {
+  const int64_t R = T * k;
+  const size_t es = elem_bytes(dt);
+  SavedLayout L;
+  size_t o = 0;
+  L.offsets = o; o += align_up((size_t)(E + 1) * 4);
+  L.sorted = o;  o += align_up((size_t)R * 4);
+  L.inv = o;     o += align_up((size_t)R * 4);
+  L.logits = o;  o += align_up((size_t)T * E * 4);
+  L.z = o;       o += align_up((size_t)R * F * es);
+  L.h = o;       o += align_up((size_t)R * F * es);
+  L.yp = o;      o += align_up((size_t)R * H * es);
+  L.total = o;
+  return L;
+}
+
+// moe_backward workspace: gate-weight and logit gradients, dyp (later dxp),
+// dz, the re-gathered token rows xp, and one region shared in time by the
+// router weight gradient's partials and the GEMMs' split-tile partials.
+struct BwdLayout {
+  size_t dw, dl, dyp, dz, xp, stage, total;
+};
+
+BwdLayout bwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_dtype dt) {
+  const int64_t R = T * k;
+  const size_t es = elem_bytes(dt);
+  BwdLayout L;
+  size_t o = 0;
+  L.dw = o;    o += align_up((size_t)R * 4);
+  L.dl = o;    o += align_up((size_t)T * E * 4);
+  L.dyp = o;   o += align_up((size_t)R * H * es);
+  L.dz = o;    o += align_up((size_t)R * F * es);
+  L.xp = o;    o += align_up((size_t)R * H * es);
+  L.stage = o;
+  size_t st = moe::router_wgrad_ws_bytes((int)T, (int)H, (int)E);
+  if (dt == MOE_BF16) st = std::max(st, moe::split_ws_bytes());
+  L.total = o + st;
+  return L;
 }
 
 }  // namespace
@@ -186,8 +238,8 @@ moe_status moe_route_ex(const void* x, const void* w_r, const float* router_bias
   if (T == 0) return MOE_OK;
   return launch_status(moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k,
                                          dtype == MOE_BF16, router_dtype != dtype,
-                                         gating == MOE_GATE_SOFTMAX_TOPK, topk_ids, topk_w, ws,
-                                         (hipStream_t)stream));
+                                         gating == MOE_GATE_SOFTMAX_TOPK, topk_ids, topk_w,
+                                         nullptr, ws, (hipStream_t)stream));
 }
 
 moe_status moe_route(const void* x, const void* w_r, const float* router_bias, int64_t T,
@@ -226,8 +278,8 @@ moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets, const v
   if (st != MOE_OK) return st;
   if (!xp || !expert_offsets || !w1 || !w2 || !yp || !ws) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < ffn_ws_bytes(R, F, dtype)) return MOE_ERR_INVALID_ARG;
-  return run_ffn(xp, nullptr, R, expert_offsets, w1, w2, R, H, E, F, dtype, yp, ws,
-                 (hipStream_t)stream);
+  return run_ffn(xp, nullptr, R, expert_offsets, w1, w2, R, H, E, F, dtype, yp, ws, nullptr,
+                 ffn_split(ws, R, F, dtype), (hipStream_t)stream);
 }
 
 moe_status moe_combine(const void* yp, const int32_t* inv_pos, const float* topk_w, int64_t T,
@@ -268,7 +320,7 @@ moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bi
 
   hipError_t err = moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k, bf16,
                                      router_dtype != dtype, gating == MOE_GATE_SOFTMAX_TOPK,
-                                     ids, w, stage, s);
+                                     ids, w, nullptr, stage, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
   // bf16: the first expert GEMM gathers the token rows from x itself, so the
   // dispatch only builds the indices; fp32 copies the rows into xp.  With a
@@ -277,8 +329,10 @@ moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bi
   err = moe::launch_permute(x, ids, (int)T, (int)H, (int)E, top_k, capacity, elem_bytes(dtype),
                             off, sorted, inv, bf16 ? nullptr : xp, stage, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
-  const moe_status fs = bf16 ? run_ffn(x, sorted, T, off, w1, w2, R, H, E, F, dtype, yp, stage, s)
-                             : run_ffn(xp, nullptr, R, off, w1, w2, R, H, E, F, dtype, yp, stage, s);
+  void* split = ffn_split(stage, R, F, dtype);
+  const moe_status fs =
+      bf16 ? run_ffn(x, sorted, T, off, w1, w2, R, H, E, F, dtype, yp, stage, nullptr, split, s)
+           : run_ffn(xp, nullptr, R, off, w1, w2, R, H, E, F, dtype, yp, stage, nullptr, split, s);
   if (fs != MOE_OK) return fs;
   return launch_status(moe::launch_combine(yp, inv, w, (int)T, (int)H, top_k, bf16, y, s));
 }
@@ -290,6 +344,158 @@ moe_status moe_forward(const void* x, const void* w_r, const float* router_bias,
   return moe_forward_ex(x, w_r, router_bias, w1, w2, T, H, E, top_k, F, dtype, dtype,
                         MOE_GATE_TOPK_SOFTMAX, 0, y, topk_ids_out, topk_w_out, ws, ws_bytes,
                         stream);
+}
+
+moe_status moe_saved_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k, int64_t F,
+                           moe_dtype dtype, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  const moe_status st = check_shape(T, H, E, top_k, F, dtype);
+  if (st != MOE_OK) return st;
+  *bytes = saved_layout(T, H, E, top_k, F, dtype).total;
+  return MOE_OK;
+}
+
+moe_status moe_backward_workspace_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k,
+                                        int64_t F, moe_dtype dtype, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  const moe_status st = check_shape(T, H, E, top_k, F, dtype);
+  if (st != MOE_OK) return st;
+  *bytes = bwd_layout(T, H, E, top_k, F, dtype).total;
+  return MOE_OK;
+}
+
+moe_status moe_forward_train(const void* x, const void* w_r, const float* router_bias,
+                             const void* w1, const void* w2, int64_t T, int64_t H, int64_t E,
+                             int32_t top_k, int64_t F, moe_dtype dtype, moe_dtype router_dtype,
+                             moe_gating gating, int32_t capacity, void* y, int32_t* topk_ids,
+                             float* topk_w, void* saved, size_t saved_bytes, void* ws,
+                             size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(T, H, E, top_k, F, dtype);
+  if (st != MOE_OK) return st;
+  st = check_router(dtype, router_dtype, gating);
+  if (st != MOE_OK) return st;
+  // (buffers of T rows are empty, and may be NULL, when T == 0)
+  if (!w_r || !w1 || !w2 || !saved || !ws) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !y || !topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
+  const FwdLayout L = fwd_layout(T, H, E, top_k, F, dtype);
+  const SavedLayout V = saved_layout(T, H, E, top_k, F, dtype);
+  if (ws_bytes < L.total || saved_bytes < V.total) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  char* sv = (char*)saved;
+  int32_t* off = (int32_t*)(sv + V.offsets);
+  int32_t* sorted = (int32_t*)(sv + V.sorted);
+  int32_t* inv = (int32_t*)(sv + V.inv);
+  float* logits = (float*)(sv + V.logits);
+  void* xp = base + L.xp;
+  void* stage = base + L.stage;
+  const bool bf16 = dtype == MOE_BF16;
+  const int64_t R = T * top_k;
+
+  hipError_t err = moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k, bf16,
+                                     router_dtype != dtype, gating == MOE_GATE_SOFTMAX_TOPK,
+                                     topk_ids, topk_w, logits, stage, s);
+  if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  err = moe::launch_permute(x, topk_ids, (int)T, (int)H, (int)E, top_k, capacity,
+                            elem_bytes(dtype), off, sorted, inv, bf16 ? nullptr : xp, stage, s);
+  if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  void* h = sv + V.h;
+  void* z = sv + V.z;
+  void* yp = sv + V.yp;
+  const moe_status fs =
+      bf16 ? run_ffn(x, sorted, T, off, w1, w2, R, H, E, F, dtype, yp, h, z, stage, s)
+           : run_ffn(xp, nullptr, R, off, w1, w2, R, H, E, F, dtype, yp, h, z, stage, s);
+  if (fs != MOE_OK) return fs;
+  return launch_status(moe::launch_combine(yp, inv, topk_w, (int)T, (int)H, top_k, bf16, y, s));
+}
+
+moe_status moe_backward(const void* dy, const void* x, const void* w_r, const void* w1,
+                        const void* w2, int64_t T, int64_t H, int64_t E, int32_t top_k,
+                        int64_t F, moe_dtype dtype, moe_dtype router_dtype, moe_gating gating,
+                        const int32_t* topk_ids, const float* topk_w, const void* saved,
+                        size_t saved_bytes, void* dx, void* dw_r, float* db_r, void* dw1,
+                        void* dw2, float* dtopk_w, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(T, H, E, top_k, F, dtype);
+  if (st != MOE_OK) return st;
+  st = check_router(dtype, router_dtype, gating);
+  if (st != MOE_OK) return st;
+  // (buffers of T rows are empty, and may be NULL, when T == 0)
+  if (!w_r || !w1 || !w2 || !saved || !dw_r || !dw1 || !dw2 || !ws) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!dy || !x || !topk_ids || !topk_w || !dx)) return MOE_ERR_INVALID_ARG;
+  const SavedLayout V = saved_layout(T, H, E, top_k, F, dtype);
+  const BwdLayout L = bwd_layout(T, H, E, top_k, F, dtype);
+  if (saved_bytes < V.total || ws_bytes < L.total) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == MOE_BF16;
+  const bool w_bf16 = router_dtype == MOE_BF16;
+  const int64_t R = T * top_k;
+  const char* sv = (const char*)saved;
+  const int32_t* off = (const int32_t*)(sv + V.offsets);
+  const int32_t* sorted = (const int32_t*)(sv + V.sorted);
+  const int32_t* inv = (const int32_t*)(sv + V.inv);
+  const float* logits = (const float*)(sv + V.logits);
+  const void* z = sv + V.z;
+  const void* h = sv + V.h;
+  const void* yp = sv + V.yp;
+  char* base = (char*)ws;
+  float* dw = dtopk_w ? dtopk_w : (float*)(base + L.dw);
+  float* dl = (float*)(base + L.dl);
+  void* dyp = base + L.dyp;
+  void* dxp = base + L.dyp;      // dyp's last reader (dW2) runs before dxp is written
+  void* dz = base + L.dz;
+  void* xp = base + L.xp;
+  void* stage = base + L.stage;
+  hipError_t err;
+  // combine and gating
+  err = moe::launch_combine_bwd(dy, yp, inv, topk_w, (int)T, (int)H, top_k, bf16, dw, dyp, s);
+  if (err == hipSuccess)
+    err = moe::launch_router_bwd(logits, topk_ids, topk_w, dw, (int)T, (int)E, top_k,
+                                 gating == MOE_GATE_SOFTMAX_TOPK, dl, s);
+  if (err == hipSuccess)
+    err = moe::launch_router_wgrad(x, dl, (int)T, (int)H, (int)E, bf16, w_bf16, dw_r, db_r,
+                                   stage, s);
+  if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  if (T == 0) {
+    // no rows (and no dispatch state): every expert's weight gradient is zero
+    const size_t wbytes = (size_t)E * H * F * elem_bytes(dtype);
+    err = moe::launch_fill_zero(dw1, wbytes, s);
+    if (err == hipSuccess) err = moe::launch_fill_zero(dw2, wbytes, s);
+    return launch_status(err);
+  }
+  // experts: dz = (dyp W2^T) * GELU'(z), dW2 = h^T dyp, dxp = dz W1^T, dW1 = xp^T dz
+  {
+    if (bf16) {
+      err = moe::launch_gemm_bf16(dyp, nullptr, (int)R, w2, true, dz, off, (int)E, (int)R,
+                                  (int)H, (int)F, moe::EP_DGELU, z, nullptr, stage, s);
+      if (err == hipSuccess)
+        err = moe::launch_gemm_bf16_wgrad(h, dyp, dw2, off, (int)E, (int)F, (int)H, s);
+      if (err == hipSuccess)
+        err = moe::launch_gemm_bf16(dz, nullptr, (int)R, w1, true, dxp, off, (int)E, (int)R,
+                                    (int)F, (int)H, moe::EP_PLAIN, nullptr, nullptr, stage, s);
+      if (err == hipSuccess)
+        err = moe::launch_gather_rows(x, sorted, off, (int)E, (int)R, (int)H, 2, xp, s);
+      if (err == hipSuccess)
+        err = moe::launch_gemm_bf16_wgrad(xp, dz, dw1, off, (int)E, (int)H, (int)F, s);
+    } else {
+      err = moe::launch_gemm_f32_nt((const float*)dyp, (const float*)w2, (float*)dz, off, (int)E,
+                                    (int)R, (int)H, (int)F, (const float*)z, s);
+      if (err == hipSuccess)
+        err = moe::launch_gemm_f32_wgrad((const float*)h, (const float*)dyp, (float*)dw2, off,
+                                         (int)E, (int)F, (int)H, s);
+      if (err == hipSuccess)
+        err = moe::launch_gemm_f32_nt((const float*)dz, (const float*)w1, (float*)dxp, off,
+                                      (int)E, (int)R, (int)F, (int)H, nullptr, s);
+      if (err == hipSuccess)
+        err = moe::launch_gather_rows(x, sorted, off, (int)E, (int)R, (int)H, 4, xp, s);
+      if (err == hipSuccess)
+        err = moe::launch_gemm_f32_wgrad((const float*)xp, (const float*)dz, (float*)dw1, off,
+                                         (int)E, (int)H, (int)F, s);
+    }
+    if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  }
+  return launch_status(moe::launch_dx_finish(dxp, inv, dl, w_r, (int)T, (int)H, (int)E, top_k,
+                                             bf16, w_bf16, dx, s));
 }
 
 }  // extern "C"

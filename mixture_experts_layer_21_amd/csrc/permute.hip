@@ -307,4 +307,14 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
   return hipGetLastError();
 }
 
+hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, const int32_t* offsets,
+                              int E, int R, int H, size_t elem_bytes, void* xp, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  const int row_chunks = (int)((size_t)H * elem_bytes / 16);
+  const int blocks = std::min(8192, (R + 3) / 4);
+  hipLaunchKernelGGL(perm_gather, dim3(blocks), dim3(256), 0, s, (const u32x4*)x, sorted_token,
+                     offsets, E, (u32x4*)xp, row_chunks);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -25,7 +25,8 @@
 //                     (value desc, index asc) arg-max, then the gate weights:
 //                     the softmax of the k winners, or (softmax-then-top-k
 //                     gating, CANN article section 2.1) their probabilities
-//                     under the softmax over all E; writes ids[T,k], w[T,k].
+//                     under the softmax over all E; writes ids[T,k], w[T,k]
+//                     and, for a training forward, the logits[T,E].
 #include "common.h"
 #include "launch.h"
 
@@ -214,7 +215,7 @@ template <int NPL>
 __global__ __launch_bounds__(256) void route_select(
     const float* __restrict__ part, const float* __restrict__ bias,
     int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int EP,
-    int S, int k, int softmax_all) {
+    int S, int k, int softmax_all, float* __restrict__ logits) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
@@ -245,6 +246,7 @@ __global__ __launch_bounds__(256) void route_select(
     const int e = lane + i * kWave;
     if (e < E) {
       if (bias) v[i] += bias[e];
+      if (logits) logits[(size_t)t * E + e] = v[i];
     } else {
       v[i] = -__builtin_inff();
     }
@@ -310,9 +312,10 @@ __global__ __launch_bounds__(256) void route_select(
 
 template <int NPL>
 void launch_select(const float* part, const float* bias, int32_t* ids, float* w,
-                   int T, int E, int EP, int S, int k, int softmax_all, hipStream_t s) {
+                   int T, int E, int EP, int S, int k, int softmax_all, float* logits,
+                   hipStream_t s) {
   hipLaunchKernelGGL((route_select<NPL>), dim3((T + 3) / 4), dim3(256), 0, s,
-                     part, bias, ids, w, T, E, EP, S, k, softmax_all);
+                     part, bias, ids, w, T, E, EP, S, k, softmax_all, logits);
 }
 
 }  // namespace
@@ -351,7 +354,7 @@ size_t route_ws_bytes(int T, int H, int E, bool bf16) {
 
 hipError_t launch_route(const void* x, const void* w_r, const float* bias,
                         int T, int H, int E, int k, bool bf16, bool wf32, bool softmax_all,
-                        int32_t* ids, float* w, void* ws, hipStream_t s) {
+                        int32_t* ids, float* w, float* logits, void* ws, hipStream_t s) {
   const RoutePlan p = plan_route(T, H, E, bf16, wf32);
   float* part = (float*)ws;
   if (bf16) {
@@ -376,18 +379,18 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
 #undef MOE_ROUTE_LOGITS
   } else {
     hipError_t err = launch_gemm_f32((const float*)x, (const float*)w_r, part, nullptr, 1, T, H, E,
-                                     p.EP, false, s);
+                                     p.EP, false, nullptr, s);
     if (err != hipSuccess) return err;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int npl = (E + kWave - 1) / kWave;
   const int sa = softmax_all ? 1 : 0;
-  if (npl <= 1) launch_select<1>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
-  else if (npl <= 2) launch_select<2>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
-  else if (npl <= 4) launch_select<4>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
-  else if (npl <= 8) launch_select<8>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
-  else launch_select<16>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, s);
+  if (npl <= 1) launch_select<1>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
+  else if (npl <= 2) launch_select<2>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
+  else if (npl <= 4) launch_select<4>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
+  else if (npl <= 8) launch_select<8>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
+  else launch_select<16>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
   return hipGetLastError();
 }
 

@@ -2,7 +2,8 @@
 bench and the oracle's callers.
 
 This module holds none of the MoE arithmetic.  It only draws the layer's
-inputs (x, W_r, router bias, W1, W2) for the five workloads, and it draws them
+inputs (x, W_r, router bias, W1, W2, and an output gradient dy for the
+backward) for the five workloads, and it draws them
 so that the bits are identical whether the tensors are made on the CPU or on a
 GPU:
 
@@ -34,7 +35,7 @@ import torch
 MASK32 = 0xFFFFFFFF
 _M1 = 0x7FEB352D
 _M2 = 0x846CA68B
-_STREAM_X, _STREAM_WR, _STREAM_W1, _STREAM_W2 = 1, 2, 3, 4
+_STREAM_X, _STREAM_WR, _STREAM_W1, _STREAM_W2, _STREAM_DY = 1, 2, 3, 4, 5
 _DRAWS = 6            # 6 hashed words -> 12 uniform 16-bit halves per value
 _CHUNK_CPU = 1 << 22  # values per generation chunk (bounds temporaries)
 _CHUNK_GPU = 1 << 25
@@ -155,6 +156,11 @@ def make_w_r_f32(cfg: MoEConfig, device="cpu") -> torch.Tensor:
     n = cfg.H * cfg.E
     return normal_fp32(n, stream_keys(cfg.seed, _STREAM_WR, 0), 1.0 / math.sqrt(cfg.H),
                        device).view(cfg.H, cfg.E)
+
+
+def make_dy(cfg: MoEConfig, device="cpu") -> torch.Tensor:
+    """An output gradient dy[T,H] ~ N(0, 1) in the layer's dtype (for the backward)."""
+    return _fill((cfg.T, cfg.H), _STREAM_DY, 0, 1.0, cfg, device)
 
 
 def make_router_bias(cfg: MoEConfig, device="cpu"):

@@ -261,3 +261,76 @@ def test_expert_capacity_matches_oracle(T, k, E, num, den):
 def test_expert_capacity_rejects(args, expect):
     assert _cap(*args)[0] == expect
     assert L.moe_expert_capacity(64, 2, 8, 6, 5, None) == INV
+
+
+# --- training: saved state, training forward, backward --------------------------
+
+def _sizes(fn, T=64, H=128, E=8, k=2, F=256, dt=BF16):
+    n = ctypes.c_size_t(0)
+    return getattr(L, fn)(T, H, E, k, F, dt, ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("fn", ["moe_saved_bytes", "moe_backward_workspace_bytes"])
+def test_training_sizes_valid_and_monotone(fn):
+    st, a = _sizes(fn)
+    assert st == OK and a > 0
+    assert _sizes(fn, T=128)[1] > a and _sizes(fn, F=512)[1] > a and _sizes(fn, H=256)[1] > a
+    if fn == "moe_saved_bytes":      # (the bf16 workspace also holds the GEMMs' split partials)
+        assert _sizes(fn, dt=F32)[1] > a
+    assert _sizes(fn, T=0)[0] == OK
+
+
+@pytest.mark.parametrize("fn", ["moe_saved_bytes", "moe_backward_workspace_bytes"])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(T=-1), INV), (dict(H=0), INV), (dict(k=0), INV), (dict(k=9), INV), (dict(F=0), INV),
+    (dict(H=12), UNS), (dict(dt=5), UNS), (dict(E=2048, k=2), UNS),
+])
+def test_training_sizes_reject(fn, kw, expect):
+    assert _sizes(fn, **kw)[0] == expect
+
+
+def test_training_sizes_null_output():
+    for fn in ("moe_saved_bytes", "moe_backward_workspace_bytes"):
+        assert getattr(L, fn)(64, 128, 8, 2, 256, BF16, None) == INV
+
+
+def _forward_train(x=P, wr=P, b=N, w1=P, w2=P, T=64, H=128, E=8, k=2, F=256, dt=BF16, rdt=BF16,
+                   g=GT, cap=0, y=P, ids=P, w=P, sv=P, svb=1 << 30, ws=P, nb=1 << 30):
+    return L.moe_forward_train(x, wr, b, w1, w2, T, H, E, k, F, dt, rdt, g, cap, y, ids, w, sv,
+                               svb, ws, nb, N)
+
+
+def _backward(dy=P, x=P, wr=P, w1=P, w2=P, T=64, H=128, E=8, k=2, F=256, dt=BF16, rdt=BF16,
+              g=GT, ids=P, w=P, sv=P, svb=1 << 30, dx=P, dwr=P, dbr=N, dw1=P, dw2=P, dtw=N,
+              ws=P, nb=1 << 30):
+    return L.moe_backward(dy, x, wr, w1, w2, T, H, E, k, F, dt, rdt, g, ids, w, sv, svb, dx, dwr,
+                          dbr, dw1, dw2, dtw, ws, nb, N)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=N), INV), (dict(wr=N), INV), (dict(w1=N), INV), (dict(w2=N), INV), (dict(y=N), INV),
+    (dict(ids=N), INV), (dict(w=N), INV), (dict(sv=N), INV), (dict(ws=N), INV),
+    (dict(svb=1024), INV), (dict(nb=1024), INV), (dict(g=3), INV), (dict(k=9), INV),
+    (dict(dt=F32, rdt=BF16), UNS), (dict(F=12), UNS), (dict(E=2048), UNS),
+])
+def test_forward_train_rejects(kw, expect):
+    assert _forward_train(**kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dy=N), INV), (dict(x=N), INV), (dict(wr=N), INV), (dict(w1=N), INV), (dict(w2=N), INV),
+    (dict(ids=N), INV), (dict(w=N), INV), (dict(sv=N), INV), (dict(dx=N), INV),
+    (dict(dwr=N), INV), (dict(dw1=N), INV), (dict(dw2=N), INV), (dict(ws=N), INV),
+    (dict(svb=1024), INV), (dict(nb=1024), INV), (dict(g=2), INV), (dict(k=0), INV),
+    (dict(T=-3), INV), (dict(dt=F32, rdt=BF16), UNS), (dict(H=20), UNS), (dict(dt=4, rdt=4), UNS),
+])
+def test_backward_rejects(kw, expect):
+    assert _backward(**kw) == expect
+
+
+def test_forward_train_empty_batch_is_a_no_op():
+    for dt, rdt in ((BF16, BF16), (BF16, F32), (F32, F32)):
+        assert _forward_train(T=0, dt=dt, rdt=rdt) == OK
+        # the empty token buffers may be NULL
+        assert _forward_train(T=0, dt=dt, rdt=rdt, x=N, y=N, ids=N, w=N) == OK
+    assert _forward_train(T=0, wr=N) == INV

@@ -1,0 +1,152 @@
+"""Parity of the training forward and the backward (moe_forward_train,
+moe_backward) with the fp64 oracle's backward.
+
+The oracle is driven by the GPU's expert ids (a near tie may legitimately
+choose either expert; the ids themselves pass the routing acceptance rule
+first).  Every gradient (dx, dW_r, dW1, dW2, the gate weights' gradient and,
+where asked, db_r) must lie within the forward's tolerance of the oracle's,
+relative to the largest magnitude of that gradient: 2e-2 for the bf16 path
+(whose intermediates dyp, z, h, dz are bf16 like its forward's h), 1e-4 for
+fp32.  Shapes cover several tiles with ragged tails, K tails that are not a
+multiple of 64 (H = 200, F = 136), the split-K path (H or F = 4096), experts
+with no rows, k = 1, and the variants (softmax-first gating, capacity drops,
+an fp32 router, a router bias)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from moe_check import TOL, assert_close_rel, check_routing, f64
+
+pytestmark = pytest.mark.gpu
+
+import mixture_experts_layer_21_amd as moe  # fails loudly if the library is missing
+
+C = mi.MoEConfig
+GS, GT = moe.MOE_GATE_SOFTMAX_TOPK, moe.MOE_GATE_TOPK_SOFTMAX
+GNAME = {GT: "topk_softmax", GS: "softmax_topk"}
+CASES = {
+    "tiny_fp32": mi.CONFIGS["tiny_fp32"],
+    "ragged_bf16": C("ragged_bf16", T=75, H=200, E=5, k=2, F=136, dtype="bf16"),
+    "multitile_bf16": C("multitile_bf16", T=1000, H=256, E=3, k=2, F=392, dtype="bf16"),
+    "ragged_f32": C("ragged_f32", T=70, H=72, E=6, k=3, F=40, dtype="f32"),
+    "top1_bf16": C("top1_bf16", T=50, H=128, E=16, k=1, F=64, dtype="bf16"),
+    "one_token_bf16": C("one_token_bf16", T=1, H=128, E=8, k=2, F=256, dtype="bf16"),
+    "many_small_bf16": C("many_small_bf16", T=128, H=128, E=128, k=8, F=64, dtype="bf16"),
+    "skewed_small_bf16": C("skewed_small_bf16", T=256, H=128, E=8, k=2, F=256, dtype="bf16",
+                           bias0=3.0),
+    "longH_bf16": C("longH_bf16", T=40, H=4096, E=24, k=3, F=64, dtype="bf16"),
+    "longF_bf16": C("longF_bf16", T=64, H=128, E=4, k=2, F=4096, dtype="bf16"),
+}
+_cache = {}
+
+
+def layer(cfg):
+    if cfg.name not in _cache:
+        if len(_cache) > 3:
+            _cache.pop(next(iter(_cache)))
+            torch.cuda.empty_cache()
+        print(f"\n[gen] {cfg.name}", flush=True)
+        L = mi.make_inputs(cfg, "cuda")
+        L["dy"] = mi.make_dy(cfg, "cuda")
+        if cfg.dtype == "bf16":
+            L["w_r32"] = mi.make_w_r_f32(cfg, "cuda")
+        _cache[cfg.name] = L
+    return _cache[cfg.name]
+
+
+def run(cfg, gating=GT, capacity=0, wf32=False, with_bias=False):
+    L = layer(cfg)
+    w_r = L["w_r32"] if wf32 else L["w_r"]
+    print(f"[case] {cfg.name} gating={GNAME[gating]} capacity={capacity} wf32={wf32}", flush=True)
+    y, ids, w, saved = moe.moe_forward_train(L["x"], w_r, L["router_bias"], L["w1"], L["w2"],
+                                             cfg.k, gating, capacity)
+    out = moe.moe_backward(L["dy"], L["x"], w_r, L["w1"], L["w2"], cfg.k, ids, w, saved, gating,
+                           with_bias_grad=with_bias)
+    torch.cuda.synchronize()
+    return L, w_r, y, ids, w, saved, out
+
+
+def check(cfg, L, w_r, ids, w, out, gating, capacity, with_bias):
+    tol = TOL[cfg.dtype]
+    x64, wr64 = f64(L["x"]), f64(w_r)
+    logits = oracle.router_logits(x64, wr64, f64(L["router_bias"]))
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    check_routing(ids_np, w.cpu().numpy(), logits, cfg.k, GNAME[gating])
+    ref = oracle.backward(x64, wr64, f64(L["router_bias"]), f64(L["w1"]), f64(L["w2"]), cfg.k,
+                          f64(L["dy"]), ids=ids_np, gating=GNAME[gating], capacity=capacity)
+    for name in ("dx", "dw_r", "dw1", "dw2", "dw"):
+        assert_close_rel(f64(out[name]), ref[name], tol, name)
+    if with_bias:
+        assert_close_rel(f64(out["db_r"]), ref["db_r"], tol, "db_r")
+    return ref
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_matches_oracle(name):
+    cfg = CASES[name]
+    bias = cfg.bias0 != 0.0
+    L, w_r, y, ids, w, saved, out = run(cfg, with_bias=bias)
+    check(cfg, L, w_r, ids, w, out, GT, 0, bias)
+
+
+@pytest.mark.parametrize("name,gating,cap_factor,wf32", [
+    ("ragged_bf16", GS, 0.0, False),
+    ("tiny_fp32", GS, 1.2, False),
+    ("skewed_small_bf16", GT, 1.2, False),
+    ("skewed_small_bf16", GS, 0.6, False),
+    ("multitile_bf16", GT, 0.0, True),
+    ("many_small_bf16", GS, 1.2, True),
+    ("ragged_f32", GT, 0.6, False),
+])
+def test_backward_variants_match_oracle(name, gating, cap_factor, wf32):
+    cfg = CASES[name]
+    cap = oracle.expert_capacity(cfg.T, cfg.k, cfg.E, cap_factor)
+    L, w_r, y, ids, w, saved, out = run(cfg, gating, cap, wf32, with_bias=True)
+    check(cfg, L, w_r, ids, w, out, gating, cap, True)
+    if cap:
+        # dropped pairs get a zero gate-weight gradient
+        _, _, _, inv = oracle.dispatch(ids.cpu().numpy().astype(np.int64), cfg.E, cap)
+        assert np.all(out["dw"].cpu().numpy()[inv < 0] == 0.0)
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "longH_bf16"])
+def test_forward_train_equals_forward(name):
+    """The training forward's y, ids and w are the plain forward's, bit for bit."""
+    cfg = CASES[name]
+    L = layer(cfg)
+    y, ids, w, _ = moe.moe_forward_train(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"],
+                                         cfg.k)
+    ids2 = torch.empty_like(ids)
+    w2 = torch.empty_like(w)
+    y2 = moe.moe_forward_ex(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k,
+                            topk_ids_out=ids2, topk_w_out=w2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w, w2) and torch.equal(y, y2)
+
+
+def test_backward_is_deterministic():
+    cfg = CASES["longH_bf16"]        # split-K partials included
+    L, w_r, y, ids, w, saved, a = run(cfg)
+    b = moe.moe_backward(L["dy"], L["x"], w_r, L["w1"], L["w2"], cfg.k, ids, w, saved)
+    torch.cuda.synchronize()
+    for name in ("dx", "dw_r", "dw1", "dw2", "dw"):
+        assert torch.equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_empty_batch_zeroes_weight_gradients(dtype):
+    cfg = C("empty", T=0, H=64, E=4, k=2, F=32, dtype=dtype)
+    L = mi.make_inputs(cfg, "cuda")
+    dy = mi.make_dy(cfg, "cuda")
+    y, ids, w, saved = moe.moe_forward_train(L["x"], L["w_r"], None, L["w1"], L["w2"], cfg.k)
+    out = {n: torch.full(s, float("nan"), dtype=cfg.torch_dtype, device="cuda")
+           for n, s in (("dw_r", (64, 4)), ("dw1", (4, 64, 32)), ("dw2", (4, 32, 64)))}
+    out["db_r"] = torch.full((4,), float("nan"), device="cuda")
+    g = moe.moe_backward(dy, L["x"], L["w_r"], L["w1"], L["w2"], cfg.k, ids, w, saved,
+                         with_bias_grad=True, out=out)
+    torch.cuda.synchronize()
+    for name in ("dw_r", "dw1", "dw2", "db_r"):
+        assert torch.count_nonzero(g[name]).item() == 0, name
+    assert g["dx"].shape == (0, 64)
