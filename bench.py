@@ -1,6 +1,6 @@
 """Throughput of the MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--pass train]
 
 A step is one moe_forward call (route, dispatch, expert FFN, combine) over one
 batch of synthetic, seeded inputs already resident in HBM.  W untimed steps,
@@ -12,6 +12,10 @@ is two launches of the grouped-GEMM kernel with equal flops, which gives the
 per-launch roofline of the dominant kernel.  The fp64 oracle is timed on the
 host cores on a bounded sample of the same workload.  One JSON line is
 printed.
+
+--pass train times a training step of the layer instead: moe_forward_train
+then moe_backward (same inputs, a seeded output gradient), with the backward's
+expert GEMMs timed through moe_expert_ffn_backward for their roofline.
 """
 from __future__ import annotations
 
@@ -52,6 +56,9 @@ def parse():
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE counter files into the traffic "
                          "record under profiles/ and exit")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy")
+    ap.add_argument("--pass", dest="pass_", default="forward", choices=["forward", "train"],
+                    help="forward (default): moe_forward steps; train: moe_forward_train + "
+                         "moe_backward steps (a training step of the layer)")
     return ap.parse_args()
 
 
@@ -250,6 +257,166 @@ def cpu_baseline(cfg, L, n_tokens):
                       f"{dt:.2f} s"}
 
 
+METRIC_TRAIN = "MoE layer fwd+bwd (training step) tokens/s + % MFMA/HBM roofline"
+
+
+def time_train(moe, L, cfg, steps, warmup, bufs):
+    y, ids, w, saved, ws_f, ws_b, out, dy = bufs
+    args = (L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k)
+
+    def step():
+        moe.moe_forward_train(*args, y=y, topk_ids=ids, topk_w=w, saved=saved, ws=ws_f)
+        moe.moe_backward(dy, L["x"], L["w_r"], L["w1"], L["w2"], cfg.k, ids, w, saved, out=out,
+                         ws=ws_b)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_train_stages(moe, L, cfg, steps, bufs):
+    """HIP events on the launch stream: the training forward, the backward, and
+    the backward's expert stage alone (moe_expert_ffn_backward: four GEMM
+    launches of equal flops, 2 R H F each)."""
+    y, ids, w, saved, ws_f, ws_b, out, dy = bufs
+    args = (L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k)
+    dev = "cuda"
+    R = cfg.R
+    off = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+    st = torch.empty(R, dtype=torch.int32, device=dev)
+    inv = torch.empty(R, dtype=torch.int32, device=dev)
+    xp = torch.empty((R, cfg.H), dtype=cfg.torch_dtype, device=dev)
+    moe.moe_permute(L["x"], ids, cfg.E, expert_offsets=off, sorted_token=st, inv_pos=inv, xp=xp,
+                    ws=ws_f)
+    rows = mi.MoEConfig("rows", T=R, H=cfg.F, E=1, k=1, F=8, dtype=cfg.dtype, seed=cfg.seed + 2)
+    z = mi.make_x(rows, dev)                 # [R, F] seeded values for z and h
+    dyp = torch.empty((R, cfg.H), dtype=cfg.torch_dtype, device=dev)
+    dyp.copy_(xp)
+    dw1, dw2 = out["dw1"], out["dw2"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        e = ev[i]
+        e[0].record()
+        moe.moe_forward_train(*args, y=y, topk_ids=ids, topk_w=w, saved=saved, ws=ws_f)
+        e[1].record()
+        moe.moe_backward(dy, L["x"], L["w_r"], L["w1"], L["w2"], cfg.k, ids, w, saved, out=out,
+                         ws=ws_b)
+        e[2].record()
+        moe.moe_expert_ffn_backward(dyp, xp, off, z, z, L["w1"], L["w2"], dxp=dyp, dw1=dw1,
+                                    dw2=dw2, ws=ws_b)
+        e[3].record()
+    torch.cuda.synchronize()
+    names = ["forward_train", "backward", "expert_ffn_backward"]
+    return {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
+            for j, n in enumerate(names)}
+
+
+def cpu_baseline_train(cfg, L, dy, n_tokens):
+    """The fp64 oracle's forward and backward on the first n_tokens tokens
+    (every expert they route to), timed on the host cores."""
+    import oracle
+    up = lambda t: t.cpu().to(torch.float64).numpy()  # noqa: E731
+    x = up(L["x"][:n_tokens])
+    g = up(dy[:n_tokens])
+    w_r = up(L["w_r"])
+    b = None if L["router_bias"] is None else up(L["router_bias"])
+    w1c, w2c = L["w1"].cpu(), L["w2"].cpu()
+    ids = oracle.topk_ids(oracle.router_logits(x, w_r, b), cfg.k)
+    used = sorted(set(ids.ravel().tolist()))
+    w1 = np.zeros((cfg.E, cfg.H, cfg.F))
+    w2 = np.zeros((cfg.E, cfg.F, cfg.H))
+    for e in used:
+        w1[e] = w1c[e].to(torch.float64).numpy()
+        w2[e] = w2c[e].to(torch.float64).numpy()
+    cores = torch.get_num_threads()
+    t0 = time.perf_counter()
+    oracle.forward(x, w_r, b, w1, w2, cfg.k)
+    oracle.backward(x, w_r, b, w1, w2, cfg.k, g)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tokens} of {cfg.T} tokens of {cfg.name}: fp64 forward + "
+                      f"backward (weight gradients of the {len(used)} experts they use), "
+                      f"{dt:.2f} s"}
+
+
+def main_train(a, moe, cfg):
+    dev = "cuda"
+    L = mi.make_inputs(cfg, dev)
+    dy = mi.make_dy(cfg, dev)
+    T, H, E, k, F, td = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.torch_dtype
+    bufs = (torch.empty((T, H), dtype=td, device=dev),
+            torch.empty((T, k), dtype=torch.int32, device=dev),
+            torch.empty((T, k), dtype=torch.float32, device=dev),
+            torch.empty(moe.moe_saved_bytes(T, H, E, k, F, td), dtype=torch.uint8, device=dev),
+            torch.empty(moe.moe_workspace_bytes(T, H, E, k, F, td), dtype=torch.uint8,
+                        device=dev),
+            torch.empty(moe.moe_backward_workspace_bytes(T, H, E, k, F, td), dtype=torch.uint8,
+                        device=dev),
+            {"dx": torch.empty((T, H), dtype=td, device=dev),
+             "dw_r": torch.empty((H, E), dtype=td, device=dev),
+             "dw1": torch.empty((E, H, F), dtype=td, device=dev),
+             "dw2": torch.empty((E, F, H), dtype=td, device=dev),
+             "dw": torch.empty((T, k), dtype=torch.float32, device=dev)},
+            dy)
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name} train: inputs ready", file=sys.stderr, flush=True)
+    sec = time_train(moe, L, cfg, a.steps, a.warmup, bufs)
+    print(f"[bench] timed region done: {sec * 1e3:.3f} ms/step", file=sys.stderr, flush=True)
+    stages = time_train_stages(moe, L, cfg, a.steps, bufs)
+    R = cfg.R
+    es = 2 if cfg.dtype == "bf16" else 4
+    # per GEMM launch of the expert backward (four of them, equal flops):
+    # 2 R H F flops; bytes: the touched experts' weight (NT) or gradient (TN)
+    # matrix plus the two R-row operands read
+    ids = bufs[1].cpu().numpy()
+    touched = len(np.unique(ids))
+    g_flops = 2 * R * H * F
+    g_bytes = es * (touched * H * F + R * H + R * F)
+    g_sec = stages["expert_ffn_backward"] / 4 * 1e-3
+    peak_mm = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if g_flops / g_bytes >= ridge:
+        roof = {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
+                "achieved": g_flops / g_sec / 1e12, "peak": peak_mm, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": g_bytes / g_sec / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = ("expert backward GEMMs: gemm_bf16_grouped NT (dz, dxp) and "
+                      "gemm_bf16_wgrad (dW2, dW1), average of the four launches"
+                      if cfg.dtype == "bf16" else "gemm_f32_bwd, average of four launches")
+    roof["per_launch"] = {"flops": g_flops, "bytes": g_bytes, "ms": g_sec * 1e3}
+    cpu = None
+    if not a.no_cpu_baseline:
+        n = a.cpu_sample_tokens or {"tiny_fp32": 64, "mixtral_bf16": 32, "skewed_bf16": 32,
+                                    "many_experts_bf16": 64, "weight_bound_bf16": 2}[cfg.name]
+        cpu = cpu_baseline_train(cfg, L, dy, min(n, T))
+    # training-step flops: forward (router + 2 GEMMs) and backward (router
+    # weight and input gradients + 4 GEMMs)
+    flops = 2 * T * H * E * 3 + 6 * 2 * R * H * F
+    out = {
+        "metric": METRIC_TRAIN, "value": T / sec, "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": sec * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded counter-based generator; random-init weights)",
+        "config": {"workload": cfg.name + " (training step)", "T": T, "H": H, "E": E,
+                   "top_k": k, "F": F, "router_bias0": cfg.bias0, "seed": cfg.seed},
+        "step_tflops": flops / sec / 1e12,
+        "stages_ms": stages,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.summarize_traffic:
@@ -264,6 +431,9 @@ def main():
     torch.cuda.set_device(0)
     if a.calibrate_copy_mib:
         calibrate_copy(a.calibrate_copy_mib)
+        return
+    if a.pass_ == "train":
+        main_train(a, moe, cfg)
         return
     L = mi.make_inputs(cfg, "cuda")
     dev = "cuda"

@@ -98,6 +98,7 @@ enum {
   MOE_STAGE_EXPERT_FFN = 2,
   MOE_STAGE_COMBINE = 3,
   MOE_STAGE_FORWARD = 4,
+  MOE_STAGE_EXPERT_FFN_BACKWARD = 5,
 };
 
 /*
@@ -105,7 +106,8 @@ enum {
  * written to *bytes (host pointer): MOE_STAGE_ROUTE -> moe_route,
  * MOE_STAGE_PERMUTE -> moe_permute, MOE_STAGE_EXPERT_FFN -> moe_expert_ffn
  * with R = T*top_k rows, MOE_STAGE_COMBINE -> 0 (no workspace),
- * MOE_STAGE_FORWARD -> moe_forward (same as moe_workspace_bytes).
+ * MOE_STAGE_FORWARD -> moe_forward (same as moe_workspace_bytes),
+ * MOE_STAGE_EXPERT_FFN_BACKWARD -> moe_expert_ffn_backward with R = T*top_k.
  * Returns MOE_ERR_INVALID_ARG for an unknown stage.
  */
 moe_status moe_stage_workspace_bytes(moe_stage stage, int64_t T, int64_t H,
@@ -278,6 +280,26 @@ moe_status moe_saved_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k, int64
 /* *bytes = workspace moe_backward needs for this shape. */
 moe_status moe_backward_workspace_bytes(int64_t T, int64_t H, int64_t E, int32_t top_k,
                                         int64_t F, moe_dtype dtype, size_t* bytes);
+
+/*
+ * Backward of moe_expert_ffn over the dispatched rows (the expert stage of
+ * moe_backward, for callers that run their own dispatch): for every expert e
+ * with rows [expert_offsets[e], expert_offsets[e+1]),
+ *   dz = (dyp W2[e]^T) * GELU'(z),   dW2[e] = h^T dyp,
+ *   dxp = dz W1[e]^T,                 dW1[e] = xp^T dz.
+ *   dyp[R,H]: gradient with respect to the expert outputs yp; xp[R,H]: the
+ *     dispatched token rows; z[R,F], h[R,F]: the first GEMM's pre-activation
+ *     and GELU(z) (as moe_forward_train keeps them); all in dtype.
+ *   dxp[R,H], dw1[E,H,F], dw2[E,F,H] (dtype) outputs.  dxp may be the same
+ *     buffer as dyp.  Experts with no rows get zero weight gradients; with
+ *     R == 0 only those are written (dyp, xp, z, h, dxp may be NULL).
+ *   ws holds dz[R,F] (moe_stage_workspace_bytes, MOE_STAGE_EXPERT_FFN_BACKWARD).
+ */
+moe_status moe_expert_ffn_backward(const void* dyp, const void* xp,
+                                   const int32_t* expert_offsets, const void* z, const void* h,
+                                   const void* w1, const void* w2, int64_t R, int64_t H,
+                                   int64_t E, int64_t F, moe_dtype dtype, void* dxp, void* dw1,
+                                   void* dw2, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_forward_ex that also fills `saved` (device, caller-owned, at least

@@ -29,11 +29,13 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_LAUNCH = 0, 1, 2, 3
 MOE_F32, MOE_BF16 = 0, 1
 MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_EXPERT_FFN, MOE_STAGE_COMBINE, MOE_STAGE_FORWARD = \
     0, 1, 2, 3, 4
+MOE_STAGE_EXPERT_FFN_BACKWARD = 5
 MOE_GATE_TOPK_SOFTMAX, MOE_GATE_SOFTMAX_TOPK = 0, 1
 EXPORTS = ("moe_status_string", "moe_workspace_bytes", "moe_stage_workspace_bytes", "moe_route",
            "moe_route_ex", "moe_expert_capacity", "moe_permute", "moe_permute_ex",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex", "moe_saved_bytes",
-           "moe_backward_workspace_bytes", "moe_forward_train", "moe_backward")
+           "moe_backward_workspace_bytes", "moe_forward_train", "moe_backward",
+           "moe_expert_ffn_backward")
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _lib.moe_status_string.restype = ctypes.c_char_p
@@ -67,6 +69,9 @@ _lib.moe_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i
 _lib.moe_forward_ex.restype = _i32
 _lib.moe_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _i32,
                                 _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_expert_ffn_backward.restype = _i32
+_lib.moe_expert_ffn_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                         _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_saved_bytes.restype = _i32
 _lib.moe_saved_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i32, ctypes.POINTER(_sz)]
 _lib.moe_backward_workspace_bytes.restype = _i32
@@ -432,3 +437,33 @@ def moe_backward(dy, x, w_r, w1, w2, top_k: int, topk_ids, topk_w, saved,
                           _ptr(out["dw2"]), _ptr(out["dw"]), _ptr(ws), ws.numel(),
                           _stream(dev)), "moe_backward")
     return out
+
+
+def moe_expert_ffn_backward(dyp, xp, expert_offsets, z, h, w1, w2, dxp=None, dw1=None, dw2=None,
+                            ws=None):
+    """Backward of moe_expert_ffn over the dispatched rows.  Returns
+    (dxp[R,H], dw1[E,H,F], dw2[E,F,H]); dxp may be dyp itself."""
+    _check(xp, "xp")
+    R, H = xp.shape
+    E, _, F = w1.shape
+    dt = xp.dtype
+    _check(dyp, "dyp", dt, (R, H))
+    _check(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    _check(z, "z", dt, (R, F))
+    _check(h, "h", dt, (R, F))
+    _check(w1, "w1", dt, (E, H, F))
+    _check(w2, "w2", dt, (E, F, H))
+    dev = xp.device
+    dxp = torch.empty((R, H), dtype=dt, device=dev) if dxp is None else \
+        _check(dxp, "dxp", dt, (R, H))
+    dw1 = torch.empty((E, H, F), dtype=dt, device=dev) if dw1 is None else \
+        _check(dw1, "dw1", dt, (E, H, F))
+    dw2 = torch.empty((E, F, H), dtype=dt, device=dev) if dw2 is None else \
+        _check(dw2, "dw2", dt, (E, F, H))
+    ws = _workspace(ws, moe_stage_workspace_bytes(MOE_STAGE_EXPERT_FFN_BACKWARD, R, H, E, 1, F,
+                                                  dt), dev)
+    _ok(_lib.moe_expert_ffn_backward(_ptr(dyp), _ptr(xp), _ptr(expert_offsets), _ptr(z), _ptr(h),
+                                     _ptr(w1), _ptr(w2), R, H, E, F, _dtype_code(dt), _ptr(dxp),
+                                     _ptr(dw1), _ptr(dw2), _ptr(ws), ws.numel(), _stream(dev)),
+        "moe_expert_ffn_backward")
+    return dxp, dw1, dw2

@@ -9,7 +9,8 @@
 //                 softmax's Jacobian (no gradient through the top-k choice)
 //   router_wgrad  dW_r = x^T dl and db_r = sum_t dl, split over tokens into
 //                 fp32 partials that router_wgrad_reduce adds in split order
-//   dx_finish     dx[t] = sum_j dxp[inv_pos[t, j]] + dl[t] . W_r^T
+//   dx_finish     dx[t] = sum_j dxp[inv_pos[t, j]] + dl[t] . W_r^T (through a
+//                 transposed copy of W_r, so that its loads are coalesced)
 // The expert GEMMs in between (dz = dyp W2^T * GELU'(z), dW2 = h^T dyp,
 // dxp = dz W1^T, dW1 = xp^T dz) run on the grouped GEMM kernels.
 // Every sum runs in a fixed order: the results are deterministic.
@@ -200,13 +201,13 @@ __global__ __launch_bounds__(256) void router_wgrad(const void* __restrict__ x,
   const int t_begin = (int)((long)s * T / S), t_end = (int)((long)(s + 1) * T / S);
   const int h = hb * kWgH + 2 * tid;
   const int e0 = eb * kWgE;
-  float acc[2][kWgE], accb[kWgE];
+  float acc[2][kWgE];
 #pragma unroll
-  for (int e = 0; e < kWgE; ++e) {
-    acc[0][e] = acc[1][e] = 0.f;
-    accb[e] = 0.f;
-  }
-  const bool bias_thread = hb == 0 && tid == 0;
+  for (int e = 0; e < kWgE; ++e) acc[0][e] = acc[1][e] = 0.f;
+  // workgroups of the first h block also sum dl over their tokens (db_r):
+  // thread e < 16 adds column e of each staged batch
+  const bool bias_thread = hb == 0 && tid < kWgE;
+  float accb1 = 0.f;
   for (int tb = t_begin; tb < t_end; tb += kWgT) {
     const int nt = min(kWgT, t_end - tb);
     __syncthreads();
@@ -215,27 +216,37 @@ __global__ __launch_bounds__(256) void router_wgrad(const void* __restrict__ x,
       dls[tt][e] = (tt < nt && e0 + e < E) ? dl[(size_t)(tb + tt) * E + e0 + e] : 0.f;
     }
     __syncthreads();
-    for (int tt = 0; tt < nt; ++tt) {
-      float x0 = 0.f, x1 = 0.f;
-      if (h < H) {
-        if constexpr (BF16) {
-          const uint32_t v = *(const uint32_t*)((const uint16_t*)x + (size_t)(tb + tt) * H + h);
-          x0 = bf16_to_f32(v & 0xFFFFu);
-          x1 = bf16_to_f32(v >> 16);
-        } else {
-          const float* r = (const float*)x + (size_t)(tb + tt) * H + h;
-          x0 = r[0];
-          x1 = r[1];
+    // 16 tokens' x values are loaded before any is used (the loads overlap)
+    for (int tt0 = 0; tt0 < nt; tt0 += 16) {
+      float xv[16][2];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        xv[u][0] = xv[u][1] = 0.f;
+        if (tt0 + u < nt && h < H) {
+          if constexpr (BF16) {
+            const uint32_t v =
+                *(const uint32_t*)((const uint16_t*)x + (size_t)(tb + tt0 + u) * H + h);
+            xv[u][0] = bf16_to_f32(v & 0xFFFFu);
+            xv[u][1] = bf16_to_f32(v >> 16);
+          } else {
+            const float* r = (const float*)x + (size_t)(tb + tt0 + u) * H + h;
+            xv[u][0] = r[0];
+            xv[u][1] = r[1];
+          }
         }
       }
 #pragma unroll
-      for (int e = 0; e < kWgE; ++e) {
-        const float d = dls[tt][e];
-        acc[0][e] = __builtin_fmaf(x0, d, acc[0][e]);
-        acc[1][e] = __builtin_fmaf(x1, d, acc[1][e]);
-        if (bias_thread) accb[e] += d;
+      for (int u = 0; u < 16; ++u) {
+#pragma unroll
+        for (int e = 0; e < kWgE; ++e) {
+          const float d = dls[tt0 + u][e];          // 0 past nt
+          acc[0][e] = __builtin_fmaf(xv[u][0], d, acc[0][e]);
+          acc[1][e] = __builtin_fmaf(xv[u][1], d, acc[1][e]);
+        }
       }
     }
+    if (bias_thread)
+      for (int tt = 0; tt < nt; ++tt) accb1 += dls[tt][tid];
   }
   if (h < H) {
 #pragma unroll
@@ -244,11 +255,7 @@ __global__ __launch_bounds__(256) void router_wgrad(const void* __restrict__ x,
       for (int e = 0; e < kWgE; ++e)
         if (e0 + e < E) part[((size_t)s * H + h + r) * E + e0 + e] = acc[r][e];
   }
-  if (bias_thread) {
-#pragma unroll
-    for (int e = 0; e < kWgE; ++e)
-      if (e0 + e < E) partb[(size_t)s * E + e0 + e] = accb[e];
-  }
+  if (bias_thread && e0 + tid < E) partb[(size_t)s * E + e0 + tid] = accb1;
 }
 
 // dW_r[h][e] = sum over splits in order; stored in W_r's type.  The first
@@ -278,94 +285,167 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(const float* __restri
   }
 }
 
-// dx for 16 tokens x 1024 columns per workgroup: thread tid owns columns
-// h0 + 4 tid .. + 3.  The router term sum_e dl[t][e] W_r[h][e] reads W_r's
-// rows (E contiguous) 8 experts at a time with dl from LDS (broadcasts); the
-// expert term adds the token's dispatched rows of dxp (slots in order).
-constexpr int kDxT = 16, kDxH = 1024;
-
-template <bool BF16, bool WBF16>
-__global__ __launch_bounds__(256) void dx_finish(const void* __restrict__ dxp,
-                                                 const int32_t* __restrict__ inv_pos,
-                                                 const float* __restrict__ dl,
-                                                 const void* __restrict__ w_r, int T, int H,
-                                                 int E, int k, void* __restrict__ dx) {
-  extern __shared__ float dls[];      // [kDxT][E]
-  const int tid = threadIdx.x;
-  const int HB = (H + kDxH - 1) / kDxH;
-  const int t0 = (blockIdx.x / HB) * kDxT;
-  const int h = (blockIdx.x % HB) * kDxH + 4 * tid;
-  const int nt = min(kDxT, T - t0);
-  for (int q = tid; q < kDxT * E; q += 256) {
-    const int tt = q / E;
-    dls[q] = tt < nt ? dl[(size_t)(t0 + tt) * E + q % E] : 0.f;
+// W_r [H][E] -> W_r^T [E][H] (same type), 32x32 tiles through LDS, so that
+// dx_finish reads W_r^T rows across the lanes.
+template <typename Tw>
+__global__ __launch_bounds__(256) void transpose_wr(const Tw* __restrict__ w, int H, int E,
+                                                    Tw* __restrict__ wt) {
+  __shared__ Tw tile[32][33];
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;     // 32 x 8
+  const int eb = blockIdx.x % ((E + 31) / 32), hb = blockIdx.x / ((E + 31) / 32);
+#pragma unroll
+  for (int r = 0; r < 32; r += 8) {
+    const int h = hb * 32 + ty + r, e = eb * 32 + tx;
+    if (h < H && e < E) tile[ty + r][tx] = w[(size_t)h * E + e];
   }
   __syncthreads();
-  if (h >= H) return;
-  float acc[kDxT][4];
 #pragma unroll
-  for (int tt = 0; tt < kDxT; ++tt)
+  for (int r = 0; r < 32; r += 8) {
+    const int e = eb * 32 + ty + r, h = hb * 32 + tx;
+    if (h < H && e < E) wt[(size_t)e * H + h] = tile[tx][ty + r];
+  }
+}
+
+// dx for TB tokens x 1024 columns per workgroup: thread tid owns columns
+// h0 + 4 tid .. + 3.  The router term sum_e dl[t][e] W_r^T[e][h] reads W_r^T
+// rows (a wave covers 256 consecutive columns), 8 experts' loads in flight,
+// with dl from LDS (broadcasts); the expert term adds the token's dispatched
+// rows of dxp (slots in order).
+constexpr int kDxH = 1024;
+
+// 4 consecutive values of a W_r^T row as fp32
+template <bool WBF16>
+__device__ __forceinline__ void load_wrt4(const void* w_rt, size_t o, float (&w)[4]) {
+  if constexpr (WBF16) {
+    const u32x2 v = *(const u32x2*)((const uint16_t*)w_rt + o);
+    w[0] = bf16_to_f32(v[0] & 0xFFFFu);
+    w[1] = bf16_to_f32(v[0] >> 16);
+    w[2] = bf16_to_f32(v[1] & 0xFFFFu);
+    w[3] = bf16_to_f32(v[1] >> 16);
+  } else {
+    const f32x4 v = *(const f32x4*)((const float*)w_rt + o);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = v[q];
+  }
+}
+
+// SPARSE (top-k then softmax gating): dl is zero outside each token's k
+// selected experts, so the router term takes k rows of W_r^T (ids), not E.
+template <bool BF16, bool WBF16, bool SPARSE, int TB>
+__global__ __launch_bounds__(256) void dx_finish(const void* __restrict__ dxp,
+                                                 const int32_t* __restrict__ inv_pos,
+                                                 const int32_t* __restrict__ ids,
+                                                 const float* __restrict__ dl,
+                                                 const void* __restrict__ w_rt, int T, int H,
+                                                 int E, int k, void* __restrict__ dx) {
+  extern __shared__ float dls[];      // [TB][E] (dense path)
+  const int tid = threadIdx.x;
+  const int HB = (H + kDxH - 1) / kDxH;
+  const int t0 = (blockIdx.x / HB) * TB;
+  const int h = (blockIdx.x % HB) * kDxH + 4 * tid;
+  const int nt = min(TB, T - t0);
+  if constexpr (!SPARSE) {
+    for (int q = tid; q < TB * E; q += 256) {
+      const int tt = q / E;
+      dls[q] = tt < nt ? dl[(size_t)(t0 + tt) * E + q % E] : 0.f;
+    }
+    __syncthreads();
+  }
+  if (h >= H) return;
+  float acc[TB][4];
+#pragma unroll
+  for (int tt = 0; tt < TB; ++tt)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[tt][q] = 0.f;
-  const bool vec = (E % 8) == 0;
-  for (int e = 0; e < E; e += 8) {
-    float wv[4][8];
+  if constexpr (SPARSE) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const size_t row = (size_t)(h + q) * E;
-      if (vec) {
-        if constexpr (WBF16) {
-          load8<true>((const uint16_t*)w_r + row, e / 8, wv[q]);
-        } else {
-          load8<false>((const float*)w_r + row, e / 8, wv[q]);
-        }
-      } else {
+    for (int tt = 0; tt < TB; ++tt) {
+      if (tt < nt) {
+        const int t = t0 + tt;
+        for (int j = 0; j < k; ++j) {
+          const int e = ids[(size_t)t * k + j];
+          const float d = dl[(size_t)t * E + e];
+          float w[4];
+          load_wrt4<WBF16>(w_rt, (size_t)e * H + h, w);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          float v = 0.f;
-          if (e + u < E) {
-            if constexpr (WBF16) v = bf16_to_f32(((const uint16_t*)w_r)[row + e + u]);
-            else v = ((const float*)w_r)[row + e + u];
-          }
-          wv[q][u] = v;
+          for (int q = 0; q < 4; ++q) acc[tt][q] = __builtin_fmaf(d, w[q], acc[tt][q]);
         }
       }
     }
+  }
+  for (int e0 = 0; !SPARSE && e0 < E; e0 += 8) {
+    float wv[8][4];
 #pragma unroll
-    for (int tt = 0; tt < kDxT; ++tt) {
+    for (int u = 0; u < 8; ++u) {
+      wv[u][0] = wv[u][1] = wv[u][2] = wv[u][3] = 0.f;
+      if (e0 + u < E) load_wrt4<WBF16>(w_rt, (size_t)(e0 + u) * H + h, wv[u]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < TB; ++tt) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float d = e + u < E ? dls[tt * E + e + u] : 0.f;
+        const float d = e0 + u < E ? dls[tt * E + e0 + u] : 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[tt][q] = __builtin_fmaf(d, wv[q][u], acc[tt][q]);
+        for (int q = 0; q < 4; ++q) acc[tt][q] = __builtin_fmaf(d, wv[u][q], acc[tt][q]);
       }
     }
   }
   const size_t es = BF16 ? 2 : 4;
-  for (int tt = 0; tt < nt; ++tt) {
-    const int t = t0 + tt;
-    for (int j = 0; j < k; ++j) {
-      const int p = inv_pos[(size_t)t * k + j];
-      if (p < 0) continue;
-      const char* src = (const char*)dxp + ((size_t)p * H + h) * es;
-      if constexpr (BF16) {
-        const u32x2 v = *(const u32x2*)src;
-        acc[tt][0] += bf16_to_f32(v[0] & 0xFFFFu);
-        acc[tt][1] += bf16_to_f32(v[0] >> 16);
-        acc[tt][2] += bf16_to_f32(v[1] & 0xFFFFu);
-        acc[tt][3] += bf16_to_f32(v[1] >> 16);
-      } else {
-        const f32x4 v = *(const f32x4*)src;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[tt][q] += v[q];
+  for (int tt = 0; tt < TB; ++tt) {
+    if (tt < nt) {
+      const int t = t0 + tt;
+      float v[4] = {acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]};
+      for (int j = 0; j < k; ++j) {
+        const int p = inv_pos[(size_t)t * k + j];
+        if (p < 0) continue;
+        const char* src = (const char*)dxp + ((size_t)p * H + h) * es;
+        if constexpr (BF16) {
+          const u32x2 q = *(const u32x2*)src;
+          v[0] += bf16_to_f32(q[0] & 0xFFFFu);
+          v[1] += bf16_to_f32(q[0] >> 16);
+          v[2] += bf16_to_f32(q[1] & 0xFFFFu);
+          v[3] += bf16_to_f32(q[1] >> 16);
+        } else {
+          const f32x4 q = *(const f32x4*)src;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] += q[u];
+        }
       }
+      char* dst = (char*)dx + ((size_t)t * H + h) * es;
+      if constexpr (BF16)
+        *(u32x2*)dst = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      else
+        *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
     }
-    char* dst = (char*)dx + ((size_t)t * H + h) * es;
-    if constexpr (BF16)
-      *(u32x2*)dst = u32x2{pack_bf16x2(acc[tt][0], acc[tt][1]), pack_bf16x2(acc[tt][2], acc[tt][3])};
-    else
-      *(f32x4*)dst = f32x4{acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]};
   }
+}
+
+template <bool BF16, bool WBF16, bool SPARSE, int TB>
+void launch_dx_tb(const void* dxp, const int32_t* inv_pos, const int32_t* ids, const float* dl,
+                  const void* w_rt, int T, int H, int E, int k, void* dx, hipStream_t s) {
+  const int HB = (H + kDxH - 1) / kDxH;
+  dim3 g((unsigned)(((T + TB - 1) / TB) * HB)), b(256);
+  const size_t lds = SPARSE ? 0 : (size_t)TB * E * sizeof(float);
+  hipLaunchKernelGGL((dx_finish<BF16, WBF16, SPARSE, TB>), g, b, lds, s, dxp, inv_pos, ids, dl,
+                     w_rt, T, H, E, k, dx);
+}
+
+template <bool BF16, bool WBF16, bool SPARSE>
+void launch_dx(const void* dxp, const int32_t* inv_pos, const int32_t* ids, const float* dl,
+               const void* w_rt, int T, int H, int E, int k, void* dx, hipStream_t s) {
+  // tokens per workgroup: 16 (dense) or 4 (sparse), fewer when that leaves
+  // the GPU without ~256 workgroups
+  const long hb = (H + kDxH - 1) / kDxH;
+  auto blocks = [&](int tb) { return ((T + tb - 1) / tb) * hb; };
+#define MOE_DX(TB_) launch_dx_tb<BF16, WBF16, SPARSE, TB_>(dxp, inv_pos, ids, dl, w_rt, T, H, E, k, dx, s)
+  if constexpr (!SPARSE) {
+    if (blocks(16) >= 256) { MOE_DX(16); return; }
+    if (blocks(8) >= 256) { MOE_DX(8); return; }
+  }
+  if (blocks(4) >= 256) MOE_DX(4);
+  else MOE_DX(2);
+#undef MOE_DX
 }
 
 // zero fill with 16-byte stores (bytes a multiple of 16, base 16-byte aligned)
@@ -375,8 +455,9 @@ __global__ __launch_bounds__(256) void fill_zero16(u32x4* __restrict__ p, size_t
 }
 
 int wgrad_splits(int T, int H, int E) {
+  // about 1024 workgroups (four per CU), at least 32 tokens per split
   const int blocks = ((H + kWgH - 1) / kWgH) * ((E + kWgE - 1) / kWgE);
-  const int s = std::max(1, std::min(T / 32, 256 / std::max(1, blocks)));
+  const int s = std::max(1, std::min(T / 32, 1024 / std::max(1, blocks)));
   return std::max(1, std::min(s, std::max(1, T)));
 }
 
@@ -439,19 +520,28 @@ hipError_t launch_router_wgrad(const void* x, const float* dl, int T, int H, int
   return hipGetLastError();
 }
 
-hipError_t launch_dx_finish(const void* dxp, const int32_t* inv_pos, const float* dl,
-                            const void* w_r, int T, int H, int E, int k, bool bf16, bool w_bf16,
-                            void* dx, hipStream_t s) {
+hipError_t launch_dx_finish(const void* dxp, const int32_t* inv_pos, const int32_t* ids,
+                            const float* dl, const void* w_r, int T, int H, int E, int k,
+                            bool bf16, bool w_bf16, bool sparse, void* w_rt, void* dx,
+                            hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int HB = (H + kDxH - 1) / kDxH;
-  dim3 g((unsigned)(((T + kDxT - 1) / kDxT) * HB)), b(256);
-  const size_t lds = (size_t)kDxT * E * sizeof(float);
+  dim3 gt((unsigned)(((E + 31) / 32) * ((H + 31) / 32))), b(256);
+  if (w_bf16)
+    hipLaunchKernelGGL((transpose_wr<uint16_t>), gt, b, 0, s, (const uint16_t*)w_r, H, E,
+                       (uint16_t*)w_rt);
+  else
+    hipLaunchKernelGGL((transpose_wr<float>), gt, b, 0, s, (const float*)w_r, H, E,
+                       (float*)w_rt);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+#define MOE_DX(B_, W_, S_) launch_dx<B_, W_, S_>(dxp, inv_pos, ids, dl, w_rt, T, H, E, k, dx, s)
   if (bf16) {
-    if (w_bf16) hipLaunchKernelGGL((dx_finish<true, true>), g, b, lds, s, dxp, inv_pos, dl, w_r, T, H, E, k, dx);
-    else hipLaunchKernelGGL((dx_finish<true, false>), g, b, lds, s, dxp, inv_pos, dl, w_r, T, H, E, k, dx);
+    if (w_bf16) { if (sparse) MOE_DX(true, true, true); else MOE_DX(true, true, false); }
+    else { if (sparse) MOE_DX(true, false, true); else MOE_DX(true, false, false); }
   } else {
-    hipLaunchKernelGGL((dx_finish<false, false>), g, b, lds, s, dxp, inv_pos, dl, w_r, T, H, E, k, dx);
+    if (sparse) MOE_DX(false, false, true); else MOE_DX(false, false, false);
   }
+#undef MOE_DX
   return hipGetLastError();
 }
 

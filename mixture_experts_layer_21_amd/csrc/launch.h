@@ -92,9 +92,11 @@ hipError_t launch_router_bwd(const float* logits, const int32_t* ids, const floa
 // dW_r = x^T dl (W_r's type), db_r = sum_t dl (skipped when db_r is null)
 hipError_t launch_router_wgrad(const void* x, const float* dl, int T, int H, int E, bool x_bf16,
                                bool w_bf16, void* dw_r, float* db_r, void* ws, hipStream_t s);
-// dx[t] = sum_j dxp[inv_pos[t,j]] + dl[t] . W_r^T
-hipError_t launch_dx_finish(const void* dxp, const int32_t* inv_pos, const float* dl,
-                            const void* w_r, int T, int H, int E, int k, bool bf16, bool w_bf16,
-                            void* dx, hipStream_t s);
+// dx[t] = sum_j dxp[inv_pos[t,j]] + dl[t] . W_r^T; w_rt: scratch for W_r^T
+// (E*H elements of W_r's type); sparse: dl is zero outside ids[t, 0..k)
+hipError_t launch_dx_finish(const void* dxp, const int32_t* inv_pos, const int32_t* ids,
+                            const float* dl, const void* w_r, int T, int H, int E, int k,
+                            bool bf16, bool w_bf16, bool sparse, void* w_rt, void* dx,
+                            hipStream_t s);
 
 }  // namespace moe

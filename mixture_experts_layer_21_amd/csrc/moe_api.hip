@@ -103,6 +103,44 @@ moe_status run_ffn(const void* xp, const int32_t* gather, int64_t a_rows, const 
   return launch_status(err);
 }
 
+// Expert FFN backward over dispatched rows: dz = (dyp W2^T) * GELU'(z),
+// dW2 = h^T dyp, dxp = dz W1^T, dW1 = xp^T dz (dz[R,F] in `dz`; split is the
+// bf16 GEMMs' split-tile workspace).  dxp may be dyp's buffer: dyp's last
+// reader (dW2) runs before dxp is written.  With R == 0 only the (zero)
+// weight gradients are written.
+moe_status run_ffn_bwd(const void* dyp, const void* xp, const int32_t* off, const void* z,
+                       const void* h, const void* w1, const void* w2, int64_t R, int64_t H,
+                       int64_t E, int64_t F, moe_dtype dt, void* dxp, void* dw1, void* dw2,
+                       void* dz, void* split, hipStream_t s) {
+  hipError_t err = hipSuccess;
+  if (dt == MOE_BF16) {
+    if (R > 0)
+      err = moe::launch_gemm_bf16(dyp, nullptr, (int)R, w2, true, dz, off, (int)E, (int)R,
+                                  (int)H, (int)F, moe::EP_DGELU, z, nullptr, split, s);
+    if (err == hipSuccess)
+      err = moe::launch_gemm_bf16_wgrad(h, dyp, dw2, off, (int)E, (int)F, (int)H, s);
+    if (err == hipSuccess && R > 0)
+      err = moe::launch_gemm_bf16(dz, nullptr, (int)R, w1, true, dxp, off, (int)E, (int)R,
+                                  (int)F, (int)H, moe::EP_PLAIN, nullptr, nullptr, split, s);
+    if (err == hipSuccess)
+      err = moe::launch_gemm_bf16_wgrad(xp, dz, dw1, off, (int)E, (int)H, (int)F, s);
+  } else {
+    if (R > 0)
+      err = moe::launch_gemm_f32_nt((const float*)dyp, (const float*)w2, (float*)dz, off, (int)E,
+                                    (int)R, (int)H, (int)F, (const float*)z, s);
+    if (err == hipSuccess)
+      err = moe::launch_gemm_f32_wgrad((const float*)h, (const float*)dyp, (float*)dw2, off,
+                                       (int)E, (int)F, (int)H, s);
+    if (err == hipSuccess && R > 0)
+      err = moe::launch_gemm_f32_nt((const float*)dz, (const float*)w1, (float*)dxp, off,
+                                    (int)E, (int)R, (int)F, (int)H, nullptr, s);
+    if (err == hipSuccess)
+      err = moe::launch_gemm_f32_wgrad((const float*)xp, (const float*)dz, (float*)dw1, off,
+                                       (int)E, (int)H, (int)F, s);
+  }
+  return launch_status(err);
+}
+
 // h[R,F] then the split workspace, inside an expert-FFN workspace
 void* ffn_split(void* ws, int64_t R, int64_t F, moe_dtype dt) {
   return (char*)ws + align_up((size_t)R * F * elem_bytes(dt));
@@ -135,7 +173,7 @@ SavedLayout saved_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, 
 // dz, the re-gathered token rows xp, and one region shared in time by the
 // router weight gradient's partials and the GEMMs' split-tile partials.
 struct BwdLayout {
-  size_t dw, dl, dyp, dz, xp, stage, total;
+  size_t dw, dl, dyp, dz, xp, wrt, stage, total;
 };
 
 BwdLayout bwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_dtype dt) {
@@ -148,6 +186,7 @@ BwdLayout bwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_
   L.dyp = o;   o += align_up((size_t)R * H * es);
   L.dz = o;    o += align_up((size_t)R * F * es);
   L.xp = o;    o += align_up((size_t)R * H * es);
+  L.wrt = o;   o += align_up((size_t)E * H * 4);      // W_r^T (fp32 at most)
   L.stage = o;
   size_t st = moe::router_wgrad_ws_bytes((int)T, (int)H, (int)E);
   if (dt == MOE_BF16) st = std::max(st, moe::split_ws_bytes());
@@ -199,6 +238,9 @@ moe_status moe_stage_workspace_bytes(moe_stage stage, int64_t T, int64_t H, int6
       return MOE_OK;
     case MOE_STAGE_FORWARD:
       *bytes = fwd_layout(T, H, E, top_k, F, dtype).total;
+      return MOE_OK;
+    case MOE_STAGE_EXPERT_FFN_BACKWARD:
+      *bytes = ffn_ws_bytes(T * top_k, F, dtype);
       return MOE_OK;
     default:
       return MOE_ERR_INVALID_ARG;
@@ -280,6 +322,20 @@ moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets, const v
   if (ws_bytes < ffn_ws_bytes(R, F, dtype)) return MOE_ERR_INVALID_ARG;
   return run_ffn(xp, nullptr, R, expert_offsets, w1, w2, R, H, E, F, dtype, yp, ws, nullptr,
                  ffn_split(ws, R, F, dtype), (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn_backward(const void* dyp, const void* xp,
+                                   const int32_t* expert_offsets, const void* z, const void* h,
+                                   const void* w1, const void* w2, int64_t R, int64_t H,
+                                   int64_t E, int64_t F, moe_dtype dtype, void* dxp, void* dw1,
+                                   void* dw2, void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st = check_shape(R, H, E, 1, F, dtype);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !w1 || !w2 || !dw1 || !dw2 || !ws) return MOE_ERR_INVALID_ARG;
+  if (R > 0 && (!dyp || !xp || !z || !h || !dxp)) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_ws_bytes(R, F, dtype)) return MOE_ERR_INVALID_ARG;
+  return run_ffn_bwd(dyp, xp, expert_offsets, z, h, w1, w2, R, H, E, F, dtype, dxp, dw1, dw2, ws,
+                     ffn_split(ws, R, F, dtype), (hipStream_t)stream);
 }
 
 moe_status moe_combine(const void* yp, const int32_t* inv_pos, const float* topk_w, int64_t T,
@@ -463,39 +519,18 @@ moe_status moe_backward(const void* dy, const void* x, const void* w_r, const vo
     if (err == hipSuccess) err = moe::launch_fill_zero(dw2, wbytes, s);
     return launch_status(err);
   }
-  // experts: dz = (dyp W2^T) * GELU'(z), dW2 = h^T dyp, dxp = dz W1^T, dW1 = xp^T dz
-  {
-    if (bf16) {
-      err = moe::launch_gemm_bf16(dyp, nullptr, (int)R, w2, true, dz, off, (int)E, (int)R,
-                                  (int)H, (int)F, moe::EP_DGELU, z, nullptr, stage, s);
-      if (err == hipSuccess)
-        err = moe::launch_gemm_bf16_wgrad(h, dyp, dw2, off, (int)E, (int)F, (int)H, s);
-      if (err == hipSuccess)
-        err = moe::launch_gemm_bf16(dz, nullptr, (int)R, w1, true, dxp, off, (int)E, (int)R,
-                                    (int)F, (int)H, moe::EP_PLAIN, nullptr, nullptr, stage, s);
-      if (err == hipSuccess)
-        err = moe::launch_gather_rows(x, sorted, off, (int)E, (int)R, (int)H, 2, xp, s);
-      if (err == hipSuccess)
-        err = moe::launch_gemm_bf16_wgrad(xp, dz, dw1, off, (int)E, (int)H, (int)F, s);
-    } else {
-      err = moe::launch_gemm_f32_nt((const float*)dyp, (const float*)w2, (float*)dz, off, (int)E,
-                                    (int)R, (int)H, (int)F, (const float*)z, s);
-      if (err == hipSuccess)
-        err = moe::launch_gemm_f32_wgrad((const float*)h, (const float*)dyp, (float*)dw2, off,
-                                         (int)E, (int)F, (int)H, s);
-      if (err == hipSuccess)
-        err = moe::launch_gemm_f32_nt((const float*)dz, (const float*)w1, (float*)dxp, off,
-                                      (int)E, (int)R, (int)F, (int)H, nullptr, s);
-      if (err == hipSuccess)
-        err = moe::launch_gather_rows(x, sorted, off, (int)E, (int)R, (int)H, 4, xp, s);
-      if (err == hipSuccess)
-        err = moe::launch_gemm_f32_wgrad((const float*)xp, (const float*)dz, (float*)dw1, off,
-                                         (int)E, (int)H, (int)F, s);
-    }
-    if (err != hipSuccess) return MOE_ERR_LAUNCH;
-  }
-  return launch_status(moe::launch_dx_finish(dxp, inv, dl, w_r, (int)T, (int)H, (int)E, top_k,
-                                             bf16, w_bf16, dx, s));
+  // experts, over the token rows re-gathered into xp
+  err = moe::launch_gather_rows(x, sorted, off, (int)E, (int)R, (int)H, elem_bytes(dtype), xp, s);
+  if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  const moe_status fs = run_ffn_bwd(dyp, xp, off, z, h, w1, w2, R, H, E, F, dtype, dxp, dw1,
+                                    dw2, dz, stage, s);
+  if (fs != MOE_OK) return fs;
+  // top-k then softmax: each token's logit gradient is zero outside its k
+  // selected experts
+  return launch_status(moe::launch_dx_finish(dxp, inv, topk_ids, dl, w_r, (int)T, (int)H, (int)E,
+                                             top_k, bf16, w_bf16,
+                                             gating == MOE_GATE_TOPK_SOFTMAX, base + L.wrt, dx,
+                                             s));
 }
 
 }  // extern "C"

@@ -316,6 +316,42 @@ def forward(x, w_r, b_r, w1, w2, k: int, ids=None, w=None, gating: str = "topk_s
     return {"y": y, "ids": ids, "w": w, "logits": logits}
 
 
+def expert_block_backward(x_e, w1_e, w2_e, dy_e):
+    """Gradients through one expert's FFN y_e = GELU(x_e W1_e) W2_e for the
+    gradient dy_e of its rows: (dx_e, dW1_e, dW2_e).
+      dW2_e = h^T dy_e,  dz = (dy_e W2_e^T) * GELU'(z),  dW1_e = x_e^T dz,
+      dx_e = dz W1_e^T,  with z = x_e W1_e and h = GELU(z)."""
+    x_e = np.asarray(x_e, np.float64)
+    w1_e = np.asarray(w1_e, np.float64)
+    w2_e = np.asarray(w2_e, np.float64)
+    dy_e = np.asarray(dy_e, np.float64)
+    z = x_e @ w1_e
+    h = gelu_tanh(z)
+    dz = (dy_e @ w2_e.T) * gelu_tanh_grad(z)
+    return dz @ w1_e.T, x_e.T @ dz, h.T @ dy_e
+
+
+def expert_ffn_backward(xp, offsets, w1, w2, dyp):
+    """(dxp[R,H], dW1[E,H,F], dW2[E,F,H]) for the dispatched rows: every
+    expert's block of rows through expert_block_backward; experts with no rows
+    get zero weight gradients."""
+    xp = np.asarray(xp, np.float64)
+    dyp = np.asarray(dyp, np.float64)
+    E = len(offsets) - 1
+    H = xp.shape[1]
+    F = np.asarray(_get(w1, 0)).shape[1]
+    dxp = np.zeros_like(dyp)
+    dw1 = np.zeros((E, H, F), dtype=np.float64)
+    dw2 = np.zeros((E, F, H), dtype=np.float64)
+    for e in range(E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        dxp[a:b], dw1[e], dw2[e] = expert_block_backward(xp[a:b], _get(w1, e), _get(w2, e),
+                                                          dyp[a:b])
+    return dxp, dw1, dw2
+
+
 def backward(x, w_r, b_r, w1, w2, k: int, dy, ids=None, gating: str = "topk_softmax",
              capacity: int = 0):
     """Gradients of the layer forward for an output gradient dy[T,H].
@@ -360,16 +396,12 @@ def backward(x, w_r, b_r, w1, w2, k: int, dy, ids=None, gating: str = "topk_soft
         w1_e = np.asarray(_get(w1, e), np.float64)
         w2_e = np.asarray(_get(w2, e), np.float64)
         x_e = x[tok]
-        z = x_e @ w1_e
-        h = gelu_tanh(z)
-        y_e = h @ w2_e
+        y_e = gelu_tanh(x_e @ w1_e) @ w2_e
         g = dy[tok]
         dw[tok, slot] = (g * y_e).sum(axis=1)
         dy_e = w[tok, slot][:, None] * g
-        dw2[e] = h.T @ dy_e
-        dz = (dy_e @ w2_e.T) * gelu_tanh_grad(z)
-        dw1[e] = x_e.T @ dz
-        np.add.at(dx, tok, dz @ w1_e.T)
+        dx_e, dw1[e], dw2[e] = expert_block_backward(x_e, w1_e, w2_e, dy_e)
+        np.add.at(dx, tok, dx_e)
     dl = gate_weights_grad(logits, ids, dw, gating)
     dx += dl @ w_r64.T
     return {"dx": dx, "dw_r": x.T @ dl, "db_r": dl.sum(axis=0), "dw1": dw1, "dw2": dw2,

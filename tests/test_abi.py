@@ -334,3 +334,27 @@ def test_forward_train_empty_batch_is_a_no_op():
         # the empty token buffers may be NULL
         assert _forward_train(T=0, dt=dt, rdt=rdt, x=N, y=N, ids=N, w=N) == OK
     assert _forward_train(T=0, wr=N) == INV
+
+
+def _ffn_bwd(dyp=P, xp=P, off=P, z=P, h=P, w1=P, w2=P, R=128, H=128, E=8, F=256, dt=BF16,
+             dxp=P, dw1=P, dw2=P, ws=P, nb=1 << 30):
+    return L.moe_expert_ffn_backward(dyp, xp, off, z, h, w1, w2, R, H, E, F, dt, dxp, dw1, dw2,
+                                     ws, nb, N)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dyp=N), INV), (dict(xp=N), INV), (dict(off=N), INV), (dict(z=N), INV),
+    (dict(h=N), INV), (dict(w1=N), INV), (dict(w2=N), INV), (dict(dxp=N), INV),
+    (dict(dw1=N), INV), (dict(dw2=N), INV), (dict(ws=N), INV), (dict(nb=64), INV),
+    (dict(R=-1), INV), (dict(E=0), INV), (dict(F=12), UNS), (dict(dt=2), UNS),
+    (dict(R=0, off=N), INV),
+])
+def test_expert_ffn_backward_rejects(kw, expect):
+    assert _ffn_bwd(**kw) == expect
+
+
+def test_expert_ffn_backward_stage_workspace():
+    st, n = stage_bytes(moe.MOE_STAGE_EXPERT_FFN_BACKWARD, 64, 128, 8, 2, 256, BF16)
+    assert st == OK and n >= 64 * 2 * 256 * 2
+    assert stage_bytes(moe.MOE_STAGE_EXPERT_FFN_BACKWARD, 64, 128, 8, 2, 256, F32)[1] >= \
+        64 * 2 * 256 * 4

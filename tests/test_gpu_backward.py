@@ -150,3 +150,41 @@ def test_backward_empty_batch_zeroes_weight_gradients(dtype):
     for name in ("dw_r", "dw1", "dw2", "db_r"):
         assert torch.count_nonzero(g[name]).item() == 0, name
     assert g["dx"].shape == (0, 64)
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "multitile_bf16", "ragged_f32", "longF_bf16"])
+def test_expert_ffn_backward_stage_matches_oracle(name):
+    """The expert stage alone, on seeded dispatched rows: an offsets table with
+    an empty expert, dyp and xp from the seeded generator, and z, h computed by
+    the oracle and rounded once to the layer's type (inputs of both sides)."""
+    cfg = CASES[name]
+    L = layer(cfg)
+    R = cfg.R
+    g = torch.Generator().manual_seed(7)
+    cuts = torch.sort(torch.randint(0, R + 1, (cfg.E - 1,), generator=g)).values
+    off = torch.cat([torch.zeros(1, dtype=torch.int64), cuts, torch.tensor([R])])
+    off[2] = off[1]                                   # expert 1 has no rows
+    off = torch.maximum(off, torch.cat([torch.zeros(1, dtype=torch.int64), off[:-1]]))
+    offsets = off.to(torch.int32)
+    big = mi.MoEConfig(cfg.name + "_rows", T=R, H=cfg.H, E=cfg.E, k=1, F=cfg.F, dtype=cfg.dtype,
+                       seed=cfg.seed + 1)
+    xp = mi.make_x(big, "cuda")
+    dyp = mi.make_dy(big, "cuda")
+    xp64, dyp64 = f64(xp), f64(dyp)
+    w1_64, w2_64 = f64(L["w1"]), f64(L["w2"])
+    z64 = np.zeros((R, cfg.F))
+    for e in range(cfg.E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        z64[a:b] = xp64[a:b] @ w1_64[e]
+    td = cfg.torch_dtype
+    z = torch.tensor(z64).to(td).cuda()
+    h = torch.tensor(oracle.gelu_tanh(z64)).to(td).cuda()
+    dxp, dw1, dw2 = moe.moe_expert_ffn_backward(dyp, xp, offsets.cuda(), z, h, L["w1"], L["w2"])
+    torch.cuda.synchronize()
+    ref_dxp, ref_dw1, ref_dw2 = oracle.expert_ffn_backward(xp64, offsets.numpy(), w1_64, w2_64,
+                                                           dyp64)
+    tol = TOL[cfg.dtype]
+    assert_close_rel(f64(dxp), ref_dxp, tol, "dxp")
+    assert_close_rel(f64(dw1), ref_dw1, tol, "dw1")
+    assert_close_rel(f64(dw2), ref_dw2, tol, "dw2")
+    assert torch.count_nonzero(dw1[1]).item() == 0 and torch.count_nonzero(dw2[1]).item() == 0

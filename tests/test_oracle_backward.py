@@ -156,3 +156,37 @@ def test_logit_gradient_is_linear_in_dw():
         rhs = 2 * oracle.gate_weights_grad(logits, ids, a, gating) - \
             oracle.gate_weights_grad(logits, ids, b, gating)
         assert np.abs(lhs - rhs).max() < 1e-13
+
+
+def test_expert_ffn_backward_matches_finite_differences():
+    """The dispatched-rows form: L = sum(dyp * expert_ffn(xp, offsets, W1, W2)),
+    with an expert that has no rows (zero weight gradients)."""
+    g = np.random.default_rng(8)
+    E, H, F = 4, 5, 6
+    offsets = np.array([0, 3, 3, 7, 9])
+    xp = g.standard_normal((9, H))
+    w1 = g.standard_normal((E, H, F)) / np.sqrt(H)
+    w2 = g.standard_normal((E, F, H)) / np.sqrt(F)
+    dyp = g.standard_normal((9, H))
+    dxp, dw1, dw2 = oracle.expert_ffn_backward(xp, offsets, w1, w2, dyp)
+    arrays = {"xp": xp, "w1": w1, "w2": w2}
+
+    def loss():
+        return float((dyp * oracle.expert_ffn(arrays["xp"], offsets, arrays["w1"],
+                                              arrays["w2"])).sum())
+
+    for name, grad in (("xp", dxp), ("w1", dw1), ("w2", dw2)):
+        a = arrays[name]
+        fd = np.zeros_like(a)
+        it = np.nditer(a, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            keep = a[i]
+            a[i] = keep + 1e-6
+            lp = loss()
+            a[i] = keep - 1e-6
+            lm = loss()
+            a[i] = keep
+            fd[i] = (lp - lm) / 2e-6
+        assert np.abs(grad - fd).max() <= 1e-6 * max(1.0, np.abs(fd).max()), name
+    assert np.abs(dw1[1]).max() == 0.0 and np.abs(dw2[1]).max() == 0.0
