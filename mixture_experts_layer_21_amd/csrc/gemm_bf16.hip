@@ -174,8 +174,9 @@ struct Lds {
 //   EP_PLAIN  C = acc;  EP_GELU  C = GELU(acc);
 //   EP_DGELU  C = acc * GELU'(z), z read from aux at the same row and column.
 // EPS: the epilogues this instantiation supports (bit 1 << EP_x), so that a
-// kernel carries only the code of its own.
-template <int BM, int BN, int WM, int WN, int EPS, int NFM, int FMA>
+// kernel carries only the code of its own.  PB: 32-row blocks per staging
+// pass (the wave's staging area is PB * 4 KB).
+template <int BM, int BN, int WM, int WN, int EPS, int NFM, int FMA, int PB = 2>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN, WM, WN>::FN][FMA],
                                            uint16_t* __restrict__ C, const Tile& tile, int N,
                                            int ep, const uint16_t* __restrict__ aux, char* stg,
@@ -197,9 +198,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
   static_assert(S::TN * 2 == 128, "staging layout");
   if constexpr (NFM > 0) {
 #pragma unroll
-    for (int p = 0; p < NFM; p += 2) {               // 2 blocks of 32 rows per pass
+    for (int p = 0; p < NFM; p += PB) {              // PB blocks of 32 rows per pass
 #pragma unroll
-      for (int j = p; j < p + 2 && j < NFM; ++j) {
+      for (int j = p; j < p + PB && j < NFM; ++j) {
         const int r = (j - p) * 32 + (lane % 32);
         u32x2 zq[S::FN][4];
         if ((EPS & (1 << EP_DGELU)) && ep == EP_DGELU) {
@@ -238,7 +239,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): this wave's writes are in
       __builtin_amdgcn_wave_barrier();
-      constexpr int ROWS = 32 * 2;
+      constexpr int ROWS = 32 * PB;
 #pragma unroll
       for (int q = 0; q < ROWS / 8; ++q) {           // 8 rows per instruction
         const int r = q * 8 + lane / 8;
@@ -703,16 +704,31 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
 }
 
 // Expert weight gradients: C_e[M][N] = P_e^T Q_e for every expert e, where
-// P_e and Q_e are rows [off[e], off[e+1]) of P [R][M] and Q [R][N].  One
-// 256x256 tile of one expert per workgroup; K = the expert's row count (an
-// expert with no rows gets a zero gradient).  Tiles are numbered expert by
-// expert, column tile outer and row tile inner, then dealt to the XCDs in
-// contiguous runs (xcd_remap).
+// P_e and Q_e are rows [off[e], off[e+1]) of P [R][M] and Q [R][N]
+// (K = the expert's row count; an expert with no rows gets a zero gradient).
+//
+// K is short here (an expert's rows: hundreds), so a tile is only a few K
+// steps and its load prologue and store epilogue would dominate.  The kernel
+// is persistent: workgroup b takes tiles b, b + G, b + 2G, ... (G = grid),
+// each padded to a multiple of 4 K steps (at least 4), and the K-step
+// pipeline runs on across tile boundaries: in a tile's last 4 steps the ring
+// loads already fetch the next tile's first 4 steps, so the next tile starts
+// with its operands in LDS.  The epilogue stages through its own 32 KB (one
+// 32-row block per pass), outside the rings (128 KB + 32 KB = the 160 KB a
+// workgroup may hold).  Both operands are k-major: 4-stage rings, transposed
+// LDS reads, one step's loads issued per step; the wait before step kt+1 is
+// "at most 2 steps' loads outstanding".  Stores share that counter on this
+// architecture; an epilogue's stores stay in flight into the next tile, which
+// keeps those waits correct: loads complete in issue order among themselves,
+// so a count at or below the bound with stores pending still means the older
+// loads have landed (pending stores only make a wait longer).
+// Tiles are numbered expert by expert, column tile outer, row tile inner.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_wgrad(
     const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, uint16_t* __restrict__ C,
     const int* __restrict__ off, int E, int M, int N) {
   using S = GemmShape<BM, BN, WM, WN>;
+  constexpr int FM = S::FM, FN = S::FN;
   __shared__ __attribute__((aligned(1024))) char p0[S::LDS_W];
   __shared__ __attribute__((aligned(1024))) char p1[S::LDS_W];
   __shared__ __attribute__((aligned(1024))) char p2[S::LDS_W];
@@ -721,42 +737,188 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   __shared__ __attribute__((aligned(1024))) char q1[S::LDS_W];
   __shared__ __attribute__((aligned(1024))) char q2[S::LDS_W];
   __shared__ __attribute__((aligned(1024))) char q3[S::LDS_W];
-  // staging: waves 0..1 in p0, 2..3 in p1, 4..5 in p2, 6..7 in p3
-  static_assert(S::NW == 8 && S::LDS_W == 16384, "staging layout");
-  const int wave = threadIdx.x / kWave;
-  char* const sbase = wave < 2 ? p0 : wave < 4 ? p1 : wave < 6 ? p2 : p3;
-  const Lds lds{{p0, p1, p2, p3}, {q0, q1, q2, q3}, sbase + (wave % 2) * 8192};
+  __shared__ __attribute__((aligned(1024))) char stg_all[S::NW * 4096];
+  static_assert(S::LDS_W == 16384 && 8 * S::LDS_W + S::NW * 4096 <= 163840, "LDS budget");
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave % WM;
+  const int wn = wave / WM;
+  const Lds lds{{p0, p1, p2, p3}, {q0, q1, q2, q3}, stg_all + wave * 4096};
 
   const int MT = (M + BM - 1) / BM, NTN = (N + BN - 1) / BN;
   const int per_e = MT * NTN;
-  const int L = xcd_remap(blockIdx.x, E * per_e);
-  if (L < 0) return;
-  const int e = L / per_e, r = L % per_e;
-  Tile tile;
-  tile.valid = 1;
-  tile.e = e;
-  tile.row0 = (r % MT) * BM;
-  tile.mrows = min(BM, M - tile.row0);
-  tile.nt = r / MT;
-  const int kb = off[e];
-  const int rows = off[e + 1] - kb;
-  GemmArgs g;
-  g.A = P + (size_t)kb * M;
-  g.gather = nullptr;
-  g.a_rows = 0;
-  g.B = Q + (size_t)kb * N;
-  g.C = C + (size_t)e * M * N;
-  g.K = rows;
-  g.N = N;
-  g.M = M;
-  g.ep = EP_PLAIN;
-  g.aux = nullptr;
-  g.zout = nullptr;
-  const int wm = wave % WM;
-  int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
-  nfm = __builtin_amdgcn_readfirstlane(nfm);
-  const Split sp{1, 0, 0, nullptr};
-  run_tile<kTN, BM, BN, WM, WN, S::FM>(nfm, g, tile, 0, (rows + BK - 1) / BK, sp, lds);
+  const int total = E * per_e;
+  const int G = gridDim.x;
+  int L = blockIdx.x;
+  if (L >= total) return;
+
+  // k-major loads (as ColLoader): instruction u of this wave covers k rows
+  // 2q, 2q + 1 (q = wave * LU + u) of a stage; the lane's offset is a part
+  // common to every tile (its k row and swizzled 16-byte chunk) plus the
+  // tile's first column
+  constexpr int LU = ColLoader<S::NW>::INSTS;
+  uint32_t pv[LU], qv[LU];
+#pragma unroll
+  for (int u = 0; u < LU; ++u) {
+    const int kr = 2 * (wave * LU + u) + lane / 32;
+    const int c = (lane % 32) ^ swz_w(kr);
+    pv[u] = (uint32_t)kr * M * 2 + c * 16;
+    qv[u] = (uint32_t)kr * N * 2 + c * 16;
+  }
+  // a tile: everything wave-uniform
+  struct State {
+    Tile tile;
+    int nsteps, rows;
+    const uint16_t* pb;      // P rows of the expert
+    const uint16_t* qb;      // Q rows of the expert
+    uint16_t* c;
+  };
+  auto make = [&](int l, State& st) {
+    const int e = l / per_e, r = l % per_e;
+    st.tile.valid = 1;
+    st.tile.e = e;
+    st.tile.row0 = (r % MT) * BM;
+    st.tile.mrows = min(BM, M - st.tile.row0);
+    st.tile.nt = r / MT;
+    const int kb = off[e];
+    st.rows = off[e + 1] - kb;
+    st.nsteps = max(4, ((st.rows + BK - 1) / BK + 3) / 4 * 4);
+    st.pb = P + (size_t)kb * M;
+    st.qb = Q + (size_t)kb * N;
+    st.c = C + (size_t)e * M * N;
+  };
+  // step ks of tile st into stage ks % 4 of both rings; rows at or past the
+  // expert's row count read zero (the descriptors end there)
+  auto load_step = [&](const State& st, int ks, int stage) {
+    const uint32_t k0 = (uint32_t)ks * BK;
+    const uint32_t lim = (uint32_t)st.rows;
+    const uint32_t nk = lim > k0 ? lim - k0 : 0u;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(st.pb + (size_t)k0 * M, nk * M * 2);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(st.qb + (size_t)k0 * N, nk * N * 2);
+    const uint32_t pc = (uint32_t)st.tile.row0 * 2, qc = (uint32_t)st.tile.nt * BN * 2;
+#pragma unroll
+    for (int u = 0; u < LU; ++u)
+      load_to_lds(rp, lds.a[stage] + (wave * LU + u) * 1024, pv[u] + pc);
+#pragma unroll
+    for (int u = 0; u < LU; ++u)
+      load_to_lds(rq, lds.w[stage] + (wave * LU + u) * 1024, qv[u] + qc);
+  };
+  State cur, nxt;
+  make(L, cur);
+  bool has_next = L + G < total;
+  if (has_next) make(L + G, nxt);
+
+  // fragment read offsets (transposed reads on both sides), for slice h = 0
+  // and the first read rd = 0: the k row is 16 h + 8 (gg/2) + 4 rd + li/4,
+  // and moving by 4 or 16 rows keeps k & 3, hence the swizzle, so rd adds
+  // 4 rows (2048 bytes) and h 16 rows (8192 bytes) to the same offset
+  const int gg = lane / 16, li = lane % 16;
+  const int kr0 = 8 * (gg / 2) + li / 4;
+  int fn_col[FN], fm_col[FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int nn = wn * S::TN + 32 * i + 16 * (gg % 2) + 4 * (li % 4);
+    fn_col[i] = kr0 * 512 + (((nn / 8) ^ swz_w(kr0)) * 16) + (nn % 8) * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int mm = wm * S::TM + 32 * j + 16 * (gg % 2) + 4 * (li % 4);
+    fm_col[j] = kr0 * 512 + (((mm / 8) ^ swz_w(kr0)) * 16) + (mm % 8) * 2;
+  }
+  auto read_frags = [&](const char* wst, const char* ast, int h, bf16x8* wf, bf16x8* af) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const u32x2 lo = read_tr(wst + fn_col[i] + h * 8192);
+      const u32x2 hi = read_tr(wst + fn_col[i] + h * 8192 + 2048);
+      wf[i] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const u32x2 lo = read_tr(ast + fm_col[j] + h * 8192);
+      const u32x2 hi = read_tr(ast + fm_col[j] + h * 8192 + 2048);
+      af[j] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+  };
+  f32x16 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
+  bf16x8 wf0[FN], af0[FM], wf1[FN], af1[FM];
+  constexpr int NRD = 2 * FN + 2 * FM;
+  constexpr int NMF = FN * FM;
+  constexpr int LI = 2 * ColLoader<S::NW>::INSTS;      // loads per step
+  auto mfma_slice = [&](const bf16x8* wf, const bf16x8* af) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [&]() {
+    constexpr int PP = NRD < NMF ? NRD : NMF;
+#pragma unroll
+    for (int r = 0; r < PP; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (NMF > PP) __builtin_amdgcn_sched_group_barrier(0x008, NMF - PP, 0);
+    if constexpr (NRD > PP) __builtin_amdgcn_sched_group_barrier(0x100, NRD - PP, 0);
+  };
+  // step kt of the current tile (stage ST = kt % 4); its loads are for step
+  // kt + 4: of this tile, else the next tile's step kt + 4 - nsteps, else
+  // (no next tile) a zero-size read that keeps the per-step load count
+  auto step = [&](int kt, auto st_c) {
+    constexpr int ST = decltype(st_c)::value;
+    read_frags(lds.w[ST], lds.a[ST], 1, wf1, af1);
+    mfma_slice(wf0, af0);
+    interleave();
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * LI));
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // (selects of wave-uniform values: no branch inside the step)
+    const int ld = kt + 4;
+    const bool own = ld < cur.nsteps || !has_next;
+    State sel;
+    sel.tile.row0 = own ? cur.tile.row0 : nxt.tile.row0;
+    sel.tile.nt = own ? cur.tile.nt : nxt.tile.nt;
+    sel.rows = own ? cur.rows : nxt.rows;
+    sel.pb = own ? cur.pb : nxt.pb;
+    sel.qb = own ? cur.qb : nxt.qb;
+    load_step(sel, own ? ld : ld - cur.nsteps, ST);
+    read_frags(lds.w[(ST + 1) % 4], lds.a[(ST + 1) % 4], 0, wf0, af0);
+    mfma_slice(wf1, af1);
+    interleave();
+  };
+
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) load_step(cur, s4, s4);
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(3 * LI));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  read_frags(lds.w[0], lds.a[0], 0, wf0, af0);
+  while (true) {
+    for (int kt = 0; kt < cur.nsteps; kt += 4) {
+      step(kt + 0, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
+      step(kt + 2, std::integral_constant<int, 2>{});
+      step(kt + 3, std::integral_constant<int, 3>{});
+    }
+    store_tile<BM, BN, WM, WN, 1 << EP_PLAIN, FM, FM, 1>(acc, cur.c, cur.tile, N, EP_PLAIN,
+                                                         nullptr, lds.stg);
+    if (!has_next) break;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = f32x16{};
+    cur = nxt;
+    L += G;
+    has_next = L + G < total;
+    if (has_next) make(L + G, nxt);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
 // Split tiles: one workgroup per (split tile, 32-row block jb of every
@@ -885,7 +1047,8 @@ hipError_t launch_gemm_bf16_wgrad(const void* P, const void* Q, void* C, const i
                                   int M, int N, hipStream_t s) {
   const long tiles = (long)E * ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles == 0) return hipSuccess;
-  const long blocks = (tiles + kXcds - 1) / kXcds * kXcds;
+  // persistent: one workgroup per CU (or per tile when there are fewer)
+  const long blocks = std::min<long>(tiles, device_slots());
   hipLaunchKernelGGL((gemm_bf16_wgrad<256, 256, kWM, kWN>), dim3((unsigned)blocks),
                      dim3(kWave * kWM * kWN), 0, s, (const uint16_t*)P, (const uint16_t*)Q,
                      (uint16_t*)C, off, E, M, N);
