@@ -159,7 +159,7 @@ struct GemmArgs {
 // LDS of one workgroup: one array per stage, so the compiler can tell that a
 // read of one stage does not wait on the loads into another.
 //   NN: a[0..1] token stages (32 KB), w[0..3] weight stages (16 KB)
-//   NT: a[0..1] token stages, w[0..1] transposed-weight stages (32 KB)
+//   NT: a[0..1] token stages, w[0..2] transposed-weight stages (32 KB)
 //   TN: a[0..3] P stages, w[0..3] Q stages (16 KB)
 // stg: this wave's 8 KB epilogue staging area (inside the rings).
 struct Lds {
@@ -264,37 +264,38 @@ template <int ROWS, int NW, bool MASK>
 struct RowLoader {
   static constexpr int INSTS = ROWS * 128 / 1024 / NW;   // 1 KB per instruction
   uint32_t voff[INSTS];
-  int dst[INSTS];
-  int ck[INSTS];          // first k of the lane's chunk inside the stage
+  int q0;                 // first instruction index of this wave (uniform)
   const uint16_t* base;
   uint32_t bytes;
   int k_limit;
+  // logical 16-byte chunk a lane moves in instruction q (rows 8q .. 8q+7)
+  __device__ __forceinline__ static int chunk(int q, int lane) {
+    return (lane % 8) ^ swz_a(q * 8 + lane / 8);
+  }
   template <class RowOf>
   __device__ __forceinline__ void init(const uint16_t* b, uint32_t nbytes, int K, int kl,
                                        int wave, int lane, RowOf row_of) {
     base = b;
     bytes = nbytes;
     k_limit = kl;
+    q0 = __builtin_amdgcn_readfirstlane(wave * INSTS);
 #pragma unroll
     for (int u = 0; u < INSTS; ++u) {
-      const int q = wave * INSTS + u;                // 8 rows per instruction
-      const int r = q * 8 + lane / 8;
-      const int c = (lane % 8) ^ swz_a(r);           // logical chunk stored at lane's slot
-      const int mr = row_of(r);
-      voff[u] = mr >= 0 ? (uint32_t)mr * K * 2 + c * 16 : kPastEnd;
-      dst[u] = q * 1024;
-      ck[u] = c * 8;
+      const int q = q0 + u;                          // 8 rows per instruction
+      const int mr = row_of(q * 8 + lane / 8);
+      voff[u] = mr >= 0 ? (uint32_t)mr * K * 2 + chunk(q, lane) * 16 : kPastEnd;
     }
   }
   // K steps k0 / BK and k0 / BK + 1
   __device__ __forceinline__ void load(int k0, char* st) const {
     const uint32_t skip = (uint32_t)k0 * 2;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0, bytes > skip ? bytes - skip : 0u);
+    const int lane = lane_id();
 #pragma unroll
     for (int u = 0; u < INSTS; ++u) {
       uint32_t vo = voff[u];
-      if constexpr (MASK) vo = (k0 + ck[u] < k_limit) ? vo : kPastEnd;
-      load_to_lds(r, st + dst[u], vo);
+      if constexpr (MASK) vo = (k0 + chunk(q0 + u, lane) * 8 < k_limit) ? vo : kPastEnd;
+      load_to_lds(r, st + (q0 + u) * 1024, vo);
     }
   }
 };
@@ -472,8 +473,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   //       odd j, A(j+3, j+4); the prologue W0 W1 A01 W2 W3 A23.  Step kt+1's
   //       data is in once at most 2 W + 2 A (even kt) or 1 W (odd kt) loads
   //       are outstanding.
-  //   NT  both stages (kt / 2) % 2.  Odd j issues A(j+3, j+4) B(j+3, j+4);
-  //       the prologue A01 B01 A23 B23.  Wait: A + B (even kt), 0 (odd kt).
+  //   NT  token stage (kt / 2) % 2, weight stage (kt / 2) % 3 (pairs of
+  //       steps).  Odd j issues A(j+3, j+4) then B(j+5, j+6); the prologue
+  //       B01 A01 B23 A23 B45.  Wait: 2 B + A (even kt), B (odd kt).
   //   TN  both stages kt % 4.  Step j issues P(j+4) Q(j+4); the prologue
   //       P0 Q0 .. P3 Q3.  Wait: 2 (P + Q).
   // (A bare s_barrier: a release fence would wait for every outstanding load.)
@@ -507,9 +509,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   auto step = [&](int kt, auto st_c) {
     constexpr int ST = decltype(st_c)::value;
     constexpr int PAR = ST % 2;
-    constexpr int WS = KIND == kNT ? ST / 2 : ST;              // n-side stage
-    constexpr int WN1 = KIND == kNT ? ((ST + 1) / 2) % 2 : (ST + 1) % 4;
-    constexpr int AS = KIND == kTN ? ST : ST / 2;              // m-side stage
+    constexpr int WS = KIND == kNT ? (ST / 2) % 3 : ST;        // n-side stage
+    constexpr int WN1 = KIND == kNT ? ((ST + 1) / 2) % 3 : (ST + 1) % 4;
+    constexpr int AS = KIND == kTN ? ST : (ST / 2) % 2;        // m-side stage
     constexpr int AN1 = KIND == kTN ? (ST + 1) % 4 : ((ST + 1) / 2) % 2;
     read_frags(lds.w[WS], lds.a[AS], PAR, 1, wf1, af1);
     mfma_slice(wf0, af0);
@@ -520,7 +522,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
       else
         __builtin_amdgcn_s_waitcnt(vmcnt_le(BI));
     } else if constexpr (KIND == kNT) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_le(PAR == 0 ? AI + BI : 0));
+      __builtin_amdgcn_s_waitcnt(vmcnt_le(PAR == 0 ? 2 * BI + AI : BI));
     } else {
       __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * (AI + BI)));
     }
@@ -532,8 +534,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
       if constexpr (PAR == 1) la.load(k0 + (kt + 3) * BK, lds.a[ST / 2]);
     } else if constexpr (KIND == kNT) {
       if constexpr (PAR == 1) {
-        la.load(k0 + (kt + 3) * BK, lds.a[ST / 2]);
-        lb.load(k0 + (kt + 3) * BK, lds.w[ST / 2]);
+        la.load(k0 + (kt + 3) * BK, lds.a[(ST / 2) % 2]);
+        lb.load(k0 + (kt + 5) * BK, lds.w[(ST / 2) % 3]);
       }
     } else {
       lp.load(k0 + (kt + 4) * BK, lds.a[ST]);
@@ -556,11 +558,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     // step 0's data (W0, A01) is in once W2, W3, A23 alone are outstanding
     __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * BI + AI));
   } else if constexpr (KIND == kNT) {
-    la.load(k0, lds.a[0]);
     lb.load(k0, lds.w[0]);
-    la.load(k0 + 2 * BK, lds.a[1]);
+    la.load(k0, lds.a[0]);
     lb.load(k0 + 2 * BK, lds.w[1]);
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(AI + BI));
+    la.load(k0 + 2 * BK, lds.a[1]);
+    lb.load(k0 + 4 * BK, lds.w[2]);
+    // pair 0 (B0, A0) is in once B1, A1, B2 alone are outstanding
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * BI + AI));
   } else {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
@@ -573,11 +577,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   read_frags(lds.w[0], lds.a[0], 0, 0, wf0, af0);
   const int nsteps = kt_end - kt_begin;
-  for (int kt = 0; kt < nsteps; kt += W_STAGES) {
-    step(kt + 0, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
-    step(kt + 2, std::integral_constant<int, 2>{});
-    step(kt + 3, std::integral_constant<int, 3>{});
+  if constexpr (KIND == kNT) {
+    // stage pattern repeats every 12 steps (2 token x 3 weight stages of two
+    // steps): whole periods in the loop, then a remainder of 4 or 8 steps
+    // (a branch inside the loop body defeats the register allocation)
+    const int nmain = nsteps / 12 * 12;
+    int kt = 0;
+    for (; kt < nmain; kt += 12) {
+      step(kt + 0, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
+      step(kt + 2, std::integral_constant<int, 2>{});
+      step(kt + 3, std::integral_constant<int, 3>{});
+      step(kt + 4, std::integral_constant<int, 4>{});
+      step(kt + 5, std::integral_constant<int, 5>{});
+      step(kt + 6, std::integral_constant<int, 6>{});
+      step(kt + 7, std::integral_constant<int, 7>{});
+      step(kt + 8, std::integral_constant<int, 8>{});
+      step(kt + 9, std::integral_constant<int, 9>{});
+      step(kt + 10, std::integral_constant<int, 10>{});
+      step(kt + 11, std::integral_constant<int, 11>{});
+    }
+    if (kt < nsteps) {
+      step(kt + 0, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
+      step(kt + 2, std::integral_constant<int, 2>{});
+      step(kt + 3, std::integral_constant<int, 3>{});
+      if (kt + 4 < nsteps) {
+        step(kt + 4, std::integral_constant<int, 4>{});
+        step(kt + 5, std::integral_constant<int, 5>{});
+        step(kt + 6, std::integral_constant<int, 6>{});
+        step(kt + 7, std::integral_constant<int, 7>{});
+      }
+    }
+  } else {
+    for (int kt = 0; kt < nsteps; kt += W_STAGES) {
+      step(kt + 0, std::integral_constant<int, 0>{});
+      step(kt + 1, std::integral_constant<int, 1>{});
+      step(kt + 2, std::integral_constant<int, 2>{});
+      step(kt + 3, std::integral_constant<int, 3>{});
+    }
   }
   // drain the loads still in flight before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
@@ -657,25 +695,12 @@ __device__ __forceinline__ char* staging(char* lo, char* hi, int nw) {
   return (wave < nw / 2 ? lo : hi) + (wave % (nw / 2)) * 8192;
 }
 
-// Grouped GEMM over dispatched rows (NN: the forward's expert products; NT:
-// the backward's products with transposed expert weights).
+// Grouped GEMM over dispatched rows: split plan, tile lookup and the tile.
 template <int KIND, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_grouped(
-    GemmArgs g, const int* __restrict__ off, int E, int R, float* __restrict__ part,
-    int slots) {
+__device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __restrict__ off,
+                                             int E, int R, float* __restrict__ part, int slots,
+                                             const Lds& lds) {
   using S = GemmShape<BM, BN, WM, WN>;
-  static_assert(KIND != kTN, "TN has its own kernel");
-  __shared__ __attribute__((aligned(1024))) char a0[S::LDS_A];
-  __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
-  constexpr int WB = KIND == kNT ? S::LDS_A : S::LDS_W;       // n-side stage bytes
-  constexpr int WST = KIND == kNT ? 2 : 4;
-  __shared__ __attribute__((aligned(1024))) char w0[WB];
-  __shared__ __attribute__((aligned(1024))) char w1[WB];
-  __shared__ __attribute__((aligned(1024))) char w2[WST == 4 ? WB : 1];
-  __shared__ __attribute__((aligned(1024))) char w3[WST == 4 ? WB : 1];
-  static_assert(S::NW * 8192 <= 2 * S::LDS_A, "staging layout");
-  const Lds lds{{a0, a1, nullptr, nullptr}, {w0, w1, w2, w3}, staging(a0, a1, S::NW)};
-
   const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots);
   const int bid = blockIdx.x;
   int L, kt_begin = 0, kt_end = pl.KT;
@@ -701,6 +726,40 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
   nfm = __builtin_amdgcn_readfirstlane(nfm);
   run_tile<KIND, BM, BN, WM, WN, S::FM>(nfm, g, tile, kt_begin, kt_end, sp, lds);
+}
+
+// The forward's expert products (NN).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_grouped(
+    GemmArgs g, const int* __restrict__ off, int E, int R, float* __restrict__ part,
+    int slots) {
+  using S = GemmShape<BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(1024))) char a0[S::LDS_A];
+  __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
+  __shared__ __attribute__((aligned(1024))) char w0[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char w1[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char w2[S::LDS_W];
+  __shared__ __attribute__((aligned(1024))) char w3[S::LDS_W];
+  static_assert(S::NW * 8192 <= 2 * S::LDS_A, "staging layout");
+  const Lds lds{{a0, a1, nullptr, nullptr}, {w0, w1, w2, w3}, staging(a0, a1, S::NW)};
+  grouped_body<kNN, BM, BN, WM, WN>(g, off, E, R, part, slots, lds);
+}
+
+// The backward's products with a transposed expert weight (NT): two token
+// stages and three weight stages of 32 KB (the 160 KB a workgroup may hold).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_nt(
+    GemmArgs g, const int* __restrict__ off, int E, int R, float* __restrict__ part,
+    int slots) {
+  using S = GemmShape<BM, BN, WM, WN>;
+  __shared__ __attribute__((aligned(1024))) char a0[S::LDS_A];
+  __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
+  __shared__ __attribute__((aligned(1024))) char b0[S::LDS_A];
+  __shared__ __attribute__((aligned(1024))) char b1[S::LDS_A];
+  __shared__ __attribute__((aligned(1024))) char b2[S::LDS_A];
+  static_assert(5 * S::LDS_A <= 163840 && S::NW * 8192 <= 2 * S::LDS_A, "LDS budget");
+  const Lds lds{{a0, a1, nullptr, nullptr}, {b0, b1, b2, nullptr}, staging(a0, a1, S::NW)};
+  grouped_body<kNT, BM, BN, WM, WN>(g, off, E, R, part, slots, lds);
 }
 
 // Expert weight gradients: C_e[M][N] = P_e^T Q_e for every expert e, where
@@ -1005,8 +1064,12 @@ hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* spl
   long blocks = mt_max * NTN + slots;
   if (blocks <= slots) return hipSuccess;
   float* part = (float*)split_ws;
-  hipLaunchKernelGGL((gemm_bf16_grouped<KIND, BM, BN, WM, WN>), dim3((unsigned)blocks),
-                     dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
+  if constexpr (KIND == kNT)
+    hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN>), dim3((unsigned)blocks),
+                       dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
+  else
+    hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN>), dim3((unsigned)blocks),
+                       dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // tiles are split only when K has at least 4 * MIN_SPLIT_STEPS steps
