@@ -579,8 +579,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   const int nsteps = kt_end - kt_begin;
   if constexpr (KIND == kNT) {
     // stage pattern repeats every 12 steps (2 token x 3 weight stages of two
-    // steps): whole periods in the loop, then a remainder of 4 or 8 steps
-    // (a branch inside the loop body defeats the register allocation)
+    // steps): whole periods in the loop, then a remainder of 4, 8 or 12
+    // steps (a branch inside the loop body defeats the register allocation)
     const int nmain = nsteps / 12 * 12;
     int kt = 0;
     for (; kt < nmain; kt += 12) {
@@ -607,6 +607,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
         step(kt + 5, std::integral_constant<int, 5>{});
         step(kt + 6, std::integral_constant<int, 6>{});
         step(kt + 7, std::integral_constant<int, 7>{});
+        if (kt + 8 < nsteps) {
+          step(kt + 8, std::integral_constant<int, 8>{});
+          step(kt + 9, std::integral_constant<int, 9>{});
+          step(kt + 10, std::integral_constant<int, 10>{});
+          step(kt + 11, std::integral_constant<int, 11>{});
+        }
       }
     }
   } else {

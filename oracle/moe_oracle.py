@@ -316,19 +316,21 @@ def forward(x, w_r, b_r, w1, w2, k: int, ids=None, w=None, gating: str = "topk_s
     return {"y": y, "ids": ids, "w": w, "logits": logits}
 
 
-def expert_block_backward(x_e, w1_e, w2_e, dy_e):
+def expert_block_backward(x_e, w1_e, w2_e, dy_e, weights: bool = True):
     """Gradients through one expert's FFN y_e = GELU(x_e W1_e) W2_e for the
     gradient dy_e of its rows: (dx_e, dW1_e, dW2_e).
       dW2_e = h^T dy_e,  dz = (dy_e W2_e^T) * GELU'(z),  dW1_e = x_e^T dz,
-      dx_e = dz W1_e^T,  with z = x_e W1_e and h = GELU(z)."""
+      dx_e = dz W1_e^T,  with z = x_e W1_e and h = GELU(z).
+    weights=False skips the two weight gradients (returned as None)."""
     x_e = np.asarray(x_e, np.float64)
     w1_e = np.asarray(w1_e, np.float64)
     w2_e = np.asarray(w2_e, np.float64)
     dy_e = np.asarray(dy_e, np.float64)
     z = x_e @ w1_e
-    h = gelu_tanh(z)
     dz = (dy_e @ w2_e.T) * gelu_tanh_grad(z)
-    return dz @ w1_e.T, x_e.T @ dz, h.T @ dy_e
+    if not weights:
+        return dz @ w1_e.T, None, None
+    return dz @ w1_e.T, x_e.T @ dz, gelu_tanh(z).T @ dy_e
 
 
 def expert_ffn_backward(xp, offsets, w1, w2, dyp):

@@ -8,7 +8,9 @@ where asked, db_r) must lie within the forward's tolerance of the oracle's,
 relative to the largest magnitude of that gradient: 2e-2 for the bf16 path
 (whose intermediates dyp, z, h, dz are bf16 like its forward's h), 1e-4 for
 fp32.  Shapes cover several tiles with ragged tails, K tails that are not a
-multiple of 64 (H = 200, F = 136), the split-K path (H or F = 4096), experts
+multiple of 64 (H = 200, F = 136), K step counts that leave 9 and 11 steps
+after the transposed-weight GEMM's 12-step period, the split-K path (H or
+F = 4096), experts
 with no rows, k = 1, and the variants (softmax-first gating, capacity drops,
 an fp32 router, a router bias)."""
 import numpy as np
@@ -38,6 +40,9 @@ CASES = {
                            bias0=3.0),
     "longH_bf16": C("longH_bf16", T=40, H=4096, E=24, k=3, F=64, dtype="bf16"),
     "longF_bf16": C("longF_bf16", T=64, H=128, E=4, k=2, F=4096, dtype="bf16"),
+    # K step counts 21 (H = 672) and 11 (F = 352): remainders of 9 and 11 steps
+    # after the transposed-weight GEMM's 12-step period
+    "period_tail_bf16": C("period_tail_bf16", T=96, H=672, E=4, k=2, F=352, dtype="bf16"),
 }
 _cache = {}
 
@@ -152,7 +157,8 @@ def test_backward_empty_batch_zeroes_weight_gradients(dtype):
     assert g["dx"].shape == (0, 64)
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "multitile_bf16", "ragged_f32", "longF_bf16"])
+@pytest.mark.parametrize("name", ["ragged_bf16", "multitile_bf16", "ragged_f32", "longF_bf16",
+                                  "period_tail_bf16"])
 def test_expert_ffn_backward_stage_matches_oracle(name):
     """The expert stage alone, on seeded dispatched rows: an offsets table with
     an empty expert, dyp and xp from the seeded generator, and z, h computed by
