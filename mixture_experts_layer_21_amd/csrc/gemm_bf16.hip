@@ -12,11 +12,14 @@
 // stream past, section "tiling") mapped onto a tile order that keeps the
 // row tiles of one weight slab adjacent (see map_tile).
 //
-// Design (one 256x256 output tile per workgroup and CU; 8 waves as 2 along
+// Design (256x256 output tiles, one workgroup per CU; 8 waves as 2 along
 // the tokens x 4 along the columns, two waves per SIMD, 128x64 per wave; K
 // step 32):
+//  * the forward kernel is persistent: a workgroup runs its tiles one after
+//    another and each tile's last steps already load the next tile's first
+//    ones, so no tile starts with an empty pipeline;
 //  * operands move global -> LDS with buffer_load ... lds (no VGPRs), 1 KB
-//    per instruction, into a 4-stage ring (128 KB), three steps in flight;
+//    per instruction, into multi-stage rings (128 KB), steps in flight;
 //  * W stays in its natural k-major layout in LDS; the MFMA operand (4
 //    consecutive k of one column) comes from ds_read_b64_tr_b16; both
 //    tiles are XOR-swizzled so the operand reads are free of bank conflicts;
@@ -28,7 +31,9 @@
 //    and MFMAs (compile-time count per wave), so a tile with few rows costs
 //    little compute;
 //  * tiles of the last partial round are split along K (deterministic
-//    stream-K, see gemm_bf16_grouped).
+//    stream-K, see split_plan).
+// The same pipeline, with other operand arrangements, serves the backward
+// (gemm_bf16_nt, gemm_bf16_wgrad).
 #include "common.h"
 #include "launch.h"
 
@@ -337,6 +342,17 @@ struct ColLoader {
   }
 };
 
+// Persistent forward GEMM: what a work item (a tile, or a split piece of one)
+// hands over to the next item of its workgroup.  The last 4 steps of an item
+// issue the next item's first 4 steps' loads, in the order the prologue
+// would, so the next item starts with them in flight.
+struct Carry {
+  bool carry_in;          // this item's prologue loads were issued by the previous item
+  bool has_next;
+  Tile next;              // the next item's tile
+  int next_kb, next_ke;   // and its K-step range
+};
+
 // One output tile.  NFM (compile time) is the number of 32-row blocks of
 // this wave that hold valid rows, so the main loop has no branches around
 // its LDS reads and MFMAs (the accumulators stay in registers).
@@ -347,9 +363,11 @@ struct ColLoader {
 // K range read as zero, so no clamping appears in the loop.  In NN, past-K
 // columns of A read the next row of the tile (or x's next row when the rows
 // are gathered) but meet zero W rows; NT masks both operands' K tails.
-template <int KIND, int BM, int BN, int WM, int WN, int NFM>
+template <int KIND, int BM, int BN, int WM, int WN, int NFM, bool PERSIST = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, int kt_begin,
-                                          int kt_end, const Split& sp, const Lds& lds) {
+                                          int kt_end, const Split& sp, const Lds& lds,
+                                          const Carry* cy = nullptr) {
+  static_assert(!PERSIST || KIND == kNN, "the persistent form is the forward's");
   using S = GemmShape<BM, BN, WM, WN>;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -391,6 +409,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   }
   constexpr int AI = KIND == kTN ? ColLoader<S::NW>::INSTS : RowLoader<BM, S::NW, false>::INSTS;
   constexpr int BI = KIND == kNT ? RowLoader<BN, S::NW, true>::INSTS : ColLoader<S::NW>::INSTS;
+  const int k0 = kt_begin * BK;
+  const int nsteps = kt_end - kt_begin;
+  // persistent: the loaders of the next item (or, with none, this item's
+  // loaders past its K range, which read zeros)
+  RowLoader<BM, S::NW, false> la_n;
+  ColLoader<S::NW> lw_n;
+  int k0n = 0;
+  const int nsr = (nsteps + 3) / 4 * 4;
+  if constexpr (PERSIST) {
+    if (cy->has_next) {
+      const Tile& t2 = cy->next;
+      const int kl2 = min(K, cy->next_ke * BK);
+      const uint32_t a_bytes2 =
+          (uint32_t)(g.gather ? g.a_rows : min(g.a_rows, t2.row0 + t2.mrows)) * K * 2;
+      la_n.init(g.A, a_bytes2, K, kl2, wave, lane, [&](int m) {
+        return m < t2.mrows ? (g.gather ? g.gather[t2.row0 + m] : t2.row0 + m) : -1;
+      });
+      lw_n.init(g.B + (size_t)t2.e * K * N, N, kl2, t2.nt * BN, wave, lane);
+      k0n = cy->next_kb * BK;
+    } else {
+      la_n = la;
+      lw_n = lw;
+      k0n = k0 + nsr * BK;
+    }
+  }
 
   // --- fragment read offsets ------------------------------------------------
   // K-contiguous operand (16-byte reads): row rbase + lane%32 (+ 32 per
@@ -504,10 +547,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     if constexpr (NRD > P) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P, 0);
   };
 
-  const int k0 = kt_begin * BK;
   // step kt of the unrolled group of 4
-  auto step = [&](int kt, auto st_c) {
+  auto step = [&](int kt, auto st_c, auto last_c) {
     constexpr int ST = decltype(st_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;   // persistent: an item's last 4 steps
     constexpr int PAR = ST % 2;
     constexpr int WS = KIND == kNT ? (ST / 2) % 3 : ST;        // n-side stage
     constexpr int WN1 = KIND == kNT ? ((ST + 1) / 2) % 3 : (ST + 1) % 4;
@@ -529,7 +572,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): reads of step kt done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if constexpr (KIND == kNN) {
+    if constexpr (KIND == kNN && LAST) {
+      // steps kt+4 (and kt+3, kt+4 for the token ring) are the next item's
+      lw_n.load(k0n + (kt + W_STAGES - nsr) * BK, lds.w[ST]);
+      if constexpr (PAR == 1) la_n.load(k0n + (kt + 3 - nsr) * BK, lds.a[ST / 2]);
+    } else if constexpr (KIND == kNN) {
       lw.load(k0 + (kt + W_STAGES) * BK, lds.w[ST]);
       if constexpr (PAR == 1) la.load(k0 + (kt + 3) * BK, lds.a[ST / 2]);
     } else if constexpr (KIND == kNT) {
@@ -549,12 +596,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   // The loop runs a multiple of 4 steps; steps past the K range meet zero
   // rows (or zero chunks) and add nothing.
   if constexpr (KIND == kNN) {
-    lw.load(k0, lds.w[0]);
-    lw.load(k0 + BK, lds.w[1]);
-    la.load(k0, lds.a[0]);
-    lw.load(k0 + 2 * BK, lds.w[2]);
-    lw.load(k0 + 3 * BK, lds.w[3]);
-    la.load(k0 + 2 * BK, lds.a[1]);
+    if (!PERSIST || !cy->carry_in) {
+      lw.load(k0, lds.w[0]);
+      lw.load(k0 + BK, lds.w[1]);
+      la.load(k0, lds.a[0]);
+      lw.load(k0 + 2 * BK, lds.w[2]);
+      lw.load(k0 + 3 * BK, lds.w[3]);
+      la.load(k0 + 2 * BK, lds.a[1]);
+    }
     // step 0's data (W0, A01) is in once W2, W3, A23 alone are outstanding
     __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * BI + AI));
   } else if constexpr (KIND == kNT) {
@@ -576,55 +625,69 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   read_frags(lds.w[0], lds.a[0], 0, 0, wf0, af0);
-  const int nsteps = kt_end - kt_begin;
-  if constexpr (KIND == kNT) {
+  if constexpr (PERSIST) {
+    // all groups but the last, then the last with the next item's loads
+    int kt = 0;
+    for (; kt + 4 < nsr; kt += 4) {
+      step(kt + 0, std::integral_constant<int, 0>{}, std::false_type{});
+      step(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
+      step(kt + 2, std::integral_constant<int, 2>{}, std::false_type{});
+      step(kt + 3, std::integral_constant<int, 3>{}, std::false_type{});
+    }
+    step(kt + 0, std::integral_constant<int, 0>{}, std::true_type{});
+    step(kt + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    step(kt + 2, std::integral_constant<int, 2>{}, std::true_type{});
+    step(kt + 3, std::integral_constant<int, 3>{}, std::true_type{});
+  } else if constexpr (KIND == kNT) {
     // stage pattern repeats every 12 steps (2 token x 3 weight stages of two
     // steps): whole periods in the loop, then a remainder of 4, 8 or 12
     // steps (a branch inside the loop body defeats the register allocation)
     const int nmain = nsteps / 12 * 12;
     int kt = 0;
     for (; kt < nmain; kt += 12) {
-      step(kt + 0, std::integral_constant<int, 0>{});
-      step(kt + 1, std::integral_constant<int, 1>{});
-      step(kt + 2, std::integral_constant<int, 2>{});
-      step(kt + 3, std::integral_constant<int, 3>{});
-      step(kt + 4, std::integral_constant<int, 4>{});
-      step(kt + 5, std::integral_constant<int, 5>{});
-      step(kt + 6, std::integral_constant<int, 6>{});
-      step(kt + 7, std::integral_constant<int, 7>{});
-      step(kt + 8, std::integral_constant<int, 8>{});
-      step(kt + 9, std::integral_constant<int, 9>{});
-      step(kt + 10, std::integral_constant<int, 10>{});
-      step(kt + 11, std::integral_constant<int, 11>{});
+      step(kt + 0, std::integral_constant<int, 0>{}, std::false_type{});
+      step(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
+      step(kt + 2, std::integral_constant<int, 2>{}, std::false_type{});
+      step(kt + 3, std::integral_constant<int, 3>{}, std::false_type{});
+      step(kt + 4, std::integral_constant<int, 4>{}, std::false_type{});
+      step(kt + 5, std::integral_constant<int, 5>{}, std::false_type{});
+      step(kt + 6, std::integral_constant<int, 6>{}, std::false_type{});
+      step(kt + 7, std::integral_constant<int, 7>{}, std::false_type{});
+      step(kt + 8, std::integral_constant<int, 8>{}, std::false_type{});
+      step(kt + 9, std::integral_constant<int, 9>{}, std::false_type{});
+      step(kt + 10, std::integral_constant<int, 10>{}, std::false_type{});
+      step(kt + 11, std::integral_constant<int, 11>{}, std::false_type{});
     }
     if (kt < nsteps) {
-      step(kt + 0, std::integral_constant<int, 0>{});
-      step(kt + 1, std::integral_constant<int, 1>{});
-      step(kt + 2, std::integral_constant<int, 2>{});
-      step(kt + 3, std::integral_constant<int, 3>{});
+      step(kt + 0, std::integral_constant<int, 0>{}, std::false_type{});
+      step(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
+      step(kt + 2, std::integral_constant<int, 2>{}, std::false_type{});
+      step(kt + 3, std::integral_constant<int, 3>{}, std::false_type{});
       if (kt + 4 < nsteps) {
-        step(kt + 4, std::integral_constant<int, 4>{});
-        step(kt + 5, std::integral_constant<int, 5>{});
-        step(kt + 6, std::integral_constant<int, 6>{});
-        step(kt + 7, std::integral_constant<int, 7>{});
+        step(kt + 4, std::integral_constant<int, 4>{}, std::false_type{});
+        step(kt + 5, std::integral_constant<int, 5>{}, std::false_type{});
+        step(kt + 6, std::integral_constant<int, 6>{}, std::false_type{});
+        step(kt + 7, std::integral_constant<int, 7>{}, std::false_type{});
         if (kt + 8 < nsteps) {
-          step(kt + 8, std::integral_constant<int, 8>{});
-          step(kt + 9, std::integral_constant<int, 9>{});
-          step(kt + 10, std::integral_constant<int, 10>{});
-          step(kt + 11, std::integral_constant<int, 11>{});
+          step(kt + 8, std::integral_constant<int, 8>{}, std::false_type{});
+          step(kt + 9, std::integral_constant<int, 9>{}, std::false_type{});
+          step(kt + 10, std::integral_constant<int, 10>{}, std::false_type{});
+          step(kt + 11, std::integral_constant<int, 11>{}, std::false_type{});
         }
       }
     }
   } else {
     for (int kt = 0; kt < nsteps; kt += W_STAGES) {
-      step(kt + 0, std::integral_constant<int, 0>{});
-      step(kt + 1, std::integral_constant<int, 1>{});
-      step(kt + 2, std::integral_constant<int, 2>{});
-      step(kt + 3, std::integral_constant<int, 3>{});
+      step(kt + 0, std::integral_constant<int, 0>{}, std::false_type{});
+      step(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
+      step(kt + 2, std::integral_constant<int, 2>{}, std::false_type{});
+      step(kt + 3, std::integral_constant<int, 3>{}, std::false_type{});
     }
   }
   // drain the loads still in flight before the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+  // (persistent: the next item's loads stay in flight; the kernel drains at
+  // its end)
+  if constexpr (!PERSIST) __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 
   // --- split tiles: the piece leaves its fp32 partial sums in the workspace
   // (in register order: thread-contiguous 16-byte groups, so every store
@@ -643,10 +706,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     }
     return;
   }
+  constexpr int EPS = kind_epilogues(KIND);
+  if constexpr (PERSIST) {
+    // staging outside the rings (4 KB per wave, one 32-row block per pass):
+    // no barrier, the next item's loads land in the rings meanwhile
+    if (g.zout)
+      store_tile<BM, BN, WM, WN, 1, NFM, FMA, 1>(acc, g.zout, tile, N, EP_PLAIN, nullptr, lds.stg);
+    store_tile<BM, BN, WM, WN, EPS, NFM, FMA, 1>(acc, g.C, tile, N, g.ep, g.aux, lds.stg);
+    return;
+  }
   // one barrier first, because other waves may still read the K loop's last
   // stages
   __syncthreads();
-  constexpr int EPS = kind_epilogues(KIND);
   if constexpr (KIND == kNN)
     if (g.zout) store_tile<BM, BN, WM, WN, 1, NFM>(acc, g.zout, tile, N, EP_PLAIN, nullptr, lds.stg);
   store_tile<BM, BN, WM, WN, EPS, NFM>(acc, g.C, tile, N, g.ep, g.aux, lds.stg);
@@ -654,17 +725,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
 
 // gemm_tile with NFM = nfm (0 <= nfm <= NF), chosen at run time from a
 // wave-uniform count.
-template <int KIND, int BM, int BN, int WM, int WN, int NF>
+template <int KIND, int BM, int BN, int WM, int WN, int NF, bool PERSIST = false>
 __device__ __forceinline__ void run_tile(int nfm, const GemmArgs& g, const Tile& tile,
                                          int kt_begin, int kt_end, const Split& sp,
-                                         const Lds& lds) {
+                                         const Lds& lds, const Carry* cy = nullptr) {
   if constexpr (NF == 0) {
-    gemm_tile<KIND, BM, BN, WM, WN, 0>(g, tile, kt_begin, kt_end, sp, lds);
+    gemm_tile<KIND, BM, BN, WM, WN, 0, PERSIST>(g, tile, kt_begin, kt_end, sp, lds, cy);
   } else {
     if (nfm == NF)
-      gemm_tile<KIND, BM, BN, WM, WN, NF>(g, tile, kt_begin, kt_end, sp, lds);
+      gemm_tile<KIND, BM, BN, WM, WN, NF, PERSIST>(g, tile, kt_begin, kt_end, sp, lds, cy);
     else
-      run_tile<KIND, BM, BN, WM, WN, NF - 1>(nfm, g, tile, kt_begin, kt_end, sp, lds);
+      run_tile<KIND, BM, BN, WM, WN, NF - 1, PERSIST>(nfm, g, tile, kt_begin, kt_end, sp, lds,
+                                                      cy);
   }
 }
 
@@ -701,7 +773,8 @@ __device__ __forceinline__ char* staging(char* lo, char* hi, int nw) {
   return (wave < nw / 2 ? lo : hi) + (wave % (nw / 2)) * 8192;
 }
 
-// Grouped GEMM over dispatched rows: split plan, tile lookup and the tile.
+// Grouped GEMM over dispatched rows, one work item per workgroup (the NT
+// kernel): split plan, tile lookup and the tile.
 template <int KIND, int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __restrict__ off,
                                              int E, int R, float* __restrict__ part, int slots,
@@ -734,7 +807,11 @@ __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __res
   run_tile<KIND, BM, BN, WM, WN, S::FM>(nfm, g, tile, kt_begin, kt_end, sp, lds);
 }
 
-// The forward's expert products (NN).
+// The forward's expert products, persistent: one workgroup per CU takes its
+// whole tiles b, b + G, ... (G = grid; the same XCD-aware order as the
+// one-tile-per-workgroup kernel) and then its split piece, if any, handing
+// the pipeline from one item to the next (Carry); the epilogue stages
+// through its own 32 KB (128 KB of rings + 32 KB = 160 KB).
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_grouped(
     GemmArgs g, const int* __restrict__ off, int E, int R, float* __restrict__ part,
@@ -746,9 +823,54 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   __shared__ __attribute__((aligned(1024))) char w1[S::LDS_W];
   __shared__ __attribute__((aligned(1024))) char w2[S::LDS_W];
   __shared__ __attribute__((aligned(1024))) char w3[S::LDS_W];
-  static_assert(S::NW * 8192 <= 2 * S::LDS_A, "staging layout");
-  const Lds lds{{a0, a1, nullptr, nullptr}, {w0, w1, w2, w3}, staging(a0, a1, S::NW)};
-  grouped_body<kNN, BM, BN, WM, WN>(g, off, E, R, part, slots, lds);
+  __shared__ __attribute__((aligned(1024))) char stg_all[S::NW * 4096];
+  static_assert(2 * S::LDS_A + 4 * S::LDS_W + S::NW * 4096 <= 163840, "LDS budget");
+  const int wave = threadIdx.x / kWave;
+  const Lds lds{{a0, a1, nullptr, nullptr}, {w0, w1, w2, w3}, stg_all + wave * 4096};
+  const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots);
+  const int G = gridDim.x, b = blockIdx.x;
+  const int NTN = (g.N + BN - 1) / BN;
+  const int n_whole = pl.dp / G;                       // pl.dp is a multiple of slots = G
+  const int n_items = n_whole + (b < pl.sk * pl.nsplit ? 1 : 0);
+  // item i: a whole tile (i < n_whole) or this workgroup's split piece
+  auto item = [&](int i, Tile& t, int& kb, int& ke, Split& sp) {
+    sp = Split{1, 0, 0, part};
+    kb = 0;
+    ke = pl.KT;
+    int L;
+    if (i < n_whole) {
+      L = xcd_remap(b + i * G, pl.dp);
+    } else {
+      L = pl.dp + b / pl.nsplit;
+      sp.S = pl.nsplit;
+      sp.s = b % pl.nsplit;
+      sp.slot = L - pl.dp;
+      kb = sp.s * pl.KT / pl.nsplit;
+      ke = (sp.s + 1) * pl.KT / pl.nsplit;
+    }
+    t = lookup_tile(off, E, R, BM, NTN, L);
+  };
+  const int wm = wave % WM;
+  Carry cy;
+  cy.carry_in = false;
+  Tile cur;
+  int ckb = 0, cke = 0;
+  Split csp;
+  if (n_items > 0) item(0, cur, ckb, cke, csp);
+  for (int i = 0; i < n_items; ++i) {
+    cy.has_next = i + 1 < n_items;
+    Split nsp;
+    if (cy.has_next) item(i + 1, cy.next, cy.next_kb, cy.next_ke, nsp);
+    int nfm = max(0, min(S::FM, (cur.mrows - wm * S::TM + 31) / 32));
+    nfm = __builtin_amdgcn_readfirstlane(nfm);
+    run_tile<kNN, BM, BN, WM, WN, S::FM, true>(nfm, g, cur, ckb, cke, csp, lds, &cy);
+    cy.carry_in = true;
+    cur = cy.next;
+    ckb = cy.next_kb;
+    cke = cy.next_ke;
+    csp = nsp;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
 }
 
 // The backward's products with a transposed expert weight (NT): two token
@@ -1073,8 +1195,8 @@ hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* spl
   if constexpr (KIND == kNT)
     hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN>), dim3((unsigned)blocks),
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
-  else
-    hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN>), dim3((unsigned)blocks),
+  else   // persistent: one workgroup per CU
+    hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN>), dim3((unsigned)slots),
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
