@@ -329,7 +329,8 @@ RoutePlan plan_route(int T, int H, int E, bool bf16, bool wf32) {
     return p;
   }
   int tpw = 1;
-  while (tpw < 16 && tpw * 4 < NET) tpw *= 2;
+  // two expert groups at most (each group re-reads x)
+  while (tpw < 16 && tpw * 2 < NET) tpw *= 2;
   p.TPW = tpw;
   p.EG = (NET + tpw - 1) / tpw;
   // about 2048 waves in all, and a staged W_r block of at most 64 KB
