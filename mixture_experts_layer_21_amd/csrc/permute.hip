@@ -58,8 +58,11 @@ __global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ co
   const int L = (nchunks + P - 1) / P;     // chunks per thread (contiguous)
   const int b0 = min(nchunks, p * L), b1 = min(nchunks, b0 + L);
   int sum = 0;
-  if (active)
+  if (active) {
+    // (unrolled: several loads in flight instead of one per trip)
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) sum += counts[(size_t)b * E + e];
+  }
   if (active) seg[p * E + e] = sum;
   __syncthreads();
   if (t < E) {
@@ -90,6 +93,7 @@ __global__ __launch_bounds__(1024) void perm_scan(const int32_t* __restrict__ co
   // chunk bases: the rank, inside its expert, of each chunk's first pair
   if (active) {
     int run = seg[p * E + e];
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) {
       const int c = counts[(size_t)b * E + e];
       base[(size_t)b * E + e] = run;
