@@ -395,8 +395,9 @@ def main_train(a, moe, cfg):
     roof["per_launch"] = {"flops": g_flops, "bytes": g_bytes, "ms": g_sec * 1e3}
     cpu = None
     if not a.no_cpu_baseline:
-        n = a.cpu_sample_tokens or {"tiny_fp32": 64, "mixtral_bf16": 32, "skewed_bf16": 32,
-                                    "many_experts_bf16": 64, "weight_bound_bf16": 2}[cfg.name]
+        # (about 10 s of host work each)
+        n = a.cpu_sample_tokens or {"tiny_fp32": 64, "mixtral_bf16": 1024, "skewed_bf16": 1024,
+                                    "many_experts_bf16": 2048, "weight_bound_bf16": 16}[cfg.name]
         cpu = cpu_baseline_train(cfg, L, dy, min(n, T))
     # training-step flops: forward (router + 2 GEMMs) and backward (router
     # weight and input gradients + 4 GEMMs)
@@ -479,8 +480,9 @@ def main():
 
     cpu = None
     if not a.no_cpu_baseline:
-        n = a.cpu_sample_tokens or {"tiny_fp32": 64, "mixtral_bf16": 128, "skewed_bf16": 128,
-                                    "many_experts_bf16": 256, "weight_bound_bf16": 4}[cfg.name]
+        # (about 10 s of host work at most: the whole batch)
+        n = a.cpu_sample_tokens or {"tiny_fp32": 64, "mixtral_bf16": 2048, "skewed_bf16": 2048,
+                                    "many_experts_bf16": 4096, "weight_bound_bf16": 64}[cfg.name]
         cpu = cpu_baseline(cfg, L, min(n, cfg.T))
 
     layer_tflops = flops / sec / 1e12
