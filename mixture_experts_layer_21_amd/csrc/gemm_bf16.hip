@@ -588,6 +588,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
       lp.load(k0 + (kt + 4) * BK, lds.a[ST]);
       lw.load(k0 + (kt + 4) * BK, lds.w[ST]);
     }
+    // this step's loads go out right after the barrier: left to itself the
+    // scheduler sinks them past the next 16 MFMAs, which shortens their lead
+    // by a step and makes the next waits (counted for the order above) wait
+    // for one step more than they need
+    constexpr int NL = KIND == kNN ? BI + (PAR == 1 ? AI : 0)
+                                   : (KIND == kNT ? (PAR == 1 ? AI + BI : 0) : AI + BI);
+    if constexpr (NL > 0) __builtin_amdgcn_sched_group_barrier(0x020, NL, 0);
     read_frags(lds.w[WN1], lds.a[AN1], 1 - PAR, 0, wf0, af0);
     mfma_slice(wf1, af1);
     interleave();
@@ -1075,6 +1082,7 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     sel.pb = own ? cur.pb : nxt.pb;
     sel.qb = own ? cur.qb : nxt.qb;
     load_step(sel, own ? ld : ld - cur.nsteps, ST);
+    __builtin_amdgcn_sched_group_barrier(0x020, LI, 0);    // loads first (as in gemm_tile)
     read_frags(lds.w[(ST + 1) % 4], lds.a[(ST + 1) % 4], 0, wf0, af0);
     mfma_slice(wf1, af1);
     interleave();
