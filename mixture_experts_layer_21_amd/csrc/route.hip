@@ -211,6 +211,41 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
   }
 }
 
+// (value, expert) pair of the lane DPP control CTRL names (every lane active)
+template <int CTRL>
+__device__ __forceinline__ void dpp_pair(float v, int e, float& ov, int& oe) {
+  ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  oe = __builtin_amdgcn_update_dpp(0, e, CTRL, 0xF, 0xF, false);
+}
+
+// keep the larger value, on equal values the lower expert
+__device__ __forceinline__ void take_better(float& bv, int& be, float ov, int oe) {
+  if (ov > bv || (ov == bv && oe < be)) {
+    bv = ov;
+    be = oe;
+  }
+}
+
+// Arg-max over the wave of (value desc, expert asc); every lane ends with
+// the winner.  Within each row of 16 lanes: the partner at lane ^ 1 and ^ 2
+// (quad permutes), then the mirrored lane of the other quad (half-row mirror)
+// and of the other half-row (row mirror); across rows: lanes 16 and 32 away.
+// The winner is unique, so the order of the exchanges does not matter.
+__device__ __forceinline__ void wave_argmax(float& bv, int& be) {
+  float ov;
+  int oe;
+  dpp_pair<0xB1>(bv, be, ov, oe);     // quad_perm [1,0,3,2]
+  take_better(bv, be, ov, oe);
+  dpp_pair<0x4E>(bv, be, ov, oe);     // quad_perm [2,3,0,1]
+  take_better(bv, be, ov, oe);
+  dpp_pair<0x141>(bv, be, ov, oe);    // row_half_mirror
+  take_better(bv, be, ov, oe);
+  dpp_pair<0x140>(bv, be, ov, oe);    // row_mirror
+  take_better(bv, be, ov, oe);
+#pragma unroll
+  for (int d = 16; d <= 32; d *= 2) take_better(bv, be, __shfl_xor(bv, d, kWave), __shfl_xor(be, d, kWave));
+}
+
 template <int NPL>
 __global__ __launch_bounds__(256) void route_select(
     const float* __restrict__ part, const float* __restrict__ bias,
@@ -221,8 +256,9 @@ __global__ __launch_bounds__(256) void route_select(
   if (t >= T) return;
 
   // sum the S partial logits in split order; all loads of a batch of SB
-  // splits (for every expert of the lane) are issued before any is added
-  constexpr int SB = NPL <= 4 ? 8 : (NPL <= 8 ? 4 : 2);
+  // splits (for every expert of the lane, 64 values) are issued before any
+  // is added
+  constexpr int SB = 64 / NPL < 16 ? 64 / NPL : 16;
   float v[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) v[i] = 0.f;
@@ -270,15 +306,7 @@ __global__ __launch_bounds__(256) void route_select(
           be = e;
         }
       }
-#pragma unroll
-      for (int d = kWave / 2; d >= 1; d >>= 1) {
-        const float ov = __shfl_xor(bv, d, kWave);
-        const int oe = __shfl_xor(be, d, kWave);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
+      wave_argmax(bv, be);
       if ((be % kWave) == lane) taken |= 1u << (be / kWave);
       sel_v[j] = bv;
       sel_e[j] = be;
