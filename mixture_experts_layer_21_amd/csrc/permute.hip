@@ -32,6 +32,23 @@ namespace {
 
 constexpr int CH = 256;    // pairs per chunk (one workgroup of 256 threads)
 
+// Bits of an expert id (ids are in [0, E)).
+__device__ __forceinline__ int id_bits(int E) { return E > 1 ? 32 - __clz(E - 1) : 0; }
+
+// The lanes of the wave whose `valid` value equals this lane's (0 for an
+// invalid lane), for values below 2^nbits: one ballot per bit, each lane
+// keeping the lanes that agree with it on that bit.  ceil(log2 E) ballots,
+// however many distinct experts the wave holds.
+__device__ __forceinline__ uint64_t wave_match(int v, bool valid, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (v >> b) & 1;
+    const uint64_t s = __ballot(valid && bit);
+    m &= bit ? s : ~s;
+  }
+  return valid ? m : 0ull;
+}
+
 __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ ids, int R,
                                                   int E, int32_t* __restrict__ counts) {
   extern __shared__ int hist[];
@@ -113,6 +130,7 @@ __global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ id
   int* wcnt = sm + E;         // [4][E]: pairs of each expert in each wave this round
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int b = blockIdx.x;
+  const int nbits = id_bits(E);
   for (int e = tid; e < E; e += 256) {
     running[e] = base[(size_t)b * E + e];
 #pragma unroll
@@ -125,15 +143,7 @@ __global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ id
     const bool valid = i < R;
     const int my_e = valid ? ids[i] : -1;
     // lanes of this wave holding the same expert
-    uint64_t remaining = __ballot(valid);
-    uint64_t peers = 0;
-    while (remaining) {
-      const int leader = __builtin_ctzll(remaining);
-      const int le = wave_bcast(my_e, leader);
-      const uint64_t m = __ballot(valid && my_e == le);
-      if (valid && my_e == le) peers = m;
-      remaining &= ~m;
-    }
+    const uint64_t peers = wave_match(my_e, valid, nbits);
     const int rank = __popcll(peers & lt_mask);
     if (valid && rank == 0) wcnt[wave * E + my_e] = __popcll(peers);
     __syncthreads();
@@ -176,8 +186,8 @@ __global__ __launch_bounds__(256) void perm_gather(const u32x4* __restrict__ x,
   }
 }
 
-constexpr int kSmallE = 256, kSmallR = 16384;
-constexpr int kSmallWaves = 16, kSmallChunks = kSmallR / (kSmallWaves * kWave);   // 16
+constexpr int kSmallE = 256, kSmallR = 16384;   // ids fit 8 bits, ranks 16
+constexpr int kSmallWaves = 16;
 
 // One workgroup of 16 waves.  Wave w owns a contiguous run of 64-pair chunks
 // (pairs in index order), ranks each pair inside its expert among the wave's
@@ -185,6 +195,7 @@ constexpr int kSmallWaves = 16, kSmallChunks = kSmallR / (kSmallWaves * kWave); 
 // barrier the per-wave counts give both the expert totals and each wave's
 // starting rank.  Every pair's id is loaded up front, so the only serial
 // latency is the ranking arithmetic itself.
+template <int kSmallChunks>   // 64-pair chunks per wave, at most
 __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int R, int E,
                                                    int k, int cap, int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ sorted_token,
@@ -194,13 +205,16 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
   __shared__ int wsum[kSmallWaves];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int nch = (R + kWave - 1) / kWave;
-  const int cpw = (nch + kSmallWaves - 1) / kSmallWaves;   // chunks per wave, <= 16
+  const int cpw = (nch + kSmallWaves - 1) / kSmallWaves;   // chunks per wave
   const int c0 = wave * cpw;
-  int my_e[kSmallChunks], rk[kSmallChunks];
+  const int nbits = id_bits(E);
+  // pair j of this lane: its expert id, then (after ranking) rank << 8 | id
+  // (ids < 256, ranks < 32768); -1 for no pair
+  int pr[kSmallChunks];
 #pragma unroll
   for (int j = 0; j < kSmallChunks; ++j) {
     const int i = (c0 + j) * kWave + lane;
-    my_e[j] = (j < cpw && i < R) ? ids[i] : -1;
+    pr[j] = (j < cpw && i < R) ? ids[i] : -1;
   }
   for (int t = tid; t < kSmallWaves * E; t += 1024) wcnt[t / E][t % E] = 0;
   __syncthreads();
@@ -208,24 +222,14 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
 #pragma unroll
   for (int j = 0; j < kSmallChunks; ++j) {
     if (j < cpw) {
-      const int e = my_e[j];
+      const int e = pr[j];
       const bool valid = e >= 0;
-      uint64_t remaining = __ballot(valid);
-      uint64_t peers = 0;
-      while (remaining) {
-        const int leader = __builtin_ctzll(remaining);
-        const int le = wave_bcast(e, leader);
-        const uint64_t m = __ballot(valid && e == le);
-        if (valid && e == le) peers = m;
-        remaining &= ~m;
-      }
+      const uint64_t peers = wave_match(e, valid, nbits);
       const int before = __popcll(peers & lt_mask);
       const int cnt = valid ? wcnt[wave][e] : 0;
-      rk[j] = cnt + before;
+      if (valid) pr[j] = (cnt + before) << 8 | e;
       // one lane per peer group advances the count, after every lane has read it
       if (valid && before == 0) wcnt[wave][e] = cnt + __popcll(peers);
-    } else {
-      rk[j] = 0;
     }
   }
   __syncthreads();
@@ -258,10 +262,10 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kSmallChunks; ++j) {
-    const int e = my_e[j];
-    if (e >= 0) {
+    if (pr[j] >= 0) {
+      const int e = pr[j] & 255;
       const int i = (c0 + j) * kWave + lane;
-      const int r_e = wcnt[wave][e] + rk[j];
+      const int r_e = wcnt[wave][e] + (pr[j] >> 8);
       if (r_e < cap) {
         const int pos = off_s[e] + r_e;
         sorted_token[pos] = i / k;
@@ -290,8 +294,10 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
   int32_t* counts = (int32_t*)ws;
   int32_t* base = (int32_t*)((char*)ws + align_up((size_t)nchunks * E * sizeof(int32_t)));
   if (R > 0 && E <= kSmallE && R <= kSmallR) {
-    hipLaunchKernelGGL(perm_small, dim3(1), dim3(1024), 0, s, ids, R, E, k, cap, offsets,
-                       sorted_token, inv_pos);
+    // (one workgroup stops paying beyond 16 chunks per wave: each chunk's
+    // rank waits on the previous chunk's count update in LDS)
+    hipLaunchKernelGGL(perm_small<kSmallR / (kSmallWaves * kWave)>, dim3(1), dim3(1024), 0, s,
+                       ids, R, E, k, cap, offsets, sorted_token, inv_pos);
   } else {
     if (nchunks > 0)
       hipLaunchKernelGGL(perm_count, dim3(nchunks), dim3(256), E * sizeof(int), s, ids, R, E,

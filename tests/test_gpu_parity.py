@@ -34,6 +34,9 @@ SMALL = {
     "wide_E_bf16": C("wide_E_bf16", T=20, H=64, E=1000, k=16, F=32, dtype="bf16"),
     "skewed_small_bf16": C("skewed_small_bf16", T=256, H=128, E=8, k=2, F=256, dtype="bf16",
                            bias0=3.0),
+    # more pairs than the one-workgroup dispatch takes (T*k > 16384): the
+    # count / scan / place kernels
+    "long_dispatch_bf16": C("long_dispatch_bf16", T=4500, H=64, E=64, k=8, F=64, dtype="bf16"),
     # few tiles with a long K: the expert GEMM splits tiles along K (partials
     # summed by the last piece), checked here on every element
     "ksplit_bf16": C("ksplit_bf16", T=300, H=4096, E=2, k=1, F=512, dtype="bf16"),
