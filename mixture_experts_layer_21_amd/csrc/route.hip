@@ -20,7 +20,10 @@
 //                     so the sum is an fp32-accumulated x . W_r.
 // fp32 path: the logits come from the fp32 grouped GEMM in dense mode.
 //
-//   route_select      one wave per token: sums the S partial logits in fixed
+//   route_select      (route_select_rows for T >= 1024 and E <= 256: one
+//                     token per row of 16 lanes, the same steps with the
+//                     arg-max exchanges kept inside the row)
+//                     one wave per token: sums the S partial logits in fixed
 //                     order, adds the bias, takes k rounds of a 64-lane
 //                     (value desc, index asc) arg-max, then the gate weights:
 //                     the softmax of the k winners, or (softmax-then-top-k
@@ -338,6 +341,122 @@ __global__ __launch_bounds__(256) void route_select(
   }
 }
 
+// Arg-max over the 16 lanes of each row (the first four exchanges of
+// wave_argmax): every lane of the row ends with the row's winner.
+__device__ __forceinline__ void row_argmax(float& bv, int& be) {
+  float ov;
+  int oe;
+  dpp_pair<0xB1>(bv, be, ov, oe);     // quad_perm [1,0,3,2]
+  take_better(bv, be, ov, oe);
+  dpp_pair<0x4E>(bv, be, ov, oe);     // quad_perm [2,3,0,1]
+  take_better(bv, be, ov, oe);
+  dpp_pair<0x141>(bv, be, ov, oe);    // row_half_mirror
+  take_better(bv, be, ov, oe);
+  dpp_pair<0x140>(bv, be, ov, oe);    // row_mirror
+  take_better(bv, be, ov, oe);
+}
+
+// Sum over the 16 lanes of each row, every lane ending with the total.
+__device__ __forceinline__ float row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// route_select for many tokens and E <= 256: one token per row of 16 lanes,
+// four per wave.  Lane r of a row holds experts r, r + 16, ... (NV values,
+// ascending), so each arg-max round is a lane-local scan plus four DPP
+// exchanges inside the row, with no cross-row permutes; the split sums, bias,
+// selection, tie rule, gate weights and outputs are those of route_select.
+template <int NV>
+__global__ __launch_bounds__(256) void route_select_rows(
+    const float* __restrict__ part, const float* __restrict__ bias,
+    int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int EP,
+    int S, int k, int softmax_all, float* __restrict__ logits) {
+  const int rl = threadIdx.x % 16;
+  const int t = (blockIdx.x * 256 + threadIdx.x) / 16;
+  if (t >= T) return;   // whole rows leave together: the DPP partners stay in the row
+
+  constexpr int SB = 64 / NV < 16 ? 64 / NV : 16;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = 0.f;
+  const size_t sstride = (size_t)T * EP;
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    float q[NV][SB];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = rl + i * 16;
+      const float* p = part + ((size_t)s0 * T + t) * EP + e;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) q[i][u] = (e < E && s0 + u < S) ? p[u * sstride] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int u = 0; u < SB; ++u) v[i] += q[i][u];
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = rl + i * 16;
+    if (e < E) {
+      if (bias) v[i] += bias[e];
+      if (logits) logits[(size_t)t * E + e] = v[i];
+    } else {
+      v[i] = -__builtin_inff();
+    }
+  }
+  uint32_t taken = 0;            // bit i: v[i] already selected
+  float sel_v[16];
+  int sel_e[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    sel_v[j] = -__builtin_inff();
+    sel_e[j] = 0;
+    if (j < k) {
+      float bv = -__builtin_inff();
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = rl + i * 16;
+        // within a lane e increases with i: strict ">" keeps the lower index
+        if (e < E && !((taken >> i) & 1u) && (v[i] > bv || be == 0x7fffffff)) {
+          bv = v[i];
+          be = e;
+        }
+      }
+      row_argmax(bv, be);
+      if ((be % 16) == rl) taken |= 1u << (be / 16);
+      sel_v[j] = bv;
+      sel_e[j] = be;
+    }
+  }
+  const float m = sel_v[0];
+  float sum = 0.f;
+  if (softmax_all) {
+    float part_sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (rl + i * 16 < E) part_sum += expf(v[i] - m);
+    sum = row_sum(part_sum);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k) sum += expf(sel_v[j] - m);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < k && rl == j) {
+      ids[(size_t)t * k + j] = sel_e[j];
+      w[(size_t)t * k + j] = expf(sel_v[j] - m) / sum;
+    }
+  }
+}
+
+constexpr int kRowSelectMinT = 1024;
+
 template <int NPL>
 void launch_select(const float* part, const float* bias, int32_t* ids, float* w,
                    int T, int E, int EP, int S, int k, int softmax_all, float* logits,
@@ -413,8 +532,22 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int npl = (E + kWave - 1) / kWave;
   const int sa = softmax_all ? 1 : 0;
+  // many tokens, E <= 256: one token per row of 16 lanes (enough waves at
+  // T / 4 to fill the GPU); otherwise one token per wave
+  if (T >= kRowSelectMinT && E <= 256) {
+    const int nv = (E + 15) / 16;
+    const dim3 g((unsigned)((T + 15) / 16)), b(256);
+#define MOE_SELECT_ROWS(NV_)                                                                        hipLaunchKernelGGL((route_select_rows<NV_>), g, b, 0, s, part, bias, ids, w, T, E, p.EP, p.S,                        k, sa, logits)
+    if (nv <= 1) MOE_SELECT_ROWS(1);
+    else if (nv <= 2) MOE_SELECT_ROWS(2);
+    else if (nv <= 4) MOE_SELECT_ROWS(4);
+    else if (nv <= 8) MOE_SELECT_ROWS(8);
+    else MOE_SELECT_ROWS(16);
+#undef MOE_SELECT_ROWS
+    return hipGetLastError();
+  }
+  const int npl = (E + kWave - 1) / kWave;
   if (npl <= 1) launch_select<1>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
   else if (npl <= 2) launch_select<2>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
   else if (npl <= 4) launch_select<4>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);

@@ -34,6 +34,8 @@ SMALL = {
     "wide_E_bf16": C("wide_E_bf16", T=20, H=64, E=1000, k=16, F=32, dtype="bf16"),
     "skewed_small_bf16": C("skewed_small_bf16", T=256, H=128, E=8, k=2, F=256, dtype="bf16",
                            bias0=3.0),
+    # T >= 1024 and E <= 256: the selection runs one token per 16-lane row
+    "rows_bf16": C("rows_bf16", T=1100, H=128, E=40, k=6, F=64, dtype="bf16"),
     # more pairs than the one-workgroup dispatch takes (T*k > 16384): the
     # count / scan / place kernels
     "long_dispatch_bf16": C("long_dispatch_bf16", T=4500, H=64, E=64, k=8, F=64, dtype="bf16"),
@@ -138,8 +140,9 @@ def test_forward_small(name):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("E,k", [(8, 1), (8, 2), (64, 8), (128, 8), (256, 8), (33, 5)])
-def test_route_exact_ties(dtype, E, k):
-    inp = mi.integer_inputs(96, 64, E, 8, -2, 2, seed=E * 31 + k, dtype=dtype, device="cuda")
+@pytest.mark.parametrize("T", [96, 1100])   # one token per wave / per 16-lane row
+def test_route_exact_ties(dtype, E, k, T):
+    inp = mi.integer_inputs(T, 64, E, 8, -2, 2, seed=E * 31 + k, dtype=dtype, device="cuda")
     ids, w = moe.moe_route(inp["x"], inp["w_r"], None, k)
     torch.cuda.synchronize()
     l = oracle.router_logits(f64(inp["x"]), f64(inp["w_r"]))

@@ -29,6 +29,10 @@ SMALL = {
     "skewed_small_bf16": C("skewed_small_bf16", T=256, H=128, E=8, k=2, F=256, dtype="bf16",
                            bias0=3.0),
     "longH_bf16": C("longH_bf16", T=40, H=4096, E=24, k=3, F=64, dtype="bf16"),
+    # T >= 1024 and E <= 256: the selection runs one token per 16-lane row
+    "rows_bf16": C("rows_bf16", T=1100, H=128, E=40, k=6, F=64, dtype="bf16"),
+    "rows_wide_E_bf16": C("rows_wide_E_bf16", T=1030, H=64, E=200, k=8, F=32, dtype="bf16"),
+    "rows_f32": C("rows_f32", T=1050, H=72, E=12, k=3, F=40, dtype="f32"),
 }
 BF16_SMALL = [n for n, c in SMALL.items() if c.dtype == "bf16"]
 _cache = {}
