@@ -169,11 +169,14 @@ moe_status moe_expert_capacity(int64_t T, int32_t top_k, int64_t E, int64_t fact
  * each expert (then ascending slot).
  *   topk_ids[T,top_k] int32 in [0,E) (as produced by moe_route).
  *   expert_offsets[E+1] int32: expert e owns dispatched rows
- *     [expert_offsets[e], expert_offsets[e+1]); expert_offsets[E] = R.
+ *     [expert_offsets[e], expert_offsets[e+1]); expert_offsets[E] = R when
+ *     every id is in [0,E).
  *   sorted_token[R] int32: source token of each dispatched row.
  *   inv_pos[T*top_k] int32: dispatched row of pair (t, j), at index t*top_k+j.
  *   xp[R,H] (dtype): xp[p,:] = x[sorted_token[p],:], a bit copy.
- * Ids outside [0,E) are not checked on the device and give undefined output.
+ * A pair whose id is outside [0,E) is dropped as a pair beyond the capacity
+ * of moe_permute_ex is (inv_pos = -1, not counted in expert_offsets): a bad
+ * id never indexes memory.
  */
 moe_status moe_permute(const void* x, const int32_t* topk_ids,
                        int64_t T, int64_t H, int64_t E, int32_t top_k,
@@ -219,7 +222,8 @@ moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets,
  * token's expert outputs,
  *   y[t,:] = sum_{j<top_k} topk_w[t,j] * yp[inv_pos[t*top_k+j],:]
  * summed in fp32 in slot order, then stored in dtype (round to nearest even).
- * A slot with inv_pos < 0 (dropped by moe_permute_ex) adds nothing.
+ * A slot whose inv_pos is outside [0, T*top_k) adds nothing (-1: a pair
+ * dropped by the dispatch); yp is never read outside its T*top_k rows.
  *   yp[T*top_k,H], y[T,H] in dtype; inv_pos int32; topk_w fp32.
  */
 moe_status moe_combine(const void* yp, const int32_t* inv_pos,

@@ -7,7 +7,8 @@
 // and the grid has one thread per output chunk (bf16: two chunks, 64 apart,
 // when the row allows it, for more loads in flight), so the pass is bound by
 // HBM bandwidth rather than by load latency even for a handful of tokens.  A
-// slot dropped by a capacity-limited dispatch (inv_pos < 0) adds nothing.
+// slot dropped by a capacity-limited dispatch (inv_pos < 0) adds nothing, and
+// so does a row index past the T*k rows of yp (never read).
 #include "common.h"
 #include "launch.h"
 
@@ -35,10 +36,11 @@ __global__ __launch_bounds__(256) void combine_bf16(const u32x4* __restrict__ yp
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
       const int p = inv_pos[t * k + j];
-      wj[j] = p >= 0 ? w[t * k + j] : 0.f;
+      const bool in = (unsigned)p < (unsigned)(T * k);   // dropped slots (p < 0) add nothing
+      wj[j] = in ? w[t * k + j] : 0.f;
 #pragma unroll
       for (int u = 0; u < CPT; ++u)
-        v[j][u] = p >= 0 ? yp[(size_t)p * chunks + c0 + u * kWave] : u32x4{0, 0, 0, 0};
+        v[j][u] = in ? yp[(size_t)p * chunks + c0 + u * kWave] : u32x4{0, 0, 0, 0};
     }
   }
 #pragma unroll
@@ -75,8 +77,9 @@ __global__ __launch_bounds__(256) void combine_f32(const float4* __restrict__ yp
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
       const int p = inv_pos[(size_t)t * k + j];
-      wj[j] = p >= 0 ? w[(size_t)t * k + j] : 0.f;
-      v[j] = p >= 0 ? yp[(size_t)p * chunks + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const bool in = (unsigned)p < (unsigned)(T * k);   // dropped slots (p < 0) add nothing
+      wj[j] = in ? w[(size_t)t * k + j] : 0.f;
+      v[j] = in ? yp[(size_t)p * chunks + c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

@@ -23,7 +23,9 @@
 //                contiguous run of pairs, the per-wave counts are scanned,
 //                then every pair is placed (the same stable order)
 //
-// All counts are integers: placement is exact and deterministic.
+// All counts are integers: placement is exact and deterministic.  A pair
+// whose id is outside [0, E) is dropped like a pair beyond the capacity
+// (inv_pos = -1), so a bad id never indexes memory.
 #include "common.h"
 #include "launch.h"
 
@@ -56,7 +58,10 @@ __global__ __launch_bounds__(256) void perm_count(const int32_t* __restrict__ id
   __syncthreads();
   const int b = blockIdx.x;
   const int end = min(R, (b + 1) * CH);
-  for (int i = b * CH + threadIdx.x; i < end; i += 256) atomicAdd(&hist[ids[i]], 1);
+  for (int i = b * CH + threadIdx.x; i < end; i += 256) {
+    const int e = ids[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);   // other ids: dropped
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) counts[(size_t)b * E + e] = hist[e];
 }
@@ -140,8 +145,9 @@ __global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ id
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   for (int r = 0; r < CH; r += 256) {
     const int i = b * CH + r + tid;
-    const bool valid = i < R;
-    const int my_e = valid ? ids[i] : -1;
+    const int my_e = i < R ? ids[i] : -1;
+    const bool valid = i < R && (unsigned)my_e < (unsigned)E;
+    if (i < R && !valid) inv_pos[i] = -1;   // an id outside [0, E): dropped
     // lanes of this wave holding the same expert
     const uint64_t peers = wave_match(my_e, valid, nbits);
     const int rank = __popcll(peers & lt_mask);
@@ -209,12 +215,13 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
   const int c0 = wave * cpw;
   const int nbits = id_bits(E);
   // pair j of this lane: its expert id, then (after ranking) rank << 8 | id
-  // (ids < 256, ranks < 32768); -1 for no pair
+  // (ids < 256, ranks < 32768); -1 for no pair, -2 for an id outside [0, E)
   int pr[kSmallChunks];
 #pragma unroll
   for (int j = 0; j < kSmallChunks; ++j) {
     const int i = (c0 + j) * kWave + lane;
-    pr[j] = (j < cpw && i < R) ? ids[i] : -1;
+    const int e = (j < cpw && i < R) ? ids[i] : -1;
+    pr[j] = (j < cpw && i < R && (unsigned)e >= (unsigned)E) ? -2 : e;
   }
   for (int t = tid; t < kSmallWaves * E; t += 1024) wcnt[t / E][t % E] = 0;
   __syncthreads();
@@ -262,6 +269,7 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kSmallChunks; ++j) {
+    if (pr[j] == -2) inv_pos[(c0 + j) * kWave + lane] = -1;   // dropped
     if (pr[j] >= 0) {
       const int e = pr[j] & 255;
       const int i = (c0 + j) * kWave + lane;

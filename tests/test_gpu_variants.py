@@ -223,3 +223,57 @@ def test_expert_ffn_ignores_rows_past_offsets(name):
     assert torch.isnan(yp[Rk:]).all()             # untouched
     ref = oracle.expert_ffn(f64(xp[:Rk]), off.cpu().numpy(), f64(L["w1"]), f64(L["w2"]))
     assert_close_rel(f64(yp[:Rk]), ref, TOL[cfg.dtype], f"{name} yp kept rows")
+
+
+# --- indices outside their ranges ---------------------------------------------
+
+BAD_IDS = [-1, -(2 ** 31), 2 ** 31 - 1]
+
+
+@pytest.mark.parametrize("T,k,E", [(50, 3, 8), (6000, 3, 8), (40, 4, 300)])
+@pytest.mark.parametrize("cap", [0, 7])
+def test_permute_drops_ids_outside_range(T, k, E, cap):
+    """A pair whose id is outside [0, E) is dropped (inv_pos = -1) and counted
+    nowhere; the other pairs are placed as if it were absent.  Expected values:
+    the oracle's dispatch with every bad id relabelled to an extra expert E,
+    whose block (the last one) is then dropped.  Covers the one-workgroup
+    dispatch (T*k <= 16384, E <= 256) and the count / scan / place kernels."""
+    g = torch.Generator().manual_seed(T * 7 + E + cap)
+    ids = torch.randint(0, E, (T, k), generator=g, dtype=torch.int32)
+    bad = torch.rand((T, k), generator=g) < 0.1
+    pick = torch.randint(0, len(BAD_IDS) + 2, (T, k), generator=g)
+    table = torch.tensor(BAD_IDS + [E, E + 7], dtype=torch.int64)
+    ids = torch.where(bad, table[pick].to(torch.int32), ids)
+    x = torch.randn(T, 64, generator=g).to(torch.bfloat16).cuda()
+    off, st, inv, xp = moe.moe_permute_ex(x, ids.cuda(), E, cap)
+    torch.cuda.synchronize()
+    ids_np = ids.numpy().astype(np.int64)
+    relabel = np.where((ids_np < 0) | (ids_np >= E), E, ids_np)
+    o_off, o_st, _, o_inv = oracle.dispatch(relabel, E + 1, cap)
+    o_inv = np.where(relabel == E, -1, o_inv)
+    np.testing.assert_array_equal(off.cpu().numpy(), o_off[:E + 1])
+    Rk = int(o_off[E])
+    np.testing.assert_array_equal(st.cpu().numpy()[:Rk], o_st[:Rk])
+    np.testing.assert_array_equal(inv.cpu().numpy(), o_inv.ravel())
+    assert torch.equal(xp[:Rk], x[st[:Rk].long()])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_combine_skips_rows_outside_yp(dtype):
+    """inv_pos entries outside [0, T*k) add nothing (yp is never read there)."""
+    T, k, H = 300, 4, 128
+    g = torch.Generator().manual_seed(5)
+    yp = torch.randn(T * k, H, generator=g).to(dtype)
+    inv = torch.randperm(T * k, generator=g).to(torch.int32)
+    w = torch.rand(T, k, generator=g)
+    w = (w / w.sum(1, keepdim=True)).contiguous()
+    bad = torch.rand(T * k, generator=g) < 0.15
+    vals = torch.tensor([-1, -7, T * k, T * k + 100, 2 ** 31 - 1], dtype=torch.int32)
+    inv = torch.where(bad, vals[torch.randint(0, len(vals), (T * k,), generator=g)], inv)
+    y = moe.moe_combine(yp.cuda(), inv.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    inv_np = inv.numpy().astype(np.int64)
+    inv_np = np.where((inv_np < 0) | (inv_np >= T * k), -1, inv_np).reshape(T, k)
+    ref = oracle.combine(f64(yp), inv_np, f64(w))
+    tol = TOL["bf16"] if dtype == torch.bfloat16 else TOL["f32"]
+    assert_close_rel(f64(y), ref, tol, "combine with out-of-range rows")
