@@ -60,15 +60,28 @@ __device__ __forceinline__ float gelu_tanh_grad(float z) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// v of the lane the DPP control CTRL names, 0 where that lane is outside the
+// row or the destination lane is masked off (ROW_MASK: rows, BANK_MASK: groups
+// of four lanes in each row).
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, all in DPP moves: shifts
+// by 1, 2 and 3 lanes, then by 4 and 8 (into the upper lanes of each row)
+// give each row's prefix; broadcasting lane 15 into rows 1 and 3 and lane 31
+// into rows 2 and 3 carries the row totals.  (No LDS permutes: seven dependent
+// VALU steps instead of six LDS round trips.)
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
-  return v;
+  int s = v + dpp_or_zero<0x111, 0xF, 0xF>(v);   // row_shr:1
+  s += dpp_or_zero<0x112, 0xF, 0xF>(v);          // row_shr:2
+  s += dpp_or_zero<0x113, 0xF, 0xF>(v);          // row_shr:3
+  s += dpp_or_zero<0x114, 0xF, 0xE>(s);          // row_shr:4, lanes 4..15 of each row
+  s += dpp_or_zero<0x118, 0xF, 0xC>(s);          // row_shr:8, lanes 8..15
+  s += dpp_or_zero<0x142, 0xA, 0xF>(s);          // row_bcast:15 into rows 1, 3
+  s += dpp_or_zero<0x143, 0xC, 0xF>(s);          // row_bcast:31 into rows 2, 3
+  return s;
 }
 
 __device__ __forceinline__ int wave_bcast(int v, int src_lane) {
