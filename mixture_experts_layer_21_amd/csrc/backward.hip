@@ -20,18 +20,6 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
-  return v;
-}
-
 // 8 consecutive elements of a row as fp32 (bf16 rows: one 16-byte load)
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* row, int c, float (&v)[8]) {

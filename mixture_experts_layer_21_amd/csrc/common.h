@@ -84,6 +84,33 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return s;
 }
 
+// Sum and maximum over the wave (every lane active, result in every lane):
+// inside each row of 16 lanes by DPP exchanges (lane ^ 1, lane ^ 2, the
+// half-row mirror, the row mirror: every lane of a row ends with the same
+// bits), then the four row results read from lanes 0, 16, 32 and 48 and
+// combined in that order.  No LDS permutes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v);   // row_half_mirror
+  v += dpp_f32<0x140>(v);   // row_mirror
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+
 __device__ __forceinline__ int wave_bcast(int v, int src_lane) {
   return __builtin_amdgcn_readlane(v, src_lane);
 }

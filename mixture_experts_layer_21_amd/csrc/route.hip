@@ -232,7 +232,8 @@ __device__ __forceinline__ void take_better(float& bv, int& be, float ov, int oe
 // Arg-max over the wave of (value desc, expert asc); every lane ends with
 // the winner.  Within each row of 16 lanes: the partner at lane ^ 1 and ^ 2
 // (quad permutes), then the mirrored lane of the other quad (half-row mirror)
-// and of the other half-row (row mirror); across rows: lanes 16 and 32 away.
+// and of the other half-row (row mirror); across rows: the four row winners
+// read from lanes 0, 16, 32 and 48.
 // The winner is unique, so the order of the exchanges does not matter.
 __device__ __forceinline__ void wave_argmax(float& bv, int& be) {
   float ov;
@@ -245,8 +246,14 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& be) {
   take_better(bv, be, ov, oe);
   dpp_pair<0x140>(bv, be, ov, oe);    // row_mirror
   take_better(bv, be, ov, oe);
+  // every lane of a row now holds the row's winner: combine the four rows
+  float rv = lane_f32(bv, 0);
+  int re = __builtin_amdgcn_readlane(be, 0);
 #pragma unroll
-  for (int d = 16; d <= 32; d *= 2) take_better(bv, be, __shfl_xor(bv, d, kWave), __shfl_xor(be, d, kWave));
+  for (int r = 16; r < kWave; r += 16)
+    take_better(rv, re, lane_f32(bv, r), __builtin_amdgcn_readlane(be, r));
+  bv = rv;
+  be = re;
 }
 
 template <int NPL>
@@ -324,9 +331,7 @@ __global__ __launch_bounds__(256) void route_select(
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if (lane + i * kWave < E) part_sum += expf(v[i] - m);
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) part_sum += __shfl_xor(part_sum, d, kWave);
-    sum = part_sum;
+    sum = wave_sum(part_sum);
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j)
