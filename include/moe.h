@@ -207,7 +207,11 @@ moe_status moe_permute_ex(const void* x, const int32_t* topk_ids,
  *   yp[rows] = GELU(xp[rows] . w1[e]) . w2[e]
  *   xp[R,H], w1[E,H,F], w2[E,F,H], yp[R,H] in dtype; expert_offsets[E+1]
  *   int32, non-decreasing, expert_offsets[0] = 0, expert_offsets[E] <= R
- *   (rows from expert_offsets[E] on are neither read nor written).
+ *   (rows from expert_offsets[E] on are neither read nor written).  Other
+ *   offsets are clamped, expert e taking rows [a, b) with
+ *   a = min(max(off[e], 0), R) and b = min(max(off[e+1], a), R): no row
+ *   outside the R rows is touched (rows two such ranges share are written
+ *   twice, in no fixed order).
  *   GELU is the tanh form 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
  *   Experts with no rows are skipped (their weights are not read).
  *   ws holds h[R,F] (dtype).

@@ -126,6 +126,18 @@ struct Tile {
   int nt;      // column tile index
 };
 
+// Rows [lo, lo + n) of expert e: the offsets' range clamped into [0, R].
+// For non-decreasing offsets within [0, R] this is [off[e], off[e+1]); for
+// any other offsets (negative, decreasing, past R) every row index formed
+// from it still lies inside the R dispatched rows.
+__device__ __forceinline__ void expert_rows(const int* __restrict__ off, int e, int R, int& lo,
+                                            int& n) {
+  const int a = min(max(off[e], 0), R);
+  const int b = min(max(off[e + 1], a), R);
+  lo = a;
+  n = b - a;
+}
+
 // Number of row tiles, sum_e ceil(rows_e / BM) (wave-uniform).
 __device__ __forceinline__ int count_row_tiles(const int* __restrict__ off, int E,
                                                int dense_rows, int BM) {
@@ -135,7 +147,11 @@ __device__ __forceinline__ int count_row_tiles(const int* __restrict__ off, int 
   for (int c = 0; c < E; c += kWave) {
     const int e = c + lane;
     int mt = 0;
-    if (e < E) mt = (off[e + 1] - off[e] + BM - 1) / BM;
+    if (e < E) {
+      int lo, n;
+      expert_rows(off, e, dense_rows, lo, n);
+      mt = (n + BM - 1) / BM;
+    }
     const int incl = wave_incl_scan(mt);
     total += wave_bcast(incl, kWave - 1);
   }
@@ -161,9 +177,9 @@ __device__ __forceinline__ Tile lookup_tile(const int* __restrict__ off, int E,
   int carry = 0;
   for (int c = 0; c < E; c += kWave) {
     const int e = c + lane;
-    int cnt = 0, mt = 0;
+    int cnt = 0, mt = 0, row_lo = 0;
     if (e < E) {
-      cnt = off[e + 1] - off[e];
+      expert_rows(off, e, dense_rows, row_lo, cnt);
       mt = (cnt + BM - 1) / BM;
     }
     const int incl = wave_incl_scan(mt);
@@ -176,12 +192,13 @@ __device__ __forceinline__ Tile lookup_tile(const int* __restrict__ off, int E,
       const int lo_hit = wave_bcast(lo, src);
       const int mt_hit = wave_bcast(mt, src);
       const int cnt_hit = wave_bcast(cnt, src);
+      const int row_hit = wave_bcast(row_lo, src);
       const int local = L - lo_hit;
       const int mi = local % mt_hit;
       tile.valid = 1;
       tile.e = e_hit;
       tile.nt = local / mt_hit;
-      tile.row0 = off[e_hit] + mi * BM;
+      tile.row0 = row_hit + mi * BM;
       tile.mrows = min(BM, cnt_hit - mi * BM);
       return tile;
     }

@@ -920,7 +920,7 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_wgrad(
     const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, uint16_t* __restrict__ C,
-    const int* __restrict__ off, int E, int M, int N) {
+    const int* __restrict__ off, int E, int R, int M, int N) {
   using S = GemmShape<BM, BN, WM, WN>;
   constexpr int FM = S::FM, FN = S::FN;
   __shared__ __attribute__((aligned(1024))) char p0[S::LDS_W];
@@ -975,8 +975,9 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     st.tile.row0 = (r % MT) * BM;
     st.tile.mrows = min(BM, M - st.tile.row0);
     st.tile.nt = r / MT;
-    const int kb = off[e];
-    st.rows = off[e + 1] - kb;
+    int kb, rows;
+    expert_rows(off, e, R, kb, rows);
+    st.rows = rows;
     st.nsteps = max(4, ((st.rows + BK - 1) / BK + 3) / 4 * 4);
     st.pb = P + (size_t)kb * M;
     st.qb = Q + (size_t)kb * N;
@@ -1243,14 +1244,14 @@ hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const 
 }
 
 hipError_t launch_gemm_bf16_wgrad(const void* P, const void* Q, void* C, const int* off, int E,
-                                  int M, int N, hipStream_t s) {
+                                  int R, int M, int N, hipStream_t s) {
   const long tiles = (long)E * ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles == 0) return hipSuccess;
   // persistent: one workgroup per CU (or per tile when there are fewer)
   const long blocks = std::min<long>(tiles, device_slots());
   hipLaunchKernelGGL((gemm_bf16_wgrad<256, 256, kWM, kWN>), dim3((unsigned)blocks),
                      dim3(kWave * kWM * kWN), 0, s, (const uint16_t*)P, (const uint16_t*)Q,
-                     (uint16_t*)C, off, E, M, N);
+                     (uint16_t*)C, off, E, R, M, N);
   return hipGetLastError();
 }
 

@@ -117,8 +117,7 @@ __global__ __launch_bounds__(256) void gemm_f32_bwd(
     tile.row0 = (r % MT) * FBM;
     tile.mrows = min(FBM, M - tile.row0);
     tile.nt = r / MT;
-    kb = off[tile.e];
-    K = off[tile.e + 1] - kb;
+    expert_rows(off, tile.e, R, kb, K);
     C += (size_t)tile.e * M * N;
   } else {
     const int NTN = (N + FBN - 1) / FBN;
@@ -229,12 +228,12 @@ hipError_t launch_gemm_f32_nt(const float* A, const float* W, float* C, const in
 }
 
 hipError_t launch_gemm_f32_wgrad(const float* P, const float* Q, float* C, const int* off, int E,
-                                 int M, int N, hipStream_t s) {
+                                 int R, int M, int N, hipStream_t s) {
   const long tiles = (long)E * ((M + FBM - 1) / FBM) * ((N + FBN - 1) / FBN);
   if (tiles == 0) return hipSuccess;
   const long blocks = (tiles + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((gemm_f32_bwd<true>), dim3((unsigned)blocks), dim3(256), 0, s, P, Q, C, off,
-                     E, 0, 0, M, N, 0, nullptr);
+                     E, R, 0, M, N, 0, nullptr);
   return hipGetLastError();
 }
 

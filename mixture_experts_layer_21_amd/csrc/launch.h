@@ -58,7 +58,7 @@ hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const 
 // C[e] = P_e^T . Q_e ([M][N] per expert) with P_e, Q_e the rows
 // [off[e], off[e+1]) of P [R][M] and Q [R][N] (expert weight gradients).
 hipError_t launch_gemm_bf16_wgrad(const void* P, const void* Q, void* C, const int* off, int E,
-                                  int M, int N, hipStream_t s);
+                                  int R, int M, int N, hipStream_t s);
 // zout != nullptr: the accumulators are also stored there before GELU
 hipError_t launch_gemm_f32(const float* A, const float* W, float* C, const int* off, int E,
                            int R, int K, int N, int ldc, bool gelu, float* zout, hipStream_t s);
@@ -68,7 +68,7 @@ hipError_t launch_gemm_f32_nt(const float* A, const float* W, float* C, const in
                               int R, int K, int N, const float* dgelu_z, hipStream_t s);
 // C[e] = P_e^T . Q_e ([M][N] per expert), rows [off[e], off[e+1]) of P [R][M], Q [R][N]
 hipError_t launch_gemm_f32_wgrad(const float* P, const float* Q, float* C, const int* off, int E,
-                                 int M, int N, hipStream_t s);
+                                 int R, int M, int N, hipStream_t s);
 
 hipError_t launch_combine(const void* yp, const int32_t* inv_pos, const float* w, int T,
                           int H, int k, bool bf16, void* y, hipStream_t s);

@@ -118,25 +118,25 @@ moe_status run_ffn_bwd(const void* dyp, const void* xp, const int32_t* off, cons
       err = moe::launch_gemm_bf16(dyp, nullptr, (int)R, w2, true, dz, off, (int)E, (int)R,
                                   (int)H, (int)F, moe::EP_DGELU, z, nullptr, split, s);
     if (err == hipSuccess)
-      err = moe::launch_gemm_bf16_wgrad(h, dyp, dw2, off, (int)E, (int)F, (int)H, s);
+      err = moe::launch_gemm_bf16_wgrad(h, dyp, dw2, off, (int)E, (int)R, (int)F, (int)H, s);
     if (err == hipSuccess && R > 0)
       err = moe::launch_gemm_bf16(dz, nullptr, (int)R, w1, true, dxp, off, (int)E, (int)R,
                                   (int)F, (int)H, moe::EP_PLAIN, nullptr, nullptr, split, s);
     if (err == hipSuccess)
-      err = moe::launch_gemm_bf16_wgrad(xp, dz, dw1, off, (int)E, (int)H, (int)F, s);
+      err = moe::launch_gemm_bf16_wgrad(xp, dz, dw1, off, (int)E, (int)R, (int)H, (int)F, s);
   } else {
     if (R > 0)
       err = moe::launch_gemm_f32_nt((const float*)dyp, (const float*)w2, (float*)dz, off, (int)E,
                                     (int)R, (int)H, (int)F, (const float*)z, s);
     if (err == hipSuccess)
       err = moe::launch_gemm_f32_wgrad((const float*)h, (const float*)dyp, (float*)dw2, off,
-                                       (int)E, (int)F, (int)H, s);
+                                       (int)E, (int)R, (int)F, (int)H, s);
     if (err == hipSuccess && R > 0)
       err = moe::launch_gemm_f32_nt((const float*)dz, (const float*)w1, (float*)dxp, off,
                                     (int)E, (int)R, (int)F, (int)H, nullptr, s);
     if (err == hipSuccess)
       err = moe::launch_gemm_f32_wgrad((const float*)xp, (const float*)dz, (float*)dw1, off,
-                                       (int)E, (int)H, (int)F, s);
+                                       (int)E, (int)R, (int)H, (int)F, s);
   }
   return launch_status(err);
 }

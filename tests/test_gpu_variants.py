@@ -277,3 +277,28 @@ def test_combine_skips_rows_outside_yp(dtype):
     ref = oracle.combine(f64(yp), inv_np, f64(w))
     tol = TOL["bf16"] if dtype == torch.bfloat16 else TOL["f32"]
     assert_close_rel(f64(y), ref, tol, "combine with out-of-range rows")
+
+
+# Offsets that break the stage's contract (negative, decreasing, past R):
+# each expert's range is clamped into [0, R], so no row outside the R
+# dispatched rows is read or written.  Rows that exactly one clamped range
+# covers are checked against the oracle; rows two ranges overlap are not.
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("off_list,checked", [
+    ([0, -17, 200, 256], [(1, 0, 200), (2, 200, 256)]),
+    ([0, 100, 50, 300, 306], [(0, 0, 50), (2, 100, 256)]),
+])
+def test_expert_ffn_clamps_offsets(dtype, off_list, checked):
+    R, H, F = 256, 128, 96
+    E = len(off_list) - 1
+    g = torch.Generator().manual_seed(11)
+    xp = torch.randn(R, H, generator=g).to(dtype)
+    w1 = (torch.randn(E, H, F, generator=g) * H ** -0.5).to(dtype)
+    w2 = (torch.randn(E, F, H, generator=g) * F ** -0.5).to(dtype)
+    off = torch.tensor(off_list, dtype=torch.int32)
+    yp = moe.moe_expert_ffn(xp.cuda(), off.cuda(), w1.cuda(), w2.cuda())
+    torch.cuda.synchronize()
+    tol = TOL["bf16"] if dtype == torch.bfloat16 else TOL["f32"]
+    for e, a, b in checked:
+        ref = oracle.expert_ffn_block(f64(xp[a:b]), f64(w1[e]), f64(w2[e]))
+        assert_close_rel(f64(yp[a:b]), ref, tol, f"expert {e} rows [{a}, {b})")
