@@ -23,6 +23,11 @@
  *     MOE_F32 (fp32 throughout) or MOE_BF16 (bf16 storage, fp32
  *     accumulation; the FFN intermediate is rounded to bf16).  Router bias
  *     and gate weights are always fp32; expert ids and indices are int32.
+ *   - Alignment: tensors in dtype (x, W_r, W1, W2, xp, yp, y and their
+ *     gradients) and every workspace or saved buffer must be 16-byte
+ *     aligned; int32 and fp32 arrays (ids, offsets, indices, gate weights,
+ *     router bias) 4-byte aligned.  (hipMalloc / torch allocations and
+ *     whole rows of them are.)
  *   - Arguments are validated on the host before anything is enqueued; a
  *     call that returns an error has no device side effects.
  *   - Results are bitwise deterministic for fixed inputs and shapes (no
@@ -32,9 +37,9 @@
  *
  * Status codes
  *   MOE_OK                 success (work enqueued)
- *   MOE_ERR_INVALID_ARG    a required pointer is NULL, a size is <= 0,
- *                          top_k is outside [1, E], or ws_bytes is smaller
- *                          than the entry point needs
+ *   MOE_ERR_INVALID_ARG    a required pointer is NULL or under-aligned, a
+ *                          size is <= 0, top_k is outside [1, E], or
+ *                          ws_bytes is smaller than the entry point needs
  *   MOE_ERR_UNSUPPORTED    dtype is not MOE_F32/MOE_BF16, H or F is not a
  *                          multiple of 8, E > 1024, top_k > 16, or a size
  *                          exceeds the int32 index range (T*top_k*max(H,F)

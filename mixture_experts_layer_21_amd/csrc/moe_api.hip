@@ -3,6 +3,8 @@
 // before enqueueing anything, so an error return leaves the device untouched.
 #include "moe.h"
 
+#include <initializer_list>
+
 #include "launch.h"
 
 namespace {
@@ -77,6 +79,18 @@ FwdLayout fwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_
 }
 
 moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+// Alignment the kernels rely on: tensors in the layer's dtype and the
+// workspaces are read and written with 16-byte vector accesses, int32 and
+// fp32 index/weight arrays with 4-byte accesses.  Null pointers pass (the
+// null checks are separate).
+bool aligned(std::initializer_list<const void*> a16, std::initializer_list<const void*> a4) {
+  for (const void* p : a16)
+    if ((uintptr_t)p & 15u) return false;
+  for (const void* p : a4)
+    if ((uintptr_t)p & 3u) return false;
+  return true;
+}
 
 // Expert FFN.  The first GEMM reads its token rows from xp (a_rows = R rows,
 // gather == nullptr) or straight from x through gather = sorted_token
@@ -275,6 +289,7 @@ moe_status moe_route_ex(const void* x, const void* w_r, const float* router_bias
   st = check_router(dtype, router_dtype, gating);
   if (st != MOE_OK) return st;
   if (!x || !w_r || !topk_ids || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned({x, w_r, ws}, {router_bias, topk_ids, topk_w})) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe::route_ws_bytes((int)T, (int)H, (int)E, dtype == MOE_BF16))
     return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
@@ -299,6 +314,8 @@ moe_status moe_permute_ex(const void* x, const int32_t* topk_ids, int64_t T, int
   if (st != MOE_OK) return st;
   if (!x || !topk_ids || !expert_offsets || !sorted_token || !inv_pos || !xp || !ws)
     return MOE_ERR_INVALID_ARG;
+  if (!aligned({x, xp, ws}, {topk_ids, expert_offsets, sorted_token, inv_pos}))
+    return MOE_ERR_INVALID_ARG;
   if (ws_bytes < moe::permute_ws_bytes((int)(T * top_k), (int)E)) return MOE_ERR_INVALID_ARG;
   return launch_status(moe::launch_permute(x, topk_ids, (int)T, (int)H, (int)E, top_k, capacity,
                                            elem_bytes(dtype), expert_offsets, sorted_token,
@@ -319,6 +336,7 @@ moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets, const v
   const moe_status st = check_shape(R, H, E, 1, F, dtype);
   if (st != MOE_OK) return st;
   if (!xp || !expert_offsets || !w1 || !w2 || !yp || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned({xp, w1, w2, yp, ws}, {expert_offsets})) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < ffn_ws_bytes(R, F, dtype)) return MOE_ERR_INVALID_ARG;
   return run_ffn(xp, nullptr, R, expert_offsets, w1, w2, R, H, E, F, dtype, yp, ws, nullptr,
                  ffn_split(ws, R, F, dtype), (hipStream_t)stream);
@@ -333,6 +351,8 @@ moe_status moe_expert_ffn_backward(const void* dyp, const void* xp,
   if (st != MOE_OK) return st;
   if (!expert_offsets || !w1 || !w2 || !dw1 || !dw2 || !ws) return MOE_ERR_INVALID_ARG;
   if (R > 0 && (!dyp || !xp || !z || !h || !dxp)) return MOE_ERR_INVALID_ARG;
+  if (!aligned({dyp, xp, z, h, w1, w2, dxp, dw1, dw2, ws}, {expert_offsets}))
+    return MOE_ERR_INVALID_ARG;
   if (ws_bytes < ffn_ws_bytes(R, F, dtype)) return MOE_ERR_INVALID_ARG;
   return run_ffn_bwd(dyp, xp, expert_offsets, z, h, w1, w2, R, H, E, F, dtype, dxp, dw1, dw2, ws,
                      ffn_split(ws, R, F, dtype), (hipStream_t)stream);
@@ -343,6 +363,7 @@ moe_status moe_combine(const void* yp, const int32_t* inv_pos, const float* topk
   const moe_status st = check_shape(T, H, top_k, top_k, 8, dtype);
   if (st != MOE_OK) return st;
   if (!yp || !inv_pos || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned({yp, y}, {inv_pos, topk_w})) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   return launch_status(moe::launch_combine(yp, inv_pos, topk_w, (int)T, (int)H, top_k,
                                            dtype == MOE_BF16, y, (hipStream_t)stream));
@@ -358,6 +379,8 @@ moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bi
   st = check_router(dtype, router_dtype, gating);
   if (st != MOE_OK) return st;
   if (!x || !w_r || !w1 || !w2 || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (!aligned({x, w_r, w1, w2, y, ws}, {router_bias, topk_ids_out, topk_w_out}))
+    return MOE_ERR_INVALID_ARG;
   const FwdLayout L = fwd_layout(T, H, E, top_k, F, dtype);
   if (ws_bytes < L.total) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
@@ -433,6 +456,8 @@ moe_status moe_forward_train(const void* x, const void* w_r, const float* router
   // (buffers of T rows are empty, and may be NULL, when T == 0)
   if (!w_r || !w1 || !w2 || !saved || !ws) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!x || !y || !topk_ids || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (!aligned({x, w_r, w1, w2, y, saved, ws}, {router_bias, topk_ids, topk_w}))
+    return MOE_ERR_INVALID_ARG;
   const FwdLayout L = fwd_layout(T, H, E, top_k, F, dtype);
   const SavedLayout V = saved_layout(T, H, E, top_k, F, dtype);
   if (ws_bytes < L.total || saved_bytes < V.total) return MOE_ERR_INVALID_ARG;
@@ -479,6 +504,9 @@ moe_status moe_backward(const void* dy, const void* x, const void* w_r, const vo
   // (buffers of T rows are empty, and may be NULL, when T == 0)
   if (!w_r || !w1 || !w2 || !saved || !dw_r || !dw1 || !dw2 || !ws) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!dy || !x || !topk_ids || !topk_w || !dx)) return MOE_ERR_INVALID_ARG;
+  if (!aligned({dy, x, w_r, w1, w2, saved, dx, dw_r, dw1, dw2, ws},
+               {topk_ids, topk_w, db_r, dtopk_w}))
+    return MOE_ERR_INVALID_ARG;
   const SavedLayout V = saved_layout(T, H, E, top_k, F, dtype);
   const BwdLayout L = bwd_layout(T, H, E, top_k, F, dtype);
   if (saved_bytes < V.total || ws_bytes < L.total) return MOE_ERR_INVALID_ARG;

@@ -358,3 +358,40 @@ def test_expert_ffn_backward_stage_workspace():
     assert st == OK and n >= 64 * 2 * 256 * 2
     assert stage_bytes(moe.MOE_STAGE_EXPERT_FFN_BACKWARD, 64, 128, 8, 2, 256, F32)[1] >= \
         64 * 2 * 256 * 4
+
+
+# --- alignment ----------------------------------------------------------------
+# Tensors in the layer's dtype and workspaces are accessed 16 bytes at a time,
+# int32 / fp32 index and weight arrays 4 bytes at a time: a pointer below that
+# alignment is rejected before anything is enqueued.
+A8 = ctypes.c_void_p(0x1008)   # 8-byte aligned: too little for a tensor or a workspace
+A2 = ctypes.c_void_p(0x1002)   # 2-byte aligned: too little for an int32 / fp32 array
+A4 = ctypes.c_void_p(0x1004)   # enough for an int32 / fp32 array
+
+
+@pytest.mark.parametrize("call,kw", [
+    (_route_ex, dict(x=A8)), (_route_ex, dict(wr=A8)), (_route_ex, dict(ws=A8)),
+    (_route_ex, dict(ids=A2)), (_route_ex, dict(w=A2)), (_route_ex, dict(b=A2)),
+    (_permute_ex, dict(x=A8)), (_permute_ex, dict(xp=A8)), (_permute_ex, dict(ws=A8)),
+    (_permute_ex, dict(ids=A2)), (_permute_ex, dict(off=A2)), (_permute_ex, dict(st=A2)),
+    (_permute_ex, dict(inv=A2)),
+    (_ffn, dict(xp=A8)), (_ffn, dict(w1=A8)), (_ffn, dict(w2=A8)), (_ffn, dict(yp=A8)),
+    (_ffn, dict(ws=A8)), (_ffn, dict(off=A2)),
+    (_combine, dict(yp=A8)), (_combine, dict(y=A8)), (_combine, dict(inv=A2)),
+    (_combine, dict(w=A2)),
+    (_forward_ex, dict(x=A8)), (_forward_ex, dict(wr=A8)), (_forward_ex, dict(w1=A8)),
+    (_forward_ex, dict(w2=A8)), (_forward_ex, dict(y=A8)), (_forward_ex, dict(ws=A8)),
+    (_forward_ex, dict(b=A2)), (_forward_ex, dict(ids=A2)), (_forward_ex, dict(w=A2)),
+    (_forward_train, dict(sv=A8)), (_forward_train, dict(y=A8)), (_forward_train, dict(ids=A2)),
+    (_backward, dict(dy=A8)), (_backward, dict(sv=A8)), (_backward, dict(dx=A8)),
+    (_backward, dict(dwr=A8)), (_backward, dict(dbr=A2)), (_backward, dict(dtw=A2)),
+    (_ffn_bwd, dict(dyp=A8)), (_ffn_bwd, dict(h=A8)), (_ffn_bwd, dict(dw1=A8)),
+    (_ffn_bwd, dict(off=A2)),
+], ids=lambda v: v.__name__ if callable(v) else next(iter(v)))
+def test_misaligned_pointers_rejected(call, kw):
+    assert call(**kw) == INV
+
+
+def test_index_arrays_need_four_bytes_only():
+    # an empty batch returns after validation: 4-byte aligned ids / weights pass
+    assert _route_ex(T=0, ids=A4, w=A4, b=A4) == OK
