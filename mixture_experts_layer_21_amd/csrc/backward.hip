@@ -183,6 +183,7 @@ __global__ __launch_bounds__(256) void router_wgrad(const void* __restrict__ x,
                                                     int E, int S, float* __restrict__ part,
                                                     float* __restrict__ partb) {
   __shared__ float dls[kWgT][kWgE];
+  __shared__ __attribute__((aligned(16))) float stg[kWgH][kWgE];   // the partials, for the store
   const int tid = threadIdx.x;
   const int HB = (H + kWgH - 1) / kWgH, EB = (E + kWgE - 1) / kWgE;
   const int hb = blockIdx.x % HB, eb = (blockIdx.x / HB) % EB, s = blockIdx.x / (HB * EB);
@@ -236,12 +237,30 @@ __global__ __launch_bounds__(256) void router_wgrad(const void* __restrict__ x,
     if (bias_thread)
       for (int tt = 0; tt < nt; ++tt) accb1 += dls[tt][tid];
   }
-  if (h < H) {
+  // partials out through LDS: each thread holds two h rows of 16 experts;
+  // stored as 16-byte runs, four lanes per 64-byte row piece (straight from
+  // the registers every lane would write 4 bytes into a different row)
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int e = 0; e < kWgE; ++e)
-        if (e0 + e < E) part[((size_t)s * H + h + r) * E + e0 + e] = acc[r][e];
+    for (int e = 0; e < kWgE; e += 4)
+      *(float4*)&stg[2 * tid + r][e] =
+          make_float4(acc[r][e], acc[r][e + 1], acc[r][e + 2], acc[r][e + 3]);
+  __syncthreads();
+  const bool full_e = e0 + kWgE <= E && E % 4 == 0;
+  for (int q = tid; q < kWgH * (kWgE / 4); q += 256) {
+    const int hl = q / (kWgE / 4), c = (q % (kWgE / 4)) * 4;
+    const int hh = hb * kWgH + hl;
+    if (hh >= H) continue;
+    float* dst = part + ((size_t)s * H + hh) * E + e0 + c;
+    const float4 v = *(const float4*)&stg[hl][c];
+    if (full_e) {
+      *(float4*)dst = v;
+    } else {
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      for (int u = 0; u < 4; ++u)
+        if (e0 + c + u < E) dst[u] = vv[u];
+    }
   }
   if (bias_thread && e0 + tid < E) partb[(size_t)s * E + e0 + tid] = accb1;
 }
