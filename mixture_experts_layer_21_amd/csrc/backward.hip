@@ -365,17 +365,33 @@ __global__ __launch_bounds__(256) void dx_finish(const void* __restrict__ dxp,
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[tt][q] = 0.f;
   if constexpr (SPARSE) {
+    // slots in chunks of 8: the chunk's ids, then its dl values, then its W_r
+    // rows are each loaded together (three round trips per chunk, not per
+    // slot); the products are added in slot order
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
       if (tt < nt) {
         const int t = t0 + tt;
-        for (int j = 0; j < k; ++j) {
-          const int e = ids[(size_t)t * k + j];
-          const float d = dl[(size_t)t * E + e];
-          float w[4];
-          load_wrt4<WBF16>(w_rt, (size_t)e * H + h, w);
+        for (int j0 = 0; j0 < k; j0 += 8) {
+          int ej[8];
+          float dj[8], wj[8][4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[tt][q] = __builtin_fmaf(d, w[q], acc[tt][q]);
+          for (int u = 0; u < 8; ++u) {   // (an id outside [0, E) adds nothing)
+            ej[u] = j0 + u < k ? ids[(size_t)t * k + j0 + u] : -1;
+            if ((unsigned)ej[u] >= (unsigned)E) ej[u] = -1;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) dj[u] = ej[u] >= 0 ? dl[(size_t)t * E + ej[u]] : 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            wj[u][0] = wj[u][1] = wj[u][2] = wj[u][3] = 0.f;
+            if (ej[u] >= 0) load_wrt4<WBF16>(w_rt, (size_t)ej[u] * H + h, wj[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (ej[u] >= 0)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[tt][q] = __builtin_fmaf(dj[u], wj[u][q], acc[tt][q]);
         }
       }
     }
@@ -403,21 +419,36 @@ __global__ __launch_bounds__(256) void dx_finish(const void* __restrict__ dxp,
     if (tt < nt) {
       const int t = t0 + tt;
       float v[4] = {acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]};
-      for (int j = 0; j < k; ++j) {
-        const int p = inv_pos[(size_t)t * k + j];
-        if (p < 0) continue;
-        const char* src = (const char*)dxp + ((size_t)p * H + h) * es;
-        if constexpr (BF16) {
-          const u32x2 q = *(const u32x2*)src;
-          v[0] += bf16_to_f32(q[0] & 0xFFFFu);
-          v[1] += bf16_to_f32(q[0] >> 16);
-          v[2] += bf16_to_f32(q[1] & 0xFFFFu);
-          v[3] += bf16_to_f32(q[1] >> 16);
-        } else {
-          const f32x4 q = *(const f32x4*)src;
+      // the slots' rows of dxp, 8 at a time: positions, then rows, loaded
+      // together; added in slot order (a dropped slot, p < 0, adds nothing)
+      for (int j0 = 0; j0 < k; j0 += 8) {
+        int pj[8];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] += q[u];
+        for (int u = 0; u < 8; ++u) pj[u] = j0 + u < k ? inv_pos[(size_t)t * k + j0 + u] : -1;
+        float r[8][4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          r[u][0] = r[u][1] = r[u][2] = r[u][3] = 0.f;
+          if (pj[u] >= 0) {
+            const char* src = (const char*)dxp + ((size_t)pj[u] * H + h) * es;
+            if constexpr (BF16) {
+              const u32x2 q = *(const u32x2*)src;
+              r[u][0] = bf16_to_f32(q[0] & 0xFFFFu);
+              r[u][1] = bf16_to_f32(q[0] >> 16);
+              r[u][2] = bf16_to_f32(q[1] & 0xFFFFu);
+              r[u][3] = bf16_to_f32(q[1] >> 16);
+            } else {
+              const f32x4 q = *(const f32x4*)src;
+#pragma unroll
+              for (int c = 0; c < 4; ++c) r[u][c] = q[c];
+            }
+          }
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (pj[u] >= 0)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] += r[u][c];
       }
       char* dst = (char*)dx + ((size_t)t * H + h) * es;
       if constexpr (BF16)
