@@ -4,13 +4,17 @@
 
 A step is one moe_forward call (route, dispatch, expert FFN, combine) over one
 batch of synthetic, seeded inputs already resident in HBM.  W untimed steps,
-then exactly K steps between two device synchronisations; value is tokens/s
-over those K steps.  A second, equally long region runs the same kernels
-through the stage entry points with HIP events between the stages (on the
-stream the kernels run on) to get each stage's duration; the expert FFN stage
+then exactly K steps back to back between two device synchronisations; value
+is tokens/s over those K steps.  A second, equally long region runs the same
+kernels through the stage entry points (route, dispatch indices, the expert
+FFN gathering its rows from x, combine: the launches moe_forward makes) with
+HIP events between the stages on the stream the kernels run on, after a
+512 MiB write that evicts the L2 and MALL caches before each step, to get
+each stage's duration and its achieved HBM bandwidth; the expert FFN stage
 is two launches of the grouped-GEMM kernel with equal flops, which gives the
 per-launch roofline of the dominant kernel.  The fp64 oracle is timed on the
-host cores on a bounded sample of the same workload.  One JSON line is
+host cores on a bounded sample of the same workload, and its result gives
+the sample's near-tie count and the GPU output's error.  One JSON line is
 printed.
 
 --pass train times a training step of the layer instead: moe_forward_train
@@ -47,6 +51,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="mixtral_bf16", choices=list(mi.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="stage timing without the cache-evicting write before each step")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="tokens in the oracle's timed sample (0: per-workload default)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -211,21 +217,35 @@ def time_forward(moe, L, cfg, steps, warmup, ws, y):
     return (time.perf_counter() - t0) / steps
 
 
-def time_stages(moe, L, cfg, steps, bufs):
-    """Per-stage durations (ms) from HIP events on the launch stream."""
+FLUSH_BYTES = 512 << 20     # twice the MALL (256 MB); the L2s are 4 MB per XCD
+
+
+def time_stages(moe, L, cfg, steps, bufs, flush=True):
+    """Per-stage durations (ms) from HIP events on the launch stream.  The
+    stages are the launches moe_forward makes: routing, the dispatch indices
+    (bf16: no row copy), the expert FFN (bf16: its first GEMM gathers the rows
+    from x), the combine.  With flush, a 512 MiB write before each step (not
+    timed) leaves nothing of the previous step in the L2 or MALL caches."""
     names = ["route", "permute", "expert_ffn", "combine"]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     ids, w, off, st, inv, xp, yp, y, ws = bufs
+    junk = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda") if flush else None
+    bf16 = cfg.dtype == "bf16"
     torch.cuda.synchronize()
     for i in range(steps):
+        if flush:
+            junk.fill_(i & 0xFF)
         e = ev[i]
         e[0].record()
         moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k, topk_ids=ids, topk_w=w, ws=ws)
         e[1].record()
         moe.moe_permute(L["x"], ids, cfg.E, expert_offsets=off, sorted_token=st, inv_pos=inv,
-                        xp=xp, ws=ws)
+                        xp=xp, ws=ws, with_rows=not bf16)
         e[2].record()
-        moe.moe_expert_ffn(xp, off, L["w1"], L["w2"], yp=yp, ws=ws)
+        if bf16:
+            moe.moe_expert_ffn_gather(L["x"], st, off, L["w1"], L["w2"], yp=yp, ws=ws)
+        else:
+            moe.moe_expert_ffn(xp, off, L["w1"], L["w2"], yp=yp, ws=ws)
         e[3].record()
         moe.moe_combine(yp, inv, w, y=y)
         e[4].record()
@@ -236,9 +256,39 @@ def time_stages(moe, L, cfg, steps, bufs):
     return out
 
 
-def cpu_baseline(cfg, L, n_tokens):
+def pass_bytes(cfg, touched):
+    """Algorithmic HBM bytes of the passes around the expert GEMMs (what each
+    must read and write at least):
+      route    x, W_r, router bias; ids and gate weights written
+      permute  ids read; offsets, sorted_token, inv_pos written
+      combine  yp, gate weights and inv_pos read; y written"""
+    es = 4 if cfg.dtype == "f32" else 2
+    T, H, E, k, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R
+    route = es * (T * H + H * E) + (4 * E if cfg.bias0 else 0) + 8 * T * k
+    permute = 4 * R + 4 * (E + 1) + 8 * R + (es * R * H * 2 if cfg.dtype == "f32" else 0)
+    combine = es * R * H + 8 * R + es * T * H
+    return {"route": route, "permute": permute, "combine": combine}
+
+
+def blas_threads() -> int:
+    """Threads of the BLAS library numpy's matmul runs on (what the oracle
+    uses); the CPU count this process may run on if it cannot be read."""
+    try:
+        import threadpoolctl
+        n = [d["num_threads"] for d in threadpoolctl.threadpool_info()
+             if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, L, n_tokens, y_gpu, ids_gpu):
     """The fp64 oracle on the first n_tokens tokens of the workload (all the
-    experts they route to), timed on the host cores."""
+    experts they route to), timed on the host cores.  Its result also gives
+    the sample's routing agreement and the GPU output's error (returned
+    separately: they are not part of the timing)."""
     import oracle
     sel = torch.arange(n_tokens, device="cuda")
     x = L["x"][sel].cpu()
@@ -246,15 +296,26 @@ def cpu_baseline(cfg, L, n_tokens):
     b = None if L["router_bias"] is None else L["router_bias"].cpu()
     w1 = L["w1"].cpu()
     w2 = L["w2"].cpu()
-    cores = torch.get_num_threads()
+    cores = blas_threads()
     t0 = time.perf_counter()
     up = lambda t: t.to(torch.float64).numpy()  # noqa: E731  (the oracle's own upcast)
-    oracle.forward(up(x), up(w_r), None if b is None else up(b),
-                   lambda e: up(w1[e]), lambda e: up(w2[e]), cfg.k)
+    ref = oracle.forward(up(x), up(w_r), None if b is None else up(b),
+                         lambda e: up(w1[e]), lambda e: up(w2[e]), cfg.k)
     dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n_tokens} of {cfg.T} tokens of {cfg.name}, fp64 numpy, "
-                      f"{dt:.2f} s"}
+    base = {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tokens} of {cfg.T} tokens of {cfg.name}, fp64 numpy "
+                      f"({cores} BLAS threads), {dt:.2f} s"}
+    # routing and output against the oracle on the same tokens: y is compared
+    # on the tokens whose ids agree (a near-tie token may pick another expert)
+    ids_g = ids_gpu[:n_tokens].astype(np.int64)
+    same = (ids_g == ref["ids"]).all(axis=1)
+    yg = y_gpu[:n_tokens].to(torch.float64).cpu().numpy()
+    err = np.abs(yg[same] - ref["y"][same]).max() / np.abs(ref["y"][same]).max()
+    check = {"tokens": n_tokens,
+             "boundary_near_ties": int(oracle.boundary_near_tie(ref["logits"], cfg.k).sum()),
+             "ids_differ": int((~same).sum()),
+             "max_err_rel": float(err)}
+    return base, check
 
 
 METRIC_TRAIN = "MoE layer fwd+bwd (training step) tokens/s + % MFMA/HBM roofline"
@@ -334,7 +395,7 @@ def cpu_baseline_train(cfg, L, dy, n_tokens):
     for e in used:
         w1[e] = w1c[e].to(torch.float64).numpy()
         w2[e] = w2c[e].to(torch.float64).numpy()
-    cores = torch.get_num_threads()
+    cores = blas_threads()
     t0 = time.perf_counter()
     oracle.forward(x, w_r, b, w1, w2, cfg.k)
     oracle.backward(x, w_r, b, w1, w2, cfg.k, g)
@@ -457,10 +518,15 @@ def main():
             torch.empty((R, cfg.H), dtype=cfg.torch_dtype, device=dev),
             torch.empty((R, cfg.H), dtype=cfg.torch_dtype, device=dev),
             torch.empty((cfg.T, cfg.H), dtype=cfg.torch_dtype, device=dev), ws)
-    stages = time_stages(moe, L, cfg, a.steps, bufs)
+    stages = time_stages(moe, L, cfg, a.steps, bufs, flush=not a.no_flush)
     ids = bufs[0].cpu().numpy()
     flops, bytes_, touched = alg_counts(cfg, ids)
     counts = np.bincount(ids.ravel(), minlength=cfg.E)
+    pb = pass_bytes(cfg, touched)
+    hbm = {}
+    for n, b in pb.items():
+        gbs = b / (stages[n] * 1e-3) / 1e9
+        hbm[n] = {"bytes": b, "gb_s": gbs, "frac": gbs / PEAK_HBM_GBS}
 
     g_flops, g_bytes = gemm_launch_counts(cfg, touched)
     g_sec = stages["expert_ffn"] / 2 * 1e-3         # two launches per FFN stage
@@ -478,12 +544,15 @@ def main():
                       else "gemm_f32_grouped")
     roof["per_launch"] = {"flops": g_flops, "bytes": g_bytes, "ms": g_sec * 1e3}
 
-    cpu = None
+    cpu = check = None
     if not a.no_cpu_baseline:
         # (about 10 s of host work at most: the whole batch)
         n = a.cpu_sample_tokens or {"tiny_fp32": 64, "mixtral_bf16": 2048, "skewed_bf16": 2048,
                                     "many_experts_bf16": 4096, "weight_bound_bf16": 64}[cfg.name]
-        cpu = cpu_baseline(cfg, L, min(n, cfg.T))
+        moe.moe_forward(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k, y=y,
+                        topk_ids_out=bufs[0], ws=ws)
+        torch.cuda.synchronize()
+        cpu, check = cpu_baseline(cfg, L, min(n, cfg.T), y, bufs[0].cpu().numpy())
 
     layer_tflops = flops / sec / 1e12
     out = {
@@ -509,6 +578,9 @@ def main():
         "experts_touched": int(touched),
         "expert_rows": {"min": int(counts.min()), "max": int(counts.max())},
         "stages_ms": stages,
+        "stages_flushed": not a.no_flush,
+        "pass_hbm": hbm,
+        "oracle_check": check,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -104,6 +104,7 @@ enum {
   MOE_STAGE_COMBINE = 3,
   MOE_STAGE_FORWARD = 4,
   MOE_STAGE_EXPERT_FFN_BACKWARD = 5,
+  MOE_STAGE_EXPERT_FFN_GATHER = 6,
 };
 
 /*
@@ -112,7 +113,8 @@ enum {
  * MOE_STAGE_PERMUTE -> moe_permute, MOE_STAGE_EXPERT_FFN -> moe_expert_ffn
  * with R = T*top_k rows, MOE_STAGE_COMBINE -> 0 (no workspace),
  * MOE_STAGE_FORWARD -> moe_forward (same as moe_workspace_bytes),
- * MOE_STAGE_EXPERT_FFN_BACKWARD -> moe_expert_ffn_backward with R = T*top_k.
+ * MOE_STAGE_EXPERT_FFN_BACKWARD -> moe_expert_ffn_backward with R = T*top_k,
+ * MOE_STAGE_EXPERT_FFN_GATHER -> moe_expert_ffn_gather with R = T*top_k.
  * Returns MOE_ERR_INVALID_ARG for an unknown stage.
  */
 moe_status moe_stage_workspace_bytes(moe_stage stage, int64_t T, int64_t H,
@@ -178,7 +180,9 @@ moe_status moe_expert_capacity(int64_t T, int32_t top_k, int64_t E, int64_t fact
  *     every id is in [0,E).
  *   sorted_token[R] int32: source token of each dispatched row.
  *   inv_pos[T*top_k] int32: dispatched row of pair (t, j), at index t*top_k+j.
- *   xp[R,H] (dtype): xp[p,:] = x[sorted_token[p],:], a bit copy.
+ *   xp[R,H] (dtype): xp[p,:] = x[sorted_token[p],:], a bit copy.  xp may be
+ *     NULL: then only the indices are built (for moe_expert_ffn_gather,
+ *     which reads the rows from x itself).
  * A pair whose id is outside [0,E) is dropped as a pair beyond the capacity
  * of moe_permute_ex is (inv_pos = -1, not counted in expert_offsets): a bad
  * id never indexes memory.
@@ -225,6 +229,27 @@ moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets,
                           const void* w1, const void* w2, int64_t R, int64_t H,
                           int64_t E, int64_t F, moe_dtype dtype, void* yp,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Experts with the dispatch fused into the first GEMM (fused article,
+ * "fusion idea": the dispatched tokens go straight into the expert compute
+ * instead of through a gathered copy): as moe_expert_ffn, except that
+ * dispatched row p is row sorted_token[p] of x, so xp is never written.
+ * This is the expert stage exactly as moe_forward runs it.
+ *   x[T,H] (dtype); sorted_token[R] int32 (as moe_permute returns it): the
+ *   source token of each dispatched row.  A sorted_token entry outside
+ *   [0,T) reads as a zero row (no memory outside x is read).
+ *   expert_offsets, w1, w2, yp, R, H, E, F, dtype: as moe_expert_ffn.
+ *   ws: h[R,F] (and, for MOE_F32, the gathered rows; the fp32 GEMM reads
+ *   contiguous rows), sized by moe_stage_workspace_bytes with
+ *   MOE_STAGE_EXPERT_FFN_GATHER.
+ * Errors as moe_expert_ffn; T < 0 is MOE_ERR_INVALID_ARG, and T*H beyond the
+ * int32 index range MOE_ERR_UNSUPPORTED.
+ */
+moe_status moe_expert_ffn_gather(const void* x, int64_t T, const int32_t* sorted_token,
+                                 const int32_t* expert_offsets, const void* w1, const void* w2,
+                                 int64_t R, int64_t H, int64_t E, int64_t F, moe_dtype dtype,
+                                 void* yp, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Combine (fused article, ScatterWithWeights): weighted accumulation of each
@@ -338,6 +363,11 @@ moe_status moe_forward_train(const void* x, const void* w_r, const float* router
  *   dtopk_w[T,top_k] fp32, optional (NULL: kept in the workspace): the
  *   gradient with respect to the gate weights (0 for dropped pairs).
  * An expert that received no rows gets zero weight gradients.
+ * topk_ids must be the training forward's.  Should a slot's id lie outside
+ * [0,E) anyway, that slot is left out of the router gradient (its weight and
+ * weight gradient take no part in the softmax Jacobian, and no logit, row of
+ * W_r or column of dW_r is addressed for it); dtopk_w, dW1 and dW2 follow
+ * the dispatch kept in `saved`.
  * ws_bytes must be at least moe_backward_workspace_bytes().  Errors as for
  * the forward; enqueued on `stream`, nothing allocated or synchronised.
  * With T == 0 the weight gradients are zero-filled and dy, x, topk_ids,

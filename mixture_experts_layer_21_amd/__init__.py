@@ -30,10 +30,12 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_STAGE_ROUTE, MOE_STAGE_PERMUTE, MOE_STAGE_EXPERT_FFN, MOE_STAGE_COMBINE, MOE_STAGE_FORWARD = \
     0, 1, 2, 3, 4
 MOE_STAGE_EXPERT_FFN_BACKWARD = 5
+MOE_STAGE_EXPERT_FFN_GATHER = 6
 MOE_GATE_TOPK_SOFTMAX, MOE_GATE_SOFTMAX_TOPK = 0, 1
 EXPORTS = ("moe_status_string", "moe_workspace_bytes", "moe_stage_workspace_bytes", "moe_route",
            "moe_route_ex", "moe_expert_capacity", "moe_permute", "moe_permute_ex",
-           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_ex", "moe_saved_bytes",
+           "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_forward",
+           "moe_forward_ex", "moe_saved_bytes",
            "moe_backward_workspace_bytes", "moe_forward_train", "moe_backward",
            "moe_expert_ffn_backward")
 
@@ -61,6 +63,9 @@ _lib.moe_permute_ex.argtypes = [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _v
 _lib.moe_expert_ffn.restype = _i32
 _lib.moe_expert_ffn.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp,
                                 _sz, _vp]
+_lib.moe_expert_ffn_gather.restype = _i32
+_lib.moe_expert_ffn_gather.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32,
+                                       _vp, _vp, _sz, _vp]
 _lib.moe_combine.restype = _i32
 _lib.moe_combine.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp, _vp]
 _lib.moe_forward.restype = _i32
@@ -215,8 +220,9 @@ def moe_expert_capacity(T: int, top_k: int, E: int, factor_num: int, factor_den:
 
 
 def moe_permute(x, topk_ids, E: int, expert_offsets=None, sorted_token=None, inv_pos=None,
-                xp=None, ws=None):
-    """Dispatch.  Returns (expert_offsets[E+1], sorted_token[R], inv_pos[R], xp[R,H])."""
+                xp=None, ws=None, with_rows: bool = True):
+    """Dispatch.  Returns (expert_offsets[E+1], sorted_token[R], inv_pos[R], xp[R,H]);
+    with_rows=False builds the indices only (xp is None)."""
     _check(x, "x")
     T, H = x.shape
     top_k = topk_ids.shape[1]
@@ -228,8 +234,11 @@ def moe_permute(x, topk_ids, E: int, expert_offsets=None, sorted_token=None, inv
         _check(sorted_token, "sorted_token", torch.int32, (R,))
     inv_pos = torch.empty(R, dtype=torch.int32, device=dev) if inv_pos is None else \
         _check(inv_pos, "inv_pos", torch.int32, (R,))
-    xp = torch.empty((R, H), dtype=x.dtype, device=dev) if xp is None else \
-        _check(xp, "xp", x.dtype, (R, H))
+    if not with_rows:
+        xp = None
+    else:
+        xp = torch.empty((R, H), dtype=x.dtype, device=dev) if xp is None else \
+            _check(xp, "xp", x.dtype, (R, H))
     ws = _workspace(ws, moe_stage_workspace_bytes(MOE_STAGE_PERMUTE, T, H, E, top_k, 8, x.dtype),
                     dev)
     _ok(_lib.moe_permute(_ptr(x), _ptr(topk_ids), T, H, E, top_k, _dtype_code(x.dtype),
@@ -239,10 +248,11 @@ def moe_permute(x, topk_ids, E: int, expert_offsets=None, sorted_token=None, inv
 
 
 def moe_permute_ex(x, topk_ids, E: int, capacity: int, expert_offsets=None, sorted_token=None,
-                   inv_pos=None, xp=None, ws=None):
+                   inv_pos=None, xp=None, ws=None, with_rows: bool = True):
     """Capacity-limited dispatch (capacity <= 0: dropless).  Returns
     (expert_offsets[E+1], sorted_token[R], inv_pos[R], xp[R,H]); dropped pairs
-    have inv_pos -1 and only the first expert_offsets[E] rows are written."""
+    have inv_pos -1 and only the first expert_offsets[E] rows are written;
+    with_rows=False builds the indices only (xp is None)."""
     _check(x, "x")
     T, H = x.shape
     top_k = topk_ids.shape[1]
@@ -254,8 +264,11 @@ def moe_permute_ex(x, topk_ids, E: int, capacity: int, expert_offsets=None, sort
         _check(sorted_token, "sorted_token", torch.int32, (R,))
     inv_pos = torch.empty(R, dtype=torch.int32, device=dev) if inv_pos is None else \
         _check(inv_pos, "inv_pos", torch.int32, (R,))
-    xp = torch.empty((R, H), dtype=x.dtype, device=dev) if xp is None else \
-        _check(xp, "xp", x.dtype, (R, H))
+    if not with_rows:
+        xp = None
+    else:
+        xp = torch.empty((R, H), dtype=x.dtype, device=dev) if xp is None else \
+            _check(xp, "xp", x.dtype, (R, H))
     ws = _workspace(ws, moe_stage_workspace_bytes(MOE_STAGE_PERMUTE, T, H, E, top_k, 8, x.dtype),
                     dev)
     _ok(_lib.moe_permute_ex(_ptr(x), _ptr(topk_ids), T, H, E, top_k, _dtype_code(x.dtype),
@@ -280,6 +293,28 @@ def moe_expert_ffn(xp, expert_offsets, w1, w2, yp=None, ws=None):
     _ok(_lib.moe_expert_ffn(_ptr(xp), _ptr(expert_offsets), _ptr(w1), _ptr(w2), R, H, E, F,
                             _dtype_code(xp.dtype), _ptr(yp), _ptr(ws), ws.numel(),
                             _stream(dev)), "moe_expert_ffn")
+    return yp
+
+
+def moe_expert_ffn_gather(x, sorted_token, expert_offsets, w1, w2, yp=None, ws=None):
+    """Experts over rows gathered from x: yp[p] = FFN_e(x[sorted_token[p]]) for
+    the rows p of expert e (the expert stage as moe_forward runs it)."""
+    _check(x, "x")
+    T, H = x.shape
+    E, _, F = w1.shape
+    _check(sorted_token, "sorted_token", torch.int32)
+    R = sorted_token.numel()
+    _check(w1, "w1", x.dtype, (E, H, F))
+    _check(w2, "w2", x.dtype, (E, F, H))
+    _check(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    dev = x.device
+    yp = torch.empty((R, H), dtype=x.dtype, device=dev) if yp is None else \
+        _check(yp, "yp", x.dtype, (R, H))
+    ws = _workspace(ws, moe_stage_workspace_bytes(MOE_STAGE_EXPERT_FFN_GATHER, R, H, E, 1, F,
+                                                  x.dtype), dev)
+    _ok(_lib.moe_expert_ffn_gather(_ptr(x), T, _ptr(sorted_token), _ptr(expert_offsets), _ptr(w1),
+                                   _ptr(w2), R, H, E, F, _dtype_code(x.dtype), _ptr(yp),
+                                   _ptr(ws), ws.numel(), _stream(dev)), "moe_expert_ffn_gather")
     return yp
 
 

@@ -103,13 +103,19 @@ __global__ __launch_bounds__(256) void router_bwd(const float* __restrict__ logi
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
-  // slot j's (id, dw, w) in lane j
+  // slot j's (id, dw, w) in lane j; a slot whose id is outside [0, E) (not
+  // an id the training forward produced) takes no part: its weight and
+  // gradient are left out of the Jacobian and no logit is addressed for it
   int my_id = -1;
   float my_dw = 0.f, my_w = 0.f;
   if (lane < k) {
     my_id = ids[(size_t)t * k + lane];
-    my_dw = dw[(size_t)t * k + lane];
-    my_w = w[(size_t)t * k + lane];
+    if ((unsigned)my_id < (unsigned)E) {
+      my_dw = dw[(size_t)t * k + lane];
+      my_w = w[(size_t)t * k + lane];
+    } else {
+      my_id = -1;
+    }
   }
   // g[i]: dw of the slot holding expert lane + 64 i (0 if none)
   float g[NPL];

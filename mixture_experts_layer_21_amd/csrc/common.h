@@ -116,6 +116,50 @@ __device__ __forceinline__ int wave_bcast(int v, int src_lane) {
 }
 
 // ---------------------------------------------------------------------------
+// Buffer loads straight into LDS, transposed LDS reads, and the wait counter.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kBufFlags = 0x00020000u;   // raw buffer, 32-bit data format
+constexpr uint32_t kPastEnd = 0xFFFFFFF0u;    // buffer offset that reads as zero
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding and does not wait on LDS/scalar or export counters
+// (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+__device__ constexpr int vmcnt_le(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// (base and size are wave-uniform; readfirstlane states it, so that the
+// descriptor is built in scalar registers and no per-lane loop appears)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           (int)kBufFlags);
+}
+
+// 64 lanes x 16 bytes from global memory straight into a 1 KB LDS block:
+// lane t's bytes land at block + 16 t (no VGPRs involved).  A lane whose
+// offset is at or past the descriptor's size writes zeros.
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, char* lds_block,
+                                            uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_block, 16, voff, 0, 0, 0);
+}
+
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16): in each group of 16 lanes,
+// lane i addresses 8 bytes of row i/4 and receives column i of the 4x16 block
+// those addresses cover, i.e. 4 consecutive k of one output column.
+__device__ __forceinline__ u32x2 read_tr(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// ---------------------------------------------------------------------------
 // Grouped GEMM tiles (see map_tile below for the numbering and XCD mapping).
 // ---------------------------------------------------------------------------
 struct Tile {
@@ -217,16 +261,18 @@ __device__ __forceinline__ Tile lookup_tile(const int* __restrict__ off, int E,
 // running together read one weight slab from HBM once.
 //
 // The grid is launched with an upper bound of tiles (the host does not know
-// the per-expert counts).  Workgroup ids are dealt to the 8 XCDs round-robin,
-// so the id is remapped so that each XCD gets a contiguous run of ceil(n/8)
-// logical tiles, which keeps the tiles that share a weight slab in one XCD's
-// L2.  Every wave of the block computes the same mapping (no LDS, no sync).
+// the per-expert counts).  Workgroup ids are dealt to the 8 XCDs round-robin
+// (id b runs on XCD b % 8), so of the ids below n, XCD x holds
+// q + (x < r ? 1 : 0) of them (q = n / 8, r = n % 8); the id is remapped so
+// that each XCD gets that many consecutive logical tiles, which keeps the
+// tiles that share a weight slab in one XCD's L2.  The map is a bijection of
+// [0, n) for every n (ids at or past n get -1).  Every wave of the block
+// computes the same mapping (no LDS, no sync).
 // With off == nullptr the matrix is a single dense group of `dense_rows` rows.
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int per = (n + kXcds - 1) / kXcds;
-  if (bid / kXcds >= per) return -1;
-  const int L = (bid % kXcds) * per + bid / kXcds;
-  return L < n ? L : -1;
+  if (bid < 0 || bid >= n) return -1;
+  const int x = bid % kXcds, q = n / kXcds, r = n % kXcds;
+  return x * q + min(x, r) + bid / kXcds;
 }
 
 __device__ __forceinline__ Tile map_tile(const int* __restrict__ off, int E,

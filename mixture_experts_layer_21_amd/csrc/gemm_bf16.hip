@@ -47,8 +47,6 @@ constexpr int kWN = 4;          // waves along the columns (8 waves: two per SIM
 constexpr int BK = 32;          // K step (bf16 elements): two 16-wide MFMA slices
 constexpr int W_STAGES = 4;     // weight ring: one K step per stage, 3 in flight
 constexpr int MIN_SPLIT_STEPS = 16;   // K steps per piece of a split tile, at least
-constexpr uint32_t kBufFlags = 0x00020000u;   // raw buffer, 32-bit data format
-constexpr uint32_t kPastEnd = 0xFFFFFFF0u;    // buffer offset that reads as zero
 
 template <int BM, int BN, int WM, int WN>
 struct GemmShape {
@@ -86,43 +84,6 @@ struct GemmShape {
 __device__ __forceinline__ int swz_a(int m) { return (m >> 1) & 7; }
 __device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
 
-
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// are outstanding and does not wait on LDS/scalar or export counters
-// (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-__device__ constexpr int vmcnt_le(int n) {
-  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// (base and size are wave-uniform; readfirstlane states it, so that the
-// descriptor is built in scalar registers and no per-lane loop appears)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = (uint64_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  void* ub = (void*)(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0,
-                                           (int)__builtin_amdgcn_readfirstlane(bytes),
-                                           (int)kBufFlags);
-}
-
-// 64 lanes x 16 bytes from global memory straight into a 1 KB LDS block:
-// lane t's bytes land at block + 16 t (no VGPRs involved).
-__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, char* lds_block,
-                                            uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_block, 16, voff, 0, 0, 0);
-}
-
-// Transposed LDS read (gfx950 ds_read_b64_tr_b16): in each group of 16 lanes,
-// lane i addresses 8 bytes of row i/4 and receives column i of the 4x16 block
-// those addresses cover, i.e. 4 consecutive k of one output column.
-__device__ __forceinline__ u32x2 read_tr(const char* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-  return __builtin_bit_cast(u32x2, v);
-}
 
 // How a tile's K range is shared: S pieces (S = 1: the whole tile in one
 // workgroup); this piece is s; partials of split tile `slot` live in `part`.
@@ -757,9 +718,10 @@ __device__ __forceinline__ void run_tile(int nfm, const GemmArgs& g, const Tile&
 struct SplitPlan {
   int dp, sk, nsplit, KT;
 };
+// (can_split false: no split workspace; the leftover tiles run whole)
 template <int BM, int BN>
 __device__ __forceinline__ SplitPlan split_plan(const int* __restrict__ off, int E, int R,
-                                                int K, int N, int slots) {
+                                                int K, int N, int slots, bool can_split) {
   SplitPlan pl;
   const int NTN = (N + BN - 1) / BN;
   pl.KT = (K + BK - 1) / BK;
@@ -769,7 +731,7 @@ __device__ __forceinline__ SplitPlan split_plan(const int* __restrict__ off, int
   pl.nsplit = 1;
   // (short-K GEMMs gain less from filling the last round than the partials
   // and shorter pipelines cost them)
-  if (pl.sk > 0 && pl.KT >= 4 * MIN_SPLIT_STEPS)
+  if (can_split && pl.sk > 0 && pl.KT >= 4 * MIN_SPLIT_STEPS)
     pl.nsplit = max(1, min(slots / pl.sk, pl.KT / MIN_SPLIT_STEPS));
   return pl;
 }
@@ -787,7 +749,7 @@ __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __res
                                              int E, int R, float* __restrict__ part, int slots,
                                              const Lds& lds) {
   using S = GemmShape<BM, BN, WM, WN>;
-  const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots);
+  const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots, part != nullptr);
   const int bid = blockIdx.x;
   int L, kt_begin = 0, kt_end = pl.KT;
   Split sp{1, 0, 0, part};
@@ -834,7 +796,7 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   static_assert(2 * S::LDS_A + 4 * S::LDS_W + S::NW * 4096 <= 163840, "LDS budget");
   const int wave = threadIdx.x / kWave;
   const Lds lds{{a0, a1, nullptr, nullptr}, {w0, w1, w2, w3}, stg_all + wave * 4096};
-  const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots);
+  const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots, part != nullptr);
   const int G = gridDim.x, b = blockIdx.x;
   const int NTN = (g.N + BN - 1) / BN;
   const int n_whole = pl.dp / G;                       // pl.dp is a multiple of slots = G
@@ -856,6 +818,15 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
       ke = (sp.s + 1) * pl.KT / pl.nsplit;
     }
     t = lookup_tile(off, E, R, BM, NTN, L);
+    if (!t.valid) {
+      // (no tile: L is always in range for offsets the counts came from; an
+      // empty item still runs the K loop to keep the carried loads in step,
+      // reading expert 0's first slab and storing nothing)
+      t.e = 0;
+      t.nt = 0;
+      t.row0 = 0;
+      t.mrows = 0;
+    }
   };
   const int wm = wave % WM;
   Carry cy;
@@ -1129,7 +1100,7 @@ __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
   __shared__ __attribute__((aligned(1024))) char a0[S::LDS_A];
   __shared__ __attribute__((aligned(1024))) char a1[S::LDS_A];
   char* const stg = staging(a0, a1, S::NW);
-  const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots);
+  const SplitPlan pl = split_plan<BM, BN>(off, E, R, g.K, g.N, slots, part != nullptr);
   const int slot = blockIdx.x / S::FM, jb = blockIdx.x % S::FM;
   if (pl.nsplit < 2 || slot >= pl.sk) return;
   const int NTN = (g.N + BN - 1) / BN;
@@ -1176,7 +1147,9 @@ __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
 }
 
 int device_slots() {
-  // one 256x256 workgroup per CU (128 KB of LDS), capped at kMaxSlots
+  // one 256x256 workgroup per CU (128 KB of LDS), capped at kMaxSlots and
+  // rounded down to a multiple of the XCD count, so that a persistent
+  // workgroup's items b, b + G, ... stay on its own XCD's share of tiles
   static int cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kMaxSlots;
@@ -1185,7 +1158,8 @@ int device_slots() {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = kMaxSlots;
-    cached[dev] = std::min(cus, kMaxSlots);
+    cus = std::min(cus, kMaxSlots);
+    cached[dev] = cus >= kXcds ? cus / kXcds * kXcds : cus;
   }
   return cached[dev];
 }
@@ -1209,8 +1183,9 @@ hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* spl
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // tiles are split only when K has at least 4 * MIN_SPLIT_STEPS steps
-  if ((g.K + BK - 1) / BK >= 4 * MIN_SPLIT_STEPS) {
+  // tiles are split only when K has at least 4 * MIN_SPLIT_STEPS steps, and
+  // only with a split workspace
+  if (part != nullptr && (g.K + BK - 1) / BK >= 4 * MIN_SPLIT_STEPS) {
     hipLaunchKernelGGL((gemm_split_reduce<KIND, BM, BN, WM, WN>),
                        dim3(kMaxSlots / 2 * GemmShape<BM, BN, WM, WN>::FM),
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, (const float*)part, slots);

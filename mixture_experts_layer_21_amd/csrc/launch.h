@@ -50,7 +50,8 @@ enum Epilogue { EP_PLAIN = 0, EP_GELU = 1, EP_DGELU = 2 };
 // (the dispatch fused into the GEMM's loads), else row p.  B_e is W[e] as
 // [K][N] (w_nk false) or its transpose, W[e] stored [N][K] (w_nk true).
 // zout != nullptr: the accumulators are also stored there before the
-// epilogue (the pre-activation a training forward keeps).
+// epilogue (the pre-activation a training forward keeps).  split_ws ==
+// nullptr: no tile is split along K (the leftover tiles run whole).
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
                             bool w_nk, void* C, const int* off, int E, int R, int K, int N,
                             int ep, const void* aux, void* zout, void* split_ws,
@@ -73,9 +74,11 @@ hipError_t launch_gemm_f32_wgrad(const float* P, const float* Q, float* C, const
 hipError_t launch_combine(const void* yp, const int32_t* inv_pos, const float* w, int T,
                           int H, int k, bool bf16, void* y, hipStream_t s);
 
-// xp[p] = x[sorted_token[p]] for the rows p < offsets[E] (grid sized by R)
+// xp[p] = x[sorted_token[p]] for the rows p < min(offsets[E], R) (a token
+// index outside [0, T) gives a zero row; grid sized by R)
 hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, const int32_t* offsets,
-                              int E, int R, int H, size_t elem_bytes, void* xp, hipStream_t s);
+                              int E, int R, int T, int H, size_t elem_bytes, void* xp,
+                              hipStream_t s);
 
 // Backward kernels (backward.hip)
 // zero `bytes` (a multiple of 16) at p (16-byte aligned) with a kernel

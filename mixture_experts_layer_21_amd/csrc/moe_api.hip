@@ -5,11 +5,16 @@
 
 #include <initializer_list>
 
+#include "forward.h"
 #include "launch.h"
 
 namespace {
 
 using moe::align_up;
+using moe::check_forward;
+using moe::forward_body;
+using moe::fwd_layout;
+using moe::FwdLayout;
 
 constexpr int64_t kMaxE = 1024;
 constexpr int32_t kMaxTopK = 16;
@@ -51,31 +56,12 @@ size_t ffn_ws_bytes(int64_t R, int64_t F, moe_dtype dt) {
   return b;
 }
 
-// moe_forward workspace: routing outputs, dispatch indices, xp, yp, and one
-// stage region shared in time by the router, the dispatch counters and h.
-struct FwdLayout {
-  size_t ids, w, offsets, sorted, inv, xp, yp, stage, total;
-};
-
-FwdLayout fwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_dtype dt) {
-  const int64_t R = T * k;
-  const size_t es = elem_bytes(dt);
-  FwdLayout L;
-  size_t o = 0;
-  L.ids = o;     o += align_up((size_t)R * 4);
-  L.w = o;       o += align_up((size_t)R * 4);
-  L.offsets = o; o += align_up((size_t)(E + 1) * 4);
-  L.sorted = o;  o += align_up((size_t)R * 4);
-  L.inv = o;     o += align_up((size_t)R * 4);
-  L.xp = o;      // fp32 only: the bf16 GEMM gathers token rows from x itself
-  if (dt == MOE_F32) o += align_up((size_t)R * H * es);
-  L.yp = o;      o += align_up((size_t)R * H * es);
-  L.stage = o;
-  size_t st = moe::route_ws_bytes((int)T, (int)H, (int)E, dt == MOE_BF16);
-  st = std::max(st, moe::permute_ws_bytes((int)R, (int)E));
-  st = std::max(st, ffn_ws_bytes(R, F, dt));
-  L.total = o + st;
-  return L;
+// expert FFN over rows gathered from x: the FFN workspace, then (fp32, whose
+// GEMM reads contiguous rows) the gathered rows xp[R,H]
+size_t ffn_gather_ws_bytes(int64_t R, int64_t H, int64_t F, moe_dtype dt) {
+  size_t b = ffn_ws_bytes(R, F, dt);
+  if (dt == MOE_F32) b += align_up((size_t)R * H * 4);
+  return b;
 }
 
 moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
@@ -256,6 +242,9 @@ moe_status moe_stage_workspace_bytes(moe_stage stage, int64_t T, int64_t H, int6
     case MOE_STAGE_EXPERT_FFN_BACKWARD:
       *bytes = ffn_ws_bytes(T * top_k, F, dtype);
       return MOE_OK;
+    case MOE_STAGE_EXPERT_FFN_GATHER:
+      *bytes = ffn_gather_ws_bytes(T * top_k, H, F, dtype);
+      return MOE_OK;
     default:
       return MOE_ERR_INVALID_ARG;
   }
@@ -312,7 +301,8 @@ moe_status moe_permute_ex(const void* x, const int32_t* topk_ids, int64_t T, int
                           void* xp, void* ws, size_t ws_bytes, void* stream) {
   const moe_status st = check_shape(T, H, E, top_k, 8, dtype);
   if (st != MOE_OK) return st;
-  if (!x || !topk_ids || !expert_offsets || !sorted_token || !inv_pos || !xp || !ws)
+  // (xp may be NULL: indices only)
+  if (!x || !topk_ids || !expert_offsets || !sorted_token || !inv_pos || !ws)
     return MOE_ERR_INVALID_ARG;
   if (!aligned({x, xp, ws}, {topk_ids, expert_offsets, sorted_token, inv_pos}))
     return MOE_ERR_INVALID_ARG;
@@ -342,6 +332,32 @@ moe_status moe_expert_ffn(const void* xp, const int32_t* expert_offsets, const v
                  ffn_split(ws, R, F, dtype), (hipStream_t)stream);
 }
 
+moe_status moe_expert_ffn_gather(const void* x, int64_t T, const int32_t* sorted_token,
+                                 const int32_t* expert_offsets, const void* w1, const void* w2,
+                                 int64_t R, int64_t H, int64_t E, int64_t F, moe_dtype dtype,
+                                 void* yp, void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st = check_shape(R, H, E, 1, F, dtype);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T >= kIndexLimit / H) return MOE_ERR_UNSUPPORTED;
+  if (!x || !sorted_token || !expert_offsets || !w1 || !w2 || !yp || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned({x, w1, w2, yp, ws}, {sorted_token, expert_offsets})) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_gather_ws_bytes(R, H, F, dtype)) return MOE_ERR_INVALID_ARG;
+  if (R == 0) return MOE_OK;
+  hipStream_t s = (hipStream_t)stream;
+  void* split = ffn_split(ws, R, F, dtype);
+  if (dtype == MOE_BF16)
+    return run_ffn(x, sorted_token, T, expert_offsets, w1, w2, R, H, E, F, dtype, yp, ws,
+                   nullptr, split, s);
+  void* xp = (char*)ws + ffn_ws_bytes(R, F, dtype);
+  if (moe::launch_gather_rows(x, sorted_token, expert_offsets, (int)E, (int)R, (int)T, (int)H,
+                              elem_bytes(dtype), xp, s) != hipSuccess)
+    return MOE_ERR_LAUNCH;
+  return run_ffn(xp, nullptr, R, expert_offsets, w1, w2, R, H, E, F, dtype, yp, ws, nullptr,
+                 split, s);
+}
+
 moe_status moe_expert_ffn_backward(const void* dyp, const void* xp,
                                    const int32_t* expert_offsets, const void* z, const void* h,
                                    const void* w1, const void* w2, int64_t R, int64_t H,
@@ -369,22 +385,41 @@ moe_status moe_combine(const void* yp, const int32_t* inv_pos, const float* topk
                                            dtype == MOE_BF16, y, (hipStream_t)stream));
 }
 
-moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bias,
-                          const void* w1, const void* w2, int64_t T, int64_t H, int64_t E,
-                          int32_t top_k, int64_t F, moe_dtype dtype, moe_dtype router_dtype,
-                          moe_gating gating, int32_t capacity, void* y, int32_t* topk_ids_out,
-                          float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
-  moe_status st = check_shape(T, H, E, top_k, F, dtype);
-  if (st != MOE_OK) return st;
-  st = check_router(dtype, router_dtype, gating);
-  if (st != MOE_OK) return st;
-  if (!x || !w_r || !w1 || !w2 || !y || !ws) return MOE_ERR_INVALID_ARG;
-  if (!aligned({x, w_r, w1, w2, y, ws}, {router_bias, topk_ids_out, topk_w_out}))
-    return MOE_ERR_INVALID_ARG;
-  const FwdLayout L = fwd_layout(T, H, E, top_k, F, dtype);
-  if (ws_bytes < L.total) return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
-  hipStream_t s = (hipStream_t)stream;
+}  // extern "C"
+
+namespace moe {
+
+FwdLayout fwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_dtype dt,
+                     bool with_split) {
+  const int64_t R = T * k;
+  const size_t es = elem_bytes(dt);
+  FwdLayout L;
+  size_t o = 0;
+  L.ids = o;     o += align_up((size_t)R * 4);
+  L.w = o;       o += align_up((size_t)R * 4);
+  L.offsets = o; o += align_up((size_t)(E + 1) * 4);
+  L.sorted = o;  o += align_up((size_t)R * 4);
+  L.inv = o;     o += align_up((size_t)R * 4);
+  L.xp = o;      // fp32 only: the bf16 GEMM gathers token rows from x itself
+  if (dt == MOE_F32) o += align_up((size_t)R * H * es);
+  L.yp = o;      o += align_up((size_t)R * H * es);
+  L.stage = o;
+  size_t st = moe::route_ws_bytes((int)T, (int)H, (int)E, dt == MOE_BF16);
+  st = std::max(st, moe::permute_ws_bytes((int)R, (int)E));
+  st = std::max(st, with_split ? ffn_ws_bytes(R, F, dt) : align_up((size_t)R * F * elem_bytes(dt)));
+  L.total = o + st;
+  return L;
+}
+
+
+// The forward's launches into a workspace of layout L (validated by the
+// caller); split: the GEMMs may split leftover tiles (L has their region).
+moe_status forward_body(const void* x, const void* w_r, const float* router_bias,
+                        const void* w1, const void* w2, int64_t T, int64_t H, int64_t E,
+                        int32_t top_k, int64_t F, moe_dtype dtype, moe_dtype router_dtype,
+                        moe_gating gating, int32_t capacity, void* y, int32_t* topk_ids_out,
+                        float* topk_w_out, void* ws, const FwdLayout& L, bool split,
+                        hipStream_t s) {
   char* base = (char*)ws;
   int32_t* ids = topk_ids_out ? topk_ids_out : (int32_t*)(base + L.ids);
   float* w = topk_w_out ? topk_w_out : (float*)(base + L.w);
@@ -408,12 +443,50 @@ moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bi
   err = moe::launch_permute(x, ids, (int)T, (int)H, (int)E, top_k, capacity, elem_bytes(dtype),
                             off, sorted, inv, bf16 ? nullptr : xp, stage, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
-  void* split = ffn_split(stage, R, F, dtype);
+  void* split_ws = split ? ffn_split(stage, R, F, dtype) : nullptr;
   const moe_status fs =
-      bf16 ? run_ffn(x, sorted, T, off, w1, w2, R, H, E, F, dtype, yp, stage, nullptr, split, s)
-           : run_ffn(xp, nullptr, R, off, w1, w2, R, H, E, F, dtype, yp, stage, nullptr, split, s);
+      bf16 ? run_ffn(x, sorted, T, off, w1, w2, R, H, E, F, dtype, yp, stage, nullptr, split_ws, s)
+           : run_ffn(xp, nullptr, R, off, w1, w2, R, H, E, F, dtype, yp, stage, nullptr, split_ws,
+                     s);
   if (fs != MOE_OK) return fs;
   return launch_status(moe::launch_combine(yp, inv, w, (int)T, (int)H, top_k, bf16, y, s));
+}
+
+// Argument checks of the forward entry points (everything but the workspace).
+moe_status check_forward(const void* x, const void* w_r, const float* router_bias,
+                         const void* w1, const void* w2, int64_t T, int64_t H, int64_t E,
+                         int32_t top_k, int64_t F, moe_dtype dtype, moe_dtype router_dtype,
+                         moe_gating gating, const void* y, const int32_t* topk_ids_out,
+                         const float* topk_w_out) {
+  moe_status st = check_shape(T, H, E, top_k, F, dtype);
+  if (st != MOE_OK) return st;
+  st = check_router(dtype, router_dtype, gating);
+  if (st != MOE_OK) return st;
+  if (!x || !w_r || !w1 || !w2 || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned({x, w_r, w1, w2, y}, {router_bias, topk_ids_out, topk_w_out}))
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bias,
+                          const void* w1, const void* w2, int64_t T, int64_t H, int64_t E,
+                          int32_t top_k, int64_t F, moe_dtype dtype, moe_dtype router_dtype,
+                          moe_gating gating, int32_t capacity, void* y, int32_t* topk_ids_out,
+                          float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  const moe_status st = check_forward(x, w_r, router_bias, w1, w2, T, H, E, top_k, F, dtype,
+                                      router_dtype, gating, y, topk_ids_out, topk_w_out);
+  if (st != MOE_OK) return st;
+  if (!ws || !aligned({ws}, {})) return MOE_ERR_INVALID_ARG;
+  const FwdLayout L = fwd_layout(T, H, E, top_k, F, dtype);
+  if (ws_bytes < L.total) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  return forward_body(x, w_r, router_bias, w1, w2, T, H, E, top_k, F, dtype, router_dtype,
+                      gating, capacity, y, topk_ids_out, topk_w_out, ws, L, true,
+                      (hipStream_t)stream);
 }
 
 moe_status moe_forward(const void* x, const void* w_r, const float* router_bias, const void* w1,
@@ -548,7 +621,8 @@ moe_status moe_backward(const void* dy, const void* x, const void* w_r, const vo
     return launch_status(err);
   }
   // experts, over the token rows re-gathered into xp
-  err = moe::launch_gather_rows(x, sorted, off, (int)E, (int)R, (int)H, elem_bytes(dtype), xp, s);
+  err = moe::launch_gather_rows(x, sorted, off, (int)E, (int)R, (int)T, (int)H, elem_bytes(dtype),
+                                xp, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
   const moe_status fs = run_ffn_bwd(dyp, xp, off, z, h, w1, w2, R, H, E, F, dtype, dxp, dw1,
                                     dw2, dz, stage, s);

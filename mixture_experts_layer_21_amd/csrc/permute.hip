@@ -181,14 +181,20 @@ __global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ id
 __global__ __launch_bounds__(256) void perm_gather(const u32x4* __restrict__ x,
                                                    const int32_t* __restrict__ sorted_token,
                                                    const int32_t* __restrict__ offsets, int E,
-                                                   u32x4* __restrict__ xp, int row_chunks) {
+                                                   int R, int T, u32x4* __restrict__ xp,
+                                                   int row_chunks) {
   const int lane = threadIdx.x % kWave;
   const int nwaves = gridDim.x * 4;
-  const int R = offsets[E];                      // kept rows
-  for (int p = blockIdx.x * 4 + threadIdx.x / kWave; p < R; p += nwaves) {
-    const u32x4* src = x + (size_t)sorted_token[p] * row_chunks;
+  const int n = min(max(offsets[E], 0), R);     // kept rows (never past the buffer)
+  for (int p = blockIdx.x * 4 + threadIdx.x / kWave; p < n; p += nwaves) {
+    const int t = sorted_token[p];
     u32x4* dst = xp + (size_t)p * row_chunks;
-    for (int c = lane; c < row_chunks; c += kWave) dst[c] = src[c];
+    if ((unsigned)t < (unsigned)T) {
+      const u32x4* src = x + (size_t)t * row_chunks;
+      for (int c = lane; c < row_chunks; c += kWave) dst[c] = src[c];
+    } else {
+      for (int c = lane; c < row_chunks; c += kWave) dst[c] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 
@@ -321,17 +327,18 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
   const int row_chunks = (int)((size_t)H * elem_bytes / 16);
   const int blocks = std::min(8192, (R + 3) / 4);
   hipLaunchKernelGGL(perm_gather, dim3(blocks), dim3(256), 0, s, (const u32x4*)x, sorted_token,
-                     offsets, E, (u32x4*)xp, row_chunks);
+                     offsets, E, R, T, (u32x4*)xp, row_chunks);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, const int32_t* offsets,
-                              int E, int R, int H, size_t elem_bytes, void* xp, hipStream_t s) {
+                              int E, int R, int T, int H, size_t elem_bytes, void* xp,
+                              hipStream_t s) {
   if (R == 0) return hipSuccess;
   const int row_chunks = (int)((size_t)H * elem_bytes / 16);
   const int blocks = std::min(8192, (R + 3) / 4);
   hipLaunchKernelGGL(perm_gather, dim3(blocks), dim3(256), 0, s, (const u32x4*)x, sorted_token,
-                     offsets, E, (u32x4*)xp, row_chunks);
+                     offsets, E, R, T, (u32x4*)xp, row_chunks);
   return hipGetLastError();
 }
 

@@ -1,8 +1,18 @@
 // Routing + gating kernels (fused MoE article, section 1: router logits on
-// the matrix unit, per-token TopK, softmax over the k selected scores; the
+// the matrix unit, per-token TopK, softmax over the k selected scores, in one
+// kernel, so that the logits never make a round trip through HBM; the
 // routing article's scan fixes ties to the lower expert index).
 //
-// bf16 path
+// bf16 path, many tokens (T >= 1024, E <= 128 in multiples of 8, H <= 4096,
+// bf16 W_r)
+//   route_fused       the whole router in one launch: one workgroup per tile
+//                     of 16 tokens, its 8 waves splitting H, W_r read in
+//                     whole rows into registers and transposed there,
+//                     partial logits summed in LDS, then top-k and softmax in
+//                     the same workgroup (see the kernel's comment).
+//
+// bf16 path, other shapes (few tokens, where 16-token tiles cannot fill the
+// GPU; more experts; an fp32 W_r)
 //   route_logits_bf16 MFMA 16x16x32 bf16 with fp32 accumulation.  A workgroup
 //                     owns one expert group (TPW tiles of 16 experts) and one
 //                     split of the H axis (KL rows) for 4 token tiles of 16,
@@ -36,15 +46,6 @@
 namespace moe {
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Transposed LDS read (gfx950 ds_read_b64_tr_b16): in each group of 16 lanes,
-// lane i addresses 8 bytes of row i/4 and receives column i of the 4x16 block
-// those addresses cover.
-__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-  return __builtin_bit_cast(u32x2, v);
-}
 
 // fp32 -> (hi, mid, lo) bf16 bits with hi + mid + lo == w up to the rounding
 // of lo (hi, mid: truncations; each remainder is exact in fp32).
@@ -189,8 +190,8 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
         for (int pl = 0; pl < NP; ++pl) {
 #pragma unroll
           for (int j = 0; j < TPW; ++j) {
-            const u32x2 lo = lds_read_tr(base + pl * plane + j * 32);
-            const u32x2 hi = lds_read_tr(base + pl * plane + 4 * ROW + j * 32);
+            const u32x2 lo = read_tr(base + pl * plane + j * 32);
+            const u32x2 hi = read_tr(base + pl * plane + 4 * ROW + j * 32);
             const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
             acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                              __builtin_bit_cast(bf16x8, b),
@@ -370,39 +371,16 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-// route_select for many tokens and E <= 256: one token per row of 16 lanes,
-// four per wave.  Lane r of a row holds experts r, r + 16, ... (NV values,
-// ascending), so each arg-max round is a lane-local scan plus four DPP
-// exchanges inside the row, with no cross-row permutes; the split sums, bias,
-// selection, tie rule, gate weights and outputs are those of route_select.
+// One token per row of 16 lanes: lane rl of the row holds the summed logits
+// (bias not yet added) of experts rl, rl + 16, ... (NV values, ascending).
+// Adds the bias, keeps the logits when asked, takes the k winners by (value
+// desc, expert asc) in k rounds of a lane-local scan plus the in-row DPP
+// arg-max, then writes token t's ids and gate weights: the softmax of the k
+// winners, or (softmax_all) their probabilities under the softmax over all E.
 template <int NV>
-__global__ __launch_bounds__(256) void route_select_rows(
-    const float* __restrict__ part, const float* __restrict__ bias,
-    int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int EP,
-    int S, int k, int softmax_all, float* __restrict__ logits) {
-  const int rl = threadIdx.x % 16;
-  const int t = (blockIdx.x * 256 + threadIdx.x) / 16;
-  if (t >= T) return;   // whole rows leave together: the DPP partners stay in the row
-
-  constexpr int SB = 64 / NV < 16 ? 64 / NV : 16;
-  float v[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = 0.f;
-  const size_t sstride = (size_t)T * EP;
-  for (int s0 = 0; s0 < S; s0 += SB) {
-    float q[NV][SB];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = rl + i * 16;
-      const float* p = part + ((size_t)s0 * T + t) * EP + e;
-#pragma unroll
-      for (int u = 0; u < SB; ++u) q[i][u] = (e < E && s0 + u < S) ? p[u * sstride] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-      for (int u = 0; u < SB; ++u) v[i] += q[i][u];
-  }
+__device__ __forceinline__ void select_row(float (&v)[NV], int rl, int t, const float* bias,
+                                           int E, int k, int softmax_all, int32_t* ids,
+                                           float* w, float* logits) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = rl + i * 16;
@@ -460,6 +438,241 @@ __global__ __launch_bounds__(256) void route_select_rows(
   }
 }
 
+// route_select for many tokens and E <= 256: one token per row of 16 lanes,
+// four per wave.  Lane r of a row holds experts r, r + 16, ... (NV values,
+// ascending), so each arg-max round is a lane-local scan plus four DPP
+// exchanges inside the row, with no cross-row permutes; the split sums, bias,
+// selection, tie rule, gate weights and outputs are those of route_select.
+template <int NV>
+__global__ __launch_bounds__(256) void route_select_rows(
+    const float* __restrict__ part, const float* __restrict__ bias,
+    int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int EP,
+    int S, int k, int softmax_all, float* __restrict__ logits) {
+  const int rl = threadIdx.x % 16;
+  const int t = (blockIdx.x * 256 + threadIdx.x) / 16;
+  if (t >= T) return;   // whole rows leave together: the DPP partners stay in the row
+
+  constexpr int SB = 64 / NV < 16 ? 64 / NV : 16;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = 0.f;
+  const size_t sstride = (size_t)T * EP;
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    float q[NV][SB];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = rl + i * 16;
+      const float* p = part + ((size_t)s0 * T + t) * EP + e;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) q[i][u] = (e < E && s0 + u < S) ? p[u * sstride] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int u = 0; u < SB; ++u) v[i] += q[i][u];
+  }
+  select_row<NV>(v, rl, t, bias, E, k, softmax_all, ids, w, logits);
+}
+
+// ---------------------------------------------------------------------------
+// The router in one launch (many tokens, E <= 128 in multiples of 8, H <=
+// 4096, bf16 W_r): one workgroup of 8 waves per tile of 16 tokens computes
+// the tile's logits, top-k and gate weights; no partial logits leave the chip.
+//   * Wave w owns the H range [32 NS w, 32 NS (w + 1)), in steps of 32 rows.
+//   * W_r is read in its own [H][E] layout in whole rows: in load i of a
+//     step, lane group g (lanes 16 g .. 16 g + 15) reads row 8 g + i, lane
+//     c of the group experts 8 c .. 8 c + 7 (one 16-byte piece; a row of 128
+//     experts is 256 contiguous bytes).  After the 8 loads of a step a lane
+//     holds experts 8 c + e (e = 0..7) of rows 8 g + i (i = 0..7), an 8 x 8
+//     block that it transposes in its own registers (byte permutes): for each
+//     e, rows 8 g + 0..7 of expert 8 c + e, which is the MFMA B fragment of
+//     lane 16 g + c for the 16 experts e, 8 + e, ..., 120 + e.  So one step
+//     is 8 MFMAs, e = 0..7, each covering 16 experts strided by 8, and a wave
+//     keeps the partial logits of all 128 experts in 8 accumulators.
+//   * The token operand of a step (16 tokens x 32 rows) is read as 64-byte
+//     runs (4 lanes per token) and moved into the MFMA A layout (lane l:
+//     token l % 16, rows 8 (l / 16) + 0..7) with LDS permutes.
+//   * Loads run D steps ahead of the MFMAs (the compiler waits on each
+//     register as it is used).  At the end a wave leaves its 16 x 128 partial
+//     logits in LDS; after one barrier the partials of the 8 waves are added
+//     in wave order, and waves 0-3 run the selection with one token per row
+//     of 16 lanes (select_row).
+constexpr int kFuseWaves = 8;
+constexpr int kFuseMaxE = 128;
+constexpr int kFuseMaxH = kFuseWaves * 16 * 32;
+constexpr int kFuseMinT = 1024;
+
+// In each group of 8 lanes, lane i holds v = row i of an 8 x 8 block of bf16
+// (element c in half c % 2 of dword c / 2); returns column i of the block in
+// the same packing (dword p = rows 2p, 2p + 1).  sel and odd2 depend on the
+// lane: sel = (lane & 1) ? 0x03020706 : 0x05040100, odd2 = (lane & 2) != 0.
+__device__ __forceinline__ u32x4 transpose8(u32x4 v, uint32_t sel, bool odd2) {
+  uint32_t d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // lane ^ 1: the even lane keeps its low halves and takes its partner's,
+    // the odd lane the high halves
+    const uint32_t q = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[i], 0xB1, 0xF, 0xF, false);
+    d[i] = __builtin_amdgcn_perm(q, v[i], sel);
+  }
+  // lanes 4 apart: lanes 0-3 of the group take dwords 0, 1 of lanes 4-7 into
+  // their dwords 2, 3 (row_shl:4, banks 0 and 2), lanes 4-7 take dwords 2, 3
+  // of lanes 0-3 into their dwords 0, 1 (row_shr:4, banks 1 and 3)
+  const uint32_t n2 = (uint32_t)__builtin_amdgcn_update_dpp((int)d[2], (int)d[0], 0x104, 0xF, 0x5, false);
+  const uint32_t n3 = (uint32_t)__builtin_amdgcn_update_dpp((int)d[3], (int)d[1], 0x104, 0xF, 0x5, false);
+  const uint32_t n0 = (uint32_t)__builtin_amdgcn_update_dpp((int)d[0], (int)d[2], 0x114, 0xF, 0xA, false);
+  const uint32_t n1 = (uint32_t)__builtin_amdgcn_update_dpp((int)d[1], (int)d[3], 0x114, 0xF, 0xA, false);
+  // lanes 2 apart (quad_perm [2,3,0,1]): odd pairs' dwords 1, 3 <-> even pairs' 0, 2
+  const uint32_t p0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)n0, 0x4E, 0xF, 0xF, false);
+  const uint32_t p1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)n1, 0x4E, 0xF, 0xF, false);
+  const uint32_t p2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)n2, 0x4E, 0xF, 0xF, false);
+  const uint32_t p3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)n3, 0x4E, 0xF, 0xF, false);
+  return u32x4{odd2 ? p1 : n0, odd2 ? n1 : p0, odd2 ? p3 : n2, odd2 ? n3 : p2};
+}
+
+// Sum of the 8 waves' partial logits (wave order) for waves 0-3's selection:
+// one token per row of 16 lanes (select_row).
+template <int EPMAX>
+__device__ __forceinline__ void fused_select(const float (&part)[kFuseWaves][16][EPMAX],
+                                             int wave, int lane, int t0, int T,
+                                             const float* bias, int E, int k, int softmax_all,
+                                             int32_t* ids, float* w, float* logits) {
+  if (wave >= 4) return;
+  const int tt = wave * 4 + lane / 16;
+  const int t = t0 + tt;
+  if (t >= T) return;   // whole rows leave together
+  const int c = lane % 16;
+  constexpr int NV = EPMAX / 16;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = c + 16 * i;
+    float sum = 0.f;
+    if (e < E) {
+#pragma unroll
+      for (int ww = 0; ww < kFuseWaves; ++ww) sum += part[ww][tt][e];
+    }
+    v[i] = sum;
+  }
+  select_row<NV>(v, c, t, bias, E, k, softmax_all, ids, w, logits);
+}
+
+// E <= 16 (one expert tile): W_r is small, the token operand is the stream.
+// Every load of a wave (its 16 tokens x 32 NS rows of x as 64-byte runs, its
+// 32 NS rows of W_r) is issued at once.  A W_r load of a step reads rows
+// 8 (lane / 16) + lane % 8, experts 8 ((lane % 16) / 8) + 0..7 (16 bytes;
+// a row of 16 experts is 32 bytes), and transpose8 turns each group of 8
+// lanes' 8 x 8 block into the MFMA B fragment (lane: expert lane % 16, rows
+// 8 (lane / 16) + 0..7).  The token operand moves into the MFMA A layout with
+// LDS permutes, as in route_fused.
+template <int NS>
+__global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_r,
+    const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ w,
+    float* __restrict__ logits, int T, int H, int E, int k, int softmax_all) {
+  __shared__ __attribute__((aligned(16))) float part[kFuseWaves][16][16];
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t0 = blockIdx.x * 16;
+  const int h0 = wave * NS * 32;
+  const uint16_t* xr = x + (size_t)min(t0 + lane / 4, T - 1) * H + 8 * (lane % 4);
+  const int xsrc = 4 * (4 * (lane % 16) + lane / 16);
+  const int r_lane = 8 * (lane / 16) + lane % 8;
+  const int e_lane = 8 * ((lane % 16) / 8);
+  u32x4 xb[NS], wb[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const int hs = h0 + 32 * st;
+    xb[st] = hs + 8 * (lane % 4) < H ? *(const u32x4*)(xr + hs) : u32x4{0u, 0u, 0u, 0u};
+    const int h = hs + r_lane;
+    wb[st] = (e_lane < E && h < H) ? *(const u32x4*)(w_r + (size_t)h * E + e_lane)
+                                   : u32x4{0u, 0u, 0u, 0u};
+  }
+  const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;
+  const bool odd2 = (lane & 2) != 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    u32x4 xf;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xf[q] = (uint32_t)__builtin_amdgcn_ds_bpermute(xsrc, (int)xb[st][q]);
+    const u32x4 b = transpose8(wb[st], sel, odd2);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+  // D: lane holds expert lane % 16, tokens 4 (lane / 16) + v
+#pragma unroll
+  for (int v = 0; v < 4; ++v) part[wave][4 * (lane / 16) + v][lane % 16] = acc[v];
+  __syncthreads();
+  fused_select<16>(part, wave, lane, t0, T, bias, E, k, softmax_all, ids, w, logits);
+}
+
+template <int NS, int D>
+__global__ __launch_bounds__(kWave * kFuseWaves) void route_fused(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_r,
+    const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ w,
+    float* __restrict__ logits, int T, int H, int E, int k, int softmax_all) {
+  __shared__ __attribute__((aligned(16))) float part[kFuseWaves][16][kFuseMaxE];
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t0 = blockIdx.x * 16;
+  const int h0 = wave * NS * 32;
+  const int g = lane / 16, c = lane % 16;
+  // token operand loads: lane reads token t0 + lane / 4 (rows past T repeat
+  // the last token), rows 8 (lane % 4) + 0..7 of the step; the A fragment of
+  // lane l comes from lane 4 (l % 16) + l / 16
+  const uint16_t* xr = x + (size_t)min(t0 + lane / 4, T - 1) * H + 8 * (lane % 4);
+  const int xsrc = 4 * (4 * (lane % 16) + lane / 16);
+  // W_r loads: row h of the step's 8 g + i, experts 8 c .. 8 c + 7
+  const bool wc = 8 * c < E;
+  const uint16_t* wr = w_r + 8 * c;
+  auto load_step = [&](int st, u32x4 (&xb), u32x4 (&wb)[8]) {
+    const int hs = h0 + 32 * st;
+    xb = (st < NS && hs + 8 * (lane % 4) < H) ? *(const u32x4*)(xr + hs) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int h = hs + 8 * g + i;
+      wb[i] = (st < NS && wc && h < H) ? *(const u32x4*)(wr + (size_t)h * E) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  u32x4 xbuf[D], wbuf[D][8];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_step(d, xbuf[d], wbuf[d]);
+  f32x4 acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const int d = st % D;
+    u32x4 xf;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xf[q] = (uint32_t)__builtin_amdgcn_ds_bpermute(xsrc, (int)xbuf[d][q]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // rows 8 g + 2 p (low half) and 8 g + 2 p + 1 (high) of expert 8 c + e
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 b;
+#pragma unroll
+      for (int pq = 0; pq < 4; ++pq)
+        b[pq] = __builtin_amdgcn_perm(wbuf[d][2 * pq + 1][e / 2], wbuf[d][2 * pq][e / 2], sel);
+      acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xf),
+                                                       __builtin_bit_cast(bf16x8, b), acc[e], 0,
+                                                       0, 0);
+    }
+    load_step(st + D, xbuf[d], wbuf[d]);
+  }
+  // D of MFMA e: lane holds tokens 4 (lane / 16) + v, expert 8 (lane % 16) + e;
+  // for each v the 8 experts of the lane are contiguous: two 16-byte stores
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float* dst = &part[wave][4 * g + v][8 * c];
+    *(f32x4*)dst = f32x4{acc[0][v], acc[1][v], acc[2][v], acc[3][v]};
+    *(f32x4*)(dst + 4) = f32x4{acc[4][v], acc[5][v], acc[6][v], acc[7][v]};
+  }
+  __syncthreads();
+  fused_select<kFuseMaxE>(part, wave, lane, t0, T, bias, E, k, softmax_all, ids, w, logits);
+}
+
 constexpr int kRowSelectMinT = 1024;
 
 template <int NPL>
@@ -505,9 +718,45 @@ size_t route_ws_bytes(int T, int H, int E, bool bf16) {
   return align_up((size_t)std::max(a.S, b.S) * T * a.EP * sizeof(float));
 }
 
+bool route_is_fused(int T, int H, int E, bool bf16, bool wf32) {
+  return bf16 && !wf32 && T >= kFuseMinT && E % 8 == 0 && E <= kFuseMaxE && H <= kFuseMaxH;
+}
+
 hipError_t launch_route(const void* x, const void* w_r, const float* bias,
                         int T, int H, int E, int k, bool bf16, bool wf32, bool softmax_all,
                         int32_t* ids, float* w, float* logits, void* ws, hipStream_t s) {
+  if (route_is_fused(T, H, E, bf16, wf32)) {
+    // one launch: NS steps of 32 rows per wave cover H (8 waves), loads D
+    // steps ahead
+    const int per_wave = (H + kFuseWaves - 1) / kFuseWaves;
+    const int ns = (per_wave + 31) / 32;
+    const dim3 g((unsigned)((T + 15) / 16)), b(kWave * kFuseWaves);
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* wb = (const uint16_t*)w_r;
+    const int sa = softmax_all ? 1 : 0;
+#define MOE_ROUTE_FUSED(NS_, D_)                                                            \
+    hipLaunchKernelGGL((route_fused<NS_, D_>), g, b, 0, s, xb, wb, bias, ids, w, logits, T, H, \
+                       E, k, sa)
+#define MOE_ROUTE_FUSED_SMALL(NS_)                                                           \
+    hipLaunchKernelGGL((route_fused_small<NS_>), g, b, 0, s, xb, wb, bias, ids, w, logits, T, \
+                       H, E, k, sa)
+    if (E <= 16) {
+      if (ns <= 1) MOE_ROUTE_FUSED_SMALL(1);
+      else if (ns <= 2) MOE_ROUTE_FUSED_SMALL(2);
+      else if (ns <= 4) MOE_ROUTE_FUSED_SMALL(4);
+      else if (ns <= 8) MOE_ROUTE_FUSED_SMALL(8);
+      else MOE_ROUTE_FUSED_SMALL(16);
+    } else {
+      if (ns <= 1) MOE_ROUTE_FUSED(1, 1);
+      else if (ns <= 2) MOE_ROUTE_FUSED(2, 2);
+      else if (ns <= 4) MOE_ROUTE_FUSED(4, 4);
+      else if (ns <= 8) MOE_ROUTE_FUSED(8, 5);
+      else MOE_ROUTE_FUSED(16, 4);
+    }
+#undef MOE_ROUTE_FUSED_SMALL
+#undef MOE_ROUTE_FUSED
+    return hipGetLastError();
+  }
   const RoutePlan p = plan_route(T, H, E, bf16, wf32);
   float* part = (float*)ws;
   if (bf16) {

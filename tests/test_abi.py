@@ -114,7 +114,7 @@ def test_route_rejects(kw, expect):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(x=N), INV), (dict(ids=N), INV), (dict(off=N), INV), (dict(st=N), INV),
-    (dict(inv=N), INV), (dict(xp=N), INV), (dict(ws=N), INV), (dict(nb=0), INV),
+    (dict(inv=N), INV), (dict(ws=N), INV), (dict(nb=0), INV),
     (dict(k=0), INV), (dict(T=-1), INV), (dict(dt=2), UNS), (dict(H=12), UNS),
 ])
 def test_permute_rejects(kw, expect):
@@ -129,6 +129,31 @@ def test_permute_rejects(kw, expect):
 ])
 def test_expert_ffn_rejects(kw, expect):
     assert _ffn(**kw) == expect
+
+
+def _ffn_gather(x=P, T=64, st=P, off=P, w1=P, w2=P, R=128, H=128, E=8, F=256, dt=BF16, yp=P,
+                ws=P, nb=1 << 30):
+    return L.moe_expert_ffn_gather(x, T, st, off, w1, w2, R, H, E, F, dt, yp, ws, nb, N)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=N), INV), (dict(st=N), INV), (dict(off=N), INV), (dict(w1=N), INV),
+    (dict(w2=N), INV), (dict(yp=N), INV), (dict(ws=N), INV), (dict(nb=100), INV),
+    (dict(R=-5), INV), (dict(T=-1), INV), (dict(F=0), INV), (dict(F=20), UNS), (dict(H=20), UNS),
+    (dict(dt=9), UNS), (dict(E=4096), UNS), (dict(T=1 << 30, H=4096), UNS),
+    (dict(x=ctypes.c_void_p(0x1008)), INV), (dict(st=ctypes.c_void_p(0x1002)), INV),
+])
+def test_expert_ffn_gather_rejects(kw, expect):
+    assert _ffn_gather(**kw) == expect
+
+
+def test_expert_ffn_gather_workspace():
+    for dt, extra in ((BF16, 0), (F32, 128 * 128 * 4)):
+        st, g = stage_bytes(moe.MOE_STAGE_EXPERT_FFN_GATHER, 64, 128, 8, 2, 256, dt)
+        st2, f = stage_bytes(moe.MOE_STAGE_EXPERT_FFN, 64, 128, 8, 2, 256, dt)
+        assert st == OK and st2 == OK and g == f + extra
+        assert _ffn_gather(R=128, dt=dt, nb=g - 1) == INV
+    assert _ffn_gather(R=0) == OK      # nothing to compute: no device access
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -213,7 +238,7 @@ def test_route_ex_rejects(kw, expect):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(x=N), INV), (dict(ids=N), INV), (dict(off=N), INV), (dict(st=N), INV),
-    (dict(inv=N), INV), (dict(xp=N), INV), (dict(ws=N), INV), (dict(nb=0), INV),
+    (dict(inv=N), INV), (dict(ws=N), INV), (dict(nb=0), INV),
     (dict(k=0), INV), (dict(dt=2), UNS), (dict(H=12), UNS),
 ])
 def test_permute_ex_rejects(kw, expect):

@@ -194,3 +194,45 @@ def test_expert_ffn_backward_stage_matches_oracle(name):
     assert_close_rel(f64(dw1), ref_dw1, tol, "dw1")
     assert_close_rel(f64(dw2), ref_dw2, tol, "dw2")
     assert torch.count_nonzero(dw1[1]).item() == 0 and torch.count_nonzero(dw2[1]).item() == 0
+
+
+@pytest.mark.parametrize("name,gating", [("ragged_bf16", GT), ("ragged_bf16", GS),
+                                         ("many_small_bf16", GT), ("tiny_fp32", GT)])
+def test_backward_skips_out_of_range_ids(name, gating):
+    """Expert ids handed back to the backward that lie outside [0, E) (-1 and
+    E; not ids the training forward produced).  Such a slot is left out of the
+    router gradient; the expert side and the gate-weight gradient follow the
+    dispatch kept in `saved`.  Reference: the oracle's backward for the
+    forward's own ids, with the softmax Jacobian redone after zeroing those
+    slots' gate-weight gradient (a dropped pair's), and (top-k then softmax)
+    no gradient for the logit an out-of-range id no longer names."""
+    cfg = CASES[name]
+    L, w_r, y, ids, w, saved, clean = run(cfg, gating, with_bias=True)
+    T, k = cfg.T, cfg.k
+    rng = np.random.default_rng(7)
+    flat = rng.choice(T * k, size=max(2, T * k // 10), replace=False)
+    vals = np.where(np.arange(len(flat)) % 2 == 0, -1, cfg.E).astype(np.int32)
+    ids_bad = ids.clone()
+    ids_bad.view(-1)[torch.from_numpy(flat).long().cuda()] = torch.from_numpy(vals).cuda()
+    out = moe.moe_backward(L["dy"], L["x"], w_r, L["w1"], L["w2"], k, ids_bad, w, saved, gating,
+                           with_bias_grad=True)
+    torch.cuda.synchronize()
+    for n in ("dw1", "dw2", "dw"):
+        assert torch.equal(out[n], clean[n]), n
+    tol = TOL[cfg.dtype]
+    x64, wr64 = f64(L["x"]), f64(w_r)
+    logits = oracle.router_logits(x64, wr64, f64(L["router_bias"]))
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    bad = np.zeros(T * k, dtype=bool)
+    bad[flat] = True
+    bad = bad.reshape(T, k)
+    ref = oracle.backward(x64, wr64, f64(L["router_bias"]), f64(L["w1"]), f64(L["w2"]), k,
+                          f64(L["dy"]), ids=ids_np, gating=GNAME[gating])
+    dl = oracle.gate_weights_grad(logits, ids_np, np.where(bad, 0.0, ref["dw"]), GNAME[gating])
+    if gating == GT:
+        tb, jb = np.nonzero(bad)
+        dl[tb, ids_np[tb, jb]] = 0.0
+    dx_ref = ref["dx"] - ref["dlogits"] @ wr64.T + dl @ wr64.T
+    assert_close_rel(f64(out["dx"]), dx_ref, tol, "dx")
+    assert_close_rel(f64(out["dw_r"]), x64.T @ dl, tol, "dw_r")
+    assert_close_rel(f64(out["db_r"]), dl.sum(axis=0), tol, "db_r")

@@ -3,17 +3,22 @@
 Small shapes are checked element by element on every output, at sizes that
 span several 256x256 GEMM tiles with ragged row, column and K tails, plus the
 degenerate cases (T=1, k=1, k=E, E=1, empty experts, skewed routing, exact
-ties).  The five full-size workloads are checked on every routing decision
-and dispatch index, and on sampled output rows that the oracle computes one
-expert at a time, in the same launch configuration the bench times."""
+ties).  The five full-size workloads, in the launch configuration the bench
+times, are checked on every routing decision and dispatch index and on every
+element of y and of the dispatched expert outputs yp, against the oracle run
+one expert at a time over the whole batch.  So is a mid-size layer whose two
+expert GEMMs both run whole rounds of 256x256 tiles on every CU and then
+split the leftover tiles along K (the persistent kernel's hand-off from whole
+tiles to split pieces), with expert row counts that leave 10- to 32-row
+tiles."""
 import numpy as np
 import pytest
 import torch
 
 import moe_inputs as mi
 import oracle
-from moe_check import (TOL, assert_close_rel, check_routing, expert_getters, f64, gpu_layer,
-                       sample_tokens)
+from moe_check import (TOL, assert_close_rel, check_routing, expert_getters, f64, f64g,
+                       gpu_layer)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,8 +47,35 @@ SMALL = {
     # few tiles with a long K: the expert GEMM splits tiles along K (partials
     # summed by the last piece), checked here on every element
     "ksplit_bf16": C("ksplit_bf16", T=300, H=4096, E=2, k=1, F=512, dtype="bf16"),
+    # the one-launch router (T >= 1024, E <= 128 in multiples of 8, H <= 4096):
+    # each of the 8 waves takes NS = 1, 2, 4, 8, 16 steps of 32 rows of H
+    # (H = 40 .. 4096: waves with partly and wholly empty ranges), in both
+    # kernels (E <= 16, and E = 24 .. 128 read in whole rows), a last token
+    # tile of 1 to 15 tokens; and one layer with H > 4096 that takes the
+    # two-kernel router at T >= 1024
+    "fused_E8_bf16": C("fused_E8_bf16", T=1031, H=4096, E=8, k=2, F=64, dtype="bf16"),
+    "fused_E8_H448_bf16": C("fused_E8_H448_bf16", T=1025, H=448, E=8, k=1, F=64, dtype="bf16"),
+    "fused_E16_H2048_bf16": C("fused_E16_H2048_bf16", T=1035, H=2048, E=16, k=4, F=64,
+                              dtype="bf16", bias0=0.5),
+    "fused_E16_H1000_bf16": C("fused_E16_H1000_bf16", T=1100, H=1000, E=16, k=3, F=64,
+                              dtype="bf16"),
+    "fused_E128_bf16": C("fused_E128_bf16", T=1027, H=2048, E=128, k=8, F=64, dtype="bf16"),
+    "fused_E64_H4096_bf16": C("fused_E64_H4096_bf16", T=1040, H=4096, E=64, k=6, F=64,
+                              dtype="bf16"),
+    "fused_H1000_bf16": C("fused_H1000_bf16", T=1033, H=1000, E=64, k=8, F=64, dtype="bf16",
+                          bias0=1.0),
+    "fused_H448_bf16": C("fused_H448_bf16", T=1049, H=448, E=24, k=3, F=64, dtype="bf16"),
+    "fused_H40_bf16": C("fused_H40_bf16", T=1300, H=40, E=16, k=4, F=64, dtype="bf16"),
+    "fused_H40_E32_bf16": C("fused_H40_E32_bf16", T=1024, H=40, E=32, k=5, F=64, dtype="bf16"),
+    "route2_H7168_bf16": C("route2_H7168_bf16", T=1039, H=7168, E=64, k=8, F=64, dtype="bf16",
+                           bias0=1.0),
 }
 FULL = [n for n in mi.CONFIG_ORDER]
+# both expert GEMMs: 4 whole rounds + 96 tiles split in 2 (GEMM1, 1120 tiles),
+# 1 whole round + 24 tiles split in 10 (GEMM2, 280 tiles); expert rows
+# [1007, 1000, 1043, 1008, 1020, 1056, 1034, 1024]
+HANDOFF = C("handoff_bf16", T=2048, H=2048, E=8, k=4, F=8192, dtype="bf16")
+FULL_CFG = {**{n: mi.CONFIGS[n] for n in FULL}, HANDOFF.name: HANDOFF}
 
 _cache = {}
 
@@ -164,11 +196,11 @@ def test_generator_is_bit_identical_on_cpu_and_gpu():
     assert torch.equal(mi.make_w2_expert(c1, 77, "cpu"), mi.make_w2_expert(c1, 77, "cuda").cpu())
 
 
-# --- full-size workloads ------------------------------------------------------
+# --- full-size workloads: every element ---------------------------------------
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", list(FULL_CFG))
 def test_forward_full(name):
-    cfg = mi.CONFIGS[name]
+    cfg = FULL_CFG[name]
     L = layer(cfg)
     ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
     w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
@@ -179,21 +211,16 @@ def test_forward_full(name):
     ids_np = ids.cpu().numpy().astype(np.int64)
     nb, nw = check_routing(ids_np, w.cpu().numpy(), logits, cfg.k)
     print(f"[{name}] near ties: boundary {nb}, within-set {nw}", flush=True)
-    excused = np.nonzero((ids_np != oracle.topk_ids(logits, cfg.k)).any(1))[0]
-    sel = sample_tokens(cfg.T, extra=excused)
-    w_ref = oracle.gate_weights(logits[sel], ids_np[sel])
     g1, g2 = expert_getters(L)
-    x_sel = f64(L["x"][torch.from_numpy(sel).cuda()])
-    y_ref = oracle.forward(x_sel, f64(L["w_r"]), None, g1, g2, cfg.k, ids=ids_np[sel],
-                           w=w_ref)["y"]
-    y_sel = f64(y[torch.from_numpy(sel).cuda()])
-    rel = assert_close_rel(y_sel, y_ref, TOL[dt(cfg)], f"{name} y (sampled)")
-    print(f"[{name}] max|err|/max|y_ref| = {rel:.3e} over {len(sel)} tokens", flush=True)
+    y_ref = oracle.forward(f64(L["x"]), f64(L["w_r"]), f64(L["router_bias"]), g1, g2, cfg.k,
+                           ids=ids_np, w=oracle.gate_weights(logits, ids_np))["y"]
+    rel = assert_close_rel(f64(y), y_ref, TOL[dt(cfg)], f"{name} y")
+    print(f"[{name}] y: max|err|/max|y_ref| = {rel:.3e} over all {cfg.T} tokens", flush=True)
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", list(FULL_CFG))
 def test_dispatch_full(name):
-    cfg = mi.CONFIGS[name]
+    cfg = FULL_CFG[name]
     L = layer(cfg)
     ids, w = moe.moe_route(L["x"], L["w_r"], L["router_bias"], cfg.k)
     off, st, inv, xp = moe.moe_permute(L["x"], ids, cfg.E)
@@ -203,18 +230,13 @@ def test_dispatch_full(name):
     np.testing.assert_array_equal(st.cpu().numpy(), o_st)
     np.testing.assert_array_equal(inv.cpu().numpy(), o_inv.ravel())
     assert torch.equal(xp, L["x"][st.long()])
-    # sampled rows of the expert FFN on the real shapes
+    # every dispatched row of the expert FFN, on the real shapes
     yp = moe.moe_expert_ffn(xp, off, L["w1"], L["w2"])
     torch.cuda.synchronize()
-    g = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([g.choice(cfg.R, 24, replace=False), [0, cfg.R - 1]]))
-    expert_of = np.searchsorted(o_off, rows, side="right") - 1
     g1, g2 = expert_getters(L)
-    ref = np.zeros((len(rows), cfg.H))
-    for e in np.unique(expert_of):
-        m = expert_of == e
-        ref[m] = oracle.expert_ffn_block(f64(xp[torch.from_numpy(rows[m]).cuda()]), g1(e), g2(e))
-    assert_close_rel(f64(yp[torch.from_numpy(rows).cuda()]), ref, TOL[dt(cfg)], f"{name} yp")
+    ref = oracle.expert_ffn(f64g(xp), o_off, g1, g2)
+    rel = assert_close_rel(f64g(yp), ref, TOL[dt(cfg)], f"{name} yp")
+    print(f"[{name}] yp: max|err|/max|yp_ref| = {rel:.3e} over all {cfg.R} rows", flush=True)
 
 
 @pytest.mark.parametrize("name", ["mixtral_bf16", "many_experts_bf16"])

@@ -9,7 +9,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from moe_check import TOL, assert_close_rel, check_routing, expert_getters, f64, sample_tokens
+from moe_check import TOL, assert_close_rel, check_routing, expert_getters, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -33,6 +33,10 @@ SMALL = {
     "rows_bf16": C("rows_bf16", T=1100, H=128, E=40, k=6, F=64, dtype="bf16"),
     "rows_wide_E_bf16": C("rows_wide_E_bf16", T=1030, H=64, E=200, k=8, F=32, dtype="bf16"),
     "rows_f32": C("rows_f32", T=1050, H=72, E=12, k=3, F=40, dtype="f32"),
+    # the one-launch router
+    "fused_E8_bf16": C("fused_E8_bf16", T=1031, H=4096, E=8, k=2, F=64, dtype="bf16"),
+    "fused_E128_bf16": C("fused_E128_bf16", T=1027, H=2048, E=128, k=8, F=64, dtype="bf16",
+                         bias0=0.5),
 }
 BF16_SMALL = [n for n, c in SMALL.items() if c.dtype == "bf16"]
 _cache = {}
@@ -191,16 +195,14 @@ def test_forward_ex_full(name, variant):
           flush=True)
     if v["cap"] and name == "skewed_bf16":
         assert n_drop > 1000          # expert 0 is far over capacity
-    dropped_tok = np.nonzero((inv < 0).any(axis=1))[0][:8]
-    sel = sample_tokens(cfg.T, extra=dropped_tok)
-    w_ref = oracle.gate_weights(logits[sel], ids_np[sel], gname)
-    w_ref = np.where(inv[sel] >= 0, w_ref, 0.0)       # dropped slots add nothing
+    # every token: the oracle's layer with the same capacity, driven by the
+    # GPU's ids (a dropped pair adds nothing, the others keep their weights)
     g1, g2 = expert_getters(L)
-    x_sel = f64(L["x"][torch.from_numpy(sel).cuda()])
-    y_ref = oracle.forward(x_sel, f64(w_r), None, g1, g2, cfg.k, ids=ids_np[sel], w=w_ref)["y"]
-    y_sel = f64(y[torch.from_numpy(sel).cuda()])
-    rel = assert_close_rel(y_sel, y_ref, TOL["bf16"], f"{name}/{variant} y (sampled)")
-    print(f"[{name}/{variant}] max|err|/max|y_ref| = {rel:.3e} over {len(sel)} tokens",
+    y_ref = oracle.forward(f64(L["x"]), f64(w_r), f64(L["router_bias"]), g1, g2, cfg.k,
+                           ids=ids_np, w=oracle.gate_weights(logits, ids_np, gname),
+                           gating=gname, capacity=cap)["y"]
+    rel = assert_close_rel(f64(y), y_ref, TOL["bf16"], f"{name}/{variant} y")
+    print(f"[{name}/{variant}] max|err|/max|y_ref| = {rel:.3e} over all {cfg.T} tokens",
           flush=True)
 
 
