@@ -292,6 +292,28 @@ moe_status moe_forward_ex(const void* x, const void* w_r, const float* router_bi
                           void* y, int32_t* topk_ids_out, float* topk_w_out,
                           void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * The layer forward for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  As
+ * moe_forward (default gating, dropless, router weights in dtype), but with
+ * no workspace argument: the workspace is a fixed 32 MiB device array inside
+ * the library (one copy per GPU, held until the process ends), so nothing is
+ * allocated by the library or the caller beyond x, the weights and the
+ * outputs.  For the layer to fit, its moe_forward workspace less the split
+ * GEMM partials (routing outputs, dispatch indices, the expert outputs
+ * yp[T*top_k,H] and the larger of h[T*top_k,F] and the router's partial
+ * logits) must be at most 32 MiB, else MOE_ERR_UNSUPPORTED: decode-sized
+ * batches (e.g. 64 tokens of a 7168-wide layer with 8 of 256 experts).  The
+ * expert GEMMs do not split tiles along K here, so y may differ from
+ * moe_forward's in rounding (ids and gate weights are identical).  Every call
+ * on a GPU uses that GPU's one array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ */
+moe_status moe_forward_noalloc(const void* x, const void* w_r, const float* router_bias,
+                               const void* w1, const void* w2, int64_t T, int64_t H, int64_t E,
+                               int32_t top_k, int64_t F, moe_dtype dtype, void* y,
+                               int32_t* topk_ids_out, float* topk_w_out, void* stream);
+
 /* ------------------------------------------------------------------------
  * Training: a forward that keeps what the backward needs, and the backward.
  *

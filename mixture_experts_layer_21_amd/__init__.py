@@ -35,7 +35,7 @@ MOE_GATE_TOPK_SOFTMAX, MOE_GATE_SOFTMAX_TOPK = 0, 1
 EXPORTS = ("moe_status_string", "moe_workspace_bytes", "moe_stage_workspace_bytes", "moe_route",
            "moe_route_ex", "moe_expert_capacity", "moe_permute", "moe_permute_ex",
            "moe_expert_ffn", "moe_expert_ffn_gather", "moe_combine", "moe_forward",
-           "moe_forward_ex", "moe_saved_bytes",
+           "moe_forward_ex", "moe_forward_noalloc", "moe_saved_bytes",
            "moe_backward_workspace_bytes", "moe_forward_train", "moe_backward",
            "moe_expert_ffn_backward")
 
@@ -74,6 +74,9 @@ _lib.moe_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i
 _lib.moe_forward_ex.restype = _i32
 _lib.moe_forward_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32, _i32,
                                 _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_forward_noalloc.restype = _i32
+_lib.moe_forward_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i64, _i32,
+                                     _vp, _vp, _vp, _vp]
 _lib.moe_expert_ffn_backward.restype = _i32
 _lib.moe_expert_ffn_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                          _i32, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -385,6 +388,32 @@ def moe_forward_ex(x, w_r, router_bias, w1, w2, top_k: int, gating: int = MOE_GA
                             top_k, F, _dtype_code(x.dtype), _dtype_code(w_r.dtype), gating,
                             capacity, _ptr(y), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(ws),
                             ws.numel(), _stream(dev)), "moe_forward_ex")
+    return y
+
+
+def moe_forward_noalloc(x, w_r, router_bias, w1, w2, top_k: int, y, topk_ids_out=None,
+                        topk_w_out=None):
+    """The layer forward with the library's own fixed scratch as workspace (for
+    callers that cannot allocate): y (preallocated, [T,H]) is filled and
+    returned.  Layers whose workspace exceeds the scratch raise MoEError
+    (MOE_ERR_UNSUPPORTED)."""
+    _check(x, "x")
+    T, H = x.shape
+    E = w_r.shape[1]
+    F = w1.shape[2]
+    _check(w_r, "w_r", x.dtype, (H, E))
+    if router_bias is not None:
+        _check(router_bias, "router_bias", torch.float32, (E,))
+    _check(w1, "w1", x.dtype, (E, H, F))
+    _check(w2, "w2", x.dtype, (E, F, H))
+    _check(y, "y", x.dtype, (T, H))
+    if topk_ids_out is not None:
+        _check(topk_ids_out, "topk_ids_out", torch.int32, (T, top_k))
+    if topk_w_out is not None:
+        _check(topk_w_out, "topk_w_out", torch.float32, (T, top_k))
+    _ok(_lib.moe_forward_noalloc(_ptr(x), _ptr(w_r), _ptr(router_bias), _ptr(w1), _ptr(w2), T, H,
+                                 E, top_k, F, _dtype_code(x.dtype), _ptr(y), _ptr(topk_ids_out),
+                                 _ptr(topk_w_out), _stream(x.device)), "moe_forward_noalloc")
     return y
 
 

@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["moe_api.hip", "route.hip", "permute.hip", "gemm_bf16.hip", "gemm_f32.hip",
-           "combine.hip", "backward.hip"]
+           "combine.hip", "backward.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 
