@@ -5,6 +5,7 @@
 // (the article's [num_experts, expert_capacity] blocks; CANN MoE article,
 // section 4.3) each expert keeps only its first `cap` pairs in that order.
 //
+//   (larger layers, three launches:)
 //   perm_count   per chunk of CH pairs: expert histogram in LDS -> counts[b][e]
 //   perm_scan    one workgroup: per-expert exclusive scan over chunks (each
 //                chunk's rank base inside its expert) and over experts of
@@ -18,10 +19,11 @@
 //                the pair is dropped, inv_pos = -1
 //   perm_gather  xp[p,:] = x[sorted_token[p],:] for p < offsets[E], 16-byte
 //                copies, one wave per row
-//   perm_small   for small layers (E <= 256, R <= 16384) the first three in one
-//                workgroup of 16 waves, one launch: each wave ranks a
-//                contiguous run of pairs, the per-wave counts are scanned,
-//                then every pair is placed (the same stable order)
+//   perm_onepass for R <= 65536 pairs the first three in one launch: each
+//                workgroup counts all pairs (totals, and those before its own
+//                1024) in LDS, so it knows the offsets and its range's base
+//                ranks without reading another workgroup's results, then
+//                ranks and places its 1024 pairs (the same stable order)
 //
 // All counts are integers: placement is exact and deterministic.  A pair
 // whose id is outside [0, E) is dropped like a pair beyond the capacity
@@ -178,6 +180,105 @@ __global__ __launch_bounds__(256) void perm_place(const int32_t* __restrict__ id
   }
 }
 
+// Dispatch in one launch for R <= kOnePassR (any E <= 1024): workgroup g of
+// 1024 threads owns the pairs [1024 g, 1024 g + 1024) (one per thread).  It
+// first counts, in LDS, every valid pair of the whole layer by expert, and
+// separately those before its own range: the totals give every expert's
+// offset (each workgroup computes the same exclusive scan of min(total,
+// cap); workgroup 0 writes them), the "before" counts give the rank at
+// which each expert's pairs of this range start.  Then each pair's rank
+// inside the range is found from the ballot peers inside the wave
+// plus the counts of the earlier waves, and the pair is placed.  No
+// workgroup reads another's results, so nothing crosses workgroups and one
+// launch suffices; every workgroup reads all R ids (L2-resident), which is
+// why this form stops at kOnePassR pairs.
+constexpr int kOnePassR = 65536;
+constexpr int kOnePassWaves = 16;
+
+__global__ __launch_bounds__(1024) void perm_onepass(const int32_t* __restrict__ ids, int R,
+                                                     int E, int k, int cap,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted_token,
+                                                     int32_t* __restrict__ inv_pos) {
+  extern __shared__ int sm[];
+  int* total = sm;                           // [E]: valid pairs of each expert
+  int* before = sm + E;                      // [E]: ... before this workgroup's range
+  int* wcnt = sm + 2 * E;                    // [16][E]: this range's pairs per wave
+  int* off_s = sm + (2 + kOnePassWaves) * E; // [E]: kept-row offset of each expert
+  __shared__ int wsum[kOnePassWaves];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int start = blockIdx.x * 1024;
+  for (int t = tid; t < (2 + kOnePassWaves) * E; t += 1024) sm[t] = 0;
+  __syncthreads();
+  // counts over all pairs: 8 ids per thread loaded before they are counted
+  for (int i0 = tid; i0 < R; i0 += 8 * 1024) {
+    int e8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 1024;
+      e8[u] = i < R ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 1024;
+      if ((unsigned)e8[u] < (unsigned)E) {
+        atomicAdd(&total[e8[u]], 1);
+        if (i < start) atomicAdd(&before[e8[u]], 1);
+      }
+    }
+  }
+  // this range: each pair's expert and its rank among the wave's peers
+  const int i = start + tid;
+  const int my_e = i < R ? ids[i] : -1;
+  const bool valid = i < R && (unsigned)my_e < (unsigned)E;
+  const uint64_t peers = wave_match(my_e, valid, id_bits(E));
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int in_wave = __popcll(peers & lt_mask);
+  if (valid && in_wave == 0) wcnt[wave * E + my_e] = __popcll(peers);
+  __syncthreads();
+  // thread e (E <= 1024): the start rank of each wave among expert e's pairs
+  // of this range (exclusive scan of the wave counts), and expert e's
+  // kept-row offset (exclusive scan of min(total, cap) over the experts)
+  const int v = tid < E ? min(total[tid], cap) : 0;
+  if (tid < E) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kOnePassWaves; ++w) {
+      const int c = wcnt[w * E + tid];
+      wcnt[w * E + tid] = run;
+      run += c;
+    }
+  }
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  if (tid < E) {
+    int wbase = 0;
+    for (int w = 0; w < wave; ++w) wbase += wsum[w];
+    off_s[tid] = wbase + incl - v;
+    if (blockIdx.x == 0) offsets[tid] = wbase + incl - v;
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    int all = 0;
+    for (int w = 0; w < kOnePassWaves; ++w) all += wsum[w];
+    offsets[E] = all;
+  }
+  __syncthreads();
+  if (i >= R) return;
+  if (!valid) {
+    inv_pos[i] = -1;   // an id outside [0, E): dropped
+    return;
+  }
+  const int r_e = before[my_e] + wcnt[wave * E + my_e] + in_wave;
+  if (r_e < cap) {
+    const int pos = off_s[my_e] + r_e;
+    sorted_token[pos] = i / k;
+    inv_pos[i] = pos;
+  } else {
+    inv_pos[i] = -1;
+  }
+}
+
 __global__ __launch_bounds__(256) void perm_gather(const u32x4* __restrict__ x,
                                                    const int32_t* __restrict__ sorted_token,
                                                    const int32_t* __restrict__ offsets, int E,
@@ -198,99 +299,6 @@ __global__ __launch_bounds__(256) void perm_gather(const u32x4* __restrict__ x,
   }
 }
 
-constexpr int kSmallE = 256, kSmallR = 16384;   // ids fit 8 bits, ranks 16
-constexpr int kSmallWaves = 16;
-
-// One workgroup of 16 waves.  Wave w owns a contiguous run of 64-pair chunks
-// (pairs in index order), ranks each pair inside its expert among the wave's
-// pairs so far (ballot peers + a wave-private running count), and after one
-// barrier the per-wave counts give both the expert totals and each wave's
-// starting rank.  Every pair's id is loaded up front, so the only serial
-// latency is the ranking arithmetic itself.
-template <int kSmallChunks>   // 64-pair chunks per wave, at most
-__global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int R, int E,
-                                                   int k, int cap, int32_t* __restrict__ offsets,
-                                                   int32_t* __restrict__ sorted_token,
-                                                   int32_t* __restrict__ inv_pos) {
-  __shared__ int wcnt[kSmallWaves][kSmallE];   // pairs per (wave, expert), then start ranks
-  __shared__ int off_s[kSmallE];               // kept-row offset of each expert
-  __shared__ int wsum[kSmallWaves];
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int nch = (R + kWave - 1) / kWave;
-  const int cpw = (nch + kSmallWaves - 1) / kSmallWaves;   // chunks per wave
-  const int c0 = wave * cpw;
-  const int nbits = id_bits(E);
-  // pair j of this lane: its expert id, then (after ranking) rank << 8 | id
-  // (ids < 256, ranks < 32768); -1 for no pair, -2 for an id outside [0, E)
-  int pr[kSmallChunks];
-#pragma unroll
-  for (int j = 0; j < kSmallChunks; ++j) {
-    const int i = (c0 + j) * kWave + lane;
-    const int e = (j < cpw && i < R) ? ids[i] : -1;
-    pr[j] = (j < cpw && i < R && (unsigned)e >= (unsigned)E) ? -2 : e;
-  }
-  for (int t = tid; t < kSmallWaves * E; t += 1024) wcnt[t / E][t % E] = 0;
-  __syncthreads();
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-#pragma unroll
-  for (int j = 0; j < kSmallChunks; ++j) {
-    if (j < cpw) {
-      const int e = pr[j];
-      const bool valid = e >= 0;
-      const uint64_t peers = wave_match(e, valid, nbits);
-      const int before = __popcll(peers & lt_mask);
-      const int cnt = valid ? wcnt[wave][e] : 0;
-      if (valid) pr[j] = (cnt + before) << 8 | e;
-      // one lane per peer group advances the count, after every lane has read it
-      if (valid && before == 0) wcnt[wave][e] = cnt + __popcll(peers);
-    }
-  }
-  __syncthreads();
-  // per expert: start rank of each wave (exclusive scan over waves), total
-  int total = 0;
-  if (tid < E) {
-#pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) {
-      const int v = wcnt[w][tid];
-      wcnt[w][tid] = total;
-      total += v;
-    }
-  }
-  // exclusive scan of the kept totals min(total, cap) over experts (4 waves)
-  const int v = tid < E ? min(total, cap) : 0;
-  const int incl = wave_incl_scan(v);
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  if (tid < E) {
-    int wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += wsum[w];
-    off_s[tid] = wbase + incl - v;
-    offsets[tid] = wbase + incl - v;
-  }
-  if (tid == 0) {
-    int all = 0;
-    for (int w = 0; w < kSmallWaves; ++w) all += wsum[w];
-    offsets[E] = all;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kSmallChunks; ++j) {
-    if (pr[j] == -2) inv_pos[(c0 + j) * kWave + lane] = -1;   // dropped
-    if (pr[j] >= 0) {
-      const int e = pr[j] & 255;
-      const int i = (c0 + j) * kWave + lane;
-      const int r_e = wcnt[wave][e] + (pr[j] >> 8);
-      if (r_e < cap) {
-        const int pos = off_s[e] + r_e;
-        sorted_token[pos] = i / k;
-        inv_pos[i] = pos;
-      } else {
-        inv_pos[i] = -1;
-      }
-    }
-  }
-}
-
 }  // namespace
 
 size_t permute_ws_bytes(int R, int E) {
@@ -307,10 +315,9 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
   const int nchunks = (R + CH - 1) / CH;
   int32_t* counts = (int32_t*)ws;
   int32_t* base = (int32_t*)((char*)ws + align_up((size_t)nchunks * E * sizeof(int32_t)));
-  if (R > 0 && E <= kSmallE && R <= kSmallR) {
-    // (one workgroup stops paying beyond 16 chunks per wave: each chunk's
-    // rank waits on the previous chunk's count update in LDS)
-    hipLaunchKernelGGL(perm_small<kSmallR / (kSmallWaves * kWave)>, dim3(1), dim3(1024), 0, s,
+  if (R > 0 && R <= kOnePassR) {
+    const size_t lds = (size_t)(3 + kOnePassWaves) * E * sizeof(int);
+    hipLaunchKernelGGL(perm_onepass, dim3((unsigned)((R + 1023) / 1024)), dim3(1024), lds, s,
                        ids, R, E, k, cap, offsets, sorted_token, inv_pos);
   } else {
     if (nchunks > 0)

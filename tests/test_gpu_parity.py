@@ -41,9 +41,14 @@ SMALL = {
                            bias0=3.0),
     # T >= 1024 and E <= 256: the selection runs one token per 16-lane row
     "rows_bf16": C("rows_bf16", T=1100, H=128, E=40, k=6, F=64, dtype="bf16"),
-    # more pairs than the one-workgroup dispatch takes (T*k > 16384): the
-    # count / scan / place kernels
+    # the one-launch dispatch over 36 workgroups (the last one partly full)
     "long_dispatch_bf16": C("long_dispatch_bf16", T=4500, H=64, E=64, k=8, F=64, dtype="bf16"),
+    # more pairs than the one-launch dispatch takes (T*k > 65536): the count /
+    # scan / place kernels
+    "huge_dispatch_bf16": C("huge_dispatch_bf16", T=9000, H=64, E=96, k=8, F=64, dtype="bf16"),
+    # the one-launch dispatch at E = 1000 (LDS tables of 19 E ints)
+    "wide_E_dispatch_bf16": C("wide_E_dispatch_bf16", T=3000, H=64, E=1000, k=4, F=32,
+                              dtype="bf16"),
     # few tiles with a long K: the expert GEMM splits tiles along K (partials
     # summed by the last piece), checked here on every element
     "ksplit_bf16": C("ksplit_bf16", T=300, H=4096, E=2, k=1, F=512, dtype="bf16"),

@@ -232,14 +232,14 @@ def test_expert_ffn_ignores_rows_past_offsets(name):
 BAD_IDS = [-1, -(2 ** 31), 2 ** 31 - 1]
 
 
-@pytest.mark.parametrize("T,k,E", [(50, 3, 8), (6000, 3, 8), (40, 4, 300)])
+@pytest.mark.parametrize("T,k,E", [(50, 3, 8), (6000, 3, 8), (40, 4, 300), (9000, 8, 20)])
 @pytest.mark.parametrize("cap", [0, 7])
 def test_permute_drops_ids_outside_range(T, k, E, cap):
     """A pair whose id is outside [0, E) is dropped (inv_pos = -1) and counted
     nowhere; the other pairs are placed as if it were absent.  Expected values:
     the oracle's dispatch with every bad id relabelled to an extra expert E,
-    whose block (the last one) is then dropped.  Covers the one-workgroup
-    dispatch (T*k <= 16384, E <= 256) and the count / scan / place kernels."""
+    whose block (the last one) is then dropped.  Covers the one-launch
+    dispatch (T*k <= 65536) and the count / scan / place kernels."""
     g = torch.Generator().manual_seed(T * 7 + E + cap)
     ids = torch.randint(0, E, (T, k), generator=g, dtype=torch.int32)
     bad = torch.rand((T, k), generator=g) < 0.1
