@@ -57,10 +57,10 @@ def parse():
                     help="tokens in the oracle's timed sample (0: per-workload default)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
-    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
-                                                              "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
-                    help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE counter files into the traffic "
-                         "record under profiles/ and exit")
+    ap.add_argument("--summarize-traffic", nargs="+", metavar="CSV",
+                    help="READ_CSV WRITE_CSV COPY_READ_CSV COPY_WRITE_CSV [MFMA_CSV]: turn "
+                         "rocprofv3 request-counter files into the traffic record under "
+                         "profiles/ and exit")
     ap.add_argument("--copy-mib", type=int, default=1024, help="size of the calibration copy")
     ap.add_argument("--pass", dest="pass_", default="forward", choices=["forward", "train"],
                     help="forward (default): moe_forward steps; train: moe_forward_train + "
@@ -108,63 +108,99 @@ def _counter_totals(csv_path: str, counter: str, kernel_substr: str, required: b
     return sum(vals.values()), len(vals)
 
 
-def _counter_per_dispatch(csv_path: str, counter: str, kernel_substr: str):
-    total, n = _counter_totals(csv_path, counter, kernel_substr)
-    return total / n, n
+READ_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                 "TCC_EA0_RDREQ_128B_sum")
+WRITE_COUNTERS = ("TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum")
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
+
+
+def _bytes(rd_csv: str, wr_csv: str, kernel: str, required: bool = True):
+    """(read bytes, written bytes, dispatches) of the L2 <-> memory traffic of
+    the matching kernels, from the request counts by size: reads 32 n32 +
+    64 n64 + 128 n128, writes 64 n64 + 32 (n - n64)."""
+    n, nd = _counter_totals(rd_csv, READ_COUNTERS[0], kernel, required)
+    n32, _ = _counter_totals(rd_csv, READ_COUNTERS[1], kernel, required)
+    n64, _ = _counter_totals(rd_csv, READ_COUNTERS[2], kernel, required)
+    n128, _ = _counter_totals(rd_csv, READ_COUNTERS[3], kernel, required)
+    w, _ = _counter_totals(wr_csv, WRITE_COUNTERS[0], kernel, required)
+    w64, _ = _counter_totals(wr_csv, WRITE_COUNTERS[1], kernel, required)
+    return (32 * n32 + 64 * n64 + 128 * n128, 64 * w64 + 32 * (w - w64), nd,
+            {"rdreq": n, "rdreq_32b": n32, "rdreq_64b": n64, "rdreq_128b": n128,
+             "wrreq": w, "wrreq_64b": w64})
 
 
 def summarize_traffic(a):
-    """FETCH_SIZE / WRITE_SIZE (KiB per launch) of the grouped GEMM, scaled by
-    what the same counters read for a plain copy of known size.  A launch of
-    the GEMM is its main kernel plus the split-tile reduce kernel that follows
-    it, so both kernels' counts are added and divided by the number of main
-    kernel dispatches."""
-    fg, nd = _counter_totals(a.summarize_traffic[0], "FETCH_SIZE", "gemm_bf16_grouped")
-    wg, _ = _counter_totals(a.summarize_traffic[1], "WRITE_SIZE", "gemm_bf16_grouped")
-    fr, nr = _counter_totals(a.summarize_traffic[0], "FETCH_SIZE", "gemm_split_reduce", False)
-    wr, _ = _counter_totals(a.summarize_traffic[1], "WRITE_SIZE", "gemm_split_reduce", False)
-    fetch = (fg + fr) / nd
-    write = (wg + wr) / nd
-    copy_kernel = "copy"
-    cf, _ = _counter_per_dispatch(a.summarize_traffic[2], "FETCH_SIZE", copy_kernel)
-    cw, _ = _counter_per_dispatch(a.summarize_traffic[3], "WRITE_SIZE", copy_kernel)
+    """HBM-side traffic of one launch of the grouped GEMM (the main kernel
+    plus the split-tile reduce that follows it) from rocprofv3 request
+    counters, checked against a plain device copy of known size under the
+    same counters, plus the matrix-pipe busy fraction of the main kernel."""
+    rd, wr, cr, cw = a.summarize_traffic[:4]
+    mf = a.summarize_traffic[4] if len(a.summarize_traffic) > 4 else None
+    rg, wg, nd, raw = _bytes(rd, wr, "gemm_bf16_grouped")
+    rr, wrr, nr, _ = _bytes(rd, wr, "gemm_split_reduce", False)
+    crd, cwr, ncopy, craw = _bytes(cr, cw, "copy")
+    crd, cwr = crd / ncopy, cwr / ncopy
     nbytes = a.copy_mib << 20
-    f_fetch = nbytes / (cf * 1024.0)
-    f_write = nbytes / (cw * 1024.0)
+    per = {"read": (rg + rr) / nd, "write": (wg + wrr) / nd}
     rec = {"kernel": "gemm_bf16_grouped", "workload": a.config, "source_hash": gemm_source_hash(),
            "dispatches": nd, "reduce_dispatches": nr,
-           "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
-           "reduce_fetch_kib_per_launch": fr / nd, "reduce_write_kib_per_launch": wr / nd,
-           "copy_bytes": nbytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
-           "fetch_factor": f_fetch, "write_factor": f_write,
-           "traffic_bytes_per_launch": fetch * 1024.0 * f_fetch + write * 1024.0 * f_write}
+           "read_bytes_per_launch": per["read"], "write_bytes_per_launch": per["write"],
+           "reduce_read_bytes_per_launch": rr / nd, "reduce_write_bytes_per_launch": wrr / nd,
+           "copy_bytes": nbytes, "copy_read_counted": crd / 1, "copy_write_counted": cwr,
+           "copy_read_ratio": crd / nbytes, "copy_write_ratio": cwr / nbytes,
+           "traffic_bytes_per_launch": per["read"] + per["write"], "counts": raw,
+           "copy_counts": craw}
+    if mf:
+        busy, n1 = _counter_totals(mf, MFMA_COUNTERS[0], "gemm_bf16_grouped")
+        mops, _ = _counter_totals(mf, MFMA_COUNTERS[1], "gemm_bf16_grouped")
+        gui, _ = _counter_totals(mf, MFMA_COUNTERS[2], "gemm_bf16_grouped")
+        # GRBM_GUI_ACTIVE is summed over the 8 XCDs (one count each);
+        # SQ_VALU_MFMA_BUSY_CYCLES over all 1024 SIMDs
+        xcds, simds = 8, 4 * 256
+        rec["mfma_busy_frac"] = busy / (gui / xcds * simds)
+        rec["mfma_flops_per_launch"] = mops * 512 / n1
+        rec["gui_active_cycles_per_launch"] = gui / xcds / n1
     path = traffic_record_path(a.config)
+    cmd = ("rocprofv3 --pmc {c} --output-format csv -d <dir> -o {o} -- python3 bench.py "
+           "--config {w} --steps 3 --warmup 1 --no-cpu-baseline")
     with open(path, "w") as fh:
         fh.write(f"# HBM traffic of gemm_bf16_grouped on {a.config}\n\n")
-        fh.write("Counters from two rocprofv3 passes over the bench (FETCH_SIZE, then "
-                 "WRITE_SIZE, KiB per launch: gemm_bf16_grouped plus the gemm_split_reduce "
-                 "kernel that follows each launch, averaged over the launches), each "
-                 "scaled by the ratio of true bytes to counted bytes for a plain "
-                 f"{a.copy_mib} MiB device copy (torch copy kernel) under the same counter.\n\n")
+        fh.write("L2-to-memory traffic of one launch of the grouped GEMM (the main kernel plus "
+                 "the gemm_split_reduce kernel that follows it), from rocprofv3 request counters "
+                 "by size: read bytes = 32 RDREQ_32B + 64 RDREQ_64B + 128 RDREQ_128B, written "
+                 "bytes = 64 WRREQ_64B + 32 (WRREQ - WRREQ_64B), summed over the 16 channels of "
+                 "the 8 XCDs and averaged over the launches.  A plain device copy of "
+                 f"{a.copy_mib} MiB (torch copy kernel) under the same counters checks the "
+                 "formula: its counted bytes over its true bytes are the ratios below (no "
+                 "scale factor is applied).\n\n")
         fh.write("Commands (run from the repository root on the GPU host):\n\n```\n")
-        fh.write(f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o f -- python3 bench.py "
-                 f"--config {a.config} --steps 3 --warmup 1 --no-cpu-baseline\n")
-        fh.write(f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o w -- python3 bench.py "
-                 f"--config {a.config} --steps 3 --warmup 1 --no-cpu-baseline\n")
-        fh.write(f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o cf -- python3 bench.py "
-                 f"--calibrate-copy-mib {a.copy_mib}\n")
-        fh.write(f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o cw -- python3 bench.py "
-                 f"--calibrate-copy-mib {a.copy_mib}\n")
-        fh.write(f"python3 bench.py --config {a.config} --summarize-traffic <f csv> <w csv> "
-                 "<cf csv> <cw csv>\n```\n\n")
-        fh.write(f"| quantity | value |\n|---|---|\n")
+        fh.write(cmd.format(c=" ".join(READ_COUNTERS), o="r", w=a.config) + "\n")
+        fh.write(cmd.format(c=" ".join(WRITE_COUNTERS), o="w", w=a.config) + "\n")
+        if mf:
+            fh.write(cmd.format(c=" ".join(MFMA_COUNTERS), o="m", w=a.config) + "\n")
+        fh.write(f"rocprofv3 --pmc {' '.join(READ_COUNTERS)} --output-format csv -d <dir> -o cr "
+                 f"-- python3 bench.py --calibrate-copy-mib {a.copy_mib}\n")
+        fh.write(f"rocprofv3 --pmc {' '.join(WRITE_COUNTERS)} --output-format csv -d <dir> -o cw "
+                 f"-- python3 bench.py --calibrate-copy-mib {a.copy_mib}\n")
+        fh.write(f"python3 bench.py --config {a.config} --summarize-traffic <r csv> <w csv> "
+                 f"<cr csv> <cw csv>{' <m csv>' if mf else ''}\n```\n\n")
+        fh.write("| quantity | value |\n|---|---|\n")
         fh.write(f"| GEMM launches averaged (reduce dispatches) | {nd} ({nr}) |\n")
-        fh.write(f"| FETCH_SIZE per launch (of it, reduce) | {fetch:.0f} KiB ({fr / nd:.0f} KiB) |\n")
-        fh.write(f"| WRITE_SIZE per launch (of it, reduce) | {write:.0f} KiB ({wr / nd:.0f} KiB) |\n")
-        fh.write(f"| copy of {nbytes} B: FETCH / WRITE | {cf:.0f} / {cw:.0f} KiB |\n")
-        fh.write(f"| scale factors fetch / write | {f_fetch:.4f} / {f_write:.4f} |\n")
-        fh.write(f"| HBM bytes per launch | {rec['traffic_bytes_per_launch'] / 1e9:.4f} GB |\n\n")
-        fh.write("The record below is read by bench.py; it is ignored once the GEMM sources "
+        fh.write(f"| read per launch (of it, reduce) | {per['read'] / 1e9:.4f} GB "
+                 f"({rr / nd / 1e9:.4f} GB) |\n")
+        fh.write(f"| written per launch (of it, reduce) | {per['write'] / 1e9:.4f} GB "
+                 f"({wrr / nd / 1e9:.4f} GB) |\n")
+        fh.write(f"| copy of {nbytes} B: counted read / written | {crd / nbytes:.4f} / "
+                 f"{cwr / nbytes:.4f} of the true bytes |\n")
+        fh.write(f"| HBM-side bytes per launch | {rec['traffic_bytes_per_launch'] / 1e9:.4f} GB |\n")
+        if mf:
+            fh.write(f"| matrix pipe busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 "
+                     f"XCDs x 1024 SIMDs)) | {rec['mfma_busy_frac']:.3f} |\n")
+            fh.write(f"| GPU active cycles per launch (one XCD) | "
+                     f"{rec['gui_active_cycles_per_launch']:.0f} |\n")
+            fh.write(f"| bf16 MFMA flops per launch (MOPS x 512) | "
+                     f"{rec['mfma_flops_per_launch'] / 1e9:.1f} G |\n")
+        fh.write("\nThe record below is read by bench.py; it is ignored once the GEMM sources "
                  "change (source_hash).\n\n```json\n" + json.dumps(rec, indent=1) + "\n```\n")
     print(f"wrote {path}")
 
