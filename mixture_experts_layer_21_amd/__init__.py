@@ -7,7 +7,9 @@ torch (device memory only), passes raw pointers and the current HIP stream,
 and raises on a non-OK status.  All computation happens in the HIP kernels.
 
 Importing this package fails if libmoe.so has not been built
-(python mixture_experts_layer_21_amd/build.py).
+(python mixture_experts_layer_21_amd/build.py).  MOE_LIBRARY, if set, names
+another build of the same library to load instead (the tests use it for the
+host-AddressSanitizer build).
 """
 from __future__ import annotations
 
@@ -17,7 +19,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_PKG, "libmoe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "

@@ -43,9 +43,16 @@ def flags() -> list[str]:
     ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer flavour (the device code is built as usual):
+# every -fsanitize flag sits right after -Xarch_host, so it reaches only the
+# host compilation of each source.
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, asan: bool = False) -> str:
+    obj = os.path.join(BUILD, src.replace(".hip", ".asan.o" if asan else ".o"))
+    cmd = [hipcc(), *flags(), *(ASAN_FLAGS if asan else []), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
@@ -56,20 +63,29 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
+ASAN_LIB = os.path.join(BUILD, "libmoe_asan.so")
+
+
+def build(verbose: bool = True, asan: bool = False) -> str:
+    """Build libmoe.so next to this file, or (asan) the host-sanitizer flavour
+    _build/libmoe_asan.so, which a process loads with the sanitizer runtime
+    preloaded (see tests/test_abi_asan.py)."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda src: _compile(src, asan), SOURCES))
+    out = ASAN_LIB if asan else LIB
+    tmp = out + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+           *(["-Xarch_host", "-fsanitize=address", "-shared-libasan"] if asan else []), *objs,
+           "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    build(asan="--asan" in sys.argv[1:])
