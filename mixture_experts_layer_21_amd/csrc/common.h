@@ -30,6 +30,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// fp32 -> (hi, mid, lo) bf16 bits with hi + mid + lo == w up to the rounding
+// of lo (hi, mid: truncations; each remainder is exact in fp32).  A product
+// of a bf16 value with each part is exact in fp32, so three bf16 matrix
+// products summed in fp32 give an fp32-accurate product with w.
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t u = __float_as_uint(w);
+  hi = u >> 16;
+  const float r1 = w - __uint_as_float(u & 0xFFFF0000u);
+  const uint32_t u1 = __float_as_uint(r1);
+  mid = u1 >> 16;
+  const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
+  const uint32_t u2 = __float_as_uint(r2);
+  lo = (u2 + 0x7FFFu + ((u2 >> 16) & 1u)) >> 16;
+}
+
 // GELU, tanh form: 0.5 z (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3).
 // Since 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), this is
 //   z / (1 + 2^(z * (c1 + c2 z^2))),  c1 = -2 sqrt(2/pi) log2(e), c2 = 0.044715 c1,

@@ -84,22 +84,30 @@ hipError_t launch_gather_rows(const void* x, const int32_t* sorted_token, const 
 // zero `bytes` (a multiple of 16) at p (16-byte aligned) with a kernel
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 size_t router_wgrad_ws_bytes(int T, int H, int E);
+// bytes of dl's three bf16 planes ([T][3][E rounded up to 16])
+size_t router_planes_bytes(int T, int E);
 // dw[T*k] = dy[t] . yp[p] and dyp[p] = w * dy[t] for every kept pair
 hipError_t launch_combine_bwd(const void* dy, const void* yp, const int32_t* inv_pos,
                               const float* w, int T, int H, int k, bool bf16, float* dw,
                               void* dyp, hipStream_t s);
-// dl[T,E] (fp32, dense) from the gate weights' gradient dw
+// dl[T,E] (fp32, dense) from the gate weights' gradient dw; with dlp, also
+// dl's three bf16 planes (router_planes_bytes) for launch_router_wgrad
+// and, with dlk (top-k then softmax gating only), each slot's own logit
+// gradient dlk[t*k + j] = dl[t, ids_j]
 hipError_t launch_router_bwd(const float* logits, const int32_t* ids, const float* w,
                              const float* dw, int T, int E, int k, bool softmax_all, float* dl,
-                             hipStream_t s);
-// dW_r = x^T dl (W_r's type), db_r = sum_t dl (skipped when db_r is null)
-hipError_t launch_router_wgrad(const void* x, const float* dl, int T, int H, int E, bool x_bf16,
-                               bool w_bf16, void* dw_r, float* db_r, void* ws, hipStream_t s);
+                             uint16_t* dlp, float* dlk, hipStream_t s);
+// dW_r = x^T dl (W_r's type), db_r = sum_t dl (skipped when db_r is null);
+// bf16 x with dlp: on the matrix cores from the planes, else from dl
+hipError_t launch_router_wgrad(const void* x, const float* dl, const uint16_t* dlp, int T,
+                               int H, int E, bool x_bf16, bool w_bf16, void* dw_r, float* db_r,
+                               void* ws, hipStream_t s);
 // dx[t] = sum_j dxp[inv_pos[t,j]] + dl[t] . W_r^T; w_rt: scratch for W_r^T
-// (E*H elements of W_r's type); sparse: dl is zero outside ids[t, 0..k)
+// (E*H elements of W_r's type); with dlk (dl zero outside ids[t, 0..k), the
+// top-k-then-softmax gating) the router term takes the k slots' rows only
 hipError_t launch_dx_finish(const void* dxp, const int32_t* inv_pos, const int32_t* ids,
-                            const float* dl, const void* w_r, int T, int H, int E, int k,
-                            bool bf16, bool w_bf16, bool sparse, void* w_rt, void* dx,
+                            const float* dl, const float* dlk, const void* w_r, int T, int H,
+                            int E, int k, bool bf16, bool w_bf16, void* w_rt, void* dx,
                             hipStream_t s);
 
 }  // namespace moe

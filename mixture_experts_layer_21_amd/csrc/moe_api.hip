@@ -173,7 +173,7 @@ SavedLayout saved_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, 
 // dz, the re-gathered token rows xp, and one region shared in time by the
 // router weight gradient's partials and the GEMMs' split-tile partials.
 struct BwdLayout {
-  size_t dw, dl, dyp, dz, xp, wrt, stage, total;
+  size_t dw, dl, dlp, dlk, dyp, dz, xp, wrt, stage, total;
 };
 
 BwdLayout bwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_dtype dt) {
@@ -183,6 +183,8 @@ BwdLayout bwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_
   size_t o = 0;
   L.dw = o;    o += align_up((size_t)R * 4);
   L.dl = o;    o += align_up((size_t)T * E * 4);
+  L.dlp = o;   o += align_up(moe::router_planes_bytes((int)T, (int)E));
+  L.dlk = o;   o += align_up((size_t)R * 4);
   L.dyp = o;   o += align_up((size_t)R * H * es);
   L.dz = o;    o += align_up((size_t)R * F * es);
   L.xp = o;    o += align_up((size_t)R * H * es);
@@ -598,6 +600,9 @@ moe_status moe_backward(const void* dy, const void* x, const void* w_r, const vo
   char* base = (char*)ws;
   float* dw = dtopk_w ? dtopk_w : (float*)(base + L.dw);
   float* dl = (float*)(base + L.dl);
+  uint16_t* dlp = bf16 ? (uint16_t*)(base + L.dlp) : nullptr;   // (for bf16 tokens only)
+  const bool sparse = gating == MOE_GATE_TOPK_SOFTMAX;   // dl zero outside the k selected experts
+  float* dlk = sparse ? (float*)(base + L.dlk) : nullptr;
   void* dyp = base + L.dyp;
   void* dxp = base + L.dyp;      // dyp's last reader (dW2) runs before dxp is written
   void* dz = base + L.dz;
@@ -608,9 +613,9 @@ moe_status moe_backward(const void* dy, const void* x, const void* w_r, const vo
   err = moe::launch_combine_bwd(dy, yp, inv, topk_w, (int)T, (int)H, top_k, bf16, dw, dyp, s);
   if (err == hipSuccess)
     err = moe::launch_router_bwd(logits, topk_ids, topk_w, dw, (int)T, (int)E, top_k,
-                                 gating == MOE_GATE_SOFTMAX_TOPK, dl, s);
+                                 gating == MOE_GATE_SOFTMAX_TOPK, dl, dlp, dlk, s);
   if (err == hipSuccess)
-    err = moe::launch_router_wgrad(x, dl, (int)T, (int)H, (int)E, bf16, w_bf16, dw_r, db_r,
+    err = moe::launch_router_wgrad(x, dl, dlp, (int)T, (int)H, (int)E, bf16, w_bf16, dw_r, db_r,
                                    stage, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
   if (T == 0) {
@@ -627,12 +632,8 @@ moe_status moe_backward(const void* dy, const void* x, const void* w_r, const vo
   const moe_status fs = run_ffn_bwd(dyp, xp, off, z, h, w1, w2, R, H, E, F, dtype, dxp, dw1,
                                     dw2, dz, stage, s);
   if (fs != MOE_OK) return fs;
-  // top-k then softmax: each token's logit gradient is zero outside its k
-  // selected experts
-  return launch_status(moe::launch_dx_finish(dxp, inv, topk_ids, dl, w_r, (int)T, (int)H, (int)E,
-                                             top_k, bf16, w_bf16,
-                                             gating == MOE_GATE_TOPK_SOFTMAX, base + L.wrt, dx,
-                                             s));
+  return launch_status(moe::launch_dx_finish(dxp, inv, topk_ids, dl, dlk, w_r, (int)T, (int)H,
+                                             (int)E, top_k, bf16, w_bf16, base + L.wrt, dx, s));
 }
 
 }  // extern "C"

@@ -46,20 +46,6 @@
 namespace moe {
 namespace {
 
-
-// fp32 -> (hi, mid, lo) bf16 bits with hi + mid + lo == w up to the rounding
-// of lo (hi, mid: truncations; each remainder is exact in fp32).
-__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  const uint32_t u = __float_as_uint(w);
-  hi = u >> 16;
-  const float r1 = w - __uint_as_float(u & 0xFFFF0000u);
-  const uint32_t u1 = __float_as_uint(r1);
-  mid = u1 >> 16;
-  const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
-  const uint32_t u2 = __float_as_uint(r2);
-  lo = (u2 + 0x7FFFu + ((u2 >> 16) & 1u)) >> 16;
-}
-
 template <int TPW, bool WF32>
 __global__ __launch_bounds__(256) void route_logits_bf16(
     const uint16_t* __restrict__ x, const void* __restrict__ w_r_any,

@@ -43,6 +43,9 @@ CASES = {
     # K step counts 21 (H = 672) and 11 (F = 352): remainders of 9 and 11 steps
     # after the transposed-weight GEMM's 12-step period
     "period_tail_bf16": C("period_tail_bf16", T=96, H=672, E=4, k=2, F=352, dtype="bf16"),
+    # 33..64 experts (the router weight gradient's 64-expert tile, 40 of them
+    # real), h blocks of 64 with a ragged last one, ragged token splits
+    "midE_bf16": C("midE_bf16", T=300, H=200, E=40, k=4, F=96, dtype="bf16"),
 }
 _cache = {}
 
