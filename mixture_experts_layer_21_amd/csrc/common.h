@@ -161,9 +161,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // 64 lanes x 16 bytes from global memory straight into a 1 KB LDS block:
 // lane t's bytes land at block + 16 t (no VGPRs involved).  A lane whose
 // offset is at or past the descriptor's size writes zeros.
+// AUX: the load's cache policy (0: default; kNonTemporal: the lines are
+// placed to be evicted first, for data that no other workgroup will read)
+constexpr int kNonTemporal = 2;
+template <int AUX = 0>
 __device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, char* lds_block,
                                             uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_block, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_block, 16, voff, 0, 0, AUX);
 }
 
 // Transposed LDS read (gfx950 ds_read_b64_tr_b16): in each group of 16 lanes,

@@ -294,12 +294,13 @@ struct ColLoader {
   }
   // k0 may pass the limit on the last steps: the size clamps to 0 and every
   // load returns zero without touching memory.
+  template <int AUX = 0>
   __device__ __forceinline__ void load(int k0, char* st) const {
     const uint32_t skip = (uint32_t)k0 * ld * 2;
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc(base + (size_t)k0 * ld, bytes > skip ? bytes - skip : 0u);
 #pragma unroll
-    for (int u = 0; u < INSTS; ++u) load_to_lds(r, st + dst[u], voff[u]);
+    for (int u = 0; u < INSTS; ++u) load_to_lds<AUX>(r, st + dst[u], voff[u]);
   }
 };
 
@@ -324,7 +325,9 @@ struct Carry {
 // K range read as zero, so no clamping appears in the loop.  In NN, past-K
 // columns of A read the next row of the tile (or x's next row when the rows
 // are gathered) but meet zero W rows; NT masks both operands' K tails.
-template <int KIND, int BM, int BN, int WM, int WN, int NFM, bool PERSIST = false>
+// WAUX: cache policy of the NN weight loads (kNonTemporal when no other
+// workgroup reads the same weight slab)
+template <int KIND, int BM, int BN, int WM, int WN, int NFM, bool PERSIST = false, int WAUX = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, int kt_begin,
                                           int kt_end, const Split& sp, const Lds& lds,
                                           const Carry* cy = nullptr) {
@@ -535,10 +538,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if constexpr (KIND == kNN && LAST) {
       // steps kt+4 (and kt+3, kt+4 for the token ring) are the next item's
-      lw_n.load(k0n + (kt + W_STAGES - nsr) * BK, lds.w[ST]);
+      lw_n.template load<WAUX>(k0n + (kt + W_STAGES - nsr) * BK, lds.w[ST]);
       if constexpr (PAR == 1) la_n.load(k0n + (kt + 3 - nsr) * BK, lds.a[ST / 2]);
     } else if constexpr (KIND == kNN) {
-      lw.load(k0 + (kt + W_STAGES) * BK, lds.w[ST]);
+      lw.template load<WAUX>(k0 + (kt + W_STAGES) * BK, lds.w[ST]);
       if constexpr (PAR == 1) la.load(k0 + (kt + 3) * BK, lds.a[ST / 2]);
     } else if constexpr (KIND == kNT) {
       if constexpr (PAR == 1) {
@@ -565,11 +568,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   // rows (or zero chunks) and add nothing.
   if constexpr (KIND == kNN) {
     if (!PERSIST || !cy->carry_in) {
-      lw.load(k0, lds.w[0]);
-      lw.load(k0 + BK, lds.w[1]);
+      lw.template load<WAUX>(k0, lds.w[0]);
+      lw.template load<WAUX>(k0 + BK, lds.w[1]);
       la.load(k0, lds.a[0]);
-      lw.load(k0 + 2 * BK, lds.w[2]);
-      lw.load(k0 + 3 * BK, lds.w[3]);
+      lw.template load<WAUX>(k0 + 2 * BK, lds.w[2]);
+      lw.template load<WAUX>(k0 + 3 * BK, lds.w[3]);
       la.load(k0 + 2 * BK, lds.a[1]);
     }
     // step 0's data (W0, A01) is in once W2, W3, A23 alone are outstanding
@@ -693,18 +696,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
 
 // gemm_tile with NFM = nfm (0 <= nfm <= NF), chosen at run time from a
 // wave-uniform count.
-template <int KIND, int BM, int BN, int WM, int WN, int NF, bool PERSIST = false>
+template <int KIND, int BM, int BN, int WM, int WN, int NF, bool PERSIST = false, int WAUX = 0>
 __device__ __forceinline__ void run_tile(int nfm, const GemmArgs& g, const Tile& tile,
                                          int kt_begin, int kt_end, const Split& sp,
                                          const Lds& lds, const Carry* cy = nullptr) {
   if constexpr (NF == 0) {
-    gemm_tile<KIND, BM, BN, WM, WN, 0, PERSIST>(g, tile, kt_begin, kt_end, sp, lds, cy);
+    gemm_tile<KIND, BM, BN, WM, WN, 0, PERSIST, WAUX>(g, tile, kt_begin, kt_end, sp, lds, cy);
   } else {
     if (nfm == NF)
-      gemm_tile<KIND, BM, BN, WM, WN, NF, PERSIST>(g, tile, kt_begin, kt_end, sp, lds, cy);
+      gemm_tile<KIND, BM, BN, WM, WN, NF, PERSIST, WAUX>(g, tile, kt_begin, kt_end, sp, lds, cy);
     else
-      run_tile<KIND, BM, BN, WM, WN, NF - 1, PERSIST>(nfm, g, tile, kt_begin, kt_end, sp, lds,
-                                                      cy);
+      run_tile<KIND, BM, BN, WM, WN, NF - 1, PERSIST, WAUX>(nfm, g, tile, kt_begin, kt_end, sp,
+                                                            lds, cy);
   }
 }
 
@@ -780,8 +783,9 @@ __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __res
 // whole tiles b, b + G, ... (G = grid; the same XCD-aware order as the
 // one-tile-per-workgroup kernel) and then its split piece, if any, handing
 // the pipeline from one item to the next (Carry); the epilogue stages
-// through its own 32 KB (128 KB of rings + 32 KB = 160 KB).
-template <int BM, int BN, int WM, int WN>
+// through its own 32 KB (128 KB of rings + 32 KB = 160 KB).  WAUX: the
+// weight loads' cache policy.
+template <int BM, int BN, int WM, int WN, int WAUX = 0>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_grouped(
     GemmArgs g, const int* __restrict__ off, int E, int R, float* __restrict__ part,
     int slots) {
@@ -841,7 +845,7 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     if (cy.has_next) item(i + 1, cy.next, cy.next_kb, cy.next_ke, nsp);
     int nfm = max(0, min(S::FM, (cur.mrows - wm * S::TM + 31) / 32));
     nfm = __builtin_amdgcn_readfirstlane(nfm);
-    run_tile<kNN, BM, BN, WM, WN, S::FM, true>(nfm, g, cur, ckb, cke, csp, lds, &cy);
+    run_tile<kNN, BM, BN, WM, WN, S::FM, true, WAUX>(nfm, g, cur, ckb, cke, csp, lds, &cy);
     cy.carry_in = true;
     cur = cy.next;
     ckb = cy.next_kb;
@@ -1178,7 +1182,14 @@ hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* spl
   if constexpr (KIND == kNT)
     hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN>), dim3((unsigned)blocks),
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
-  else   // persistent: one workgroup per CU
+  else if ((long)R * 2 <= (long)E * BM)
+    // persistent, one workgroup per CU.  At most half a row tile per expert
+    // on average: nearly every weight slab is read by one tile only, so its
+    // loads are non-temporal (their L2 lines go first) rather than displacing
+    // the token rows that other tiles read again
+    hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN, kNonTemporal>), dim3((unsigned)slots),
+                       dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
+  else
     hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN>), dim3((unsigned)slots),
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
   hipError_t err = hipGetLastError();
