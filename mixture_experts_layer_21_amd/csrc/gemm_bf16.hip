@@ -253,6 +253,7 @@ struct RowLoader {
     }
   }
   // K steps k0 / BK and k0 / BK + 1
+  template <int AUX = 0>
   __device__ __forceinline__ void load(int k0, char* st) const {
     const uint32_t skip = (uint32_t)k0 * 2;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0, bytes > skip ? bytes - skip : 0u);
@@ -261,7 +262,7 @@ struct RowLoader {
     for (int u = 0; u < INSTS; ++u) {
       uint32_t vo = voff[u];
       if constexpr (MASK) vo = (k0 + chunk(q0 + u, lane) * 8 < k_limit) ? vo : kPastEnd;
-      load_to_lds(r, st + (q0 + u) * 1024, vo);
+      load_to_lds<AUX>(r, st + (q0 + u) * 1024, vo);
     }
   }
 };
@@ -325,8 +326,8 @@ struct Carry {
 // K range read as zero, so no clamping appears in the loop.  In NN, past-K
 // columns of A read the next row of the tile (or x's next row when the rows
 // are gathered) but meet zero W rows; NT masks both operands' K tails.
-// WAUX: cache policy of the NN weight loads (kNonTemporal when no other
-// workgroup reads the same weight slab)
+// WAUX: cache policy of the weight loads, NN and NT (kNonTemporal when no
+// other workgroup reads the same weight slab)
 template <int KIND, int BM, int BN, int WM, int WN, int NFM, bool PERSIST = false, int WAUX = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, int kt_begin,
                                           int kt_end, const Split& sp, const Lds& lds,
@@ -546,7 +547,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     } else if constexpr (KIND == kNT) {
       if constexpr (PAR == 1) {
         la.load(k0 + (kt + 3) * BK, lds.a[(ST / 2) % 2]);
-        lb.load(k0 + (kt + 5) * BK, lds.w[(ST / 2) % 3]);
+        lb.template load<WAUX>(k0 + (kt + 5) * BK, lds.w[(ST / 2) % 3]);
       }
     } else {
       lp.load(k0 + (kt + 4) * BK, lds.a[ST]);
@@ -578,11 +579,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     // step 0's data (W0, A01) is in once W2, W3, A23 alone are outstanding
     __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * BI + AI));
   } else if constexpr (KIND == kNT) {
-    lb.load(k0, lds.w[0]);
+    lb.template load<WAUX>(k0, lds.w[0]);
     la.load(k0, lds.a[0]);
-    lb.load(k0 + 2 * BK, lds.w[1]);
+    lb.template load<WAUX>(k0 + 2 * BK, lds.w[1]);
     la.load(k0 + 2 * BK, lds.a[1]);
-    lb.load(k0 + 4 * BK, lds.w[2]);
+    lb.template load<WAUX>(k0 + 4 * BK, lds.w[2]);
     // pair 0 (B0, A0) is in once B1, A1, B2 alone are outstanding
     __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * BI + AI));
   } else {
@@ -747,7 +748,7 @@ __device__ __forceinline__ char* staging(char* lo, char* hi, int nw) {
 
 // Grouped GEMM over dispatched rows, one work item per workgroup (the NT
 // kernel): split plan, tile lookup and the tile.
-template <int KIND, int BM, int BN, int WM, int WN>
+template <int KIND, int BM, int BN, int WM, int WN, int WAUX = 0>
 __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __restrict__ off,
                                              int E, int R, float* __restrict__ part, int slots,
                                              const Lds& lds) {
@@ -776,7 +777,7 @@ __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __res
   const int wm = (threadIdx.x / kWave) % WM;
   int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
   nfm = __builtin_amdgcn_readfirstlane(nfm);
-  run_tile<KIND, BM, BN, WM, WN, S::FM>(nfm, g, tile, kt_begin, kt_end, sp, lds);
+  run_tile<KIND, BM, BN, WM, WN, S::FM, false, WAUX>(nfm, g, tile, kt_begin, kt_end, sp, lds);
 }
 
 // The forward's expert products, persistent: one workgroup per CU takes its
@@ -857,7 +858,8 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
 
 // The backward's products with a transposed expert weight (NT): two token
 // stages and three weight stages of 32 KB (the 160 KB a workgroup may hold).
-template <int BM, int BN, int WM, int WN>
+// WAUX: the weight loads' cache policy.
+template <int BM, int BN, int WM, int WN, int WAUX = 0>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_nt(
     GemmArgs g, const int* __restrict__ off, int E, int R, float* __restrict__ part,
     int slots) {
@@ -869,7 +871,7 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
   __shared__ __attribute__((aligned(1024))) char b2[S::LDS_A];
   static_assert(5 * S::LDS_A <= 163840 && S::NW * 8192 <= 2 * S::LDS_A, "LDS budget");
   const Lds lds{{a0, a1, nullptr, nullptr}, {b0, b1, b2, nullptr}, staging(a0, a1, S::NW)};
-  grouped_body<kNT, BM, BN, WM, WN>(g, off, E, R, part, slots, lds);
+  grouped_body<kNT, BM, BN, WM, WN, WAUX>(g, off, E, R, part, slots, lds);
 }
 
 // Expert weight gradients: C_e[M][N] = P_e^T Q_e for every expert e, where
@@ -1179,14 +1181,20 @@ hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* spl
   long blocks = mt_max * NTN + slots;
   if (blocks <= slots) return hipSuccess;
   float* part = (float*)split_ws;
-  if constexpr (KIND == kNT)
-    hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN>), dim3((unsigned)blocks),
-                       dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
-  else if ((long)R * 2 <= (long)E * BM)
-    // persistent, one workgroup per CU.  At most half a row tile per expert
-    // on average: nearly every weight slab is read by one tile only, so its
-    // loads are non-temporal (their L2 lines go first) rather than displacing
-    // the token rows that other tiles read again
+  // At most half a row tile per expert on average: nearly every weight slab
+  // is read by one tile only, so its loads are non-temporal (their L2 lines
+  // go first) rather than displacing the token rows that other tiles read
+  // again
+  const bool stream_w = (long)R * 2 <= (long)E * BM;
+  if constexpr (KIND == kNT) {
+    if (stream_w)
+      hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN, kNonTemporal>), dim3((unsigned)blocks),
+                         dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
+    else
+      hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN>), dim3((unsigned)blocks),
+                         dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
+  } else if (stream_w)
+    // (persistent: one workgroup per CU)
     hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN, kNonTemporal>), dim3((unsigned)slots),
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
   else
