@@ -141,8 +141,10 @@ struct Lds {
 //   EP_DGELU  C = acc * GELU'(z), z read from aux at the same row and column.
 // EPS: the epilogues this instantiation supports (bit 1 << EP_x), so that a
 // kernel carries only the code of its own.  PB: 32-row blocks per staging
-// pass (the wave's staging area is PB * 4 KB).
-template <int BM, int BN, int WM, int WN, int EPS, int NFM, int FMA, int PB = 2>
+// pass (the wave's staging area is PB * 4 KB).  NTS: non-temporal stores, for
+// output that this launch's readers will not read back soon.
+template <int BM, int BN, int WM, int WN, int EPS, int NFM, int FMA, int PB = 2,
+          bool NTS = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN, WM, WN>::FN][FMA],
                                            uint16_t* __restrict__ C, const Tile& tile, int N,
                                            int ep, const uint16_t* __restrict__ aux, char* stg,
@@ -214,7 +216,13 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
         const int m = wrow0 + (jbase + p) * 32 + r;
         const int n = n0 + wn * S::TN + (slot ^ (r & 7)) * 8;
         const u32x4 v = *(const u32x4*)(stg + r * 128 + slot * 16);
-        if (m < tile.mrows && n < N) *(u32x4*)(C + (size_t)(tile.row0 + m) * N + n) = v;
+        if (m < tile.mrows && n < N) {
+          u32x4* dst = (u32x4*)(C + (size_t)(tile.row0 + m) * N + n);
+          if constexpr (NTS)
+            __builtin_nontemporal_store(v, dst);
+          else
+            *dst = v;
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);            // reads done before the next pass writes
       __builtin_amdgcn_wave_barrier();
@@ -1079,8 +1087,9 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
       step(kt + 2, std::integral_constant<int, 2>{});
       step(kt + 3, std::integral_constant<int, 3>{});
     }
-    store_tile<BM, BN, WM, WN, 1 << EP_PLAIN, FM, FM, 1>(acc, cur.c, cur.tile, N, EP_PLAIN,
-                                                         nullptr, lds.stg);
+    // (the weight gradients: written once, read by no kernel of this pass)
+    store_tile<BM, BN, WM, WN, 1 << EP_PLAIN, FM, FM, 1, true>(acc, cur.c, cur.tile, N,
+                                                               EP_PLAIN, nullptr, lds.stg);
     if (!has_next) break;
 #pragma unroll
     for (int i = 0; i < FN; ++i)
