@@ -50,3 +50,21 @@ def test_gate_weights_are_checked():
     w[0, 0] += 2e-3
     with pytest.raises(AssertionError):
         check_routing(np.array(ids), w, L, 2)
+
+
+@pytest.mark.parametrize("ids,kinds", [
+    ([[0, 1], [0, 1], [0, 1]], (0, 0, 0)),
+    ([[0, 1], [0, 2], [0, 1]], (1, 0, 0)),     # boundary near tie
+    ([[0, 1], [0, 1], [1, 0]], (0, 1, 0)),     # near-equal slots swapped
+    ([[0, 2], [0, 1], [0, 1]], (0, 0, 1)),     # set change without a near tie
+    ([[1, 0], [0, 1], [0, 1]], (0, 0, 1)),     # slot swap of clearly different logits
+])
+def test_bench_counts_follow_the_rule(ids, kinds):
+    """bench.py's near-tie counts (its oracle check) sort mismatches the way
+    the rule above does: what the rule excuses is counted as boundary or
+    within, what it fails as other."""
+    import bench
+    import oracle
+    ref = oracle.topk_ids(L, 2)
+    got = bench.classify_ids(np.array(ids), ref, L, oracle.boundary_near_tie(L, 2))
+    assert (got["boundary"], got["within"], got["other"]) == kinds
