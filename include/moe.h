@@ -385,11 +385,12 @@ moe_status moe_forward_train(const void* x, const void* w_r, const float* router
  *   dtopk_w[T,top_k] fp32, optional (NULL: kept in the workspace): the
  *   gradient with respect to the gate weights (0 for dropped pairs).
  * An expert that received no rows gets zero weight gradients.
- * topk_ids must be the training forward's.  Should a slot's id lie outside
- * [0,E) anyway, that slot is left out of the router gradient (its weight and
- * weight gradient take no part in the softmax Jacobian, and no logit, row of
- * W_r or column of dW_r is addressed for it); dtopk_w, dW1 and dW2 follow
- * the dispatch kept in `saved`.
+ * topk_ids must be the training forward's (k distinct experts per token;
+ * the gradient assumes no expert repeats within a token).  Should a slot's
+ * id lie outside [0,E) anyway, that slot is left out of the router gradient
+ * (its weight and weight gradient take no part in the softmax Jacobian, and
+ * no logit, row of W_r or column of dW_r is addressed for it); dtopk_w, dW1
+ * and dW2 follow the dispatch kept in `saved`.
  * ws_bytes must be at least moe_backward_workspace_bytes().  Errors as for
  * the forward; enqueued on `stream`, nothing allocated or synchronised.
  * With T == 0 the weight gradients are zero-filled and dy, x, topk_ids,
