@@ -518,12 +518,12 @@ __device__ __forceinline__ u32x4 transpose8(u32x4 v, uint32_t sel, bool odd2) {
 
 // Sum of the 8 waves' partial logits (wave order) for waves 0-3's selection:
 // one token per row of 16 lanes (select_row).
-template <int EPMAX>
+template <int EPMAX, int TOK = 16>
 __device__ __forceinline__ void fused_select(const float (&part)[kFuseWaves][16][EPMAX],
                                              int wave, int lane, int t0, int T,
                                              const float* bias, int E, int k, int softmax_all,
                                              int32_t* ids, float* w, float* logits) {
-  if (wave >= 4) return;
+  if (wave >= TOK / 4) return;
   const int tt = wave * 4 + lane / 16;
   const int t = t0 + tt;
   if (t >= T) return;   // whole rows leave together
@@ -550,8 +550,11 @@ __device__ __forceinline__ void fused_select(const float (&part)[kFuseWaves][16]
 // a row of 16 experts is 32 bytes), and transpose8 turns each group of 8
 // lanes' 8 x 8 block into the MFMA B fragment (lane: expert lane % 16, rows
 // 8 (lane / 16) + 0..7).  The token operand moves into the MFMA A layout with
-// LDS permutes, as in route_fused.
-template <int NS>
+// LDS permutes, as in route_fused.  TOK: tokens per workgroup, 16 or 8 (then
+// the lanes of tokens 8-15 load nothing, the MFMA rows 8-15 stay zero and
+// the workgroup streams half as much x: used when 16-token tiles would leave
+// CUs without a workgroup).
+template <int NS, int TOK = 16>
 __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_r,
     const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ w,
@@ -559,8 +562,9 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
   __shared__ __attribute__((aligned(16))) float part[kFuseWaves][16][16];
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int t0 = blockIdx.x * 16;
+  const int t0 = blockIdx.x * TOK;
   const int h0 = wave * NS * 32;
+  const bool xl = lane / 4 < TOK;
   const uint16_t* xr = x + (size_t)min(t0 + lane / 4, T - 1) * H + 8 * (lane % 4);
   const int xsrc = 4 * (4 * (lane % 16) + lane / 16);
   const int r_lane = 8 * (lane / 16) + lane % 8;
@@ -569,7 +573,7 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     const int hs = h0 + 32 * st;
-    xb[st] = hs + 8 * (lane % 4) < H ? *(const u32x4*)(xr + hs) : u32x4{0u, 0u, 0u, 0u};
+    xb[st] = xl && hs + 8 * (lane % 4) < H ? *(const u32x4*)(xr + hs) : u32x4{0u, 0u, 0u, 0u};
     const int h = hs + r_lane;
     wb[st] = (e_lane < E && h < H) ? *(const u32x4*)(w_r + (size_t)h * E + e_lane)
                                    : u32x4{0u, 0u, 0u, 0u};
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
 #pragma unroll
   for (int v = 0; v < 4; ++v) part[wave][4 * (lane / 16) + v][lane % 16] = acc[v];
   __syncthreads();
-  fused_select<16>(part, wave, lane, t0, T, bias, E, k, softmax_all, ids, w, logits);
+  fused_select<16, TOK>(part, wave, lane, t0, T, bias, E, k, softmax_all, ids, w, logits);
 }
 
 template <int NS, int D>
@@ -602,7 +606,12 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused(
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t0 = blockIdx.x * 16;
-  const int h0 = wave * NS * 32;
+  // The workgroups of one XCD (b, b + 8, ...) start at different rows of W_r:
+  // wave w takes range (w + b / 8) % 8 and starts at step (b / 8) % NS, so
+  // they do not all request the same L2 lines at once.  The per-range sums
+  // are still added in a fixed order for each workgroup (deterministic).
+  const int rot = blockIdx.x / 8;
+  const int h0 = ((wave + rot) % kFuseWaves) * NS * 32;
   const int g = lane / 16, c = lane % 16;
   // token operand loads: lane reads token t0 + lane / 4 (rows past T repeat
   // the last token), rows 8 (lane % 4) + 0..7 of the step; the A fragment of
@@ -613,7 +622,7 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused(
   const bool wc = 8 * c < E;
   const uint16_t* wr = w_r + 8 * c;
   auto load_step = [&](int st, u32x4 (&xb), u32x4 (&wb)[8]) {
-    const int hs = h0 + 32 * st;
+    const int hs = h0 + 32 * ((st + rot) % NS);
     xb = (st < NS && hs + 8 * (lane % 4) < H) ? *(const u32x4*)(xr + hs) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -723,9 +732,17 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
 #define MOE_ROUTE_FUSED(NS_, D_)                                                            \
     hipLaunchKernelGGL((route_fused<NS_, D_>), g, b, 0, s, xb, wb, bias, ids, w, logits, T, H, \
                        E, k, sa)
-#define MOE_ROUTE_FUSED_SMALL(NS_)                                                           \
-    hipLaunchKernelGGL((route_fused_small<NS_>), g, b, 0, s, xb, wb, bias, ids, w, logits, T, \
-                       H, E, k, sa)
+    const bool tok8 = (T + 15) / 16 < 256;
+    const dim3 g8((unsigned)((T + 7) / 8));
+#define MOE_ROUTE_FUSED_SMALL(NS_)                                                             \
+    do {                                                                                       \
+      if (tok8)                                                                                \
+        hipLaunchKernelGGL((route_fused_small<NS_, 8>), g8, b, 0, s, xb, wb, bias, ids, w,       \
+                           logits, T, H, E, k, sa);                                            \
+      else                                                                                     \
+        hipLaunchKernelGGL((route_fused_small<NS_>), g, b, 0, s, xb, wb, bias, ids, w, logits,   \
+                           T, H, E, k, sa);                                                    \
+    } while (0)
     if (E <= 16) {
       if (ns <= 1) MOE_ROUTE_FUSED_SMALL(1);
       else if (ns <= 2) MOE_ROUTE_FUSED_SMALL(2);
