@@ -56,8 +56,9 @@ SMALL = {
     # each of the 8 waves takes NS = 1, 2, 4, 8, 16 steps of 32 rows of H
     # (H = 40 .. 4096: waves with partly and wholly empty ranges), in both
     # kernels (E <= 16, and E = 24 .. 128 read in whole rows), a last token
-    # tile of 1 to 15 tokens; and one layer with H > 4096 that takes the
-    # two-kernel router at T >= 1024
+    # tile of 1 to 15 tokens; E <= 16 in 8-token tiles (fewer than 256 tiles
+    # of 16) and, at T = 4100, in 16-token tiles; and one layer with H > 4096
+    # that takes the two-kernel router at T >= 1024
     "fused_E8_bf16": C("fused_E8_bf16", T=1031, H=4096, E=8, k=2, F=64, dtype="bf16"),
     "fused_E8_H448_bf16": C("fused_E8_H448_bf16", T=1025, H=448, E=8, k=1, F=64, dtype="bf16"),
     "fused_E16_H2048_bf16": C("fused_E16_H2048_bf16", T=1035, H=2048, E=16, k=4, F=64,
@@ -72,6 +73,8 @@ SMALL = {
     "fused_H448_bf16": C("fused_H448_bf16", T=1049, H=448, E=24, k=3, F=64, dtype="bf16"),
     "fused_H40_bf16": C("fused_H40_bf16", T=1300, H=40, E=16, k=4, F=64, dtype="bf16"),
     "fused_H40_E32_bf16": C("fused_H40_E32_bf16", T=1024, H=40, E=32, k=5, F=64, dtype="bf16"),
+    "fused_E16_T4100_bf16": C("fused_E16_T4100_bf16", T=4100, H=256, E=16, k=2, F=64,
+                              dtype="bf16"),
     "route2_H7168_bf16": C("route2_H7168_bf16", T=1039, H=7168, E=64, k=8, F=64, dtype="bf16",
                            bias0=1.0),
 }
