@@ -210,7 +210,9 @@ __global__ __launch_bounds__(1024) void perm_onepass(const int32_t* __restrict__
   const int start = blockIdx.x * 1024;
   for (int t = tid; t < (2 + kOnePassWaves) * E; t += 1024) sm[t] = 0;
   __syncthreads();
-  // counts over all pairs: 8 ids per thread loaded before they are counted
+  // counts over all pairs (8 ids per thread loaded before they are counted),
+  // one LDS atomic per pair: the pairs before this range into `before`, the
+  // others into `total`, which then takes `before` in
   for (int i0 = tid; i0 < R; i0 += 8 * 1024) {
     int e8[8];
 #pragma unroll
@@ -221,12 +223,11 @@ __global__ __launch_bounds__(1024) void perm_onepass(const int32_t* __restrict__
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int i = i0 + u * 1024;
-      if ((unsigned)e8[u] < (unsigned)E) {
-        atomicAdd(&total[e8[u]], 1);
-        if (i < start) atomicAdd(&before[e8[u]], 1);
-      }
+      if ((unsigned)e8[u] < (unsigned)E) atomicAdd(i < start ? &before[e8[u]] : &total[e8[u]], 1);
     }
   }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) total[e] += before[e];
   // this range: each pair's expert and its rank among the wave's peers
   const int i = start + tid;
   const int my_e = i < R ? ids[i] : -1;
