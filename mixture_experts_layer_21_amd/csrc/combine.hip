@@ -18,8 +18,10 @@ namespace {
 constexpr int kMaxK = 16;
 
 // bf16: a chunk is 8 elements; CPT chunks per thread (the wave's first
-// chunk c, then c + 64, ...)
-template <int CPT>
+// chunk c, then c + 64, ...).  UNI: a token's threads fill whole waves, so
+// the token index is wave-uniform and its k row positions and weights are
+// fetched with scalar loads.
+template <int CPT, bool UNI>
 __global__ __launch_bounds__(256) void combine_bf16(const u32x4* __restrict__ yp,
                                                     const int32_t* __restrict__ inv_pos,
                                                     const float* __restrict__ w,
@@ -28,7 +30,8 @@ __global__ __launch_bounds__(256) void combine_bf16(const u32x4* __restrict__ yp
   const int per_tok = chunks / CPT;                  // threads per token
   const int item = blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= T * per_tok) return;
-  const int t = item / per_tok, r = item % per_tok;
+  const int t = UNI ? __builtin_amdgcn_readfirstlane(item / per_tok) : item / per_tok;
+  const int r = item % per_tok;
   const int c0 = (r / kWave) * (kWave * CPT) + (r % kWave);
   u32x4 v[kMaxK][CPT];
   float wj[kMaxK];
@@ -105,11 +108,14 @@ hipError_t launch_combine(const void* yp, const int32_t* inv_pos, const float* w
   if (bf16) {
     if (chunks % (2 * kWave) == 0 && k <= 8) {
       dim3 g2((unsigned)((items / 2 + 255) / 256));
-      hipLaunchKernelGGL(combine_bf16<2>, g2, b, 0, s, (const u32x4*)yp, inv_pos, w, (u32x4*)y, T,
-                         chunks, k);
+      hipLaunchKernelGGL((combine_bf16<2, true>), g2, b, 0, s, (const u32x4*)yp, inv_pos, w,
+                         (u32x4*)y, T, chunks, k);
+    } else if (chunks % kWave == 0) {
+      hipLaunchKernelGGL((combine_bf16<1, true>), g, b, 0, s, (const u32x4*)yp, inv_pos, w,
+                         (u32x4*)y, T, chunks, k);
     } else {
-      hipLaunchKernelGGL(combine_bf16<1>, g, b, 0, s, (const u32x4*)yp, inv_pos, w, (u32x4*)y, T,
-                         chunks, k);
+      hipLaunchKernelGGL((combine_bf16<1, false>), g, b, 0, s, (const u32x4*)yp, inv_pos, w,
+                         (u32x4*)y, T, chunks, k);
     }
   } else {
     hipLaunchKernelGGL(combine_f32, g, b, 0, s, (const float4*)yp, inv_pos, w, (float4*)y, T,
