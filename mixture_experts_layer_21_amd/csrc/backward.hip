@@ -90,7 +90,8 @@ __global__ __launch_bounds__(256) void combine_bwd(const void* __restrict__ dy,
                                                    void* __restrict__ dyp) {
   constexpr int U = 4;
   const int lane = threadIdx.x % kWave;
-  const int i = blockIdx.x * 4 + threadIdx.x / kWave;
+  // (wave-uniform: the pair's row position and weight come by scalar loads)
+  const int i = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + threadIdx.x / kWave);
   if (i >= T * k) return;
   const int p = inv_pos[i];
   if (p < 0) {
@@ -681,11 +682,11 @@ __global__ __launch_bounds__(256) void dx_finish(const void* __restrict__ dxp,
 
 // dx with top-k-then-softmax gating (dl zero outside each token's k experts):
 // one wave per (token, 512 columns), lane l owning columns 8 l .. 8 l + 7 of
-// the chunk.  Lane j < k fetches slot j's expert id, dispatched row and
-// logit gradient dlk (router_bwd's per-slot copy of dl[t, id]) in one round
-// trip, the wave reads them as scalars, and then every slot's W_r^T row and
-// dxp row are loaded before any is used, so the token's 2k row loads are in
-// flight together.  Router term first (slots in order, fp32 FMAs), then the
+// the chunk.  The wave fetches every slot's expert id, dispatched row and
+// logit gradient dlk (router_bwd's per-slot copy of dl[t, id]) with scalar
+// loads in one round trip, and then every slot's W_r^T row and dxp row are
+// loaded before any is used, so the token's 2k row loads are in flight
+// together.  Router term first (slots in order, fp32 FMAs), then the
 // dispatched rows in slot order, as in dx_finish.
 template <bool BF16, bool WBF16, int KM>
 __global__ __launch_bounds__(256) void dx_finish_sparse(const void* __restrict__ dxp,
@@ -697,24 +698,18 @@ __global__ __launch_bounds__(256) void dx_finish_sparse(const void* __restrict__
                                                         void* __restrict__ dx) {
   const int lane = threadIdx.x % kWave;
   const int HC = (H + 511) / 512;
-  const int item = blockIdx.x * 4 + threadIdx.x / kWave;
+  // (wave-uniform: the slots' ids, rows and dl come by scalar loads)
+  const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + threadIdx.x / kWave);
   if (item >= T * HC) return;
   const int t = item / HC, h = (item % HC) * 512 + 8 * lane;
-  int my_e = -1, my_p = -1;
-  float my_d = 0.f;
-  if (lane < k) {
-    my_e = ids[(size_t)t * k + lane];
-    if ((unsigned)my_e >= (unsigned)E) my_e = -1;       // (an id outside [0, E) adds nothing)
-    my_p = inv_pos[(size_t)t * k + lane];
-    my_d = dlk[(size_t)t * k + lane];
-  }
   int ej[KM], pj[KM];
   float dj[KM];
 #pragma unroll
   for (int u = 0; u < KM; ++u) {
-    ej[u] = u < k ? __builtin_amdgcn_readlane(my_e, u) : -1;
-    pj[u] = u < k ? __builtin_amdgcn_readlane(my_p, u) : -1;
-    dj[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_d), u));
+    ej[u] = u < k ? ids[(size_t)t * k + u] : -1;
+    if ((unsigned)ej[u] >= (unsigned)E) ej[u] = -1;     // (an id outside [0, E) adds nothing)
+    pj[u] = u < k ? inv_pos[(size_t)t * k + u] : -1;
+    dj[u] = u < k ? dlk[(size_t)t * k + u] : 0.f;
   }
   const bool col = h < H;
   Raw8<WBF16> wv[KM];
