@@ -266,7 +266,10 @@ moe_status moe_combine(const void* yp, const int32_t* inv_pos,
 
 /*
  * The whole layer forward (fused article, section 3 "full call"): route,
- * dispatch, experts and combine, enqueued back to back on `stream`.
+ * dispatch, experts and combine, enqueued back to back on `stream`.  For a
+ * bf16 layer with top_k = 1 the combine runs inside the second expert GEMM
+ * (fused article, "fusion idea": each token's single row, weighted, is
+ * written straight to y); y is the same bits either way.
  *   y[T,H] (dtype) output.
  *   topk_ids_out[T,top_k] / topk_w_out[T,top_k]: optional (may be NULL)
  *     copies of the routing decision and gate weights.

@@ -117,9 +117,11 @@ struct GemmArgs {
   const uint16_t* B;      // NN: W [E][K][N]; NT: W [E][N][K]; TN: Q (this expert's rows first)
   uint16_t* C;            // NN/NT: [R][N] dispatched rows; TN: this expert's [M][N]
   int K, N, M;            // M: TN only (row length of P)
-  int ep;                 // epilogue (EP_PLAIN, EP_GELU, EP_DGELU)
+  int ep;                 // epilogue (EP_PLAIN, EP_GELU, EP_DGELU, EP_SCATTER)
   const uint16_t* aux;    // EP_DGELU: z [R][N], read where C is written
   uint16_t* zout;         // NN: also store the accumulators before GELU here ([R][N])
+  const int* scatter;     // EP_SCATTER: row p goes to row scatter[p] of C ...
+  const float* row_w;     // ... scaled by row_w[scatter[p]]
 };
 
 // LDS of one workgroup: one array per stage, so the compiler can tell that a
@@ -138,7 +140,8 @@ struct Lds {
 // block jbase + j of the wave (callers have made the rings free: no wave
 // reads them any more).
 //   EP_PLAIN  C = acc;  EP_GELU  C = GELU(acc);
-//   EP_DGELU  C = acc * GELU'(z), z read from aux at the same row and column.
+//   EP_DGELU  C = acc * GELU'(z), z read from aux at the same row and column;
+//   EP_SCATTER  row scat[p] of C = bf16(fma(sw[scat[p]], bf16(acc row p), 0)).
 // EPS: the epilogues this instantiation supports (bit 1 << EP_x), so that a
 // kernel carries only the code of its own.  PB: 32-row blocks per staging
 // pass (the wave's staging area is PB * 4 KB).  NTS: non-temporal stores, for
@@ -147,7 +150,9 @@ template <int BM, int BN, int WM, int WN, int EPS, int NFM, int FMA, int PB = 2,
           bool NTS = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN, WM, WN>::FN][FMA],
                                            uint16_t* __restrict__ C, const Tile& tile, int N,
-                                           int ep, const uint16_t* __restrict__ aux, char* stg,
+                                           int ep, const uint16_t* __restrict__ aux,
+                                           const int* __restrict__ scat,
+                                           const float* __restrict__ sw, char* stg,
                                            int jbase = 0) {
   using S = GemmShape<BM, BN, WM, WN>;
   const int tid = threadIdx.x;
@@ -165,6 +170,24 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
   // row by row: each instruction then stores 8 whole 128-byte row pieces.
   static_assert(S::TN * 2 == 128, "staging layout");
   if constexpr (NFM > 0) {
+    // EP_SCATTER: the destination row and the weight of the row this lane
+    // stages in each 32-row block (m = lane % 32), loaded before anything is
+    // staged; the store loop takes the destinations from these lanes
+    constexpr bool SC = (EPS & (1 << EP_SCATTER)) != 0;
+    const bool scatter = SC && (EPS == (1 << EP_SCATTER) || ep == EP_SCATTER);
+    int dst[NFM];
+    float scl[NFM];
+    if constexpr (SC) {
+      if (scatter) {
+#pragma unroll
+        for (int j = 0; j < NFM; ++j) {
+          const int m = wrow0 + (jbase + j) * 32 + (lane % 32);
+          dst[j] = scat[tile.row0 + min(m, tile.mrows - 1)];   // (rows past the tile: unused)
+        }
+#pragma unroll
+        for (int j = 0; j < NFM; ++j) scl[j] = sw[dst[j]];
+      }
+    }
 #pragma unroll
     for (int p = 0; p < NFM; p += PB) {              // PB blocks of 32 rows per pass
 #pragma unroll
@@ -198,6 +221,13 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
               v1 *= gelu_tanh_grad(bf16_to_f32(z[0] >> 16));
               v2 *= gelu_tanh_grad(bf16_to_f32(z[1] & 0xFFFFu));
               v3 *= gelu_tanh_grad(bf16_to_f32(z[1] >> 16));
+            } else if (SC && scatter) {
+              // the dispatched row as stored in bf16, then its gate weight
+              // applied as the combine applies it
+              v0 = __builtin_fmaf(scl[j], bf16_to_f32(f32_to_bf16(v0)), 0.f);
+              v1 = __builtin_fmaf(scl[j], bf16_to_f32(f32_to_bf16(v1)), 0.f);
+              v2 = __builtin_fmaf(scl[j], bf16_to_f32(f32_to_bf16(v2)), 0.f);
+              v3 = __builtin_fmaf(scl[j], bf16_to_f32(f32_to_bf16(v3)), 0.f);
             }
             const int c = i * 4 + gq;                // 16-byte chunk of the 128-byte row
             *(u32x2*)(stg + r * 128 + ((c ^ (r & 7)) * 16) + (lane / 32) * 8) =
@@ -216,12 +246,15 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
         const int m = wrow0 + (jbase + p) * 32 + r;
         const int n = n0 + wn * S::TN + (slot ^ (r & 7)) * 8;
         const u32x4 v = *(const u32x4*)(stg + r * 128 + slot * 16);
+        int row = tile.row0 + m;
+        if constexpr (SC)   // (row r of the pass: lane r % 32 of its block holds it)
+          if (scatter) row = __shfl(dst[min(p + q / 4, NFM - 1)], r % 32);
         if (m < tile.mrows && n < N) {
-          u32x4* dst = (u32x4*)(C + (size_t)(tile.row0 + m) * N + n);
+          u32x4* out = (u32x4*)(C + (size_t)row * N + n);
           if constexpr (NTS)
-            __builtin_nontemporal_store(v, dst);
+            __builtin_nontemporal_store(v, out);
           else
-            *dst = v;
+            *out = v;
         }
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);            // reads done before the next pass writes
@@ -335,8 +368,10 @@ struct Carry {
 // columns of A read the next row of the tile (or x's next row when the rows
 // are gathered) but meet zero W rows; NT masks both operands' K tails.
 // WAUX: cache policy of the weight loads, NN and NT (kNonTemporal when no
-// other workgroup reads the same weight slab)
-template <int KIND, int BM, int BN, int WM, int WN, int NFM, bool PERSIST = false, int WAUX = 0>
+// other workgroup reads the same weight slab).  XEP != 0: the epilogues of
+// this instantiation (bit 1 << EP_x) in place of the arrangement's own.
+template <int KIND, int BM, int BN, int WM, int WN, int NFM, bool PERSIST = false, int WAUX = 0,
+          int XEP = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, int kt_begin,
                                           int kt_end, const Split& sp, const Lds& lds,
                                           const Carry* cy = nullptr) {
@@ -686,37 +721,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     }
     return;
   }
-  constexpr int EPS = kind_epilogues(KIND);
+  constexpr int EPS = XEP ? XEP : kind_epilogues(KIND);
   if constexpr (PERSIST) {
     // staging outside the rings (4 KB per wave, one 32-row block per pass):
     // no barrier, the next item's loads land in the rings meanwhile
     if (g.zout)
-      store_tile<BM, BN, WM, WN, 1, NFM, FMA, 1>(acc, g.zout, tile, N, EP_PLAIN, nullptr, lds.stg);
-    store_tile<BM, BN, WM, WN, EPS, NFM, FMA, 1>(acc, g.C, tile, N, g.ep, g.aux, lds.stg);
+      store_tile<BM, BN, WM, WN, 1, NFM, FMA, 1>(acc, g.zout, tile, N, EP_PLAIN, nullptr,
+                                                 nullptr, nullptr, lds.stg);
+    store_tile<BM, BN, WM, WN, EPS, NFM, FMA, 1>(acc, g.C, tile, N, g.ep, g.aux, g.scatter,
+                                                 g.row_w, lds.stg);
     return;
   }
   // one barrier first, because other waves may still read the K loop's last
   // stages
   __syncthreads();
   if constexpr (KIND == kNN)
-    if (g.zout) store_tile<BM, BN, WM, WN, 1, NFM>(acc, g.zout, tile, N, EP_PLAIN, nullptr, lds.stg);
-  store_tile<BM, BN, WM, WN, EPS, NFM>(acc, g.C, tile, N, g.ep, g.aux, lds.stg);
+    if (g.zout)
+      store_tile<BM, BN, WM, WN, 1, NFM>(acc, g.zout, tile, N, EP_PLAIN, nullptr, nullptr,
+                                         nullptr, lds.stg);
+  store_tile<BM, BN, WM, WN, EPS, NFM>(acc, g.C, tile, N, g.ep, g.aux, g.scatter, g.row_w,
+                                       lds.stg);
 }
 
 // gemm_tile with NFM = nfm (0 <= nfm <= NF), chosen at run time from a
 // wave-uniform count.
-template <int KIND, int BM, int BN, int WM, int WN, int NF, bool PERSIST = false, int WAUX = 0>
+template <int KIND, int BM, int BN, int WM, int WN, int NF, bool PERSIST = false, int WAUX = 0,
+          int XEP = 0>
 __device__ __forceinline__ void run_tile(int nfm, const GemmArgs& g, const Tile& tile,
                                          int kt_begin, int kt_end, const Split& sp,
                                          const Lds& lds, const Carry* cy = nullptr) {
   if constexpr (NF == 0) {
-    gemm_tile<KIND, BM, BN, WM, WN, 0, PERSIST, WAUX>(g, tile, kt_begin, kt_end, sp, lds, cy);
+    gemm_tile<KIND, BM, BN, WM, WN, 0, PERSIST, WAUX, XEP>(g, tile, kt_begin, kt_end, sp, lds,
+                                                           cy);
   } else {
     if (nfm == NF)
-      gemm_tile<KIND, BM, BN, WM, WN, NF, PERSIST, WAUX>(g, tile, kt_begin, kt_end, sp, lds, cy);
+      gemm_tile<KIND, BM, BN, WM, WN, NF, PERSIST, WAUX, XEP>(g, tile, kt_begin, kt_end, sp, lds,
+                                                              cy);
     else
-      run_tile<KIND, BM, BN, WM, WN, NF - 1, PERSIST, WAUX>(nfm, g, tile, kt_begin, kt_end, sp,
-                                                            lds, cy);
+      run_tile<KIND, BM, BN, WM, WN, NF - 1, PERSIST, WAUX, XEP>(nfm, g, tile, kt_begin, kt_end,
+                                                                 sp, lds, cy);
   }
 }
 
@@ -793,8 +836,8 @@ __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __res
 // one-tile-per-workgroup kernel) and then its split piece, if any, handing
 // the pipeline from one item to the next (Carry); the epilogue stages
 // through its own 32 KB (128 KB of rings + 32 KB = 160 KB).  WAUX: the
-// weight loads' cache policy.
-template <int BM, int BN, int WM, int WN, int WAUX = 0>
+// weight loads' cache policy; XEP: as in gemm_tile.
+template <int BM, int BN, int WM, int WN, int WAUX = 0, int XEP = 0>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_grouped(
     GemmArgs g, const int* __restrict__ off, int E, int R, float* __restrict__ part,
     int slots) {
@@ -854,7 +897,7 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     if (cy.has_next) item(i + 1, cy.next, cy.next_kb, cy.next_ke, nsp);
     int nfm = max(0, min(S::FM, (cur.mrows - wm * S::TM + 31) / 32));
     nfm = __builtin_amdgcn_readfirstlane(nfm);
-    run_tile<kNN, BM, BN, WM, WN, S::FM, true, WAUX>(nfm, g, cur, ckb, cke, csp, lds, &cy);
+    run_tile<kNN, BM, BN, WM, WN, S::FM, true, WAUX, XEP>(nfm, g, cur, ckb, cke, csp, lds, &cy);
     cy.carry_in = true;
     cur = cy.next;
     ckb = cy.next_kb;
@@ -1088,8 +1131,8 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
       step(kt + 3, std::integral_constant<int, 3>{});
     }
     // (the weight gradients: written once, read by no kernel of this pass)
-    store_tile<BM, BN, WM, WN, 1 << EP_PLAIN, FM, FM, 1, true>(acc, cur.c, cur.tile, N,
-                                                               EP_PLAIN, nullptr, lds.stg);
+    store_tile<BM, BN, WM, WN, 1 << EP_PLAIN, FM, FM, 1, true>(
+        acc, cur.c, cur.tile, N, EP_PLAIN, nullptr, nullptr, nullptr, lds.stg);
     if (!has_next) break;
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -1106,8 +1149,8 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
 // Split tiles: one workgroup per (split tile, 32-row block jb of every
 // wave).  Each wave adds the S partials of its block in split order, two
 // pieces' loads in flight per round trip, and stores the block (with the
-// launch's epilogue; zout as in the GEMM).
-template <int KIND, int BM, int BN, int WM, int WN>
+// launch's epilogue; zout as in the GEMM; XEP as in gemm_tile).
+template <int KIND, int BM, int BN, int WM, int WN, int XEP = 0>
 __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
     GemmArgs g, const int* __restrict__ off, int E, int R, const float* __restrict__ part,
     int slots) {
@@ -1157,8 +1200,12 @@ __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][0][4 * vq + e] = run[i][vq][e];
   if constexpr (KIND == kNN)
-    if (g.zout) store_tile<BM, BN, WM, WN, 1, 1>(acc, g.zout, tile, g.N, EP_PLAIN, nullptr, stg, jb);
-  store_tile<BM, BN, WM, WN, kind_epilogues(KIND), 1>(acc, g.C, tile, g.N, g.ep, g.aux, stg, jb);
+    if (g.zout)
+      store_tile<BM, BN, WM, WN, 1, 1>(acc, g.zout, tile, g.N, EP_PLAIN, nullptr, nullptr,
+                                       nullptr, stg, jb);
+  store_tile<BM, BN, WM, WN, XEP ? XEP : kind_epilogues(KIND), 1>(acc, g.C, tile, g.N, g.ep,
+                                                                  g.aux, g.scatter, g.row_w, stg,
+                                                                  jb);
 }
 
 int device_slots() {
@@ -1179,9 +1226,10 @@ int device_slots() {
   return cached[dev];
 }
 
-template <int KIND, int BM, int BN, int WM, int WN>
+template <int KIND, int BM, int BN, int WM, int WN, int XEP = 0>
 hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* split_ws,
                       hipStream_t s) {
+  static_assert(XEP == 0 || KIND == kNN, "own epilogues: the forward's products only");
   const int NTN = (g.N + BN - 1) / BN;
   // upper bound of row tiles: sum_e ceil(rows_e / BM) <= ceil(R / BM) + min(E, R)
   const long mt_max = off ? (long)(R + BM - 1) / BM + (long)min(E, R) : (long)(R + BM - 1) / BM;
@@ -1204,17 +1252,18 @@ hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* spl
                          dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
   } else if (stream_w)
     // (persistent: one workgroup per CU)
-    hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN, kNonTemporal>), dim3((unsigned)slots),
-                       dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
+    hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN, kNonTemporal, XEP>),
+                       dim3((unsigned)slots), dim3(kWave * WM * WN), 0, s, g, off, E, R, part,
+                       slots);
   else
-    hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN>), dim3((unsigned)slots),
+    hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN, 0, XEP>), dim3((unsigned)slots),
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // tiles are split only when K has at least 4 * MIN_SPLIT_STEPS steps, and
   // only with a split workspace
   if (part != nullptr && (g.K + BK - 1) / BK >= 4 * MIN_SPLIT_STEPS) {
-    hipLaunchKernelGGL((gemm_split_reduce<KIND, BM, BN, WM, WN>),
+    hipLaunchKernelGGL((gemm_split_reduce<KIND, BM, BN, WM, WN, XEP>),
                        dim3(kMaxSlots / 2 * GemmShape<BM, BN, WM, WN>::FM),
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, (const float*)part, slots);
     err = hipGetLastError();
@@ -1242,8 +1291,31 @@ hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const 
   g.ep = ep;
   g.aux = (const uint16_t*)aux;
   g.zout = (uint16_t*)zout;
+  g.scatter = nullptr;
+  g.row_w = nullptr;
+  if (ep == EP_SCATTER) return hipErrorInvalidValue;   // (launch_gemm_bf16_scatter)
   if (w_nk) return launch_cfg<kNT, 256, 256, kWM, kWN>(g, off, E, R, split_ws, s);
   return launch_cfg<kNN, 256, 256, kWM, kWN>(g, off, E, R, split_ws, s);
+}
+
+hipError_t launch_gemm_bf16_scatter(const void* A, const void* W, void* C, const int* off,
+                                    int E, int R, int K, int N, const int* scatter,
+                                    const float* row_w, void* split_ws, hipStream_t s) {
+  GemmArgs g;
+  g.A = (const uint16_t*)A;
+  g.gather = nullptr;
+  g.a_rows = R;
+  g.B = (const uint16_t*)W;
+  g.C = (uint16_t*)C;
+  g.K = K;
+  g.N = N;
+  g.M = 0;
+  g.ep = EP_SCATTER;
+  g.aux = nullptr;
+  g.zout = nullptr;
+  g.scatter = scatter;
+  g.row_w = row_w;
+  return launch_cfg<kNN, 256, 256, kWM, kWN, 1 << EP_SCATTER>(g, off, E, R, split_ws, s);
 }
 
 hipError_t launch_gemm_bf16_wgrad(const void* P, const void* Q, void* C, const int* off, int E,

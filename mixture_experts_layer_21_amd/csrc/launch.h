@@ -43,8 +43,10 @@ hipError_t launch_permute(const void* x, const int32_t* ids, int T, int H, int E
 constexpr int kMaxSlots = 256;
 size_t split_ws_bytes();
 // GEMM epilogues: C = acc, GELU(acc), or acc * GELU'(z) with z read from an
-// [R][N] matrix at the place C is written.
-enum Epilogue { EP_PLAIN = 0, EP_GELU = 1, EP_DGELU = 2 };
+// [R][N] matrix at the place C is written; EP_SCATTER (launch_gemm_bf16_scatter
+// only): row p of the product, rounded to bf16 and scaled by row_w[scatter[p]],
+// becomes row scatter[p] of C.
+enum Epilogue { EP_PLAIN = 0, EP_GELU = 1, EP_DGELU = 2, EP_SCATTER = 3 };
 // C[rows_e] = epilogue(A[rows_e] . B_e) for every expert e.  A holds a_rows
 // rows of K; with gather != nullptr, dispatched row p is row gather[p] of A
 // (the dispatch fused into the GEMM's loads), else row p.  B_e is W[e] as
@@ -56,6 +58,16 @@ hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const 
                             bool w_nk, void* C, const int* off, int E, int R, int K, int N,
                             int ep, const void* aux, void* zout, void* split_ws,
                             hipStream_t s);
+// The second expert GEMM with the combine of a top-1 layer in its epilogue:
+// product row p (A's row p, expert e's W[K][N]) is rounded to bf16, scaled by
+// row_w[scatter[p]] in fp32 (an fma with a zero addend) and rounded again into
+// row scatter[p] of C.  With one dispatched row per token (scatter = the
+// dispatch's sorted_token, row_w = the gate weights) that is y, bit for bit
+// what storing the rows and then launch_combine would give; C rows that no p
+// names are not written.
+hipError_t launch_gemm_bf16_scatter(const void* A, const void* W, void* C, const int* off,
+                                    int E, int R, int K, int N, const int* scatter,
+                                    const float* row_w, void* split_ws, hipStream_t s);
 // C[e] = P_e^T . Q_e ([M][N] per expert) with P_e, Q_e the rows
 // [off[e], off[e+1]) of P [R][M] and Q [R][N] (expert weight gradients).
 hipError_t launch_gemm_bf16_wgrad(const void* P, const void* Q, void* C, const int* off, int E,

@@ -446,6 +446,19 @@ moe_status forward_body(const void* x, const void* w_r, const float* router_bias
                             off, sorted, inv, bf16 ? nullptr : xp, stage, s);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
   void* split_ws = split ? ffn_split(stage, R, F, dtype) : nullptr;
+  if (bf16 && top_k == 1 && capacity <= 0) {
+    // Top-1 and dropless: every token owns exactly one dispatched row, so
+    // the second GEMM's epilogue writes it, weighted, straight to the
+    // token's row of y (the combine fused in; no yp, no cross-workgroup
+    // sums, the same bits as the separate pass)
+    hipError_t e2 = moe::launch_gemm_bf16(x, sorted, (int)T, w1, false, stage, off, (int)E,
+                                          (int)R, (int)H, (int)F, moe::EP_GELU, nullptr,
+                                          nullptr, split_ws, s);
+    if (e2 == hipSuccess)
+      e2 = moe::launch_gemm_bf16_scatter(stage, w2, y, off, (int)E, (int)R, (int)F, (int)H,
+                                         sorted, w, split_ws, s);
+    return launch_status(e2);
+  }
   const moe_status fs =
       bf16 ? run_ffn(x, sorted, T, off, w1, w2, R, H, E, F, dtype, yp, stage, nullptr, split_ws, s)
            : run_ffn(xp, nullptr, R, off, w1, w2, R, H, E, F, dtype, yp, stage, nullptr, split_ws,

@@ -247,6 +247,44 @@ def test_dispatch_full(name):
     print(f"[{name}] yp: max|err|/max|yp_ref| = {rel:.3e} over all {cfg.R} rows", flush=True)
 
 
+# top_k = 1, bf16, dropless: the second expert GEMM writes each token's row
+# of y itself (its dispatched row, weighted); the result must be bit for bit
+# the staged path's (dispatched rows stored, then the combine pass) and agree
+# with the oracle on every token.  The last two shapes run that epilogue in
+# the split reduce: every second-GEMM tile split along K (24 tiles, K = 4096),
+# and one whole round of 256 tiles followed by split leftover tiles.
+TOP1 = {
+    **{n: SMALL[n] for n in ("top1_bf16", "one_expert_bf16", "ksplit_bf16",
+                             "fused_E8_H448_bf16")},
+    "top1_split_bf16": C("top1_split_bf16", T=2100, H=512, E=4, k=1, F=4096, dtype="bf16"),
+    "top1_rounds_bf16": C("top1_rounds_bf16", T=4096, H=4096, E=16, k=1, F=2048,
+                          dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(TOP1))
+def test_top1_fused_combine(name):
+    cfg = TOP1[name]
+    L = layer(cfg)
+    ids = torch.empty((cfg.T, 1), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, 1), dtype=torch.float32, device="cuda")
+    y = moe.moe_forward(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], 1,
+                        topk_ids_out=ids, topk_w_out=w)
+    off, st, inv, xp = moe.moe_permute(L["x"], ids, cfg.E)
+    yp = moe.moe_expert_ffn(xp, off, L["w1"], L["w2"])
+    y_staged = moe.moe_combine(yp, inv, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_staged)
+    logits = ref_logits(cfg, L)
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    check_routing(ids_np, w.cpu().numpy(), logits, 1)
+    g1, g2 = expert_getters(L)
+    y_ref = oracle.forward(f64(L["x"]), f64(L["w_r"]), f64(L["router_bias"]), g1, g2, 1,
+                           ids=ids_np, w=oracle.gate_weights(logits, ids_np))["y"]
+    rel = assert_close_rel(f64(y), y_ref, TOL[dt(cfg)], f"{name} y")
+    print(f"[{name}] y: max|err|/max|y_ref| = {rel:.3e} over all {cfg.T} tokens", flush=True)
+
+
 @pytest.mark.parametrize("name", ["mixtral_bf16", "many_experts_bf16"])
 def test_forward_is_deterministic(name):
     cfg = mi.CONFIGS[name]
