@@ -187,6 +187,7 @@ struct Tile {
   int row0;    // first dispatched row of the tile
   int mrows;   // valid rows in the tile (1..BM)
   int nt;      // column tile index
+  int mi;      // row tile index within the expert (0: its first rows)
 };
 
 // Rows [lo, lo + n) of expert e: the offsets' range clamped into [0, R].
@@ -233,6 +234,7 @@ __device__ __forceinline__ Tile lookup_tile(const int* __restrict__ off, int E,
     tile.e = 0;
     tile.nt = L / mt;
     const int mi = L % mt;
+    tile.mi = mi;
     tile.row0 = mi * BM;
     tile.mrows = min(BM, dense_rows - tile.row0);
     return tile;
@@ -261,6 +263,7 @@ __device__ __forceinline__ Tile lookup_tile(const int* __restrict__ off, int E,
       tile.valid = 1;
       tile.e = e_hit;
       tile.nt = local / mt_hit;
+      tile.mi = mi;
       tile.row0 = row_hit + mi * BM;
       tile.mrows = min(BM, cnt_hit - mi * BM);
       return tile;

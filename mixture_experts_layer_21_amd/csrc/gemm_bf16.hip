@@ -47,6 +47,9 @@ constexpr int kWN = 4;          // waves along the columns (8 waves: two per SIM
 constexpr int BK = 32;          // K step (bf16 elements): two 16-wide MFMA slices
 constexpr int W_STAGES = 4;     // weight ring: one K step per stage, 3 in flight
 constexpr int MIN_SPLIT_STEPS = 16;   // K steps per piece of a split tile, at least
+// Pacing of a light tile (s_sleep units of 64 cycles per missing 32-row block
+// per K step; see gemm_bf16_grouped)
+constexpr int kPaceSleep = 3;
 
 template <int BM, int BN, int WM, int WN>
 struct GemmShape {
@@ -352,6 +355,7 @@ struct ColLoader {
 // would, so the next item starts with them in flight.
 struct Carry {
   bool carry_in;          // this item's prologue loads were issued by the previous item
+  bool pace;              // this wave sleeps in each K step (see gemm_bf16_grouped)
   bool has_next;
   Tile next;              // the next item's tile
   int next_kb, next_ke;   // and its K-step range
@@ -555,6 +559,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     if constexpr (NRD > P) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P, 0);
   };
 
+  bool pace = false;
+  if constexpr (PERSIST) pace = cy->pace;
   // step kt of the unrolled group of 4
   auto step = [&](int kt, auto st_c, auto last_c) {
     constexpr int ST = decltype(st_c)::value;
@@ -578,6 +584,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
       __builtin_amdgcn_s_waitcnt(vmcnt_le(2 * (AI + BI)));
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): reads of step kt done
+    if constexpr (KIND == kNN && PERSIST && NFM < S::FM)
+      if (pace) __builtin_amdgcn_s_sleep(kPaceSleep * (S::FM - NFM));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     if constexpr (KIND == kNN && LAST) {
@@ -882,6 +890,7 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
       t.nt = 0;
       t.row0 = 0;
       t.mrows = 0;
+      t.mi = 0;
     }
   };
   const int wm = wave % WM;
@@ -897,6 +906,14 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     if (cy.has_next) item(i + 1, cy.next, cy.next_kb, cy.next_ke, nsp);
     int nfm = max(0, min(S::FM, (cur.mrows - wm * S::TM + 31) / 32));
     nfm = __builtin_amdgcn_readfirstlane(nfm);
+    // A whole tile holding an expert's last rows (not its first) shares its
+    // weight slab with the expert's other row tiles, which run beside it on
+    // this XCD.  With few rows it would run ahead of them and read the slab
+    // from memory a second time; instead the waves of its first 128 rows
+    // sleep in each K step in proportion to their missing 32-row blocks, so
+    // the tile keeps pace and finds the slab in L2 (not with non-temporal
+    // weight loads, where slabs are not shared)
+    cy.pace = WAUX == 0 && wm == 0 && cur.mi > 0 && csp.S == 1;
     run_tile<kNN, BM, BN, WM, WN, S::FM, true, WAUX, XEP>(nfm, g, cur, ckb, cke, csp, lds, &cy);
     cy.carry_in = true;
     cur = cy.next;
