@@ -799,6 +799,18 @@ __device__ __forceinline__ SplitPlan split_plan(const int* __restrict__ off, int
   return pl;
 }
 
+// The split piece that workgroup slot p (0 <= p < sk * nsplit) runs: tile
+// L, K range s.  Pieces are listed K range by K range (range s of every
+// split tile, then range s + 1, ...) and each XCD takes a contiguous run of
+// the list, so the pieces one XCD runs together cover one K range of
+// consecutive tiles: row tiles that share a weight slab, and slabs that
+// share token rows, meet in its L2.
+__device__ __forceinline__ void split_piece(const SplitPlan& pl, int p, int& L, int& s) {
+  const int q = xcd_remap(p, pl.sk * pl.nsplit);
+  L = pl.dp + q % pl.sk;
+  s = q / pl.sk;
+}
+
 // this wave's 8 KB of epilogue staging inside two 32 KB regions
 __device__ __forceinline__ char* staging(char* lo, char* hi, int nw) {
   const int wave = threadIdx.x / kWave;
@@ -819,11 +831,10 @@ __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __res
   if (bid < pl.dp) {
     L = xcd_remap(bid, pl.dp);
   } else {
-    const int p = bid - pl.dp;
+    const int p = bid - pl.dp;              // (pl.dp: a multiple of the XCD count)
     if (p >= pl.sk * pl.nsplit) return;
-    L = pl.dp + p / pl.nsplit;
+    split_piece(pl, p, L, sp.s);
     sp.S = pl.nsplit;
-    sp.s = p % pl.nsplit;
     sp.slot = L - pl.dp;
     kt_begin = sp.s * pl.KT / pl.nsplit;
     kt_end = (sp.s + 1) * pl.KT / pl.nsplit;
@@ -874,9 +885,8 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     if (i < n_whole) {
       L = xcd_remap(b + i * G, pl.dp);
     } else {
-      L = pl.dp + b / pl.nsplit;
+      split_piece(pl, b, L, sp.s);
       sp.S = pl.nsplit;
-      sp.s = b % pl.nsplit;
       sp.slot = L - pl.dp;
       kb = sp.s * pl.KT / pl.nsplit;
       ke = (sp.s + 1) * pl.KT / pl.nsplit;
