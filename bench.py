@@ -114,6 +114,31 @@ def attainable_hbm(mib: int = 1024, reps: int = 5) -> dict:
     return {"hbm_copy_gbs": 2 * n / best / 1e9, "copy_bytes": 2 * n}
 
 
+def attainable_gemm(reps: int = 5) -> dict:
+    """Diagnostics beside the published bf16 peak: torch.matmul (hipBLASLt)
+    in bf16 on an 8192^3 product and on one expert's first GEMM at the
+    Mixtral shape (512 x 4096 by 4096 x 14336), best of `reps` with HIP
+    events.  Not part of the hot path."""
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for name, (m, k, n) in {"matmul_8192_tflops": (8192, 8192, 8192),
+                            "matmul_expert_tflops": (512, 4096, 14336)}.items():
+        a = torch.randn(m, k, device="cuda", generator=g).bfloat16()
+        b = torch.randn(k, n, device="cuda", generator=g).bfloat16()
+        c = a @ b
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, b, out=c)
+            e1.record()
+            e1.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        out[name] = 2 * m * k * n / best / 1e12
+        del a, b, c
+    return out
+
+
 def _counter_totals(csv_path: str, counter: str, kernel_substr: str, required: bool = True):
     """(sum over dispatches, number of dispatches) of a counter for the kernels
     whose name contains kernel_substr."""
@@ -657,7 +682,7 @@ def main():
         "stages_flushed": not a.no_flush,
         "pass_hbm": hbm,
         "oracle_check": check,
-        "attainable": attainable_hbm(),
+        "attainable": {**attainable_hbm(), **attainable_gemm()},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
