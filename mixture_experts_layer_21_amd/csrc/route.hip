@@ -564,8 +564,16 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t0 = blockIdx.x * TOK;
   const int h0 = wave * NS * 32;
-  const bool xl = lane / 4 < TOK;
-  const uint16_t* xr = x + (size_t)min(t0 + lane / 4, T - 1) * H + 8 * (lane % 4);
+  // Buffer loads (an offset past the descriptor's end reads zero, so no
+  // load sits behind a branch, which would make the compiler wait for all
+  // loads in flight before the first use): lane reads token t0 + lane / 4
+  // (tokens past the tile or past T read zero), 16 bytes at h = 8 (lane % 4)
+  // of each step, and W_r row 8 (lane / 16) + lane % 8 of the step, experts
+  // 8 ((lane % 16) / 8) + 0..7 (rows past H read zero)
+  const __amdgpu_buffer_rsrc_t xs =
+      make_rsrc(x + (size_t)t0 * H, (uint32_t)(min(TOK, T - t0) * H * 2));
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(w_r, (uint32_t)(H * E * 2));
+  const uint32_t xo = (uint32_t)(((lane / 4) * H + 8 * (lane % 4)) * 2);
   const int xsrc = 4 * (4 * (lane % 16) + lane / 16);
   const int r_lane = 8 * (lane / 16) + lane % 8;
   const int e_lane = 8 * ((lane % 16) / 8);
@@ -573,10 +581,11 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
     const int hs = h0 + 32 * st;
-    xb[st] = xl && hs + 8 * (lane % 4) < H ? *(const u32x4*)(xr + hs) : u32x4{0u, 0u, 0u, 0u};
+    xb[st] = __builtin_amdgcn_raw_buffer_load_b128(
+        xs, hs + 8 * (lane % 4) < H ? xo + 2u * (uint32_t)hs : kPastEnd, 0, 0);
     const int h = hs + r_lane;
-    wb[st] = (e_lane < E && h < H) ? *(const u32x4*)(w_r + (size_t)h * E + e_lane)
-                                   : u32x4{0u, 0u, 0u, 0u};
+    wb[st] = __builtin_amdgcn_raw_buffer_load_b128(
+        ws, e_lane < E ? (uint32_t)((h * E + e_lane) * 2) : kPastEnd, 0, 0);
   }
   const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;
   const bool odd2 = (lane & 2) != 0;
@@ -613,21 +622,30 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused(
   const int rot = blockIdx.x / 8;
   const int h0 = ((wave + rot) % kFuseWaves) * NS * 32;
   const int g = lane / 16, c = lane % 16;
-  // token operand loads: lane reads token t0 + lane / 4 (rows past T repeat
-  // the last token), rows 8 (lane % 4) + 0..7 of the step; the A fragment of
-  // lane l comes from lane 4 (l % 16) + l / 16
-  const uint16_t* xr = x + (size_t)min(t0 + lane / 4, T - 1) * H + 8 * (lane % 4);
+  // Buffer loads, as in route_fused_small (no load behind a branch, so each
+  // step waits for its own loads only).  Token operand: lane reads token
+  // t0 + lane / 4 (tokens past T read zero), rows 8 (lane % 4) + 0..7 of the
+  // step; the A fragment of lane l comes from lane 4 (l % 16) + l / 16.
+  // W_r: row h of the step's 8 g + i, experts 8 c .. 8 c + 7 (rows past H
+  // read zero).
+  const __amdgpu_buffer_rsrc_t xs =
+      make_rsrc(x + (size_t)t0 * H, (uint32_t)(min(16, T - t0) * H * 2));
+  const __amdgpu_buffer_rsrc_t ws = make_rsrc(w_r, (uint32_t)(H * E * 2));
+  const uint32_t xo = (uint32_t)(((lane / 4) * H + 8 * (lane % 4)) * 2);
   const int xsrc = 4 * (4 * (lane % 16) + lane / 16);
-  // W_r loads: row h of the step's 8 g + i, experts 8 c .. 8 c + 7
-  const bool wc = 8 * c < E;
-  const uint16_t* wr = w_r + 8 * c;
+  // (lanes of experts past E: every offset ORed past the end; a select per
+  // load here became a branch around each load)
+  const uint32_t wmask = 8 * c < E ? 0u : kPastEnd;
   auto load_step = [&](int st, u32x4 (&xb), u32x4 (&wb)[8]) {
+    if (st >= NS) return;   // (a constant once the step loop is unrolled)
     const int hs = h0 + 32 * ((st + rot) % NS);
-    xb = (st < NS && hs + 8 * (lane % 4) < H) ? *(const u32x4*)(xr + hs) : u32x4{0u, 0u, 0u, 0u};
+    xb = __builtin_amdgcn_raw_buffer_load_b128(
+        xs, hs + 8 * (lane % 4) < H ? xo + 2u * (uint32_t)hs : kPastEnd, 0, 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int h = hs + 8 * g + i;
-      wb[i] = (st < NS && wc && h < H) ? *(const u32x4*)(wr + (size_t)h * E) : u32x4{0u, 0u, 0u, 0u};
+      wb[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          ws, (uint32_t)((h * E + 8 * c) * 2) | wmask, 0, 0);
     }
   };
   u32x4 xbuf[D], wbuf[D][8];
