@@ -618,11 +618,17 @@ __global__ __launch_bounds__(256) void dx_finish(const void* __restrict__ dxp,
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[tt][q] = 0.f;
   for (int e0 = 0; e0 < E; e0 += 8) {
+    // (every load unconditional, rows past E clamped and their values
+    // zeroed after the load: a load behind a branch makes the compiler wait
+    // for all loads in flight before the next use)
     float wv[8][4];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      wv[u][0] = wv[u][1] = wv[u][2] = wv[u][3] = 0.f;
-      if (e0 + u < E) load_wrt4<WBF16>(w_rt, (size_t)(e0 + u) * H + h, wv[u]);
+      float t4[4];
+      load_wrt4<WBF16>(w_rt, (size_t)min(e0 + u, E - 1) * H + h, t4);
+      const bool in = e0 + u < E;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wv[u][q] = in ? t4[q] : 0.f;
     }
 #pragma unroll
     for (int tt = 0; tt < TB; ++tt) {
@@ -645,24 +651,26 @@ __global__ __launch_bounds__(256) void dx_finish(const void* __restrict__ dxp,
       for (int j0 = 0; j0 < k; j0 += 8) {
         int pj[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) pj[u] = j0 + u < k ? inv_pos[(size_t)t * k + j0 + u] : -1;
+        for (int u = 0; u < 8; ++u) {
+          const int pv = inv_pos[(size_t)t * k + min(j0 + u, k - 1)];
+          pj[u] = j0 + u < k ? pv : -1;
+        }
+        // (unconditional loads; a dropped or absent slot reads row 0 and adds
+        // nothing)
         float r[8][4];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          r[u][0] = r[u][1] = r[u][2] = r[u][3] = 0.f;
-          if (pj[u] >= 0) {
-            const char* src = (const char*)dxp + ((size_t)pj[u] * H + h) * es;
-            if constexpr (BF16) {
-              const u32x2 q = *(const u32x2*)src;
-              r[u][0] = bf16_to_f32(q[0] & 0xFFFFu);
-              r[u][1] = bf16_to_f32(q[0] >> 16);
-              r[u][2] = bf16_to_f32(q[1] & 0xFFFFu);
-              r[u][3] = bf16_to_f32(q[1] >> 16);
-            } else {
-              const f32x4 q = *(const f32x4*)src;
+          const char* src = (const char*)dxp + ((size_t)max(pj[u], 0) * H + h) * es;
+          if constexpr (BF16) {
+            const u32x2 q = *(const u32x2*)src;
+            r[u][0] = bf16_to_f32(q[0] & 0xFFFFu);
+            r[u][1] = bf16_to_f32(q[0] >> 16);
+            r[u][2] = bf16_to_f32(q[1] & 0xFFFFu);
+            r[u][3] = bf16_to_f32(q[1] >> 16);
+          } else {
+            const f32x4 q = *(const f32x4*)src;
 #pragma unroll
-              for (int c = 0; c < 4; ++c) r[u][c] = q[c];
-            }
+            for (int c = 0; c < 4; ++c) r[u][c] = q[c];
           }
         }
 #pragma unroll
