@@ -119,9 +119,11 @@ def test_backward_variants_match_oracle(name, gating, cap_factor, wf32):
         assert np.all(out["dw"].cpu().numpy()[inv < 0] == 0.0)
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "longH_bf16"])
+@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "longH_bf16", "top1_bf16"])
 def test_forward_train_equals_forward(name):
-    """The training forward's y, ids and w are the plain forward's, bit for bit."""
+    """The training forward's y, ids and w are the plain forward's, bit for bit
+    (top1_bf16: the plain forward combines inside its second expert GEMM, the
+    training forward keeps yp and runs the combine pass)."""
     cfg = CASES[name]
     L = layer(cfg)
     y, ids, w, _ = moe.moe_forward_train(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"],

@@ -270,6 +270,7 @@ def test_top1_fused_combine(name):
     w = torch.empty((cfg.T, 1), dtype=torch.float32, device="cuda")
     y = moe.moe_forward(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], 1,
                         topk_ids_out=ids, topk_w_out=w)
+    assert torch.all(w == 1.0)          # top-1 then softmax: a weight of exactly 1
     off, st, inv, xp = moe.moe_permute(L["x"], ids, cfg.E)
     yp = moe.moe_expert_ffn(xp, off, L["w1"], L["w2"])
     y_staged = moe.moe_combine(yp, inv, w)
@@ -283,6 +284,27 @@ def test_top1_fused_combine(name):
                            ids=ids_np, w=oracle.gate_weights(logits, ids_np))["y"]
     rel = assert_close_rel(f64(y), y_ref, TOL[dt(cfg)], f"{name} y")
     print(f"[{name}] y: max|err|/max|y_ref| = {rel:.3e} over all {cfg.T} tokens", flush=True)
+
+
+@pytest.mark.parametrize("name", ["top1_bf16", "top1_split_bf16"])
+def test_top1_fused_combine_softmax_first(name):
+    """Softmax over all experts, then the top 1 (gate weight below 1): the
+    second GEMM's epilogue applies the weight as the combine pass does."""
+    cfg = TOP1[name]
+    L = layer(cfg)
+    gs = moe.MOE_GATE_SOFTMAX_TOPK
+    ids = torch.empty((cfg.T, 1), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, 1), dtype=torch.float32, device="cuda")
+    y = moe.moe_forward_ex(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], 1, gating=gs,
+                           topk_ids_out=ids, topk_w_out=w)
+    ids2, w2 = moe.moe_route_ex(L["x"], L["w_r"], L["router_bias"], 1, gating=gs)
+    off, st, inv, xp = moe.moe_permute(L["x"], ids2, cfg.E)
+    yp = moe.moe_expert_ffn(xp, off, L["w1"], L["w2"])
+    y_staged = moe.moe_combine(yp, inv, w2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+    assert bool(torch.all(w < 1.0))
+    assert torch.equal(y, y_staged)
 
 
 @pytest.mark.parametrize("name", ["mixtral_bf16", "many_experts_bf16"])
