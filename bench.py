@@ -44,12 +44,27 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "MoE layer fwd tokens/s (T=2048,H=4096,E=8,k=2) + % MFMA/HBM roofline"
 
 
+def workload(a) -> "mi.MoEConfig":
+    """--shape's layer, else the named workload."""
+    if not a.shape:
+        return mi.CONFIGS[a.config]
+    f = a.shape.split(",")
+    if len(f) not in (5, 6) or (len(f) == 6 and f[5] not in ("bf16", "f32")):
+        raise SystemExit(f"--shape wants T,H,E,K,F[,bf16|f32], got {a.shape!r}")
+    T, H, E, k, F = (int(v) for v in f[:5])
+    dt = f[5] if len(f) == 6 else "bf16"
+    return mi.MoEConfig(f"shape_T{T}_H{H}_E{E}_k{k}_F{F}_{dt}", T=T, H=H, E=E, k=k, F=F, dtype=dt)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="mixtral_bf16", choices=list(mi.CONFIGS))
+    ap.add_argument("--shape", default=None, metavar="T,H,E,K,F[,DTYPE]",
+                    help="a layer of this shape (DTYPE bf16, the default, or f32; seed 0, "
+                         "the workloads' input recipe) instead of --config")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true",
                     help="stage timing without the cache-evicting write before each step")
@@ -559,7 +574,8 @@ def main_train(a, moe, cfg):
     if not a.no_cpu_baseline:
         # (about 10 s of host work each)
         n = a.cpu_sample_tokens or {"tiny_fp32": 64, "mixtral_bf16": 1024, "skewed_bf16": 1024,
-                                    "many_experts_bf16": 2048, "weight_bound_bf16": 16}[cfg.name]
+                                    "many_experts_bf16": 2048,
+                                    "weight_bound_bf16": 16}.get(cfg.name, min(T, 64))
         cpu = cpu_baseline_train(cfg, L, dy, min(n, T))
     # training-step flops: forward (router + 2 GEMMs) and backward (router
     # weight and input gradients + 4 GEMMs)
@@ -590,7 +606,7 @@ def main():
               "here is a single-GPU hot path with no collectives.", file=sys.stderr)
         sys.exit(2)
     import mixture_experts_layer_21_amd as moe
-    cfg = mi.CONFIGS[a.config]
+    cfg = workload(a)
     torch.cuda.set_device(0)
     if a.calibrate_copy_mib:
         calibrate_copy(a.calibrate_copy_mib)
@@ -649,7 +665,8 @@ def main():
     if not a.no_cpu_baseline:
         # (about 10 s of host work at most: the whole batch)
         n = a.cpu_sample_tokens or {"tiny_fp32": 64, "mixtral_bf16": 2048, "skewed_bf16": 2048,
-                                    "many_experts_bf16": 4096, "weight_bound_bf16": 64}[cfg.name]
+                                    "many_experts_bf16": 4096,
+                                    "weight_bound_bf16": 64}.get(cfg.name, min(cfg.T, 256))
         moe.moe_forward(L["x"], L["w_r"], L["router_bias"], L["w1"], L["w2"], cfg.k, y=y,
                         topk_ids_out=bufs[0], ws=ws)
         torch.cuda.synchronize()

@@ -68,3 +68,17 @@ def test_bench_counts_follow_the_rule(ids, kinds):
     ref = oracle.topk_ids(L, 2)
     got = bench.classify_ids(np.array(ids), ref, L, oracle.boundary_near_tie(L, 2))
     assert (got["boundary"], got["within"], got["other"]) == kinds
+
+
+def test_bench_shape_option():
+    """bench.py --shape builds a layer of the given shape (bf16 by default)."""
+    import argparse
+
+    import bench
+    cfg = bench.workload(argparse.Namespace(shape="64,4096,8,2,14336", config="mixtral_bf16"))
+    assert (cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.dtype) == (64, 4096, 8, 2, 14336, "bf16")
+    cfg = bench.workload(argparse.Namespace(shape="70,72,6,3,40,f32", config="mixtral_bf16"))
+    assert (cfg.T, cfg.dtype) == (70, "f32")
+    assert bench.workload(argparse.Namespace(shape=None, config="skewed_bf16")).bias0 == 3.0
+    with pytest.raises(SystemExit):
+        bench.workload(argparse.Namespace(shape="1,2,3", config="mixtral_bf16"))
