@@ -15,13 +15,15 @@
 // GPU; more experts; an fp32 W_r)
 //   route_logits_bf16 MFMA 16x16x32 bf16 with fp32 accumulation.  A workgroup
 //                     owns one expert group (TPW tiles of 16 experts) and one
-//                     split of the H axis (KL rows) for 4 token tiles of 16,
-//                     one per wave.  The W_r block [KL][16 TPW] is staged in
-//                     LDS once in its natural k-major layout and read by the
-//                     waves with transposed LDS reads (4 consecutive k of one
-//                     expert per lane and read); the token operand comes
-//                     straight from global memory.  Partial logits go to
-//                     part[S][T][EP] (fp32, EP = E rounded up to 16).
+//                     split of the H axis (KL rows) for 8 token tiles of 16,
+//                     one per wave.  The split's W_r rows [KL][16 TPW] are
+//                     staged in LDS chunk by chunk (64 KB each) in their
+//                     natural k-major layout and read by the waves with
+//                     transposed LDS reads (4 consecutive k of one expert per
+//                     lane and read); the token operand comes straight from
+//                     global memory.  Partial logits go to part[S][T][EP]
+//                     (fp32, EP = E rounded up to 16); many tokens take few
+//                     splits, so that traffic stays small.
 //                     With an fp32 W_r (an fp32 router for bf16 tokens, the
 //                     CANN article's section 4.2) each weight is staged as
 //                     three bf16 planes, w = hi + mid + lo (hi and mid
@@ -46,15 +48,25 @@
 namespace moe {
 namespace {
 
+constexpr int kLogitWaves = 8;                    // token tiles of 16 per workgroup
+constexpr int kLogitThreads = kLogitWaves * kWave;
+constexpr int kLogitLds = 65536;                  // bytes of one staged W_r chunk
+
 template <int TPW, bool WF32>
-__global__ __launch_bounds__(256) void route_logits_bf16(
+__global__ __launch_bounds__(kLogitThreads) void route_logits_bf16(
     const uint16_t* __restrict__ x, const void* __restrict__ w_r_any,
     float* __restrict__ part, int T, int H, int E, int EP, int EG, int S, int KL) {
-  // [NP][KL][16 TPW] bf16: one plane, or the hi/mid/lo planes of an fp32 W_r
+  // [NP][KC][16 TPW] bf16: one plane, or the hi/mid/lo planes of an fp32 W_r
   extern __shared__ __attribute__((aligned(16))) char wb[];
   constexpr int NP = WF32 ? 3 : 1;
   constexpr int ROW = TPW * 16 * 2;                            // bytes per k row
-  const size_t plane = (size_t)KL * ROW;
+  // rows per staged chunk: whole groups of 8 steps where the budget allows
+  constexpr int RAW = kLogitLds / (NP * ROW);
+  constexpr int KC = RAW >= 256 ? RAW / 256 * 256 : RAW / 32 * 32;
+  constexpr int CST = KC / 32;                                 // K steps per chunk
+  constexpr int PF = CST < 8 ? CST : 8;                        // token steps in flight
+  static_assert(KC >= 32 && CST % PF == 0, "chunk of whole prefetch groups");
+  constexpr size_t plane = (size_t)KC * ROW;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int eg = blockIdx.x % EG;
@@ -62,88 +74,26 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
   const int tg = blockIdx.x / (EG * S);
   const int k_begin = s * KL;
   const int k_end = min(H, k_begin + KL);
+  const int nst = (k_end - k_begin + 31) / 32;
   const int e0 = eg * TPW * 16;
 
-  // stage W_r[k_begin:k_begin+KL, e0:e0+16 TPW]; rows past H and experts
-  // past E are zero.  Each thread moves 8-expert chunks, SB of them per
-  // batch with all the batch's loads issued before its LDS stores.
-  {
-    constexpr int CH = TPW * 2;                    // 8-expert chunks per row
-    constexpr int SB = WF32 ? 4 : 8;               // chunks per thread per batch
-    const bool vec = (E % 8) == 0;
-    const int total = KL * CH;
-    for (int q0 = threadIdx.x; q0 < total; q0 += SB * 256) {
-      if constexpr (!WF32) {
-        const uint16_t* w_r = (const uint16_t*)w_r_any;
-        u32x4 v[SB];
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const int q = q0 + u * 256;
-          const int r = q / CH, c = q % CH;
-          const int k = k_begin + r, e = e0 + c * 8;
-          v[u] = u32x4{0, 0, 0, 0};
-          if (q < total && k < k_end) {
-            if (vec) {
-              if (e < E) v[u] = *(const u32x4*)(w_r + (size_t)k * E + e);
-            } else {
-              uint16_t h[8];
-#pragma unroll
-              for (int t = 0; t < 8; ++t)
-                h[t] = (e + t < E) ? w_r[(size_t)k * E + e + t] : (uint16_t)0;
-              v[u] = u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
-                           h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
-            }
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const int q = q0 + u * 256;
-          if (q < total) *(u32x4*)(wb + (q / CH) * ROW + (q % CH) * 16) = v[u];
-        }
-      } else {
-        const float* w_r = (const float*)w_r_any;
-        float f[SB][8];
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const int q = q0 + u * 256;
-          const int r = q / CH, c = q % CH;
-          const int k = k_begin + r, e = e0 + c * 8;
-          if (q < total && k < k_end && vec && e < E) {
-            const float4 a = *(const float4*)(w_r + (size_t)k * E + e);
-            const float4 b = *(const float4*)(w_r + (size_t)k * E + e + 4);
-            f[u][0] = a.x; f[u][1] = a.y; f[u][2] = a.z; f[u][3] = a.w;
-            f[u][4] = b.x; f[u][5] = b.y; f[u][6] = b.z; f[u][7] = b.w;
-          } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-              f[u][t] = (q < total && k < k_end && e + t < E) ? w_r[(size_t)k * E + e + t] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-          const int q = q0 + u * 256;
-          if (q >= total) continue;
-          const int r = q / CH, c = q % CH;
-          uint32_t hi[8], mid[8], lo[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) split3(f[u][t], hi[t], mid[t], lo[t]);
-          *(u32x4*)(wb + r * ROW + c * 16) =
-              u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-          *(u32x4*)(wb + plane + r * ROW + c * 16) =
-              u32x4{mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16), mid[4] | (mid[5] << 16), mid[6] | (mid[7] << 16)};
-          *(u32x4*)(wb + 2 * plane + r * ROW + c * 16) =
-              u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  const int tt = tg * 4 + wave;
-  if (tt * 16 >= T) return;
-  const int tok = min(tt * 16 + (lane % 16), T - 1);
+  // Token operand: wave w's tile of 16 tokens, lane l reading token l % 16,
+  // k = 8 (l / 16) + 0..7 of each step, through a buffer descriptor that ends
+  // at the tile's last token (tokens past T, and a tile wholly past T, read
+  // zero; k past the split reads zero through the offset), so that no load
+  // sits behind a branch.
+  const int tt = tg * kLogitWaves + wave;
+  const bool active = tt * 16 < T;
+  const int ntok = active ? min(16, T - tt * 16) : 0;
+  const __amdgpu_buffer_rsrc_t xs =
+      make_rsrc(x + (size_t)min(tt * 16, T - 1) * H, (uint32_t)(ntok * H * 2));
   const int kl = (lane / 16) * 8;
-  const uint16_t* xr = x + (size_t)tok * H + kl;
+  const uint32_t xo = (uint32_t)(((lane % 16) * H + kl) * 2);
+  auto load_x = [&](int st) -> u32x4 {
+    const int k0 = k_begin + st * 32;
+    return __builtin_amdgcn_raw_buffer_load_b128(
+        xs, k0 + kl < k_end ? xo + 2u * (uint32_t)k0 : kPastEnd, 0, 0);
+  };
   // B operand: lane holds expert e0 + 16 j + lane%16 and k = 8 (lane/16) + 0..7
   // of the step, as two transposed reads of 4 rows each
   const int li = lane % 16;
@@ -152,41 +102,118 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
   f32x4 acc[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) acc[j] = f32x4{};
-
-  // token rows: PF K steps of loads in flight ahead of the MFMAs (each step's
-  // 16 bytes per lane would otherwise wait a full memory latency)
-  constexpr int PF = 8;
-  const int nst = (k_end - k_begin + 31) / 32;
-  auto load_x = [&](int st) -> u32x4 {
-    const int k0 = k_begin + st * 32;
-    return (st < nst && k0 + kl < k_end) ? *(const u32x4*)(xr + k0) : u32x4{0, 0, 0, 0};
-  };
   u32x4 abuf[PF];
 #pragma unroll
   for (int p = 0; p < PF; ++p) abuf[p] = load_x(p);
-  for (int s0 = 0; s0 < nst; s0 += PF) {
+
+  // The split's rows are staged and consumed chunk by chunk (KC rows, the
+  // LDS budget); every wave takes part in staging and barriers.  A chunk's
+  // steps run in whole prefetch groups: rows past the split are staged as
+  // zero and their token loads read zero, so the extra steps add nothing.
+  for (int c0 = 0; c0 < nst; c0 += CST) {
+    const int c1 = min(nst, c0 + CST);
+    const int rows = min(KC, (c1 - c0 + PF - 1) / PF * PF * 32);   // rows the steps read
+    const int kc = k_begin + c0 * 32;
+    if (c0 > 0) __syncthreads();                   // the previous chunk's reads are done
+    // stage W_r[kc : kc + rows, e0 : e0 + 16 TPW]; rows past the split and
+    // experts past E are zero.  Each thread moves 8-expert chunks, SB of them
+    // per batch with all the batch's loads issued before its LDS stores.
+    {
+      constexpr int CH = TPW * 2;                  // 8-expert chunks per row
+      constexpr int SB = WF32 ? 4 : 8;             // chunks per thread per batch
+      const bool vec = (E % 8) == 0;
+      const int total = rows * CH;
+      for (int q0 = threadIdx.x; q0 < total; q0 += SB * kLogitThreads) {
+        if constexpr (!WF32) {
+          const uint16_t* w_r = (const uint16_t*)w_r_any;
+          u32x4 v[SB];
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int st = s0 + p;
-      if (st < nst) {
-        const u32x4 a = abuf[p];
-        abuf[p] = load_x(st + PF);
-        const char* base = wb + st * 32 * ROW + rd_off;
+          for (int u = 0; u < SB; ++u) {
+            const int q = q0 + u * kLogitThreads;
+            const int r = q / CH, c = q % CH;
+            const int k = kc + r, e = e0 + c * 8;
+            v[u] = u32x4{0, 0, 0, 0};
+            if (q < total && k < k_end) {
+              if (vec) {
+                if (e < E) v[u] = *(const u32x4*)(w_r + (size_t)k * E + e);
+              } else {
+                uint16_t h[8];
 #pragma unroll
-        for (int pl = 0; pl < NP; ++pl) {
+                for (int t = 0; t < 8; ++t)
+                  h[t] = (e + t < E) ? w_r[(size_t)k * E + e + t] : (uint16_t)0;
+                v[u] = u32x4{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16),
+                             h[4] | ((uint32_t)h[5] << 16), h[6] | ((uint32_t)h[7] << 16)};
+              }
+            }
+          }
 #pragma unroll
-          for (int j = 0; j < TPW; ++j) {
-            const u32x2 lo = read_tr(base + pl * plane + j * 32);
-            const u32x2 hi = read_tr(base + pl * plane + 4 * ROW + j * 32);
-            const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                             __builtin_bit_cast(bf16x8, b),
-                                                             acc[j], 0, 0, 0);
+          for (int u = 0; u < SB; ++u) {
+            const int q = q0 + u * kLogitThreads;
+            if (q < total) *(u32x4*)(wb + (q / CH) * ROW + (q % CH) * 16) = v[u];
+          }
+        } else {
+          const float* w_r = (const float*)w_r_any;
+          float f[SB][8];
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            const int q = q0 + u * kLogitThreads;
+            const int r = q / CH, c = q % CH;
+            const int k = kc + r, e = e0 + c * 8;
+            if (q < total && k < k_end && vec && e < E) {
+              const float4 a = *(const float4*)(w_r + (size_t)k * E + e);
+              const float4 b = *(const float4*)(w_r + (size_t)k * E + e + 4);
+              f[u][0] = a.x; f[u][1] = a.y; f[u][2] = a.z; f[u][3] = a.w;
+              f[u][4] = b.x; f[u][5] = b.y; f[u][6] = b.z; f[u][7] = b.w;
+            } else {
+#pragma unroll
+              for (int t = 0; t < 8; ++t)
+                f[u][t] = (q < total && k < k_end && e + t < E) ? w_r[(size_t)k * E + e + t] : 0.f;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            const int q = q0 + u * kLogitThreads;
+            if (q >= total) continue;
+            const int r = q / CH, c = q % CH;
+            uint32_t hi[8], mid[8], lo[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) split3(f[u][t], hi[t], mid[t], lo[t]);
+            *(u32x4*)(wb + r * ROW + c * 16) =
+                u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+            *(u32x4*)(wb + plane + r * ROW + c * 16) =
+                u32x4{mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16), mid[4] | (mid[5] << 16), mid[6] | (mid[7] << 16)};
+            *(u32x4*)(wb + 2 * plane + r * ROW + c * 16) =
+                u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (active) {
+      for (int s0 = c0; s0 < c1; s0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+          const int st = s0 + p;
+          const u32x4 a = abuf[p];
+          abuf[p] = load_x(st + PF);
+          const char* base = wb + (st - c0) * 32 * ROW + rd_off;
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) {
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+              const u32x2 lo = read_tr(base + pl * plane + j * 32);
+              const u32x2 hi = read_tr(base + pl * plane + 4 * ROW + j * 32);
+              const u32x4 b = {lo[0], lo[1], hi[0], hi[1]};
+              acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                               __builtin_bit_cast(bf16x8, b),
+                                                               acc[j], 0, 0, 0);
+            }
           }
         }
       }
     }
   }
+  if (!active) return;
   // D: lane holds expert column lane%16 of tile j, token rows 4*(lane/16)+v
   const int NET = EP / 16;
 #pragma unroll
@@ -711,16 +738,18 @@ RoutePlan plan_route(int T, int H, int E, bool bf16, bool wf32) {
   while (tpw < 16 && tpw * 2 < NET) tpw *= 2;
   p.TPW = tpw;
   p.EG = (NET + tpw - 1) / tpw;
-  // about 2048 waves in all, and a staged W_r block of at most 64 KB
-  // (KL * 32 TPW bytes per bf16 plane; three planes for an fp32 W_r)
-  const int TT = (T + 15) / 16;
-  const long base_items = std::max<long>(1, (long)TT * p.EG);
-  int S = (int)std::min<long>(64, std::max<long>(1, (2048 + base_items - 1) / base_items));
+  // about 512 workgroups in all (each a group of 8 token tiles, one expert
+  // group and one split of H, which it stages through LDS in chunks): few
+  // splits for many tokens (the partial logits are S * T * EP floats written
+  // and read back), up to 64 for few
+  const int TG = (T + 16 * kLogitWaves - 1) / (16 * kLogitWaves);
+  const long items = std::max<long>(1, (long)TG * p.EG);
+  int S = (int)std::min<long>(64, std::max<long>(1, (512 + items - 1) / items));
   int KL = (H + S - 1) / S;
   KL = (KL + 31) / 32 * 32;
-  KL = std::min(KL, (wf32 ? 512 : 2048) / tpw);
   p.KL = KL;
   p.S = (H + KL - 1) / KL;
+  (void)wf32;
   return p;
 }
 
@@ -781,9 +810,9 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
   const RoutePlan p = plan_route(T, H, E, bf16, wf32);
   float* part = (float*)ws;
   if (bf16) {
-    const int TG = ((T + 15) / 16 + 3) / 4;
-    dim3 g((unsigned)(TG * p.EG * p.S)), b(256);
-    const size_t lds = (size_t)p.KL * p.TPW * 32 * (wf32 ? 3 : 1);
+    const int TG = (T + 16 * kLogitWaves - 1) / (16 * kLogitWaves);
+    dim3 g((unsigned)(TG * p.EG * p.S)), b(kLogitThreads);
+    const size_t lds = kLogitLds;
     const uint16_t* xb = (const uint16_t*)x;
 #define MOE_ROUTE_LOGITS(TPW_)                                                              \
     if (wf32)                                                                                \
