@@ -125,7 +125,19 @@ struct GemmArgs {
   uint16_t* zout;         // NN: also store the accumulators before GELU here ([R][N])
   const int* scatter;     // EP_SCATTER: row p goes to row scatter[p] of C ...
   const float* row_w;     // ... scaled by row_w[scatter[p]]
+  int wrow;               // wave layout (wave_mn)
 };
+
+// Which row half (wm) and column quarter (wn) of the tile wave w computes.
+// wrow 0: wm = w % WM, so the two waves of a SIMD (w and w + 4) share a row
+// half; wrow 1: wm = w / WN, so every SIMD holds one wave of each half and a
+// tile whose rows fit in the first half still keeps all four SIMDs' matrix
+// units busy (for launches whose tiles are mostly that short).
+template <int WM, int WN>
+__device__ __forceinline__ void wave_mn(int wave, int wrow, int& wm, int& wn) {
+  wm = wrow ? wave / WN : wave % WM;
+  wn = wrow ? wave % WN : wave / WM;
+}
 
 // LDS of one workgroup: one array per stage, so the compiler can tell that a
 // read of one stage does not wait on the loads into another.
@@ -155,14 +167,14 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
                                            uint16_t* __restrict__ C, const Tile& tile, int N,
                                            int ep, const uint16_t* __restrict__ aux,
                                            const int* __restrict__ scat,
-                                           const float* __restrict__ sw, char* stg,
+                                           const float* __restrict__ sw, char* stg, int wrow,
                                            int jbase = 0) {
   using S = GemmShape<BM, BN, WM, WN>;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wm = wave % WM;
-  const int wn = wave / WM;
+  int wm, wn;
+  wave_mn<WM, WN>(wave, wrow, wm, wn);
   const int n0 = tile.nt * BN;
   const int wrow0 = wm * S::TM;
   // Lane holds D[n][m] for m = lane%32 and 4 consecutive n.  Stored straight
@@ -384,8 +396,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wm = wave % WM;
-  const int wn = wave / WM;
+  int wm, wn;
+  wave_mn<WM, WN>(wave, g.wrow, wm, wn);
   const int n0 = tile.nt * BN;
   const int wrow0 = wm * S::TM;
   const int K = g.K, N = g.N;
@@ -735,9 +747,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
     // no barrier, the next item's loads land in the rings meanwhile
     if (g.zout)
       store_tile<BM, BN, WM, WN, 1, NFM, FMA, 1>(acc, g.zout, tile, N, EP_PLAIN, nullptr,
-                                                 nullptr, nullptr, lds.stg);
+                                                 nullptr, nullptr, lds.stg, g.wrow);
     store_tile<BM, BN, WM, WN, EPS, NFM, FMA, 1>(acc, g.C, tile, N, g.ep, g.aux, g.scatter,
-                                                 g.row_w, lds.stg);
+                                                 g.row_w, lds.stg, g.wrow);
     return;
   }
   // one barrier first, because other waves may still read the K loop's last
@@ -746,9 +758,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   if constexpr (KIND == kNN)
     if (g.zout)
       store_tile<BM, BN, WM, WN, 1, NFM>(acc, g.zout, tile, N, EP_PLAIN, nullptr, nullptr,
-                                         nullptr, lds.stg);
+                                         nullptr, lds.stg, g.wrow);
   store_tile<BM, BN, WM, WN, EPS, NFM>(acc, g.C, tile, N, g.ep, g.aux, g.scatter, g.row_w,
-                                       lds.stg);
+                                       lds.stg, g.wrow);
 }
 
 // gemm_tile with NFM = nfm (0 <= nfm <= NF), chosen at run time from a
@@ -844,7 +856,8 @@ __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __res
   if (!tile.valid) return;
 
   // 32-row token blocks of this wave that hold valid rows (wave-uniform)
-  const int wm = (threadIdx.x / kWave) % WM;
+  int wm, wn;
+  wave_mn<WM, WN>(threadIdx.x / kWave, g.wrow, wm, wn);
   int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
   nfm = __builtin_amdgcn_readfirstlane(nfm);
   run_tile<KIND, BM, BN, WM, WN, S::FM, false, WAUX>(nfm, g, tile, kt_begin, kt_end, sp, lds);
@@ -903,7 +916,8 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
       t.mi = 0;
     }
   };
-  const int wm = wave % WM;
+  int wm, wn;
+  wave_mn<WM, WN>(wave, g.wrow, wm, wn);
   Carry cy;
   cy.carry_in = false;
   Tile cur;
@@ -1159,7 +1173,7 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     }
     // (the weight gradients: written once, read by no kernel of this pass)
     store_tile<BM, BN, WM, WN, 1 << EP_PLAIN, FM, FM, 1, true>(
-        acc, cur.c, cur.tile, N, EP_PLAIN, nullptr, nullptr, nullptr, lds.stg);
+        acc, cur.c, cur.tile, N, EP_PLAIN, nullptr, nullptr, nullptr, lds.stg, 0);
     if (!has_next) break;
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -1192,7 +1206,8 @@ __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
   const Tile tile = lookup_tile(off, E, R, BM, NTN, pl.dp + slot);
   if (!tile.valid) return;
   const int tid = threadIdx.x;
-  const int wm = (tid / kWave) % WM;
+  int wm, wn;
+  wave_mn<WM, WN>(tid / kWave, g.wrow, wm, wn);
   const int nfm = max(0, min(S::FM, (tile.mrows - wm * S::TM + 31) / 32));
   if (__builtin_amdgcn_readfirstlane(nfm) <= jb) return;   // no valid rows in this block
   const float* all = part + (size_t)slot * pl.nsplit * S::PER_PIECE;
@@ -1229,10 +1244,10 @@ __global__ __launch_bounds__(kWave * WM * WN) void gemm_split_reduce(
   if constexpr (KIND == kNN)
     if (g.zout)
       store_tile<BM, BN, WM, WN, 1, 1>(acc, g.zout, tile, g.N, EP_PLAIN, nullptr, nullptr,
-                                       nullptr, stg, jb);
+                                       nullptr, stg, g.wrow, jb);
   store_tile<BM, BN, WM, WN, XEP ? XEP : kind_epilogues(KIND), 1>(acc, g.C, tile, g.N, g.ep,
                                                                   g.aux, g.scatter, g.row_w, stg,
-                                                                  jb);
+                                                                  g.wrow, jb);
 }
 
 int device_slots() {
@@ -1302,6 +1317,14 @@ hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* spl
 
 size_t split_ws_bytes() { return (size_t)kMaxSlots * 256 * 256 * sizeof(float); }
 
+namespace {
+// Wave layout of a launch (wave_mn): with at most 160 rows per expert on
+// average most tiles hold one row half or less, and spreading each half over
+// all four SIMDs doubles their matrix throughput; fuller tiles keep the
+// layout that measured best for them.
+int wave_layout(int R, int E) { return (long)R <= 160L * E ? 1 : 0; }
+}  // namespace
+
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
                             bool w_nk, void* C, const int* off, int E, int R, int K, int N,
                             int ep, const void* aux, void* zout, void* split_ws,
@@ -1320,6 +1343,7 @@ hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const 
   g.zout = (uint16_t*)zout;
   g.scatter = nullptr;
   g.row_w = nullptr;
+  g.wrow = wave_layout(R, E);
   if (ep == EP_SCATTER) return hipErrorInvalidValue;   // (launch_gemm_bf16_scatter)
   if (w_nk) return launch_cfg<kNT, 256, 256, kWM, kWN>(g, off, E, R, split_ws, s);
   return launch_cfg<kNN, 256, 256, kWM, kWN>(g, off, E, R, split_ws, s);
@@ -1342,6 +1366,7 @@ hipError_t launch_gemm_bf16_scatter(const void* A, const void* W, void* C, const
   g.zout = nullptr;
   g.scatter = scatter;
   g.row_w = row_w;
+  g.wrow = wave_layout(R, E);
   return launch_cfg<kNN, 256, 256, kWM, kWN, 1 << EP_SCATTER>(g, off, E, R, split_ws, s);
 }
 
