@@ -77,6 +77,11 @@ SMALL = {
                               dtype="bf16"),
     "route2_H7168_bf16": C("route2_H7168_bf16", T=1039, H=7168, E=64, k=8, F=64, dtype="bf16",
                            bias0=1.0),
+    # the two-kernel router with a split longer than one staged W_r chunk
+    # (16 splits of 384 rows: chunks of 256 + 128 rows; with an fp32 W_r,
+    # six chunks of 64)
+    "route2_chunks_bf16": C("route2_chunks_bf16", T=2100, H=6144, E=256, k=8, F=64,
+                            dtype="bf16"),
 }
 FULL = [n for n in mi.CONFIG_ORDER]
 # both expert GEMMs: 4 whole rounds + 96 tiles split in 2 (GEMM1, 1120 tiles),

@@ -37,6 +37,11 @@ SMALL = {
     "fused_E8_bf16": C("fused_E8_bf16", T=1031, H=4096, E=8, k=2, F=64, dtype="bf16"),
     "fused_E128_bf16": C("fused_E128_bf16", T=1027, H=2048, E=128, k=8, F=64, dtype="bf16",
                          bias0=0.5),
+    # the two-kernel router with a split longer than one staged W_r chunk
+    # (16 splits of 384 rows: chunks of 256 + 128 rows; with an fp32 W_r,
+    # six chunks of 64)
+    "route2_chunks_bf16": C("route2_chunks_bf16", T=2100, H=6144, E=256, k=8, F=64,
+                            dtype="bf16"),
 }
 BF16_SMALL = [n for n, c in SMALL.items() if c.dtype == "bf16"]
 _cache = {}
