@@ -745,11 +745,16 @@ RoutePlan plan_route(int T, int H, int E, bool bf16, bool wf32) {
   const int TG = (T + 16 * kLogitWaves - 1) / (16 * kLogitWaves);
   const long items = std::max<long>(1, (long)TG * p.EG);
   int S = (int)std::min<long>(64, std::max<long>(1, (512 + items - 1) / items));
+  // splits of whole prefetch groups of the logits kernel (8 steps, or its
+  // chunk when that is shorter), so that no split runs steps of zero rows
+  const int row = tpw * 32 * (wf32 ? 3 : 1);
+  const int raw = kLogitLds / row;
+  const int kc = raw >= 256 ? raw / 256 * 256 : raw / 32 * 32;
+  const int grp = std::min(kc, 256);
   int KL = (H + S - 1) / S;
-  KL = (KL + 31) / 32 * 32;
+  KL = (KL + grp - 1) / grp * grp;
   p.KL = KL;
   p.S = (H + KL - 1) / KL;
-  (void)wf32;
   return p;
 }
 
