@@ -6,6 +6,9 @@ tensor devices, dtypes and shapes, allocates outputs and the workspace with
 torch (device memory only), passes raw pointers and the current HIP stream,
 and raises on a non-OK status.  All computation happens in the HIP kernels.
 
+MoEFunction and MoELayer wrap moe_forward_train and moe_backward as a torch
+autograd operation and module (again only calls into the library).
+
 Importing this package fails if libmoe.so has not been built
 (python mixture_experts_layer_21_amd/build.py).  MOE_LIBRARY, if set, names
 another build of the same library to load instead (the tests use it for the
@@ -533,3 +536,56 @@ def moe_expert_ffn_backward(dyp, xp, expert_offsets, z, h, w1, w2, dxp=None, dw1
                                      _ptr(dw1), _ptr(dw2), _ptr(ws), ws.numel(), _stream(dev)),
         "moe_expert_ffn_backward")
     return dxp, dw1, dw2
+
+
+class MoEFunction(torch.autograd.Function):
+    """The layer as a differentiable torch operation: forward runs
+    moe_forward_train (keeping its state for the backward) and backward runs
+    moe_backward.  apply(x, w_r, router_bias, w1, w2, top_k, gating, capacity)
+    returns y; gradients reach x, w_r, router_bias (when given), w1 and w2.
+    The expert choice itself carries no gradient (the gate weights do)."""
+
+    @staticmethod
+    def forward(ctx, x, w_r, router_bias, w1, w2, top_k: int,
+                gating: int = MOE_GATE_TOPK_SOFTMAX, capacity: int = 0):
+        y, ids, w, saved = moe_forward_train(x, w_r, router_bias, w1, w2, top_k, gating,
+                                             capacity)
+        ctx.save_for_backward(x, w_r, w1, w2, ids, w, saved)
+        ctx.top_k, ctx.gating, ctx.has_bias = top_k, gating, router_bias is not None
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w_r, w1, w2, ids, w, saved = ctx.saved_tensors
+        g = moe_backward(dy.contiguous(), x, w_r, w1, w2, ctx.top_k, ids, w, saved,
+                         gating=ctx.gating, with_bias_grad=ctx.has_bias)
+        return g["dx"], g["dw_r"], g["db_r"], g["dw1"], g["dw2"], None, None, None
+
+
+class MoELayer(torch.nn.Module):
+    """A Mixture-of-Experts layer with this library's kernels, forward and
+    backward: y = sum over the top_k experts e of x of gate_e * GELU(x W1[e]) W2[e],
+    routed by x W_r (+ bias).  Parameters: w_r [H,E], w1 [E,H,F], w2 [E,F,H]
+    (dtype: torch.bfloat16 or torch.float32), bias [E] fp32 when bias=True;
+    initialised N(0, 1/fan_in).  forward(x) takes [..., H] on the GPU."""
+
+    def __init__(self, hidden: int, experts: int, ffn: int, top_k: int,
+                 dtype: torch.dtype = torch.bfloat16, bias: bool = False,
+                 gating: int = MOE_GATE_TOPK_SOFTMAX, capacity: int = 0, device="cuda"):
+        super().__init__()
+        self.top_k, self.gating, self.capacity = top_k, gating, capacity
+
+        def init(shape, fan_in):
+            return torch.nn.Parameter(
+                (torch.randn(shape, device=device) / fan_in ** 0.5).to(dtype))
+
+        self.w_r = init((hidden, experts), hidden)
+        self.w1 = init((experts, hidden, ffn), hidden)
+        self.w2 = init((experts, ffn, hidden), ffn)
+        self.bias = torch.nn.Parameter(torch.zeros(experts, device=device)) if bias else None
+
+    def forward(self, x):
+        shape = x.shape
+        y = MoEFunction.apply(x.reshape(-1, shape[-1]).contiguous(), self.w_r, self.bias,
+                              self.w1, self.w2, self.top_k, self.gating, self.capacity)
+        return y.reshape(shape)
