@@ -241,3 +241,35 @@ def test_backward_skips_out_of_range_ids(name, gating):
     assert_close_rel(f64(out["dx"]), dx_ref, tol, "dx")
     assert_close_rel(f64(out["dw_r"]), x64.T @ dl, tol, "dw_r")
     assert_close_rel(f64(out["db_r"]), dl.sum(axis=0), tol, "db_r")
+
+
+def random_cases(n=12, seed=77):
+    """Seeded random training shapes (both gatings, with and without a
+    capacity, bf16 and fp32), small enough for the oracle's dense backward."""
+    g = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(g.choice([1, 3, 8, 16, 40, 64, 130]))
+        k = int(min(E, g.choice([1, 2, 2, 4, 8])))
+        T = int(g.choice([1, 5, 48, 200, 600, 1100]))
+        H = int(8 * g.integers(1, 48))
+        F = int(8 * g.integers(1, 48))
+        dt = "f32" if g.random() < 0.25 else "bf16"
+        gating = GS if g.random() < 0.3 else GT
+        capf = float(g.choice([0.0, 0.0, 0.6, 1.2]))
+        cap = oracle.expert_capacity(T, k, E, capf) if capf else 0
+        cfg = C(f"rb{i}_T{T}_H{H}_E{E}_k{k}_F{F}_{dt}", T=T, H=H, E=E, k=k, F=F, dtype=dt,
+                bias0=float(g.choice([0.0, 1.0])), seed=300 + i)
+        out.append((cfg, gating, cap))
+    return out
+
+
+RANDOM = random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0].name for c in RANDOM])
+def test_backward_random_shape(case):
+    cfg, gating, cap = case
+    bias = cfg.bias0 != 0.0
+    L, w_r, y, ids, w, saved, out = run(cfg, gating=gating, capacity=cap, with_bias=bias)
+    check(cfg, L, w_r, ids, w, out, gating, cap, bias)
