@@ -130,6 +130,9 @@ moe_status moe_stage_workspace_bytes(moe_stage stage, int64_t T, int64_t H,
  *     logit order; equal logits go to the lower expert index.
  *   topk_w[T,top_k] fp32: softmax over the top_k selected logits, in the
  *     same slot order (so each row sums to 1).
+ *   A NaN logit ranks as -inf, so every token still gets top_k distinct
+ *     experts in [0, E); a token with any NaN logit gets NaN weights in all
+ *     its slots (so NaN inputs show in y instead of being dropped).
  *   ws/ws_bytes: device workspace (partial logits).
  */
 moe_status moe_route(const void* x, const void* w_r, const float* router_bias,

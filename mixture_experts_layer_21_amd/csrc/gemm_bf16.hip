@@ -280,8 +280,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[GemmShape<BM, BN,
 
 // K-contiguous operand loader: ROWS rows of 128 bytes (two K steps) per
 // stage, row r of the stage is memory row row_of(r) (-1: none, reads zero).
-// With MASK, 8-element chunks at or past k_limit read zero (for operands
-// whose K tail would otherwise read the next row's data).
+// A stage that starts at or past k_limit reads zero (an empty descriptor: a
+// scalar choice).  With MASK, 8-element chunks at or past k_limit read zero
+// in every stage, for a stage that can straddle k_limit (read unmasked, its
+// chunks past K would hold the next row's leading elements).
 template <int ROWS, int NW, bool MASK>
 struct RowLoader {
   static constexpr int INSTS = ROWS * 128 / 1024 / NW;   // 1 KB per instruction
@@ -312,7 +314,8 @@ struct RowLoader {
   template <int AUX = 0>
   __device__ __forceinline__ void load(int k0, char* st) const {
     const uint32_t skip = (uint32_t)k0 * 2;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0, bytes > skip ? bytes - skip : 0u);
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(base + k0, k0 < k_limit && bytes > skip ? bytes - skip : 0u);
     const int lane = lane_id();
 #pragma unroll
     for (int u = 0; u < INSTS; ++u) {
@@ -380,14 +383,18 @@ struct Carry {
 // Global loads use buffer descriptors whose base advances with k0 and whose
 // size ends at the last valid row of the tile (token rows) or at the piece's
 // K limit (k-major operands): rows past the tile and k rows past the piece's
-// K range read as zero, so no clamping appears in the loop.  In NN, past-K
-// columns of A read the next row of the tile (or x's next row when the rows
-// are gathered) but meet zero W rows; NT masks both operands' K tails.
+// K range read as zero, so no clamping appears in the loop.  No token row
+// may take in elements past its K range, not even against zero W rows: a
+// NaN or Inf in the next row times zero would reach this row's outputs.
+// Stages start at even K steps (pieces of split tiles start at even steps);
+// with K a multiple of 64 they never straddle the range's end and a stage
+// past it reads zero; otherwise (KM, and always in NT, which masks W's K
+// tail too) the token rows' K tail is masked in 8-element chunks.
 // WAUX: cache policy of the weight loads, NN and NT (kNonTemporal when no
 // other workgroup reads the same weight slab).  XEP != 0: the epilogues of
 // this instantiation (bit 1 << EP_x) in place of the arrangement's own.
 template <int KIND, int BM, int BN, int WM, int WN, int NFM, bool PERSIST = false, int WAUX = 0,
-          int XEP = 0>
+          int XEP = 0, bool KM = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, int kt_begin,
                                           int kt_end, const Split& sp, const Lds& lds,
                                           const Carry* cy = nullptr) {
@@ -406,7 +413,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   // --- loaders (offsets constant over the K loop) ----------------------------
   // m side: token rows (NN, NT), or P's k rows (TN)
   // n side: W's k rows (NN), W's rows n (NT), or Q's k rows (TN)
-  RowLoader<BM, S::NW, KIND == kNT> la;
+  RowLoader<BM, S::NW, KIND == kNT || KM> la;
   ColLoader<S::NW> lp;
   ColLoader<S::NW> lw;
   RowLoader<BN, S::NW, true> lb;
@@ -437,7 +444,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
   const int nsteps = kt_end - kt_begin;
   // persistent: the loaders of the next item (or, with none, this item's
   // loaders past its K range, which read zeros)
-  RowLoader<BM, S::NW, false> la_n;
+  RowLoader<BM, S::NW, KIND == kNT || KM> la_n;
   ColLoader<S::NW> lw_n;
   int k0n = 0;
   const int nsr = (nsteps + 3) / 4 * 4;
@@ -766,20 +773,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const Tile& tile, i
 // gemm_tile with NFM = nfm (0 <= nfm <= NF), chosen at run time from a
 // wave-uniform count.
 template <int KIND, int BM, int BN, int WM, int WN, int NF, bool PERSIST = false, int WAUX = 0,
-          int XEP = 0>
+          int XEP = 0, bool KM = false>
 __device__ __forceinline__ void run_tile(int nfm, const GemmArgs& g, const Tile& tile,
                                          int kt_begin, int kt_end, const Split& sp,
                                          const Lds& lds, const Carry* cy = nullptr) {
   if constexpr (NF == 0) {
-    gemm_tile<KIND, BM, BN, WM, WN, 0, PERSIST, WAUX, XEP>(g, tile, kt_begin, kt_end, sp, lds,
-                                                           cy);
+    gemm_tile<KIND, BM, BN, WM, WN, 0, PERSIST, WAUX, XEP, KM>(g, tile, kt_begin, kt_end, sp,
+                                                               lds, cy);
   } else {
     if (nfm == NF)
-      gemm_tile<KIND, BM, BN, WM, WN, NF, PERSIST, WAUX, XEP>(g, tile, kt_begin, kt_end, sp, lds,
-                                                              cy);
+      gemm_tile<KIND, BM, BN, WM, WN, NF, PERSIST, WAUX, XEP, KM>(g, tile, kt_begin, kt_end, sp,
+                                                                  lds, cy);
     else
-      run_tile<KIND, BM, BN, WM, WN, NF - 1, PERSIST, WAUX, XEP>(nfm, g, tile, kt_begin, kt_end,
-                                                                 sp, lds, cy);
+      run_tile<KIND, BM, BN, WM, WN, NF - 1, PERSIST, WAUX, XEP, KM>(nfm, g, tile, kt_begin,
+                                                                     kt_end, sp, lds, cy);
   }
 }
 
@@ -821,6 +828,13 @@ __device__ __forceinline__ void split_piece(const SplitPlan& pl, int p, int& L, 
   const int q = xcd_remap(p, pl.sk * pl.nsplit);
   L = pl.dp + q % pl.sk;
   s = q / pl.sk;
+}
+
+// K steps [kb, ke) of range s: near-equal ranges whose bounds are even (a
+// stage of two steps never straddles one), the last ending at KT.
+__device__ __forceinline__ void piece_steps(const SplitPlan& pl, int s, int& kb, int& ke) {
+  kb = (s * pl.KT / pl.nsplit) & ~1;
+  ke = s + 1 == pl.nsplit ? pl.KT : ((s + 1) * pl.KT / pl.nsplit) & ~1;
 }
 
 // this wave's 8 KB of epilogue staging inside two 32 KB regions
@@ -869,7 +883,7 @@ __device__ __forceinline__ void grouped_body(const GemmArgs& g, const int* __res
 // the pipeline from one item to the next (Carry); the epilogue stages
 // through its own 32 KB (128 KB of rings + 32 KB = 160 KB).  WAUX: the
 // weight loads' cache policy; XEP: as in gemm_tile.
-template <int BM, int BN, int WM, int WN, int WAUX = 0, int XEP = 0>
+template <int BM, int BN, int WM, int WN, int WAUX = 0, int XEP = 0, bool KM = false>
 __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4))) void gemm_bf16_grouped(
     GemmArgs g, const int* __restrict__ off, int E, int R, float* __restrict__ part,
     int slots) {
@@ -901,8 +915,7 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
       split_piece(pl, b, L, sp.s);
       sp.S = pl.nsplit;
       sp.slot = L - pl.dp;
-      kb = sp.s * pl.KT / pl.nsplit;
-      ke = (sp.s + 1) * pl.KT / pl.nsplit;
+      piece_steps(pl, sp.s, kb, ke);
     }
     t = lookup_tile(off, E, R, BM, NTN, L);
     if (!t.valid) {
@@ -938,7 +951,8 @@ __global__ __launch_bounds__(kWave * WM * WN) __attribute__((amdgpu_waves_per_eu
     // the tile keeps pace and finds the slab in L2 (not with non-temporal
     // weight loads, where slabs are not shared)
     cy.pace = WAUX == 0 && wm == 0 && cur.mi > 0 && csp.S == 1;
-    run_tile<kNN, BM, BN, WM, WN, S::FM, true, WAUX, XEP>(nfm, g, cur, ckb, cke, csp, lds, &cy);
+    run_tile<kNN, BM, BN, WM, WN, S::FM, true, WAUX, XEP, KM>(nfm, g, cur, ckb, cke, csp, lds,
+                                                              &cy);
     cy.carry_in = true;
     cur = cy.next;
     ckb = cy.next_kb;
@@ -1292,8 +1306,11 @@ hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* spl
     else
       hipLaunchKernelGGL((gemm_bf16_nt<BM, BN, WM, WN>), dim3((unsigned)blocks),
                          dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
-  } else if (stream_w)
-    // (persistent: one workgroup per CU)
+  } else if (g.K % 64 != 0)
+    // (persistent: one workgroup per CU; K tails masked, default cache policy)
+    hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN, 0, XEP, true>), dim3((unsigned)slots),
+                       dim3(kWave * WM * WN), 0, s, g, off, E, R, part, slots);
+  else if (stream_w)
     hipLaunchKernelGGL((gemm_bf16_grouped<BM, BN, WM, WN, kNonTemporal, XEP>),
                        dim3((unsigned)slots), dim3(kWave * WM * WN), 0, s, g, off, E, R, part,
                        slots);

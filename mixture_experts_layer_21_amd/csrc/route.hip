@@ -235,7 +235,9 @@ __device__ __forceinline__ void dpp_pair(float v, int e, float& ov, int& oe) {
   oe = __builtin_amdgcn_update_dpp(0, e, CTRL, 0xF, 0xF, false);
 }
 
-// keep the larger value, on equal values the lower expert
+// keep the larger value, on equal values the lower expert (the values are
+// never NaN: the selection ranks a NaN logit as -inf, so this is a total
+// order and every lane that exchanges ends with the same winner)
 __device__ __forceinline__ void take_better(float& bv, int& be, float ov, int oe) {
   if (ov > bv || (ov == bv && oe < be)) {
     bv = ov;
@@ -301,12 +303,15 @@ __global__ __launch_bounds__(256) void route_select(
 #pragma unroll
       for (int u = 0; u < SB; ++u) v[i] += q[i][u];
   }
+  bool nan_seen = false;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + i * kWave;
     if (e < E) {
       if (bias) v[i] += bias[e];
       if (logits) logits[(size_t)t * E + e] = v[i];
+      nan_seen |= __builtin_isnan(v[i]);
+      v[i] = __builtin_isnan(v[i]) ? -__builtin_inff() : v[i];   // ranks as -inf
     } else {
       v[i] = -__builtin_inff();
     }
@@ -351,11 +356,13 @@ __global__ __launch_bounds__(256) void route_select(
     for (int j = 0; j < 16; ++j)
       if (j < k) sum += expf(sel_v[j] - m);
   }
+  // a token with a NaN logit keeps its k distinct experts, with NaN weights
+  const bool tok_nan = __ballot(nan_seen) != 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (j < k && lane == j) {
       ids[(size_t)t * k + j] = sel_e[j];
-      w[(size_t)t * k + j] = expf(sel_v[j] - m) / sum;
+      w[(size_t)t * k + j] = tok_nan ? __builtin_nanf("") : expf(sel_v[j] - m) / sum;
     }
   }
 }
@@ -394,12 +401,15 @@ template <int NV>
 __device__ __forceinline__ void select_row(float (&v)[NV], int rl, int t, const float* bias,
                                            int E, int k, int softmax_all, int32_t* ids,
                                            float* w, float* logits) {
+  bool nan_seen = false;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = rl + i * 16;
     if (e < E) {
       if (bias) v[i] += bias[e];
       if (logits) logits[(size_t)t * E + e] = v[i];
+      nan_seen |= __builtin_isnan(v[i]);
+      v[i] = __builtin_isnan(v[i]) ? -__builtin_inff() : v[i];   // ranks as -inf
     } else {
       v[i] = -__builtin_inff();
     }
@@ -442,11 +452,14 @@ __device__ __forceinline__ void select_row(float (&v)[NV], int rl, int t, const 
     for (int j = 0; j < 16; ++j)
       if (j < k) sum += expf(sel_v[j] - m);
   }
+  // a token with a NaN logit keeps its k distinct experts, with NaN weights
+  // (the row's 16 bits of the wave's ballot; rows leave only whole)
+  const bool tok_nan = ((__ballot(nan_seen) >> (threadIdx.x & 48)) & 0xFFFFull) != 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     if (j < k && rl == j) {
       ids[(size_t)t * k + j] = sel_e[j];
-      w[(size_t)t * k + j] = expf(sel_v[j] - m) / sum;
+      w[(size_t)t * k + j] = tok_nan ? __builtin_nanf("") : expf(sel_v[j] - m) / sum;
     }
   }
 }
