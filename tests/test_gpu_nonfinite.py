@@ -70,3 +70,32 @@ def test_nan_tokens(name):
     ref = oracle.forward_tokens(xg, ids_np[good], oracle.gate_weights(logits, ids_np[good]),
                                 f64(L["w1"]), f64(L["w2"]))
     assert_close_rel(f64(y)[good], ref, TOL[cfg.dtype], f"{name} y")
+
+
+@pytest.mark.parametrize("name", ["top1_bf16", "ragged_bf16", "ktail32_bf16",
+                                  "top2_fused_router_bf16", "ragged_f32"])
+def test_nan_tokens_backward(name):
+    """The training step with NaN tokens in the batch: the other tokens' dx
+    and the weight gradients of the experts no NaN token reached (experts
+    k .. E-1) match the oracle's backward over the finite tokens alone."""
+    cfg = CASES[name]
+    L = gpu_layer(cfg)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    bad = sorted({0, 17 % T, T // 2, T - 1})
+    x = L["x"].clone()
+    x[bad, 3] = float("nan")
+    dy = mi.make_dy(cfg, "cuda")
+    print(f"[nonfinite] backward {name} NaN tokens {bad}", flush=True)
+    y, ids, w, saved = moe.moe_forward_train(x, L["w_r"], L["router_bias"], L["w1"], L["w2"], k)
+    out = moe.moe_backward(dy, x, L["w_r"], L["w1"], L["w2"], k, ids, w, saved)
+    torch.cuda.synchronize()
+    ids_np = ids.cpu().numpy().astype(np.int64)
+    good = np.setdiff1d(np.arange(T), bad)
+    dx = f64(out["dx"])
+    assert np.isnan(dx[bad]).all()
+    ref = oracle.backward(f64(x)[good], f64(L["w_r"]), f64(L["router_bias"]), f64(L["w1"]),
+                          f64(L["w2"]), k, f64(dy)[good], ids=ids_np[good])
+    tol = TOL[cfg.dtype]
+    assert_close_rel(dx[good], ref["dx"], tol, f"{name} dx")
+    assert_close_rel(f64(out["dw1"])[k:], ref["dw1"][k:], tol, f"{name} dW1 of experts >= k")
+    assert_close_rel(f64(out["dw2"])[k:], ref["dw2"][k:], tol, f"{name} dW2 of experts >= k")
