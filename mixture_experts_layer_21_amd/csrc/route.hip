@@ -3,16 +3,17 @@
 // kernel, so that the logits never make a round trip through HBM; the
 // routing article's scan fixes ties to the lower expert index).
 //
-// bf16 path, many tokens (T >= 1024, E <= 128 in multiples of 8, H <= 4096,
-// bf16 W_r)
+// bf16 path, E <= 128 in multiples of 8, H <= 4096, a bf16 W_r, and either
+// E <= 16 (any T) or T >= 1024
 //   route_fused       the whole router in one launch: one workgroup per tile
 //                     of 16 tokens, its 8 waves splitting H, W_r read in
 //                     whole rows into registers and transposed there,
 //                     partial logits summed in LDS, then top-k and softmax in
 //                     the same workgroup (see the kernel's comment).
 //
-// bf16 path, other shapes (few tokens, where 16-token tiles cannot fill the
-// GPU; more experts; an fp32 W_r)
+// bf16 path, other shapes (E = 24 .. 128 with few tokens, where the
+// one-launch form's workgroups, each reading all of W_r, are too few to
+// hide its latency; more experts; an fp32 W_r)
 //   route_logits_bf16 MFMA 16x16x32 bf16 with fp32 accumulation.  A workgroup
 //                     owns one expert group (TPW tiles of 16 experts) and one
 //                     split of the H axis (KL rows) for 8 token tiles of 16,
@@ -778,8 +779,12 @@ size_t route_ws_bytes(int T, int H, int E, bool bf16) {
   return align_up((size_t)std::max(a.S, b.S) * T * a.EP * sizeof(float));
 }
 
+// (E <= 16: one launch at any T; measured against the two kernels at
+// T = 1 .. 512, it saves 1-3 us.  E = 24 .. 128 at T = 64: 16.6 -> 24.5 us,
+// so those keep the two kernels below kFuseMinT tokens.)
 bool route_is_fused(int T, int H, int E, bool bf16, bool wf32) {
-  return bf16 && !wf32 && T >= kFuseMinT && E % 8 == 0 && E <= kFuseMaxE && H <= kFuseMaxH;
+  return bf16 && !wf32 && (E <= 16 || T >= kFuseMinT) && E % 8 == 0 && E <= kFuseMaxE &&
+         H <= kFuseMaxH;
 }
 
 hipError_t launch_route(const void* x, const void* w_r, const float* bias,

@@ -52,7 +52,14 @@ SMALL = {
     # few tiles with a long K: the expert GEMM splits tiles along K (partials
     # summed by the last piece), checked here on every element
     "ksplit_bf16": C("ksplit_bf16", T=300, H=4096, E=2, k=1, F=512, dtype="bf16"),
-    # the one-launch router (T >= 1024, E <= 128 in multiples of 8, H <= 4096):
+    # the one-launch router for E <= 16 at few tokens (8-token tiles, the last
+    # one partly or, at T = 1, mostly empty)
+    "fused_T1_E8_bf16": C("fused_T1_E8_bf16", T=1, H=4096, E=8, k=2, F=64, dtype="bf16"),
+    "fused_T37_E16_bf16": C("fused_T37_E16_bf16", T=37, H=1000, E=16, k=3, F=64,
+                            dtype="bf16", bias0=0.5),
+    "fused_T200_E8_bf16": C("fused_T200_E8_bf16", T=200, H=448, E=8, k=1, F=64, dtype="bf16"),
+    # the one-launch router (E <= 128 in multiples of 8, H <= 4096; E > 16 at
+    # T >= 1024 only):
     # each of the 8 waves takes NS = 1, 2, 4, 8, 16 steps of 32 rows of H
     # (H = 40 .. 4096: waves with partly and wholly empty ranges), in both
     # kernels (E <= 16, and E = 24 .. 128 read in whole rows), a last token
