@@ -26,6 +26,8 @@ CASES = {
     "ragged_bf16": C("g_ragged_bf16", T=75, H=200, E=5, k=2, F=136, dtype="bf16"),
     # one-launch router, top-1 (the combine inside the second GEMM)
     "top1_bf16": C("g_top1_bf16", T=1025, H=448, E=8, k=1, F=64, dtype="bf16"),
+    # one token (decode): the one-launch router's single, mostly empty tile
+    "decode_bf16": C("g_decode_bf16", T=1, H=4096, E=8, k=2, F=512, dtype="bf16"),
     # few tiles with a long K: split tiles and their reduce launch
     "ksplit_bf16": C("g_ksplit_bf16", T=300, H=4096, E=2, k=2, F=512, dtype="bf16"),
     "many_bf16": C("g_many_bf16", T=1100, H=128, E=40, k=6, F=64, dtype="bf16"),
@@ -106,7 +108,8 @@ def test_forward_graph_replays(name, entry):
         assert torch.equal(y, y_ref), f"replay {i}: y"
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "ksplit_bf16", "many_bf16", "ragged_f32"])
+@pytest.mark.parametrize("name", ["ragged_bf16", "decode_bf16", "ksplit_bf16", "many_bf16",
+                                  "ragged_f32"])
 def test_training_step_graph_replays(name):
     cfg = CASES[name]
     L = gpu_layer(cfg)
