@@ -24,9 +24,17 @@ size_t route_ws_bytes(int T, int H, int E, bool bf16);
 // softmax_all: gate weights are the top-k probabilities of the softmax over
 // all E logits (not renormalised); otherwise the softmax of the k winners.
 // logits != nullptr: the fp32 logits [T,E] (bias included) are kept there.
+// doff != nullptr (only where route_dispatches): the router's one workgroup
+// also does the dropless dispatch of the pairs (expert offsets doff[E+1],
+// sorted_token, inv_pos), as launch_permute with xp == nullptr would.
 hipError_t launch_route(const void* x, const void* w_r, const float* bias, int T, int H,
                         int E, int k, bool bf16, bool wf32, bool softmax_all, int32_t* ids,
-                        float* w, float* logits, void* ws, hipStream_t s);
+                        float* w, float* logits, void* ws, hipStream_t s,
+                        int32_t* doff = nullptr, int32_t* dsorted = nullptr,
+                        int32_t* dinv = nullptr);
+// One-launch routing of a decode-sized batch (E <= 16, T <= 8 tokens, bf16)
+// that can take the dispatch along (see launch_route).
+bool route_dispatches(int T, int H, int E, bool bf16, bool wf32);
 
 size_t permute_ws_bytes(int R, int E);
 // xp == nullptr: indices only (the rows are gathered later by the GEMM).

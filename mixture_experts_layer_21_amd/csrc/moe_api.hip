@@ -434,17 +434,23 @@ moe_status forward_body(const void* x, const void* w_r, const float* router_bias
   const bool bf16 = dtype == MOE_BF16;
   const int64_t R = T * top_k;
 
+  // a decode-sized bf16 batch: the router's one workgroup also dispatches
+  const bool rd = bf16 && capacity <= 0 &&
+                  moe::route_dispatches((int)T, (int)H, (int)E, bf16, router_dtype != dtype);
   hipError_t err = moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k, bf16,
                                      router_dtype != dtype, gating == MOE_GATE_SOFTMAX_TOPK,
-                                     ids, w, nullptr, stage, s);
+                                     ids, w, nullptr, stage, s, rd ? off : nullptr,
+                                     rd ? sorted : nullptr, rd ? inv : nullptr);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
   // bf16: the first expert GEMM gathers the token rows from x itself, so the
   // dispatch only builds the indices; fp32 copies the rows into xp.  With a
   // capacity fewer than R rows are kept; the GEMMs take their row counts from
   // the offsets, so R only bounds the grid.
-  err = moe::launch_permute(x, ids, (int)T, (int)H, (int)E, top_k, capacity, elem_bytes(dtype),
-                            off, sorted, inv, bf16 ? nullptr : xp, stage, s);
-  if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  if (!rd) {
+    err = moe::launch_permute(x, ids, (int)T, (int)H, (int)E, top_k, capacity,
+                              elem_bytes(dtype), off, sorted, inv, bf16 ? nullptr : xp, stage, s);
+    if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  }
   void* split_ws = split ? ffn_split(stage, R, F, dtype) : nullptr;
   if (bf16 && top_k == 1 && capacity <= 0) {
     // Top-1 and dropless: every token owns exactly one dispatched row, so
@@ -562,13 +568,18 @@ moe_status moe_forward_train(const void* x, const void* w_r, const float* router
   const bool bf16 = dtype == MOE_BF16;
   const int64_t R = T * top_k;
 
+  const bool rd = bf16 && capacity <= 0 &&
+                  moe::route_dispatches((int)T, (int)H, (int)E, bf16, router_dtype != dtype);
   hipError_t err = moe::launch_route(x, w_r, router_bias, (int)T, (int)H, (int)E, top_k, bf16,
                                      router_dtype != dtype, gating == MOE_GATE_SOFTMAX_TOPK,
-                                     topk_ids, topk_w, logits, stage, s);
+                                     topk_ids, topk_w, logits, stage, s, rd ? off : nullptr,
+                                     rd ? sorted : nullptr, rd ? inv : nullptr);
   if (err != hipSuccess) return MOE_ERR_LAUNCH;
-  err = moe::launch_permute(x, topk_ids, (int)T, (int)H, (int)E, top_k, capacity,
-                            elem_bytes(dtype), off, sorted, inv, bf16 ? nullptr : xp, stage, s);
-  if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  if (!rd) {
+    err = moe::launch_permute(x, topk_ids, (int)T, (int)H, (int)E, top_k, capacity,
+                              elem_bytes(dtype), off, sorted, inv, bf16 ? nullptr : xp, stage, s);
+    if (err != hipSuccess) return MOE_ERR_LAUNCH;
+  }
   void* h = sv + V.h;
   void* z = sv + V.z;
   void* yp = sv + V.yp;

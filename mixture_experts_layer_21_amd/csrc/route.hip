@@ -401,7 +401,7 @@ __device__ __forceinline__ float row_sum(float v) {
 template <int NV>
 __device__ __forceinline__ void select_row(float (&v)[NV], int rl, int t, const float* bias,
                                            int E, int k, int softmax_all, int32_t* ids,
-                                           float* w, float* logits) {
+                                           float* w, float* logits, int* sid = nullptr) {
   bool nan_seen = false;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -460,6 +460,7 @@ __device__ __forceinline__ void select_row(float (&v)[NV], int rl, int t, const 
   for (int j = 0; j < 16; ++j) {
     if (j < k && rl == j) {
       ids[(size_t)t * k + j] = sel_e[j];
+      if (sid) sid[t * k + j] = sel_e[j];
       w[(size_t)t * k + j] = tok_nan ? __builtin_nanf("") : expf(sel_v[j] - m) / sum;
     }
   }
@@ -563,7 +564,8 @@ template <int EPMAX, int TOK = 16>
 __device__ __forceinline__ void fused_select(const float (&part)[kFuseWaves][16][EPMAX],
                                              int wave, int lane, int t0, int T,
                                              const float* bias, int E, int k, int softmax_all,
-                                             int32_t* ids, float* w, float* logits) {
+                                             int32_t* ids, float* w, float* logits,
+                                             int* sid = nullptr) {
   if (wave >= TOK / 4) return;
   const int tt = wave * 4 + lane / 16;
   const int t = t0 + tt;
@@ -581,7 +583,7 @@ __device__ __forceinline__ void fused_select(const float (&part)[kFuseWaves][16]
     }
     v[i] = sum;
   }
-  select_row<NV>(v, c, t, bias, E, k, softmax_all, ids, w, logits);
+  select_row<NV>(v, c, t, bias, E, k, softmax_all, ids, w, logits, sid);
 }
 
 // E <= 16 (one expert tile): W_r is small, the token operand is the stream.
@@ -595,12 +597,20 @@ __device__ __forceinline__ void fused_select(const float (&part)[kFuseWaves][16]
 // the lanes of tokens 8-15 load nothing, the MFMA rows 8-15 stay zero and
 // the workgroup streams half as much x: used when 16-token tiles would leave
 // CUs without a workgroup).
+//
+// With doff != nullptr (one workgroup: T <= TOK) the kernel also does the
+// dropless dispatch of its T k pairs (what perm_onepass computes, for a
+// decode-sized batch, without a second launch): expert offsets doff[E+1],
+// sorted_token and inv_pos, in the stable (token, slot) order.
 template <int NS, int TOK = 16>
 __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_r,
     const float* __restrict__ bias, int32_t* __restrict__ ids, float* __restrict__ w,
-    float* __restrict__ logits, int T, int H, int E, int k, int softmax_all) {
+    float* __restrict__ logits, int T, int H, int E, int k, int softmax_all,
+    int32_t* __restrict__ doff, int32_t* __restrict__ dsorted, int32_t* __restrict__ dinv) {
   __shared__ __attribute__((aligned(16))) float part[kFuseWaves][16][16];
+  __shared__ int sid[16 * 16];                   // the tile's ids (dispatch only)
+  __shared__ int scnt[17];                       // pairs per expert, then offsets
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t0 = blockIdx.x * TOK;
@@ -644,7 +654,40 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
 #pragma unroll
   for (int v = 0; v < 4; ++v) part[wave][4 * (lane / 16) + v][lane % 16] = acc[v];
   __syncthreads();
-  fused_select<16, TOK>(part, wave, lane, t0, T, bias, E, k, softmax_all, ids, w, logits);
+  fused_select<16, TOK>(part, wave, lane, t0, T, bias, E, k, softmax_all, ids, w, logits,
+                        doff ? sid : nullptr);
+  if (doff == nullptr) return;
+  // dispatch of pairs i = t k + j (t0 = 0): expert e_i's count before i
+  // gives the pair's rank among its expert's pairs
+  __syncthreads();
+  const int R = T * k, i = threadIdx.x;
+  int ei = 0, rank = 0;
+  if (i < R) {
+    ei = sid[i];
+    for (int q = 0; q < i; ++q) rank += sid[q] == ei ? 1 : 0;
+  }
+  if (i < E) {
+    int c = 0;
+    for (int q = 0; q < R; ++q) c += sid[q] == i ? 1 : 0;
+    scnt[i] = c;
+  }
+  __syncthreads();
+  if (i == 0) {
+    int o = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = scnt[e];
+      scnt[e] = o;
+      doff[e] = o;
+      o += c;
+    }
+    doff[E] = o;
+  }
+  __syncthreads();
+  if (i < R) {
+    const int p = scnt[ei] + rank;
+    dsorted[p] = i / k;
+    dinv[i] = p;
+  }
 }
 
 template <int NS, int D>
@@ -787,9 +830,15 @@ bool route_is_fused(int T, int H, int E, bool bf16, bool wf32) {
          H <= kFuseMaxH;
 }
 
+bool route_dispatches(int T, int H, int E, bool bf16, bool wf32) {
+  return route_is_fused(T, H, E, bf16, wf32) && E <= 16 && T >= 1 && T <= 8;
+}
+
 hipError_t launch_route(const void* x, const void* w_r, const float* bias,
                         int T, int H, int E, int k, bool bf16, bool wf32, bool softmax_all,
-                        int32_t* ids, float* w, float* logits, void* ws, hipStream_t s) {
+                        int32_t* ids, float* w, float* logits, void* ws, hipStream_t s,
+                        int32_t* doff, int32_t* dsorted, int32_t* dinv) {
+  if (doff != nullptr && !route_dispatches(T, H, E, bf16, wf32)) return hipErrorInvalidValue;
   if (route_is_fused(T, H, E, bf16, wf32)) {
     // one launch: NS steps of 32 rows per wave cover H (8 waves), loads D
     // steps ahead
@@ -808,10 +857,10 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
     do {                                                                                       \
       if (tok8)                                                                                \
         hipLaunchKernelGGL((route_fused_small<NS_, 8>), g8, b, 0, s, xb, wb, bias, ids, w,       \
-                           logits, T, H, E, k, sa);                                            \
+                           logits, T, H, E, k, sa, doff, dsorted, dinv);                       \
       else                                                                                     \
         hipLaunchKernelGGL((route_fused_small<NS_>), g, b, 0, s, xb, wb, bias, ids, w, logits,   \
-                           T, H, E, k, sa);                                                    \
+                           T, H, E, k, sa, nullptr, nullptr, nullptr);                         \
     } while (0)
     if (E <= 16) {
       if (ns <= 1) MOE_ROUTE_FUSED_SMALL(1);
