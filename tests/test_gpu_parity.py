@@ -64,6 +64,8 @@ SMALL = {
                                 dtype="bf16"),
     "route_dispatch_T8_kE_bf16": C("route_dispatch_T8_kE_bf16", T=8, H=512, E=8, k=8, F=64,
                                    dtype="bf16"),
+    "route_dispatch_top1_T3_bf16": C("route_dispatch_top1_T3_bf16", T=3, H=128, E=8, k=1,
+                                     F=64, dtype="bf16"),
     # the one-launch router (E <= 128 in multiples of 8, H <= 4096; E > 16 at
     # T >= 1024 only):
     # each of the 8 waves takes NS = 1, 2, 4, 8, 16 steps of 32 rows of H
@@ -273,7 +275,7 @@ def test_dispatch_full(name):
 # and one whole round of 256 tiles followed by split leftover tiles.
 TOP1 = {
     **{n: SMALL[n] for n in ("top1_bf16", "one_expert_bf16", "ksplit_bf16",
-                             "fused_E8_H448_bf16")},
+                             "fused_E8_H448_bf16", "route_dispatch_top1_T3_bf16")},
     "top1_split_bf16": C("top1_split_bf16", T=2100, H=512, E=4, k=1, F=4096, dtype="bf16"),
     "top1_rounds_bf16": C("top1_rounds_bf16", T=4096, H=4096, E=16, k=1, F=2048,
                           dtype="bf16"),
