@@ -32,7 +32,7 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias, int T
                         float* w, float* logits, void* ws, hipStream_t s,
                         int32_t* doff = nullptr, int32_t* dsorted = nullptr,
                         int32_t* dinv = nullptr);
-// One-launch routing of a decode-sized batch (E <= 16, T <= 8 tokens, bf16)
+// One-launch routing of a decode-sized batch (E <= 16, T <= 16 tokens, bf16)
 // that can take the dispatch along (see launch_route).
 bool route_dispatches(int T, int H, int E, bool bf16, bool wf32);
 

@@ -831,7 +831,7 @@ bool route_is_fused(int T, int H, int E, bool bf16, bool wf32) {
 }
 
 bool route_dispatches(int T, int H, int E, bool bf16, bool wf32) {
-  return route_is_fused(T, H, E, bf16, wf32) && E <= 16 && T >= 1 && T <= 8;
+  return route_is_fused(T, H, E, bf16, wf32) && E <= 16 && T >= 1 && T <= 16;
 }
 
 hipError_t launch_route(const void* x, const void* w_r, const float* bias,
@@ -851,7 +851,8 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
 #define MOE_ROUTE_FUSED(NS_, D_)                                                            \
     hipLaunchKernelGGL((route_fused<NS_, D_>), g, b, 0, s, xb, wb, bias, ids, w, logits, T, H, \
                        E, k, sa)
-    const bool tok8 = (T + 15) / 16 < 256;
+    // (dispatching: one workgroup, 8-token tiles up to 8 tokens, else 16)
+    const bool tok8 = (T + 15) / 16 < 256 && !(doff != nullptr && T > 8);
     const dim3 g8((unsigned)((T + 7) / 8));
 #define MOE_ROUTE_FUSED_SMALL(NS_)                                                             \
     do {                                                                                       \
@@ -860,7 +861,7 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
                            logits, T, H, E, k, sa, doff, dsorted, dinv);                       \
       else                                                                                     \
         hipLaunchKernelGGL((route_fused_small<NS_>), g, b, 0, s, xb, wb, bias, ids, w, logits,   \
-                           T, H, E, k, sa, nullptr, nullptr, nullptr);                         \
+                           T, H, E, k, sa, doff, dsorted, dinv);                               \
     } while (0)
     if (E <= 16) {
       if (ns <= 1) MOE_ROUTE_FUSED_SMALL(1);

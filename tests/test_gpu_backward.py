@@ -37,6 +37,7 @@ CASES = {
     "one_token_bf16": C("one_token_bf16", T=1, H=128, E=8, k=2, F=256, dtype="bf16"),
     # the router's one workgroup dispatching a decode-sized batch (saved indices)
     "decode_T7_bf16": C("decode_T7_bf16", T=7, H=256, E=16, k=3, F=128, dtype="bf16"),
+    "decode_T12_bf16": C("decode_T12_bf16", T=12, H=512, E=8, k=2, F=128, dtype="bf16"),
     "many_small_bf16": C("many_small_bf16", T=128, H=128, E=128, k=8, F=64, dtype="bf16"),
     "skewed_small_bf16": C("skewed_small_bf16", T=256, H=128, E=8, k=2, F=256, dtype="bf16",
                            bias0=3.0),

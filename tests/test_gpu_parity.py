@@ -58,14 +58,19 @@ SMALL = {
     "fused_T37_E16_bf16": C("fused_T37_E16_bf16", T=37, H=1000, E=16, k=3, F=64,
                             dtype="bf16", bias0=0.5),
     "fused_T200_E8_bf16": C("fused_T200_E8_bf16", T=200, H=448, E=8, k=1, F=64, dtype="bf16"),
-    # up to 8 tokens with E <= 16: the router's one workgroup also does the
-    # dispatch (no separate dispatch launch in moe_forward)
+    # up to 16 tokens with E <= 16: the router's one workgroup (8-token tile
+    # up to 8 tokens, else 16) also does the dispatch (no separate dispatch
+    # launch in moe_forward)
     "route_dispatch_T5_bf16": C("route_dispatch_T5_bf16", T=5, H=256, E=16, k=4, F=64,
                                 dtype="bf16"),
     "route_dispatch_T8_kE_bf16": C("route_dispatch_T8_kE_bf16", T=8, H=512, E=8, k=8, F=64,
                                    dtype="bf16"),
     "route_dispatch_top1_T3_bf16": C("route_dispatch_top1_T3_bf16", T=3, H=128, E=8, k=1,
                                      F=64, dtype="bf16"),
+    "route_dispatch_T13_bf16": C("route_dispatch_T13_bf16", T=13, H=1000, E=16, k=5, F=64,
+                                 dtype="bf16"),
+    "route_dispatch_T16_kE_bf16": C("route_dispatch_T16_kE_bf16", T=16, H=4096, E=8, k=8,
+                                    F=64, dtype="bf16"),
     # the one-launch router (E <= 128 in multiples of 8, H <= 4096; E > 16 at
     # T >= 1024 only):
     # each of the 8 waves takes NS = 1, 2, 4, 8, 16 steps of 32 rows of H
