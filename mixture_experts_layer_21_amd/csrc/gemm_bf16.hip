@@ -1282,9 +1282,86 @@ int device_slots() {
   return cached[dev];
 }
 
+constexpr int kMaxExperts = 1024;   // (the ABI's limit on E)
+
+// The second expert GEMM's split sums and the combine in one launch, for a
+// decode-sized batch (a few dispatched rows; the GEMM launch then skips its
+// split reduce).  Workgroup (t, column tile) forms 256 columns of y[t] from
+// the token's k rows: a row of a whole tile is read from yp as the GEMM
+// stored it; a row of a split tile is the sum of its pieces' fp32 partials
+// in split order, rounded to bf16 as the reduce would store it.  The k rows
+// are then weighted and summed in slot order as the combine does, so y is
+// bit for bit that of the separate reduce and combine passes.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256) void reduce_combine_rows(
+    const uint16_t* __restrict__ yp, const float* __restrict__ part,
+    const int* __restrict__ off, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ inv, const float* __restrict__ w, uint16_t* __restrict__ y,
+    int T, int k, int E, int R, int K, int N, int slots, int wrow) {
+  static_assert(BN == 256, "one column per thread");
+  using S = GemmShape<BM, BN, WM, WN>;
+  __shared__ int pre[kMaxExperts];           // row tiles of the experts before e
+  const int t = blockIdx.x, nt = blockIdx.y, tid = threadIdx.x;
+  const int NTN = (N + BN - 1) / BN;
+  const SplitPlan pl = split_plan<BM, BN>(off, E, R, K, N, slots, part != nullptr);
+  if (tid < kWave) {
+    int carry = 0;
+    for (int c = 0; c < E; c += kWave) {
+      const int e = c + tid;
+      int mt = 0;
+      if (e < E) {
+        int lo, cnt;
+        expert_rows(off, e, R, lo, cnt);
+        mt = (cnt + BM - 1) / BM;
+      }
+      const int incl = wave_incl_scan(mt);
+      if (e < E) pre[e] = carry + incl - mt;
+      carry += wave_bcast(incl, kWave - 1);
+    }
+  }
+  __syncthreads();
+  const int nl = tid, n = nt * BN + nl;
+  if (n >= N) return;
+  // place of column nl in a piece's partials (the accumulator order the
+  // pieces store): column block, 8-column group, half-lane and element
+  const int wn = nl / S::TN, nn = nl % S::TN;
+  const int ci = nn / 32, r32 = nn % 32;
+  const int gq = r32 / 8, hl = (r32 % 8) / 4, e4 = r32 % 4;
+  float acc = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int p = inv[t * k + j];
+    const bool in = (unsigned)p < (unsigned)(T * k);
+    float v = 0.f, wj = 0.f;
+    if (in) {
+      wj = w[t * k + j];
+      const int e = ids[t * k + j];
+      int lo, cnt;
+      expert_rows(off, e, R, lo, cnt);
+      const int mt = (cnt + BM - 1) / BM;
+      const int rr = p - lo, mi = rr / BM, m = rr % BM;
+      const int L = pre[e] * NTN + nt * mt + mi;
+      if (L < pl.dp || pl.nsplit < 2) {
+        v = bf16_to_f32(yp[(size_t)p * N + n]);
+      } else {
+        const int wm = m / S::TM, jj = (m % S::TM) / 32;
+        const int wave = wrow ? wm * WN + wn : wn * WM + wm;
+        const int lane = hl * 32 + m % 32;
+        const size_t o =
+            (size_t)((ci * S::FM + jj) * 16 + 4 * gq) * S::NT + (wave * kWave + lane) * 4 + e4;
+        const float* base = part + (size_t)(L - pl.dp) * pl.nsplit * S::PER_PIECE + o;
+        float run = base[0];
+        for (int sp = 1; sp < pl.nsplit; ++sp) run += base[(size_t)sp * S::PER_PIECE];
+        v = bf16_to_f32(f32_to_bf16(run));
+      }
+    }
+    acc = __builtin_fmaf(wj, v, acc);
+  }
+  y[(size_t)t * N + n] = (uint16_t)f32_to_bf16(acc);
+}
+
 template <int KIND, int BM, int BN, int WM, int WN, int XEP = 0>
 hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* split_ws,
-                      hipStream_t s) {
+                      hipStream_t s, bool reduce = true) {
   static_assert(XEP == 0 || KIND == kNN, "own epilogues: the forward's products only");
   const int NTN = (g.N + BN - 1) / BN;
   // upper bound of row tiles: sum_e ceil(rows_e / BM) <= ceil(R / BM) + min(E, R)
@@ -1321,7 +1398,7 @@ hipError_t launch_cfg(const GemmArgs& g, const int* off, int E, int R, void* spl
   if (err != hipSuccess) return err;
   // tiles are split only when K has at least 4 * MIN_SPLIT_STEPS steps, and
   // only with a split workspace
-  if (part != nullptr && (g.K + BK - 1) / BK >= 4 * MIN_SPLIT_STEPS) {
+  if (reduce && part != nullptr && (g.K + BK - 1) / BK >= 4 * MIN_SPLIT_STEPS) {
     hipLaunchKernelGGL((gemm_split_reduce<KIND, BM, BN, WM, WN, XEP>),
                        dim3(kMaxSlots / 2 * GemmShape<BM, BN, WM, WN>::FM),
                        dim3(kWave * WM * WN), 0, s, g, off, E, R, (const float*)part, slots);
@@ -1345,7 +1422,7 @@ int wave_layout(int R, int E) { return (long)R <= 160L * E ? 1 : 0; }
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
                             bool w_nk, void* C, const int* off, int E, int R, int K, int N,
                             int ep, const void* aux, void* zout, void* split_ws,
-                            hipStream_t s) {
+                            hipStream_t s, bool defer_reduce) {
   GemmArgs g;
   g.A = (const uint16_t*)A;
   g.gather = gather;
@@ -1363,7 +1440,20 @@ hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const 
   g.wrow = wave_layout(R, E);
   if (ep == EP_SCATTER) return hipErrorInvalidValue;   // (launch_gemm_bf16_scatter)
   if (w_nk) return launch_cfg<kNT, 256, 256, kWM, kWN>(g, off, E, R, split_ws, s);
-  return launch_cfg<kNN, 256, 256, kWM, kWN>(g, off, E, R, split_ws, s);
+  return launch_cfg<kNN, 256, 256, kWM, kWN>(g, off, E, R, split_ws, s, !defer_reduce);
+}
+
+hipError_t launch_reduce_combine(const void* yp, void* split_ws, const int* off,
+                                 const int32_t* ids, const int32_t* inv_pos, const float* w,
+                                 void* y, int T, int k, int E, int R, int K, int N,
+                                 hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (E > kMaxExperts) return hipErrorInvalidValue;
+  const dim3 g((unsigned)T, (unsigned)((N + 255) / 256)), b(256);
+  hipLaunchKernelGGL((reduce_combine_rows<256, 256, kWM, kWN>), g, b, 0, s, (const uint16_t*)yp,
+                     (const float*)split_ws, off, ids, inv_pos, w, (uint16_t*)y, T, k, E, R, K,
+                     N, device_slots(), wave_layout(R, E));
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16_scatter(const void* A, const void* W, void* C, const int* off,

@@ -62,10 +62,22 @@ enum Epilogue { EP_PLAIN = 0, EP_GELU = 1, EP_DGELU = 2, EP_SCATTER = 3 };
 // zout != nullptr: the accumulators are also stored there before the
 // epilogue (the pre-activation a training forward keeps).  split_ws ==
 // nullptr: no tile is split along K (the leftover tiles run whole).
+// defer_reduce: the split tiles' partials stay in split_ws for
+// launch_reduce_combine (no split reduce launch, their rows of C unwritten).
 hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const void* W,
                             bool w_nk, void* C, const int* off, int E, int R, int K, int N,
                             int ep, const void* aux, void* zout, void* split_ws,
-                            hipStream_t s);
+                            hipStream_t s, bool defer_reduce = false);
+// After launch_gemm_bf16(..., defer_reduce = true) of the second expert GEMM
+// (EP_PLAIN, C = yp [R][N], the same off, E, R, K, N and split_ws): the
+// combine y[t] = sum_j w[t,j] yp[inv_pos[t,j]] in slot order, each row of a
+// split tile summed from its partials and rounded to bf16 first, as the
+// split reduce and launch_combine would give (bf16; one workgroup per token
+// and 256 columns: for decode-sized batches).
+hipError_t launch_reduce_combine(const void* yp, void* split_ws, const int* off,
+                                 const int32_t* ids, const int32_t* inv_pos, const float* w,
+                                 void* y, int T, int k, int E, int R, int K, int N,
+                                 hipStream_t s);
 // The second expert GEMM with the combine of a top-1 layer in its epilogue:
 // product row p (A's row p, expert e's W[K][N]) is rounded to bf16, scaled by
 // row_w[scatter[p]] in fp32 (an fma with a zero addend) and rounded again into

@@ -414,6 +414,10 @@ FwdLayout fwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_
 }
 
 
+// Token counts up to which the forward adds the second GEMM's split tiles and
+// combines in one launch (launch_reduce_combine).
+constexpr int64_t kFusedCombineMaxT = 16;
+
 // The forward's launches into a workspace of layout L (validated by the
 // caller); split: the GEMMs may split leftover tiles (L has their region).
 moe_status forward_body(const void* x, const void* w_r, const float* router_bias,
@@ -463,6 +467,22 @@ moe_status forward_body(const void* x, const void* w_r, const float* router_bias
     if (e2 == hipSuccess)
       e2 = moe::launch_gemm_bf16_scatter(stage, w2, y, off, (int)E, (int)R, (int)F, (int)H,
                                          sorted, w, split_ws, s);
+    return launch_status(e2);
+  }
+  if (bf16 && split_ws != nullptr && T <= kFusedCombineMaxT) {
+    // A decode-sized batch: the second GEMM leaves its split tiles' partials
+    // and one launch adds them up and combines (no separate reduce and
+    // combine launches; y is bit for bit theirs)
+    hipError_t e2 = moe::launch_gemm_bf16(x, sorted, (int)T, w1, false, stage, off, (int)E,
+                                          (int)R, (int)H, (int)F, moe::EP_GELU, nullptr,
+                                          nullptr, split_ws, s);
+    if (e2 == hipSuccess)
+      e2 = moe::launch_gemm_bf16(stage, nullptr, (int)R, w2, false, yp, off, (int)E, (int)R,
+                                 (int)F, (int)H, moe::EP_PLAIN, nullptr, nullptr, split_ws, s,
+                                 true);
+    if (e2 == hipSuccess)
+      e2 = moe::launch_reduce_combine(yp, split_ws, off, ids, inv, w, y, (int)T, top_k, (int)E,
+                                      (int)R, (int)F, (int)H, s);
     return launch_status(e2);
   }
   const moe_status fs =

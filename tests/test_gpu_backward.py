@@ -122,7 +122,10 @@ def test_backward_variants_match_oracle(name, gating, cap_factor, wf32):
         assert np.all(out["dw"].cpu().numpy()[inv < 0] == 0.0)
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "longH_bf16", "top1_bf16"])
+# (one_token and decode_T12: moe_forward sums the split tiles inside its
+# combine launch, moe_forward_train runs the split reduce and the combine)
+@pytest.mark.parametrize("name", ["ragged_bf16", "tiny_fp32", "longH_bf16", "top1_bf16",
+                                  "one_token_bf16", "decode_T12_bf16"])
 def test_forward_train_equals_forward(name):
     """The training forward's y, ids and w are the plain forward's, bit for bit
     (top1_bf16: the plain forward combines inside its second expert GEMM, the
