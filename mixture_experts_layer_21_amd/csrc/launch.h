@@ -73,7 +73,7 @@ hipError_t launch_gemm_bf16(const void* A, const int* gather, int a_rows, const 
 // combine y[t] = sum_j w[t,j] yp[inv_pos[t,j]] in slot order, each row of a
 // split tile summed from its partials and rounded to bf16 first, as the
 // split reduce and launch_combine would give (bf16; one workgroup per token
-// and 256 columns: for decode-sized batches).
+// and 256 columns: for decode-sized batches of up to 128 rows).
 hipError_t launch_reduce_combine(const void* yp, void* split_ws, const int* off,
                                  const int32_t* ids, const int32_t* inv_pos, const float* w,
                                  void* y, int T, int k, int E, int R, int K, int N,

@@ -414,9 +414,12 @@ FwdLayout fwd_layout(int64_t T, int64_t H, int64_t E, int32_t k, int64_t F, moe_
 }
 
 
-// Token counts up to which the forward adds the second GEMM's split tiles and
-// combines in one launch (launch_reduce_combine).
-constexpr int64_t kFusedCombineMaxT = 16;
+// Dispatched rows (T * top_k) up to which the forward adds the second GEMM's
+// split tiles and combines in one launch (launch_reduce_combine).  Against
+// the split reduce and the combine pass it saved 2-3% at 1-16 tokens of
+// top-2 and 1-2% at 32-64 (up to 128 rows), and lost 2-3% at 256 and
+// 2048 tokens and at 512 rows of 64 tokens x 8 slots.
+constexpr int64_t kFusedCombineMaxRows = 128;
 
 // The forward's launches into a workspace of layout L (validated by the
 // caller); split: the GEMMs may split leftover tiles (L has their region).
@@ -469,7 +472,7 @@ moe_status forward_body(const void* x, const void* w_r, const float* router_bias
                                          sorted, w, split_ws, s);
     return launch_status(e2);
   }
-  if (bf16 && split_ws != nullptr && T <= kFusedCombineMaxT) {
+  if (bf16 && split_ws != nullptr && R <= kFusedCombineMaxRows) {
     // A decode-sized batch: the second GEMM leaves its split tiles' partials
     // and one launch adds them up and combines (no separate reduce and
     // combine launches; y is bit for bit theirs)
