@@ -32,8 +32,9 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias, int T
                         float* w, float* logits, void* ws, hipStream_t s,
                         int32_t* doff = nullptr, int32_t* dsorted = nullptr,
                         int32_t* dinv = nullptr);
-// One-launch routing of a decode-sized batch (E <= 16, T <= 16 tokens, bf16)
-// that can take the dispatch along (see launch_route).
+// A bf16 routing of a few tokens (16 with E <= 16 on the one-launch router,
+// else 4), whose selection kernel (one workgroup) can take the dispatch
+// along (see launch_route).
 bool route_dispatches(int T, int H, int E, bool bf16, bool wf32);
 
 size_t permute_ws_bytes(int R, int E);

@@ -273,14 +273,16 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& be) {
   be = re;
 }
 
+// Token t's selection by one wave (see route_select); sid != nullptr: the
+// ids also go to LDS, sid[t k + j].
 template <int NPL>
-__global__ __launch_bounds__(256) void route_select(
-    const float* __restrict__ part, const float* __restrict__ bias,
-    int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int EP,
-    int S, int k, int softmax_all, float* __restrict__ logits) {
+__device__ __forceinline__ void select_token(const float* __restrict__ part,
+                                             const float* __restrict__ bias,
+                                             int32_t* __restrict__ ids, float* __restrict__ w,
+                                             int T, int E, int EP, int S, int k,
+                                             int softmax_all, float* __restrict__ logits, int t,
+                                             int* sid) {
   const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-  if (t >= T) return;
 
   // sum the S partial logits in split order; all loads of a batch of SB
   // splits (for every expert of the lane, 64 values) are issued before any
@@ -363,9 +365,79 @@ __global__ __launch_bounds__(256) void route_select(
   for (int j = 0; j < 16; ++j) {
     if (j < k && lane == j) {
       ids[(size_t)t * k + j] = sel_e[j];
+      if (sid) sid[t * k + j] = sel_e[j];
       w[(size_t)t * k + j] = tok_nan ? __builtin_nanf("") : expf(sel_v[j] - m) / sum;
     }
   }
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void route_select(
+    const float* __restrict__ part, const float* __restrict__ bias,
+    int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int EP,
+    int S, int k, int softmax_all, float* __restrict__ logits) {
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  select_token<NPL>(part, bias, ids, w, T, E, EP, S, k, softmax_all, logits, t, nullptr);
+}
+
+// The dropless dispatch of the T k pairs whose ids one workgroup holds in
+// LDS (sid, pair i = t k + j): what perm_onepass computes, for a batch of a
+// few tokens, without a launch of its own.  Expert e's pair count, a
+// one-wave exclusive scan of the counts into doff[0..E] (scnt: LDS, E ints,
+// then the offsets), and for each pair its rank among its expert's pairs in
+// (token, slot) order: sorted_token[doff[e] + rank] = t, inv_pos[i] = that
+// row.
+__device__ void wg_dispatch(const int* sid, int T, int k, int E, int* scnt,
+                            int32_t* __restrict__ doff, int32_t* __restrict__ dsorted,
+                            int32_t* __restrict__ dinv) {
+  __syncthreads();
+  const int R = T * k, nth = blockDim.x, i0 = threadIdx.x;
+  for (int e = i0; e < E; e += nth) {
+    int c = 0;
+    for (int q = 0; q < R; ++q) c += sid[q] == e ? 1 : 0;
+    scnt[e] = c;
+  }
+  __syncthreads();
+  if (i0 < kWave) {
+    int carry = 0;
+    for (int c0 = 0; c0 < E; c0 += kWave) {
+      const int e = c0 + i0;
+      const int v = e < E ? scnt[e] : 0;
+      const int incl = wave_incl_scan(v);
+      if (e < E) {
+        scnt[e] = carry + incl - v;
+        doff[e] = carry + incl - v;
+      }
+      carry += wave_bcast(incl, kWave - 1);
+    }
+    if (i0 == 0) doff[E] = carry;
+  }
+  __syncthreads();
+  for (int q = i0; q < R; q += nth) {
+    const int e = sid[q];
+    int rank = 0;
+    for (int q2 = 0; q2 < q; ++q2) rank += sid[q2] == e ? 1 : 0;
+    const int p = scnt[e] + rank;
+    dsorted[p] = q / k;
+    dinv[q] = p;
+  }
+}
+
+// route_select for a batch of at most 16 tokens (one workgroup, a wave per
+// token) that also does the dispatch (wg_dispatch).
+template <int NPL>
+__global__ __launch_bounds__(1024) void route_select_dispatch(
+    const float* __restrict__ part, const float* __restrict__ bias,
+    int32_t* __restrict__ ids, float* __restrict__ w, int T, int E, int EP,
+    int S, int k, int softmax_all, float* __restrict__ logits, int32_t* __restrict__ doff,
+    int32_t* __restrict__ dsorted, int32_t* __restrict__ dinv) {
+  __shared__ int sid[16 * 16];
+  __shared__ int scnt[1024];
+  const int t = threadIdx.x / kWave;
+  if (t < T)
+    select_token<NPL>(part, bias, ids, w, T, E, EP, S, k, softmax_all, logits, t, sid);
+  wg_dispatch(sid, T, k, E, scnt, doff, dsorted, dinv);
 }
 
 // Arg-max over the 16 lanes of each row (the first four exchanges of
@@ -610,7 +682,7 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
     int32_t* __restrict__ doff, int32_t* __restrict__ dsorted, int32_t* __restrict__ dinv) {
   __shared__ __attribute__((aligned(16))) float part[kFuseWaves][16][16];
   __shared__ int sid[16 * 16];                   // the tile's ids (dispatch only)
-  __shared__ int scnt[17];                       // pairs per expert, then offsets
+  __shared__ int scnt[16];                       // pairs per expert, then offsets
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int t0 = blockIdx.x * TOK;
@@ -657,37 +729,7 @@ __global__ __launch_bounds__(kWave * kFuseWaves) void route_fused_small(
   fused_select<16, TOK>(part, wave, lane, t0, T, bias, E, k, softmax_all, ids, w, logits,
                         doff ? sid : nullptr);
   if (doff == nullptr) return;
-  // dispatch of pairs i = t k + j (t0 = 0): expert e_i's count before i
-  // gives the pair's rank among its expert's pairs
-  __syncthreads();
-  const int R = T * k, i = threadIdx.x;
-  int ei = 0, rank = 0;
-  if (i < R) {
-    ei = sid[i];
-    for (int q = 0; q < i; ++q) rank += sid[q] == ei ? 1 : 0;
-  }
-  if (i < E) {
-    int c = 0;
-    for (int q = 0; q < R; ++q) c += sid[q] == i ? 1 : 0;
-    scnt[i] = c;
-  }
-  __syncthreads();
-  if (i == 0) {
-    int o = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = scnt[e];
-      scnt[e] = o;
-      doff[e] = o;
-      o += c;
-    }
-    doff[E] = o;
-  }
-  __syncthreads();
-  if (i < R) {
-    const int p = scnt[ei] + rank;
-    dsorted[p] = i / k;
-    dinv[i] = p;
-  }
+  wg_dispatch(sid, T, k, E, scnt, doff, dsorted, dinv);   // (t0 = 0: the one workgroup)
 }
 
 template <int NS, int D>
@@ -775,9 +817,13 @@ constexpr int kRowSelectMinT = 1024;
 template <int NPL>
 void launch_select(const float* part, const float* bias, int32_t* ids, float* w,
                    int T, int E, int EP, int S, int k, int softmax_all, float* logits,
-                   hipStream_t s) {
-  hipLaunchKernelGGL((route_select<NPL>), dim3((T + 3) / 4), dim3(256), 0, s,
-                     part, bias, ids, w, T, E, EP, S, k, softmax_all, logits);
+                   hipStream_t s, int32_t* doff, int32_t* dsorted, int32_t* dinv) {
+  if (doff != nullptr)   // (T <= 4: one workgroup, a wave per token)
+    hipLaunchKernelGGL((route_select_dispatch<NPL>), dim3(1), dim3(kWave * T), 0, s, part, bias,
+                       ids, w, T, E, EP, S, k, softmax_all, logits, doff, dsorted, dinv);
+  else
+    hipLaunchKernelGGL((route_select<NPL>), dim3((T + 3) / 4), dim3(256), 0, s,
+                       part, bias, ids, w, T, E, EP, S, k, softmax_all, logits);
 }
 
 }  // namespace
@@ -830,8 +876,14 @@ bool route_is_fused(int T, int H, int E, bool bf16, bool wf32) {
          H <= kFuseMaxH;
 }
 
+// (route_fused_small up to 16 tokens, or route_select_dispatch after the
+// logits kernel up to 4: one workgroup of a wave per token; at 16 tokens
+// that one workgroup was slower than four of route_select plus the
+// dispatch launch: 256 experts, k = 8 0.857 -> 0.863 ms per forward;
+// 64 experts, k = 6 0.173 -> 0.176 ms; at one token it gained 0.6-3%)
 bool route_dispatches(int T, int H, int E, bool bf16, bool wf32) {
-  return route_is_fused(T, H, E, bf16, wf32) && E <= 16 && T >= 1 && T <= 16;
+  if (!bf16 || T < 1) return false;
+  return route_is_fused(T, H, E, bf16, wf32) ? T <= 16 : T <= 4;
 }
 
 hipError_t launch_route(const void* x, const void* w_r, const float* bias,
@@ -912,7 +964,7 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
   const int sa = softmax_all ? 1 : 0;
   // many tokens, E <= 256: one token per row of 16 lanes (enough waves at
   // T / 4 to fill the GPU); otherwise one token per wave
-  if (T >= kRowSelectMinT && E <= 256) {
+  if (doff == nullptr && T >= kRowSelectMinT && E <= 256) {
     const int nv = (E + 15) / 16;
     const dim3 g((unsigned)((T + 15) / 16)), b(256);
 #define MOE_SELECT_ROWS(NV_)                                                                        hipLaunchKernelGGL((route_select_rows<NV_>), g, b, 0, s, part, bias, ids, w, T, E, p.EP, p.S,                        k, sa, logits)
@@ -925,11 +977,16 @@ hipError_t launch_route(const void* x, const void* w_r, const float* bias,
     return hipGetLastError();
   }
   const int npl = (E + kWave - 1) / kWave;
-  if (npl <= 1) launch_select<1>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
-  else if (npl <= 2) launch_select<2>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
-  else if (npl <= 4) launch_select<4>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
-  else if (npl <= 8) launch_select<8>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
-  else launch_select<16>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s);
+  if (npl <= 1) launch_select<1>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s, doff,
+                                    dsorted, dinv);
+  else if (npl <= 2) launch_select<2>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s, doff,
+                                    dsorted, dinv);
+  else if (npl <= 4) launch_select<4>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s, doff,
+                                    dsorted, dinv);
+  else if (npl <= 8) launch_select<8>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s, doff,
+                                    dsorted, dinv);
+  else launch_select<16>(part, bias, ids, w, T, E, p.EP, p.S, k, sa, logits, s, doff, dsorted,
+                          dinv);
   return hipGetLastError();
 }
 

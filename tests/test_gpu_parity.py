@@ -71,6 +71,14 @@ SMALL = {
                                  dtype="bf16"),
     "route_dispatch_T16_kE_bf16": C("route_dispatch_T16_kE_bf16", T=16, H=4096, E=8, k=8,
                                     F=64, dtype="bf16"),
+    # more experts (or H > 4096) at up to 4 tokens: the two-kernel router's
+    # selection launch (one workgroup) does the dispatch
+    "select_dispatch_E256_bf16": C("select_dispatch_E256_bf16", T=4, H=512, E=256, k=8,
+                                   F=64, dtype="bf16", bias0=1.0),
+    "select_dispatch_E1000_bf16": C("select_dispatch_E1000_bf16", T=3, H=64, E=1000, k=16,
+                                    F=32, dtype="bf16"),
+    "select_dispatch_H8192_bf16": C("select_dispatch_H8192_bf16", T=4, H=8192, E=8, k=2,
+                                    F=64, dtype="bf16"),
     # the one-launch router (E <= 128 in multiples of 8, H <= 4096; E > 16 at
     # T >= 1024 only):
     # each of the 8 waves takes NS = 1, 2, 4, 8, 16 steps of 32 rows of H
